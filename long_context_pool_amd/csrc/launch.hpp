@@ -1,0 +1,43 @@
+// Host-side launchers of the MISA kernels (internal; the public ABI is misa.h).
+// Each returns the hipError_t of its launch(es).  Arguments were validated by
+// the caller (api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace misa {
+
+struct Shape {
+  int32_t batch, L, T, H, d, B, dtype;
+  int64_t M() const { return (static_cast<int64_t>(L) + B - 1) / B; }
+};
+
+hipError_t launch_pool(const Shape& s, int32_t block_begin, int32_t block_count, const void* k,
+                       const float* k_scale, float* pooled, hipStream_t st);
+
+// Router: E and top-h heads.  ws must hold route_ws_bytes(s).
+size_t route_ws_bytes(const Shape& s);
+hipError_t launch_route(const Shape& s, int32_t h, const void* q, const float* q_scale,
+                        const float* w, const float* pooled, const void* k, const float* k_scale,
+                        int32_t* heads, float* E_out, void* ws, hipStream_t st);
+
+// Token scoring + top-k over each query's causal prefix.  heads == nullptr
+// scores with all H heads (dense DSA); otherwise with the nh listed heads.
+size_t score_ws_bytes(const Shape& s, int32_t nh, int32_t k);
+hipError_t launch_score_topk(const Shape& s, int32_t nh, const int32_t* heads, int32_t k,
+                             const void* q, const float* q_scale, const float* w, const void* kk,
+                             const float* k_scale, int32_t* idx, float* scores_out, void* ws,
+                             hipStream_t st);
+
+// MISA-dagger fine stage.
+size_t rerank_ws_bytes(const Shape& s, int32_t kprime);
+hipError_t launch_rerank(const Shape& s, int32_t kprime, int32_t k, const void* q,
+                         const float* q_scale, const float* w, const void* kk, const float* k_scale,
+                         const int32_t* cand, int32_t* idx, float* scores_out, void* ws,
+                         hipStream_t st);
+
+inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+}  // namespace misa

@@ -1,0 +1,103 @@
+"""Host-only checks of the C-ABI library: it loads, exports every entry point
+that include/misa.h declares, and rejects bad arguments before launching
+anything (these calls never reach the GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "misa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:misa|dsa)_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("misa_pool_keys", "misa_route", "misa_score_topk", "misa_rerank", "dsa_index_dense",
+              "misa_workspace_bytes", "misa_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import long_context_pool_amd as misa
+
+    lib = ctypes.CDLL(misa.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert set(misa.EXPORTED) == set(_declared())
+
+
+def test_status_strings():
+    import long_context_pool_amd as misa
+
+    assert misa.status_string(0) == "MISA_OK"
+    assert misa.status_string(-3) == "MISA_ERR_WORKSPACE"
+
+
+def test_workspace_bytes_zero_on_bad_shape():
+    import long_context_pool_amd as misa
+
+    assert misa.misa_workspace_bytes(misa.shape(1, 10, 20, 64, 128, 4, 1), 8, 4, 4) == 0  # T > L
+    assert misa.misa_workspace_bytes(misa.shape(1, 100, 10, 64, 128, 4, 1), 8, 4, 4) > 0
+
+
+FAKE = 1 << 20  # an aligned non-null address; never dereferenced (calls fail validation)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("T>L", -1), ("d!=128", -2), ("h>H", -1), ("h>16", -2), ("k=0", -1), ("k>8192", -2),
+    ("misaligned", -1), ("null q", -1), ("ws too small", -3), ("bad dtype", -1),
+])
+def test_argument_checks(case, expect):
+    import long_context_pool_amd as misa
+
+    lib = misa.lib()
+    shp = misa.shape(1, 1024, 16, 64, 128, 64, misa.MISA_BF16)
+    h, k, q, ws_bytes = 8, 32, FAKE, 1 << 40
+    if case == "T>L":
+        shp = misa.shape(1, 8, 16, 64, 128, 64, misa.MISA_BF16)
+    elif case == "d!=128":
+        shp = misa.shape(1, 1024, 16, 64, 64, 64, misa.MISA_BF16)
+    elif case == "h>H":
+        shp = misa.shape(1, 1024, 16, 8, 128, 64, misa.MISA_BF16)
+        h = 9
+    elif case == "h>16":
+        h = 17
+    elif case == "k=0":
+        k = 0
+    elif case == "k>8192":
+        k = 8193
+    elif case == "misaligned":
+        q = FAKE + 4
+    elif case == "null q":
+        q = None
+    elif case == "ws too small":
+        ws_bytes = 16
+    elif case == "bad dtype":
+        shp = misa.shape(1, 1024, 16, 64, 128, 64, 7)
+    st = lib.misa_score_topk(ctypes.byref(shp), h, k, q, None, FAKE, FAKE, None, FAKE, FAKE, None,
+                             FAKE, ws_bytes, None)
+    assert st == expect
+
+
+def test_fp8_requires_scales_and_rerank_requires_kprime_ge_k():
+    import long_context_pool_amd as misa
+
+    lib = misa.lib()
+    shp = misa.shape(1, 1024, 16, 64, 128, 64, misa.MISA_FP8_E4M3)
+    st = lib.dsa_index_dense(ctypes.byref(shp), 32, FAKE, None, FAKE, FAKE, None, FAKE, None, FAKE,
+                             1 << 40, None)
+    assert st == misa.MISA_ERR_INVALID_ARG
+    shp = misa.shape(1, 1024, 16, 64, 128, 64, misa.MISA_BF16)
+    st = lib.misa_rerank(ctypes.byref(shp), 16, 32, FAKE, None, FAKE, FAKE, None, FAKE, FAKE, None,
+                         FAKE, 1 << 40, None)
+    assert st == misa.MISA_ERR_INVALID_ARG
+    st = lib.misa_pool_keys_range(ctypes.byref(shp), 10, 7, FAKE, None, FAKE, None)  # 17 > M=16
+    assert st == misa.MISA_ERR_INVALID_ARG
