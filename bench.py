@@ -1,0 +1,311 @@
+"""Benchmark of the MISA indexer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+
+A step is one pass of the hot path over one batch of synthetic input:
+  decode (T = 1): refresh the pooled key of the block holding the newest token
+                  (the pooled-key cache update) -> route -> routed score + top-k
+                  [-> rerank when the workload has k'];
+  prefill:        pool all keys -> route -> routed score + top-k [-> rerank].
+The dense DSA indexer (all heads, same library) is timed the same way for the
+MISA-vs-DSA speedup.  Inputs are resident in HBM before timing starts; several
+input sets are rotated so that the decode workloads stream their keys from
+HBM instead of the 256 MB last-level cache.
+
+Prints one JSON line (metric/value = scored (query, token) pairs per second).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "scored (query,token) pairs/s + MISA-vs-dense-DSA speedup, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "long_context_pool_amd", "csrc")
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", help="c1..c5 (default c2, the decode workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU work budget of the oracle baseline")
+    return ap.parse_args()
+
+
+class Runner:
+    """Device buffers of several input sets and the per-step call sequence."""
+
+    def __init__(self, x, n_sets, stream):
+        import torch
+
+        import long_context_pool_amd as misa
+        import synth
+
+        self.misa = misa
+        self.p = p = x.problem
+        self.stream = stream
+        dev = torch.device("cuda:0")
+        fp8 = p.dtype == synth.FP8_E4M3
+        self.shp = misa.shape(p.batch, p.L, p.T, p.H, p.d, p.B, p.dtype)
+        kp = p.kprime or p.k
+        self.ws = torch.empty(misa.misa_workspace_bytes(self.shp, p.h, p.k, kp), dtype=torch.uint8,
+                              device=dev)
+        self.sets = []
+        with torch.cuda.stream(stream):
+            for i in range(n_sets):
+                s = {
+                    "q": x.q.to(dev), "k": x.k.to(dev), "w": x.w.to(dev),
+                    "qs": x.q_scale.to(dev) if fp8 else None,
+                    "ks": x.k_scale.to(dev) if fp8 else None,
+                    "pooled": torch.empty((p.batch, p.M, p.d), dtype=torch.float32, device=dev),
+                }
+                misa.misa_pool_keys(self.shp, s["k"], s["ks"], s["pooled"], stream)
+                self.sets.append(s)
+            self.heads = torch.empty((p.batch, p.T, p.h), dtype=torch.int32, device=dev)
+            self.cand = torch.empty((p.batch, p.T, kp), dtype=torch.int32, device=dev)
+            self.idx = torch.empty((p.batch, p.T, p.k), dtype=torch.int32, device=dev)
+            self.didx = torch.empty((p.batch, p.T, p.k), dtype=torch.int32, device=dev)
+        self.decode = p.T == 1
+
+    def misa_step(self, i, ev=None):
+        """One MISA pass on input set i; ev = (before, after) events around the
+        routed score + top-k call."""
+        m, p, s, st = self.misa, self.p, self.sets[i % len(self.sets)], self.stream
+        if self.decode:
+            m.misa_pool_keys_range(self.shp, p.M - 1, 1, s["k"], s["ks"], s["pooled"], st)
+        else:
+            m.misa_pool_keys(self.shp, s["k"], s["ks"], s["pooled"], st)
+        m.misa_route(self.shp, p.h, s["q"], s["qs"], s["w"], s["pooled"], s["k"], s["ks"],
+                     self.heads, None, self.ws, st)
+        out = self.cand if p.kprime else self.idx
+        if ev:
+            ev[0].record(st)
+        m.misa_score_topk(self.shp, p.h, p.kprime or p.k, s["q"], s["qs"], s["w"], s["k"], s["ks"],
+                          self.heads, out, None, self.ws, st)
+        if ev:
+            ev[1].record(st)
+        if p.kprime:
+            m.misa_rerank(self.shp, p.kprime, p.k, s["q"], s["qs"], s["w"], s["k"], s["ks"],
+                          self.cand, self.idx, None, self.ws, st)
+
+    def dense_step(self, i, ev=None):
+        m, p, s, st = self.misa, self.p, self.sets[i % len(self.sets)], self.stream
+        if ev:
+            ev[0].record(st)
+        m.dsa_index_dense(self.shp, p.k, s["q"], s["qs"], s["w"], s["k"], s["ks"], self.didx, None,
+                          self.ws, st)
+        if ev:
+            ev[1].record(st)
+
+
+def time_steps(fn, steps, warmup, stream):
+    """Run warmup then exactly `steps` steps; returns (wall ms per step,
+    mean ms of the bracketed call measured with events on `stream`)."""
+    import torch
+
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        fn(i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    host_ms = (time.perf_counter() - t0) * 1e3 / steps
+    step_ms = start.elapsed_time(end) / steps
+    call_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    return step_ms, call_ms, host_ms
+
+
+def cpu_baseline(x, budget_s):
+    """The oracle as it stands, on a bounded sample of the same workload,
+    over a thread pool of host cores (ctypes releases the GIL)."""
+    import concurrent.futures
+
+    import numpy as np
+
+    import oracle
+    import synth
+
+    p = x.problem
+    odt = {synth.F32: oracle.F32, synth.BF16: oracle.BF16, synth.FP8_E4M3: oracle.FP8_E4M3}[p.dtype]
+    cores = min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count())
+    if p.T == 1:
+        sample = [(b, 0) for b in range(p.batch)]
+    else:
+        sample = [(0, int(t)) for t in np.linspace(0, p.T - 1, 32).round()]
+    # Per-query cost model to bound the sample at about budget_s of CPU work.
+    n_avg = p.L
+    mac_per_q = p.h * p.d * n_avg + p.H * p.d * p.M
+    est_s_per_q = mac_per_q / 1.5e8
+    max_q = max(cores, int(budget_s * cores / max(est_s_per_q, 1e-6)))
+    sample = sample[:max_q]
+    seqs = {}
+    qraw = x.raw_numpy("q")
+    for b in sorted({b for b, _ in sample}):
+        ks = x.k_scale[b].numpy() if p.dtype == synth.FP8_E4M3 else None
+        seqs[b] = oracle.Sequence(oracle.decode(x.raw_numpy("k")[b], odt, ks), p.B)
+
+    def query_inputs(bt):
+        b, t = bt
+        qs = x.q_scale[b, t:t + 1].numpy() if p.dtype == synth.FP8_E4M3 else None
+        q = oracle.decode(qraw[b, t].reshape(1, -1), odt, qs).reshape(p.H, p.d)
+        return q, x.w[b, t].double().numpy()
+
+    inputs = {bt: query_inputs(bt) for bt in sample}
+
+    def one(bt):
+        b, t = bt
+        q, w = inputs[bt]
+        pos = p.L - p.T + t
+        r = seqs[b].misa(pos, q, w, p.h, p.kprime or p.k)
+        if p.kprime:
+            oracle.rerank(seqs[b].K, q, w, r["idx"], p.k)
+        return pos + 1
+
+    with concurrent.futures.ThreadPoolExecutor(cores) as ex:
+        t0 = time.perf_counter()
+        pairs = sum(ex.map(one, sample))
+        dt = time.perf_counter() - t0
+    desc = f"{len(sample)} queries ({'all sequences' if p.T == 1 else 'evenly spaced'}) of the workload"
+    return {"value": pairs / dt, "unit": "pairs/s", "cores": cores, "kind": "oracle",
+            "sample": desc, "seconds": round(dt, 3)}
+
+
+def traffic_from_profile(kernel, workload, sha):
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("source_sha") != sha:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the MISA indexer path is single-GPU "
+              "(no collectives); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+
+    p = synth.CONFIGS[args.workload]
+    x = synth.generate(p)
+    set_bytes = (x.q.numel() * x.q.element_size() + x.k.numel() * x.k.element_size() +
+                 p.batch * p.M * p.d * 4)
+    n_sets = max(2, min(16, math.ceil(768 * 2**20 / set_bytes)))
+    stream = torch.cuda.Stream()  # default priority
+    r = Runner(x, n_sets, stream)
+    torch.cuda.synchronize()
+
+    m_step, m_call, m_host = time_steps(r.misa_step, args.steps, args.warmup, stream)
+    pairs = p.pairs
+    res_dense = None
+    if not args.no_dense:
+        d_step, d_call, _ = time_steps(r.dense_step, args.steps, args.warmup, stream)
+        res_dense = {"value": pairs / (d_step / 1e3), "ms_per_step": d_step}
+    torch.cuda.synchronize()
+
+    # Recall of the dense top-k by MISA (sets; last step's outputs, same input set).
+    recall = None
+    if res_dense is not None:
+        r.misa_step(0)
+        r.dense_step(0)
+        torch.cuda.synchronize()
+        a, b = r.idx.cpu().numpy(), r.didx.cpu().numpy()
+        tot = 0
+        for bi in range(p.batch):
+            for t in range(p.T):
+                tot += len(set(a[bi, t].tolist()) & set(b[bi, t].tolist()))
+        recall = tot / (p.batch * p.T * p.k)
+
+    e = {synth.F32: 4, synth.BF16: 2, synth.FP8_E4M3: 1}[p.dtype]
+    dtype = {synth.F32: "f32", synth.BF16: "bf16", synth.FP8_E4M3: "fp8"}[p.dtype]
+    sha = source_sha()
+    kp = p.kprime or p.k
+    if p.T == 1:
+        # Decode: the routed score + top-k call streams every key once.
+        alg_bytes = p.batch * p.L * p.d * e + p.batch * p.h * p.d * e + p.batch * p.H * 4 \
+            + p.batch * kp * 4
+        achieved = alg_bytes / (m_call * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "kernel": "misa_score_topk",
+                "algorithmic_bytes": alg_bytes,
+                "traffic": traffic_from_profile("misa_score_topk", args.workload, sha)}
+    else:
+        flops = 2 * p.h * p.d * pairs
+        achieved = flops / (m_call * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS[dtype]
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                "frac": achieved / peak, "kernel": "misa_score_topk", "algorithmic_flops": flops,
+                "traffic": traffic_from_profile("misa_score_topk", args.workload, sha)}
+    roof["call_ms"] = m_call
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(x, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": pairs / (m_step / 1e3),
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": p.name, "batch": p.batch, "L": p.L, "T": p.T, "H": p.H, "h": p.h,
+                   "d": p.d, "B": p.B, "k": p.k, "kprime": p.kprime, "pairs_per_step": pairs,
+                   "input_sets": n_sets, "parallelism": "single-gpu"},
+        "dense_dsa": res_dense,
+        "speedup_vs_dense": (res_dense["ms_per_step"] / m_step) if res_dense else None,
+        "recall_vs_dense": recall,
+        "host_ms_per_step": m_host,
+        "source_sha": sha,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

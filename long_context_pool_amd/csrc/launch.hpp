@@ -23,6 +23,19 @@ hipError_t launch_route(const Shape& s, int32_t h, const void* q, const float* q
                         const float* w, const float* pooled, const void* k, const float* k_scale,
                         int32_t* heads, float* E_out, void* ws, hipStream_t st);
 
+// Router on the matrix cores (bf16/fp8 inputs); no workspace.
+bool route_mfma_supported(const Shape& s);
+hipError_t launch_route_mfma(const Shape& s, int32_t h, const void* q, const float* q_scale,
+                             const float* w, const float* pooled, const void* k,
+                             const float* k_scale, int32_t* heads, float* E_out, hipStream_t st);
+
+// Decode router (T == 1) on the vector ALU: chunked partial sums + finalize.
+size_t route_decode_ws_bytes(const Shape& s);
+hipError_t launch_route_decode(const Shape& s, int32_t h, const void* q, const float* q_scale,
+                               const float* w, const float* pooled, const void* k,
+                               const float* k_scale, int32_t* heads, float* E_out, void* ws,
+                               hipStream_t st);
+
 // Token scoring + top-k over each query's causal prefix.  heads == nullptr
 // scores with all H heads (dense DSA); otherwise with the nh listed heads.
 size_t score_ws_bytes(const Shape& s, int32_t nh, int32_t k);
@@ -30,6 +43,14 @@ hipError_t launch_score_topk(const Shape& s, int32_t nh, const int32_t* heads, i
                              const void* q, const float* q_scale, const float* w, const void* kk,
                              const float* k_scale, int32_t* idx, float* scores_out, void* ws,
                              hipStream_t st);
+
+// Decode (T == 1, bf16/fp8) token scoring + top-k: MFMA key streaming, then a
+// per-sequence select.  ws must hold decode_ws_bytes(s).
+size_t decode_ws_bytes(const Shape& s);
+hipError_t launch_decode_score_topk(const Shape& s, int32_t nh, const int32_t* heads, int32_t k,
+                                    const void* q, const float* q_scale, const float* w,
+                                    const void* kk, const float* k_scale, int32_t* idx,
+                                    float* scores_out, void* ws, hipStream_t st);
 
 // MISA-dagger fine stage.
 size_t rerank_ws_bytes(const Shape& s, int32_t kprime);

@@ -1,11 +1,11 @@
 // Eq. (4) of the MISA summary page ("Methodology" 1, block-pooled router):
 // each block of B consecutive keys is summarised by the mean of its members.
 //
-// One workgroup of 4 waves per (block, sequence).  Lane l of every wave owns
-// dims 2l and 2l+1; wave w sums rows s0+w, s0+w+4, ...  in fp32 (fp8 codes are
-// scaled by their per-token scale first); the four wave partials are added
-// in fixed order, so the result is deterministic.  Bandwidth-bound: one read
-// of the keys, d*4 bytes written per block.
+// One workgroup per (block, sequence).  The block's rows are read 64 at a
+// time (thread t: row t/4, 32 consecutive dims, one vector load run), widened
+// to fp32 (fp8 codes times their per-token scale) into an LDS tile, and
+// thread d < 128 adds column d in row order, so the sum is deterministic.
+// Bandwidth-bound: one read of the keys, d*4 bytes written per block.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -14,6 +14,7 @@ namespace misa {
 namespace {
 
 constexpr int kPoolThreads = 256;
+constexpr int kPoolRows = 64;  // rows per chunk: thread t loads row t/4, dims [32(t%4), +32)
 
 template <int DT>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const void* __restrict__ k,
@@ -21,35 +22,63 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const void* __restri
                                                             float* __restrict__ pooled, int32_t L,
                                                             int32_t B, int32_t block_begin,
                                                             int64_t M) {
-  __shared__ float part[kPoolThreads / kWave][kD];
+  __shared__ float tile[kPoolRows][kD + 4];
   const int64_t blk = block_begin + blockIdx.x;
   const int64_t seq = blockIdx.y;
   const int64_t s0 = blk * B;
   const int64_t s1 = min<int64_t>(s0 + B, L);
-  const int lane = lane_id();
-  const int wv = threadIdx.x / kWave;
-  float a0 = 0.f, a1 = 0.f;
-  for (int64_t s = s0 + wv; s < s1; s += kPoolThreads / kWave) {
-    const int64_t row = (seq * L + s) * kD;
-    float x0 = load_elem<DT>(k, row + 2 * lane);
-    float x1 = load_elem<DT>(k, row + 2 * lane + 1);
-    if constexpr (DT == kFP8) {
-      const float sc = k_scale[seq * L + s];
-      x0 *= sc;
-      x1 *= sc;
-    }
-    a0 += x0;
-    a1 += x1;
-  }
-  part[wv][2 * lane] = a0;
-  part[wv][2 * lane + 1] = a1;
-  __syncthreads();
-  if (threadIdx.x < kD) {
-    float acc = part[0][threadIdx.x];
+  const int lr = threadIdx.x >> 2;
+  const int dc = (threadIdx.x & 3) * 32;
+  float acc = 0.f;  // thread t < 128: sum of dim t over the block
+  for (int64_t c0 = s0; c0 < s1; c0 += kPoolRows) {
+    const int64_t s = c0 + lr;
+    float x[32];
+    if (s < s1) {
+      const int64_t base = (seq * L + s) * kD + dc;
+      const float sc = (DT == kFP8) ? k_scale[seq * L + s] : 1.f;
+      if constexpr (DT == kF32) {
+        const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(k) + base);
 #pragma unroll
-    for (int w = 1; w < kPoolThreads / kWave; ++w) acc += part[w][threadIdx.x];
-    pooled[(seq * M + blk) * kD + threadIdx.x] = acc / static_cast<float>(s1 - s0);
+        for (int u = 0; u < 8; ++u) {
+          const float4 v = src[u];
+          x[4 * u] = v.x; x[4 * u + 1] = v.y; x[4 * u + 2] = v.z; x[4 * u + 3] = v.w;
+        }
+      } else if constexpr (DT == kBF16) {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(k) + base);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint4 v = src[u];
+          const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[8 * u + 2 * e] = __uint_as_float(wd[e] << 16);
+            x[8 * u + 2 * e + 1] = __uint_as_float(wd[e] & 0xFFFF0000u);
+          }
+        }
+      } else {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(k) + base);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const uint4 v = src[u];
+          const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 16; ++e) x[16 * u + e] = fp8_to_f32((wd[e / 4] >> (8 * (e % 4))) & 0xFF) * sc;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) x[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 32; ++e) tile[lr][dc + e] = x[e];
+    __syncthreads();
+    if (threadIdx.x < kD) {
+      const int rows = static_cast<int>(min<int64_t>(kPoolRows, s1 - c0));
+      for (int rr = 0; rr < rows; ++rr) acc += tile[rr][threadIdx.x];  // fixed row order
+    }
+    __syncthreads();
   }
+  if (threadIdx.x < kD) pooled[(seq * M + blk) * kD + threadIdx.x] = acc / static_cast<float>(s1 - s0);
 }
 
 }  // namespace

@@ -62,16 +62,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_list_kernel(const float* __
                                                                  int32_t T, int32_t k,
                                                                  int32_t* __restrict__ idx,
                                                                  float* __restrict__ scores_out) {
-  __shared__ TopkSmem sm;
+  __shared__ TopkFastSmem sm;
   const int64_t r = static_cast<int64_t>(blockIdx.y) * T + blockIdx.x;
   const int64_t pos = static_cast<int64_t>(L) - T + blockIdx.x;
   const float* srow = sc + r * kprime;
   const int32_t* crow = cand + r * kprime;
-  block_topk<kTopkThreads>(
-      kprime, k, [&](int64_t i) { return crow[i] >= 0 && crow[i] <= pos; },
-      [&](int64_t i) { return float_key(srow[i]); }, [&](int64_t i) { return crow[i]; },
-      [&](int64_t i) { return srow[i]; }, idx + r * k, scores_out ? scores_out + r * k : nullptr,
-      sm);
+  block_topk_fast<kTopkThreads>(
+      kprime, k, [=](int64_t i) { return crow[i] >= 0 && crow[i] <= pos; },
+      [=](int64_t i) { return srow[i]; }, [=](int64_t i) { return crow[i]; }, idx + r * k,
+      scores_out ? scores_out + r * k : nullptr, sm);
 }
 
 }  // namespace

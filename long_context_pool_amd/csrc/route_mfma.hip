@@ -1,0 +1,271 @@
+// Eq. (7)-(8) of the MISA summary page ("Methodology" 1) on the matrix cores,
+// for bf16 and fp8 inputs.
+//
+// For query t the router needs S_{t,j} = sum over the floor(n_t/B) complete
+// blocks of ReLU(q_{t,j} . p_b): a dense contraction of the query's H head rows
+// (A operand, bf16; fp8 codes widen to bf16 exactly) with the pooled keys (B
+// operand: fp32 rounded to bf16, and for bf16 inputs also the bf16 rounding of
+// the remainder, so q.p = q.p_hi + q.p_lo holds to ~2^-16 -- a single bf16
+// rounding of p costs ~1e-3 relative in E on short prefixes), 32x32x16 MFMA
+// tiles, ReLU and a masked
+// running sum on the accumulators, then one cross-lane reduction per row.
+// The partial last block (B not dividing n_t) is averaged from the raw keys
+// and dotted in fp32.  Then E_{t,j} = |w_{t,j}| * s_t * (S + partial) / M_t
+// (s_t = the fp8 query scale, else 1) and the h best heads are picked by h
+// rounds of a wave arg-max (ties to the lower head) and written ascending.
+//
+// Prefill: one wave per query (4 per workgroup); the pooled tile is converted
+// to bf16 once into LDS and shared by the four waves.  (Decode has a single
+// query per sequence and is routed on the vector ALU, route_decode.hip.)
+#include "common.hpp"
+#include "launch.hpp"
+#include "mfma.hpp"
+#include "route_common.hpp"
+
+namespace misa {
+
+namespace {
+
+constexpr int kRThreads = 256;
+constexpr int kRWaves = 4;
+constexpr int kLdsRow = kD * 2 + 16;  // bytes per pooled row in LDS (bf16 + pad)
+
+// Load the A operand: head rows rt*32 + l%32 of query r, head-dim elements
+// [64*(l/32), 64*(l/32)+64) split over 8 k-steps.  Rows >= H are zero.
+template <int DT, int RT>
+__device__ __forceinline__ void load_q_rows(const void* q, int64_t r, int H, bf16x8 (&a)[RT][8]) {
+  const int lane = lane_id();
+  const int hf = lane >> 5;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int j = rt * 32 + (lane & 31);
+    if (j >= H) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) a[rt][ks] = as_bf16x8(make_uint4(0, 0, 0, 0));
+      continue;
+    }
+    if constexpr (DT == kBF16) {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) +
+                                                        (r * H + j) * kD + 64 * hf);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) a[rt][ks] = as_bf16x8(src[ks]);
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(q) +
+                                                        (r * H + j) * kD + 64 * hf);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 v = src[c];  // 16 fp8 codes = k-steps 2c, 2c+1
+        const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          // e4m3 -> fp32 is exact and bf16 holds the 4-bit significand exactly.
+          const float f0 = fp8_to_f32(wds[u] & 0xFF), f1 = fp8_to_f32((wds[u] >> 8) & 0xFF);
+          const float f2 = fp8_to_f32((wds[u] >> 16) & 0xFF), f3 = fp8_to_f32(wds[u] >> 24);
+          o[2 * u] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+          o[2 * u + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u);
+        }
+        a[rt][2 * c] = as_bf16x8(make_uint4(o[0], o[1], o[2], o[3]));
+        a[rt][2 * c + 1] = as_bf16x8(make_uint4(o[4], o[5], o[6], o[7]));
+      }
+    }
+  }
+}
+
+// Split an fp32 quad into bf16 hi (RNE) and lo (RNE of the remainder) pairs.
+__device__ __forceinline__ void split_bf16(float4 x, uint32_t& h0, uint32_t& h1, uint32_t& l0,
+                                           uint32_t& l1) {
+  const uint32_t a = f32_to_bf16_bits(x.x), b = f32_to_bf16_bits(x.y);
+  const uint32_t c = f32_to_bf16_bits(x.z), d = f32_to_bf16_bits(x.w);
+  h0 = a | (b << 16);
+  h1 = c | (d << 16);
+  l0 = f32_to_bf16_bits(x.x - __uint_as_float(a << 16)) |
+       (f32_to_bf16_bits(x.y - __uint_as_float(b << 16)) << 16);
+  l1 = f32_to_bf16_bits(x.z - __uint_as_float(c << 16)) |
+       (f32_to_bf16_bits(x.w - __uint_as_float(d << 16)) << 16);
+}
+
+// B operand of pooled block `b` (fp32 row -> bf16 hi [+ lo]), elements
+// [64hf, 64hf+64).
+template <bool SPLIT>
+__device__ __forceinline__ void load_pooled_b(const float* prow, bool ok, bf16x8 (&bh)[8],
+                                              bf16x8 (&bl)[8]) {
+  const int hf = lane_id() >> 5;
+  const float4* src = reinterpret_cast<const float4*>(prow + 64 * hf);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const float4 x0 = ok ? src[2 * ks] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 x1 = ok ? src[2 * ks + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
+    uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+    split_bf16(x0, h0, h1, l0, l1);
+    split_bf16(x1, h2, h3, l2, l3);
+    bh[ks] = as_bf16x8(make_uint4(h0, h1, h2, h3));
+    if constexpr (SPLIT) bl[ks] = as_bf16x8(make_uint4(l0, l1, l2, l3));
+  }
+}
+
+// acc (rows x 32 blocks) = A . (B_hi [+ B_lo]); rs += ReLU(acc) when col_ok.
+// The hi and lo products of every row tile go to separate accumulators so the
+// MFMA chains are independent.
+template <int RT, bool SPLIT>
+__device__ __forceinline__ void accumulate_tile(const bf16x8 (&a)[RT][8], const bf16x8 (&bh)[8],
+                                                const bf16x8 (&bl)[8], bool col_ok,
+                                                f32x16 (&rs)[RT]) {
+  f32x16 acc[RT], acl[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    acc[rt] = f32x16{};
+    acl[rt] = f32x16{};
+  }
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      acc[rt] = mfma32_bf16(a[rt][ks], bh[ks], acc[rt]);
+      if constexpr (SPLIT) acl[rt] = mfma32_bf16(a[rt][ks], bl[ks], acl[rt]);
+    }
+  if (col_ok) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) rs[rt][i] += fmaxf(SPLIT ? acc[rt][i] + acl[rt][i] : acc[rt][i], 0.f);
+  }
+}
+
+// Sum rs over the 32 columns held by each half-wave; returns through LDS
+// rowsum[row] for rows of this wave (row = rt*32 + 8*(i/4) + 4*hf + i%4).
+template <int RT>
+__device__ __forceinline__ void reduce_rows(f32x16 (&rs)[RT], float* rowsum) {
+  const int lane = lane_id();
+  const int hf = lane >> 5;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float v = rs[rt][i];
+#pragma unroll
+      for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+      if ((lane & 31) == 0) {
+        const int row = rt * 32 + 8 * (i / 4) + 4 * hf + (i % 4);
+        rowsum[row] = v;
+      }
+    }
+}
+
+template <int DT, int RT>
+__global__ __launch_bounds__(kRThreads) void route_prefill_kernel(
+    const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const float* __restrict__ pooled, const void* __restrict__ k, const float* __restrict__ k_scale,
+    int32_t* __restrict__ heads, float* __restrict__ E_out, int32_t L, int32_t T, int32_t H,
+    int32_t B, int64_t M, int32_t h) {
+  constexpr bool SPLIT = DT == kBF16;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[SPLIT ? 2 : 1][32 * kLdsRow];
+  __shared__ float rowsum[kRWaves][64];
+  __shared__ float kp[kRWaves][kD];
+  __shared__ float partial[kRWaves][64];
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int64_t seq = blockIdx.y;
+  const int t0 = blockIdx.x * kRWaves;
+  const int t = t0 + wave;
+  const bool active = t < T;
+  const int64_t r = seq * T + (active ? t : t0);
+  const int64_t pos = static_cast<int64_t>(L) - T + (active ? t : t0);
+  const int64_t n = pos + 1;
+  const int64_t full = n / B;
+  const int64_t Mt = (n + B - 1) / B;
+  // Largest complete-block count among the workgroup's queries.
+  const int tl = min(t0 + kRWaves - 1, T - 1);
+  const int64_t full_max = (static_cast<int64_t>(L) - T + tl + 1) / B;
+
+  bf16x8 a[RT][8];
+  load_q_rows<DT, RT>(q, r, H, a);
+  f32x16 rs[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) rs[rt] = f32x16{};
+
+  const int64_t ntiles = (full_max + 31) / 32;
+  const int ld_row = threadIdx.x >> 3;        // 32 rows x 8 chunks of 16 floats
+  const int ld_chunk = threadIdx.x & 7;
+  for (int64_t bt = 0; bt < ntiles; ++bt) {
+    {
+      const int64_t b = bt * 32 + ld_row;
+      const bool ok = b < full_max;
+      const float4* src = reinterpret_cast<const float4*>(pooled + (seq * M + (ok ? b : 0)) * kD +
+                                                          16 * ld_chunk);
+      uint32_t o[8], lo[8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 x = ok ? src[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+        split_bf16(x, o[2 * u], o[2 * u + 1], lo[2 * u], lo[2 * u + 1]);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(tile[0] + ld_row * kLdsRow + 32 * ld_chunk);
+      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+      if constexpr (SPLIT) {
+        uint4* dl = reinterpret_cast<uint4*>(tile[SPLIT ? 1 : 0] + ld_row * kLdsRow + 32 * ld_chunk);
+        dl[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        dl[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+      }
+    }
+    __syncthreads();
+    bf16x8 bh[8], bl[8];
+    const int boff = (lane & 31) * kLdsRow + 128 * (lane >> 5);
+    const uint4* brow = reinterpret_cast<const uint4*>(tile[0] + boff);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) bh[ks] = as_bf16x8(brow[ks]);
+    if constexpr (SPLIT) {
+      const uint4* blow = reinterpret_cast<const uint4*>(tile[SPLIT ? 1 : 0] + boff);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) bl[ks] = as_bf16x8(blow[ks]);
+    }
+    const bool ok = bt * 32 + (lane & 31) < full;
+    accumulate_tile<RT, SPLIT>(a, bh, bl, ok, rs);
+    __syncthreads();
+  }
+  reduce_rows<RT>(rs, rowsum[wave]);
+  const bool has_partial = Mt > full;
+  if (has_partial) {
+    // Partial mean of keys [full*B, pos] by this wave (two dims per lane).
+    for (int c = 0; c < 2; ++c) {
+      const int dim = lane + 64 * c;
+      float acc = 0.f;
+      for (int64_t s = full * B; s <= pos; ++s) {
+        float x = load_elem<DT>(k, (seq * L + s) * kD + dim);
+        if constexpr (DT == kFP8) x *= k_scale[seq * L + s];
+        acc += x;
+      }
+      kp[wave][dim] = acc / static_cast<float>(pos - full * B + 1);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < H) {
+      float dot = 0.f;
+      for (int i = 0; i < kD; ++i) dot += load_elem<DT>(q, (r * H + lane) * kD + i) * kp[wave][i];
+      partial[wave][lane] = fmaxf(dot, 0.f);
+    }
+  }
+  __syncthreads();
+  if (active) {
+    const float sq = (DT == kFP8) ? q_scale[r] : 1.f;
+    finalize_query(&rowsum[wave], 1, has_partial ? partial[wave] : nullptr, H, h, w, sq, r, Mt,
+                   heads, E_out);
+  }
+}
+
+}  // namespace
+
+bool route_mfma_supported(const Shape& s) { return s.dtype != kF32 && s.H <= 64 && s.T > 1; }
+
+hipError_t launch_route_mfma(const Shape& s, int32_t h, const void* q, const float* q_scale,
+                             const float* w, const float* pooled, const void* k,
+                             const float* k_scale, int32_t* heads, float* E_out, hipStream_t st) {
+  const bool two = s.H > 32;
+  dim3 grid((s.T + kRWaves - 1) / kRWaves, s.batch);
+#define RP(DT, RT) route_prefill_kernel<DT, RT><<<grid, kRThreads, 0, st>>>(q, q_scale, w, pooled, k, k_scale, heads, E_out, s.L, s.T, s.H, s.B, s.M(), h)
+  if (s.dtype == kBF16) { if (two) RP(kBF16, 2); else RP(kBF16, 1); }
+  else { if (two) RP(kFP8, 2); else RP(kFP8, 1); }
+#undef RP
+  return hipGetLastError();
+}
+
+}  // namespace misa

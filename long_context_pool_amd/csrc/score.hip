@@ -65,20 +65,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
                                                                  int32_t L, int32_t T, int32_t k,
                                                                  int32_t* __restrict__ idx,
                                                                  float* __restrict__ scores_out) {
-  __shared__ TopkSmem sm;
+  __shared__ TopkFastSmem sm;
   const int t = blockIdx.x;
   const int64_t r = static_cast<int64_t>(blockIdx.y) * T + t;
   const int64_t n = static_cast<int64_t>(L) - T + t + 1;
   const float* row = rows + r * static_cast<int64_t>(L);
-  block_topk<kTopkThreads>(
-      n, k, [](int64_t) { return true; }, [&](int64_t i) { return float_key(row[i]); },
-      [](int64_t i) { return static_cast<int32_t>(i); }, [&](int64_t i) { return row[i]; },
-      idx + r * k, scores_out ? scores_out + r * k : nullptr, sm);
+  block_topk_fast<kTopkThreads>(
+      n, k, [](int64_t) { return true; }, [=](int64_t i) { return row[i]; },
+      [](int64_t i) { return static_cast<int32_t>(i); }, idx + r * k,
+      scores_out ? scores_out + r * k : nullptr, sm);
 }
 
 }  // namespace
 
 size_t score_ws_bytes(const Shape& s, int32_t, int32_t) {
+  if (s.T == 1 && s.dtype != kF32) return decode_ws_bytes(s);
   return align_up(static_cast<size_t>(s.batch) * s.T * s.L * sizeof(float));
 }
 
@@ -86,6 +87,9 @@ hipError_t launch_score_topk(const Shape& s, int32_t nh, const int32_t* heads, i
                              const void* q, const float* q_scale, const float* w, const void* kk,
                              const float* k_scale, int32_t* idx, float* scores_out, void* ws,
                              hipStream_t st) {
+  if (s.T == 1 && s.dtype != kF32)
+    return launch_decode_score_topk(s, nh, heads, k, q, q_scale, w, kk, k_scale, idx, scores_out,
+                                    ws, st);
   float* rows = static_cast<float*>(ws);
   dim3 g1((s.L + kScoreThreads - 1) / kScoreThreads, s.T, s.batch);
   switch (s.dtype) {

@@ -28,17 +28,16 @@ struct TopkSmem {
 // strictly larger value, `equal` = how many equal it.  Requires the number of
 // elements with pred(i) >= want >= 1.
 template <int NT, class Pred, class Val>
-__device__ uint32_t block_select_kth(int64_t n, int want, Pred pred, Val val, TopkSmem& sm,
+__device__ __forceinline__ uint32_t block_select_kth(int64_t n, int want, Pred pred, Val val, TopkSmem& sm,
                                      int& above, int& equal) {
-  constexpr int shifts[3] = {21, 10, 0};
-  constexpr uint32_t masks[3] = {0x7FFu, 0x7FFu, 0x3FFu};
   uint32_t prefix = 0, prefix_mask = 0;
   int remaining = want;
   int above_total = 0;
   int eq = 0;
   for (int pass = 0; pass < 3; ++pass) {
-    const int shift = shifts[pass];
-    const uint32_t m = masks[pass];
+    // Digits: bits 31..21, 20..10, 9..0.
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t m = pass == 2 ? 0x3FFu : 0x7FFu;
     for (int b = threadIdx.x; b < kRadixBins; b += NT) sm.hist[b] = 0;
     __syncthreads();
     for (int64_t i = threadIdx.x; i < n; i += NT) {
@@ -90,7 +89,7 @@ __device__ uint32_t block_select_kth(int64_t n, int want, Pred pred, Val val, To
 // out_idx/out_score[0..k) in source order.  Unused slots (fewer than k valid
 // elements) get idx -1 and score -inf.  All threads of the block must call.
 template <int NT, class Valid, class Key, class Idx, class Score>
-__device__ void block_topk(int64_t n, int k, Valid valid, Key key, Idx idx, Score score,
+__device__ __forceinline__ void block_topk(int64_t n, int k, Valid valid, Key key, Idx idx, Score score,
                            int32_t* out_idx, float* out_score, TopkSmem& sm) {
   // Count valid elements.
   int cnt = 0;
@@ -108,8 +107,8 @@ __device__ void block_topk(int64_t n, int k, Valid valid, Key key, Idx idx, Scor
     if (equal > need) {
       tiebreak = true;
       int a2, e2;
-      auto tie = [&](int64_t i) { return valid(i) && key(i) == kth; };
-      auto inv_idx = [&](int64_t i) { return ~static_cast<uint32_t>(idx(i)); };
+      auto tie = [=](int64_t i) { return valid(i) && key(i) == kth; };
+      auto inv_idx = [=](int64_t i) { return ~static_cast<uint32_t>(idx(i)); };
       ith = block_select_kth<NT>(n, need, tie, inv_idx, sm, a2, e2);
     }
   }
@@ -138,6 +137,258 @@ __device__ void block_topk(int64_t n, int k, Valid valid, Key key, Idx idx, Scor
     out_idx[p] = -1;
     if (out_score) out_score[p] = -__builtin_inff();
   }
+}
+
+// ---------------------------------------------------------------- fast path
+//
+// Same contract as block_topk, for scores held as fp32.  Wave w owns the
+// contiguous range [w*CW, (w+1)*CW) (CW a multiple of 64); at step j lane l
+// handles element w*CW + 64j + l, so every load is coalesced and (step, lane)
+// order is index order.  Ranges of at most kRegCache steps stay in registers
+// across the passes:
+//   1. count + min/max of the valid scores (block reductions);
+//   2. a histogram over kLinBins bins of the order-preserving key range
+//      [key(min), key(max)] (bin = (key - key(min)) >> shift, shift chosen so
+//      the range fits): the bin is a monotone function of the score, so every
+//      element of a higher bin has a strictly larger score, and the bins are
+//      log-spaced in value, so a few large outliers cannot crowd all scores
+//      into a few bins.  A suffix scan gives the bin b* holding the k-th best
+//      and `above`, the count in higher bins;
+//   3. one ordered compaction (wave ballots + a scan over the waves): elements
+//      of bins above b* go straight to the output, those of b* to an LDS list;
+//   4. the b* list is resolved exactly: by pairwise rank when it is short,
+//      else by block_topk.
+// When the range is degenerate or b* holds more than kLinCap elements the
+// whole input goes through block_topk instead.
+
+constexpr int kLinBins = 4096;
+constexpr int kLinCap = 4096;
+constexpr int kRegCache = 32;
+constexpr int kRankMax = 256;
+
+struct TopkFastSmem {
+  TopkSmem base;
+  uint32_t hist[kLinBins];
+  float cand_score[kLinCap];
+  int32_t cand_idx[kLinCap];
+  float red[2][32];
+  int wtot[2][32];
+  int sel_bin, sel_above, sel_count;
+};
+
+__device__ __forceinline__ int lin_bin(float s, uint32_t kmin, int shift) {
+  const uint32_t d = float_key(s) - kmin;  // < 2^(shift+12) for s in [min, max]
+  const uint32_t b = d >> shift;
+  return b < static_cast<uint32_t>(kLinBins) ? static_cast<int>(b) : kLinBins - 1;
+}
+
+template <int NT, class Valid, class Score, class Idx>
+__device__ __forceinline__ void block_topk_fast(int64_t n, int k, Valid valid, Score score, Idx idx,
+                                                int32_t* out_idx, float* out_score,
+                                                TopkFastSmem& sm) {
+  constexpr int NW = NT / kWave;
+  const int lane = lane_id();
+  const int wid = threadIdx.x / kWave;
+  const int64_t CW = ((n + NW - 1) / NW + kWave - 1) / kWave * kWave;
+  const int J = static_cast<int>(CW / kWave);
+  const int64_t wbase = static_cast<int64_t>(wid) * CW + lane;
+  const bool cached = J <= kRegCache;
+  // Register cache of this lane's elements; ok bit j marks a valid element.
+  float rc[kRegCache];
+  uint32_t okm = 0;
+  // 1. count, min, max.
+  int cnt = 0;
+  float mn = __builtin_inff(), mx = -__builtin_inff();
+  if (cached) {
+#pragma unroll
+    for (int j = 0; j < kRegCache; ++j) {
+      const int64_t i = wbase + 64 * j;
+      const bool ok = j < J && i < n && valid(i);
+      const float v = ok ? score(i) : 0.f;
+      rc[j] = v;
+      okm |= ok ? (1u << j) : 0u;
+      cnt += ok ? 1 : 0;
+      mn = ok ? fminf(mn, v) : mn;
+      mx = ok ? fmaxf(mx, v) : mx;
+    }
+  } else {
+    for (int j = 0; j < J; ++j) {
+      const int64_t i = wbase + 64 * j;
+      if (i >= n || !valid(i)) continue;
+      const float v = score(i);
+      ++cnt;
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
+    }
+  }
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) {
+    cnt += __shfl_xor(cnt, o, kWave);
+    mn = fminf(mn, __shfl_xor(mn, o, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  }
+  if (lane == 0) {
+    sm.base.scan_tmp[wid] = cnt;
+    sm.red[0][wid] = mn;
+    sm.red[1][wid] = mx;
+  }
+  for (int b = threadIdx.x; b < kLinBins; b += NT) sm.hist[b] = 0;
+  __syncthreads();
+  int nvalid = 0;
+  mn = __builtin_inff();
+  mx = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    nvalid += sm.base.scan_tmp[i];
+    mn = fminf(mn, sm.red[0][i]);
+    mx = fmaxf(mx, sm.red[1][i]);
+  }
+  __syncthreads();
+  const uint32_t kmin = float_key(mn);
+  const uint32_t kspan = float_key(mx) - kmin;
+  // Smallest shift with (kspan >> shift) < kLinBins.
+  const int shift = kspan < static_cast<uint32_t>(kLinBins) ? 0 : 32 - __clz(kspan) - 12;
+  const bool degenerate = !(mx > mn);  // all equal (or NaN): one bin
+  if (nvalid <= k || degenerate) {
+    block_topk<NT>(n, k, valid, [=](int64_t i) { return float_key(score(i)); }, idx, score,
+                   out_idx, out_score, sm.base);
+    return;
+  }
+  // 2. histogram of the linear bins, then the bin holding the k-th best.
+  if (cached) {
+#pragma unroll
+    for (int j = 0; j < kRegCache; ++j)
+      if (okm & (1u << j)) atomicAdd(&sm.hist[lin_bin(rc[j], kmin, shift)], 1u);
+  } else {
+    for (int j = 0; j < J; ++j) {
+      const int64_t i = wbase + 64 * j;
+      if (i < n && valid(i)) atomicAdd(&sm.hist[lin_bin(score(i), kmin, shift)], 1u);
+    }
+  }
+  __syncthreads();
+  {
+    constexpr int BPT = kLinBins / NT;
+    int local[BPT];
+    int lsum = 0;
+#pragma unroll
+    for (int c = 0; c < BPT; ++c) {
+      local[c] = static_cast<int>(sm.hist[kLinBins - 1 - (threadIdx.x * BPT + c)]);
+      lsum += local[c];
+    }
+    int total;
+    int run = block_exclusive_sum<NT>(lsum, sm.base.scan_tmp, total);
+#pragma unroll
+    for (int c = 0; c < BPT; ++c) {
+      if (run < k && run + local[c] >= k) {
+        sm.sel_bin = kLinBins - 1 - (threadIdx.x * BPT + c);
+        sm.sel_above = run;
+        sm.sel_count = local[c];
+      }
+      run += local[c];
+    }
+    __syncthreads();
+  }
+  const int bstar = sm.sel_bin;
+  const int above = sm.sel_above;
+  const int bcount = sm.sel_count;
+  __syncthreads();
+  if (bcount > kLinCap) {
+    block_topk<NT>(n, k, valid, [=](int64_t i) { return float_key(score(i)); }, idx, score,
+                   out_idx, out_score, sm.base);
+    return;
+  }
+  // 3. ordered compaction: wave totals, a scan over the waves, then per-step
+  //    ballots place each element at its index-order position.
+  int na = 0, nc = 0;
+  if (cached) {
+#pragma unroll
+    for (int j = 0; j < kRegCache; ++j) {
+      const bool ok = okm & (1u << j);
+      const int b = lin_bin(rc[j], kmin, shift);
+      na += __popcll(__ballot(ok && b > bstar));
+      nc += __popcll(__ballot(ok && b == bstar));
+    }
+  } else {
+    for (int j = 0; j < J; ++j) {
+      const int64_t i = wbase + 64 * j;
+      const bool ok = i < n && valid(i);
+      const int b = ok ? lin_bin(score(i), kmin, shift) : -1;
+      na += __popcll(__ballot(ok && b > bstar));
+      nc += __popcll(__ballot(ok && b == bstar));
+    }
+  }
+  if (lane == 0) {
+    sm.wtot[0][wid] = na;
+    sm.wtot[1][wid] = nc;
+  }
+  __syncthreads();
+  int pa = 0, pc = 0;
+  for (int u = 0; u < wid; ++u) {
+    pa += sm.wtot[0][u];
+    pc += sm.wtot[1][u];
+  }
+  auto emit = [&](int64_t i, bool ok, float v) {
+    const int b = ok ? lin_bin(v, kmin, shift) : -1;
+    const uint64_t mh = __ballot(b > bstar);
+    const uint64_t mc = __ballot(b == bstar);
+    if (b > bstar) {
+      const int p = pa + lanes_below(mh);
+      if (p < k) {
+        out_idx[p] = idx(i);
+        if (out_score) out_score[p] = v;
+      }
+    } else if (b == bstar) {
+      const int p = pc + lanes_below(mc);
+      if (p < kLinCap) {
+        sm.cand_score[p] = v;
+        sm.cand_idx[p] = idx(i);
+      }
+    }
+    pa += __popcll(mh);
+    pc += __popcll(mc);
+  };
+  if (cached) {
+#pragma unroll
+    for (int j = 0; j < kRegCache; ++j) {
+      const bool ok = okm & (1u << j);
+      emit(wbase + 64 * j, ok, rc[j]);
+    }
+  } else {
+    for (int j = 0; j < J; ++j) {
+      const int64_t i = wbase + 64 * j;
+      const bool ok = i < n && valid(i);
+      emit(i, ok, ok ? score(i) : 0.f);
+    }
+  }
+  __syncthreads();
+  // 4. the (k - above) best of the b* list, written after the `above` slots.
+  const int need = k - above;
+  if (bcount <= kRankMax) {
+    // Every slot of [above, k) receives exactly one rank (ranks are distinct
+    // for distinct token ids); prefill guards against duplicated ids.
+    for (int p = above + threadIdx.x; p < k; p += NT) out_idx[p] = -1;
+    __syncthreads();
+    if (threadIdx.x < bcount) {
+      const uint32_t key = float_key(sm.cand_score[threadIdx.x]);
+      const int32_t id = sm.cand_idx[threadIdx.x];
+      int rank = 0;
+      for (int j = 0; j < bcount; ++j) {
+        const uint32_t kj = float_key(sm.cand_score[j]);
+        rank += (kj > key || (kj == key && sm.cand_idx[j] < id)) ? 1 : 0;
+      }
+      if (rank < need) {
+        out_idx[above + rank] = id;
+        if (out_score) out_score[above + rank] = sm.cand_score[threadIdx.x];
+      }
+    }
+    return;
+  }
+  const float* cs = sm.cand_score;
+  const int32_t* ci = sm.cand_idx;
+  block_topk<NT>(
+      bcount, need, [](int64_t) { return true; }, [=](int64_t j) { return float_key(cs[j]); },
+      [=](int64_t j) { return ci[j]; }, [=](int64_t j) { return cs[j]; }, out_idx + above,
+      out_score ? out_score + above : nullptr, sm.base);
 }
 
 }  // namespace misa
