@@ -40,6 +40,10 @@ constexpr int elem_bytes() {
   return DT == kF32 ? 4 : (DT == kBF16 ? 2 : 1);
 }
 
+// ReLU as one v_med3_f32: clamp(x, 0, 3e38) equals max(x, 0) for every finite
+// score (fmaxf adds a NaN-quieting v_max per element).
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 3.0e38f); }
+
 // ---------------------------------------------------------------- ordering keys
 
 // Order-preserving map fp32 -> u32 (larger float <=> larger key); -0 maps like +0.

@@ -19,6 +19,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma.hpp"
+#include "row_scorer.hpp"
 #include "topk.hpp"
 
 namespace misa {
@@ -40,14 +41,6 @@ constexpr int kCandCap = 8192;
 
 __device__ __forceinline__ uint32_t key_digit(float v) { return float_key(v) >> kDigitShift; }
 
-// Rows scored for sequence r: head ids (heads != nullptr) or 0..nh-1.
-__device__ __forceinline__ int scored_head(const int32_t* heads, int64_t r, int nh, int row,
-                                           int H) {
-  if (row >= nh) return -1;
-  const int j = heads ? heads[r * nh + row] : row;
-  return (j >= 0 && j < H) ? j : -1;
-}
-
 template <int DT, int NRT>
 __global__ __launch_bounds__(kDecThreads) void decode_score_kernel(
     const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
@@ -59,86 +52,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_score_kernel(
   __syncthreads();
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
-  const int col = lane & 15;
-  const int qq = lane >> 4;  // lane group: head-dim elements [32qq, 32qq+32)
   const int64_t r = blockIdx.y;  // sequence (T == 1)
-  const float sq = (DT == kFP8) ? q_scale[r] : 1.f;
-
-  // Per-lane weights of the accumulator rows 4qq..4qq+3 of every row tile
-  // (fp8: the query scale is folded in; scales are positive).
-  float wl[NRT][4];
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = scored_head(heads, r, nh, rt * 16 + 4 * qq + i, H);
-      wl[rt][i] = (j >= 0) ? w[r * H + j] * sq : 0.f;
-    }
-
-  // A operand: row (rt*16 + col), head-dim elements [32qq, 32qq+32).
-  bf16x8 a16[NRT][4];
-  i32x8 a8[NRT];
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    const int j = scored_head(heads, r, nh, rt * 16 + col, H);
-    if constexpr (DT == kBF16) {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) +
-                                                        (r * H + (j < 0 ? 0 : j)) * kD + 32 * qq);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) a16[rt][ks] = as_bf16x8(j < 0 ? make_uint4(0, 0, 0, 0) : src[ks]);
-    } else {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(q) +
-                                                        (r * H + (j < 0 ? 0 : j)) * kD + 32 * qq);
-      const uint4 lo = j < 0 ? make_uint4(0, 0, 0, 0) : src[0];
-      const uint4 hi = j < 0 ? make_uint4(0, 0, 0, 0) : src[1];
-      a8[rt] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    }
-  }
-
+  RowScorer<DT, NRT> sc;
+  sc.init(q, q_scale, w, heads, nh, r, H);
+  const void* krows = (DT == kBF16) ? static_cast<const void*>(static_cast<const uint16_t*>(k) + r * L * kD)
+                                    : static_cast<const void*>(static_cast<const uint8_t*>(k) + r * L * kD);
   const int64_t s_begin = (static_cast<int64_t>(blockIdx.x) * kDecWaves + wave) * keys_per_wave;
   const int64_t s_end = min<int64_t>(s_begin + keys_per_wave, L);
   for (int64_t s0 = s_begin; s0 < s_end; s0 += 64) {
-    float res = 0.f;
-    // Four 16-key groups per iteration; all loads are issued before the MFMAs.
-    uint4 kb[4][DT == kBF16 ? 4 : 2];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int64_t s = s0 + 16 * g + col;
-      const bool ok = s < s_end;
-      const int64_t row = (r * L + (ok ? s : s_begin)) * kD;
-      if constexpr (DT == kBF16) {
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(k) + row + 32 * qq);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kb[g][ks] = ok ? src[ks] : make_uint4(0, 0, 0, 0);
-      } else {
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(k) + row + 32 * qq);
-        kb[g][0] = ok ? src[0] : make_uint4(0, 0, 0, 0);
-        kb[g][1] = ok ? src[1] : make_uint4(0, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      float part = 0.f;
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (DT == kBF16) {
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) acc = mfma16_bf16(a16[rt][ks], as_bf16x8(kb[g][ks]), acc);
-        } else {
-          const i32x8 b8{(int)kb[g][0].x, (int)kb[g][0].y, (int)kb[g][0].z, (int)kb[g][0].w,
-                         (int)kb[g][1].x, (int)kb[g][1].y, (int)kb[g][1].z, (int)kb[g][1].w};
-          acc = mfma16_fp8(a8[rt], b8, acc);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part += wl[rt][i] * fmaxf(acc[i], 0.f);
-      }
-      // Sum the four lane groups holding rows 0-3, 4-7, 8-11, 12-15 of key col.
-      part += __shfl_xor(part, 16, kWave);
-      part += __shfl_xor(part, 32, kWave);
-      if (qq == g) res = part;  // lane group g keeps the scores of key group g
-    }
-    const int64_t s = s0 + lane;  // = s0 + 16*qq + col
+    const float res = sc.score64(krows, s0, s_end, s_begin);
+    const int64_t s = s0 + lane;
     if (s < s_end) {
       float v = res;
       if constexpr (DT == kFP8) v *= k_scale[r * L + s];

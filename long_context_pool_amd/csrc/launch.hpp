@@ -25,9 +25,11 @@ hipError_t launch_route(const Shape& s, int32_t h, const void* q, const float* q
 
 // Router on the matrix cores (bf16/fp8 inputs); no workspace.
 bool route_mfma_supported(const Shape& s);
+size_t route_mfma_ws_bytes(const Shape& s);
 hipError_t launch_route_mfma(const Shape& s, int32_t h, const void* q, const float* q_scale,
                              const float* w, const float* pooled, const void* k,
-                             const float* k_scale, int32_t* heads, float* E_out, hipStream_t st);
+                             const float* k_scale, int32_t* heads, float* E_out, void* ws,
+                             hipStream_t st);
 
 // Decode router (T == 1) on the vector ALU: chunked partial sums + finalize.
 size_t route_decode_ws_bytes(const Shape& s);
@@ -51,6 +53,15 @@ hipError_t launch_decode_score_topk(const Shape& s, int32_t nh, const int32_t* h
                                     const void* q, const float* q_scale, const float* w,
                                     const void* kk, const float* k_scale, int32_t* idx,
                                     float* scores_out, void* ws, hipStream_t st);
+
+// Prefill (T > 1, bf16/fp8) token scoring + top-k on 32x32 MFMA tiles with
+// sampled thresholds, certified candidate selection and a repair path.
+bool prefill_supported(const Shape& s);
+size_t prefill_ws_bytes(const Shape& s, int32_t nh, int32_t k);
+hipError_t launch_prefill_score_topk(const Shape& s, int32_t nh, const int32_t* heads, int32_t k,
+                                     const void* q, const float* q_scale, const float* w,
+                                     const void* kk, const float* k_scale, int32_t* idx,
+                                     float* scores_out, void* ws, hipStream_t st);
 
 // MISA-dagger fine stage.
 size_t rerank_ws_bytes(const Shape& s, int32_t kprime);

@@ -1,0 +1,651 @@
+// Prefill token scoring + top-k, Eq. (9)-(10) (routed heads) and Eq. (1)-(2)
+// (all heads) of the MISA summary page, on the gfx950 matrix cores.
+//
+// Every indexer head scores the same key, so for a tile of queries the scores
+// are one dense contraction: the gathered head rows of the tile (A operand,
+// held in registers for the whole pass) times K^T (B operand, 64-key tiles
+// staged through LDS, double-buffered, shared by the workgroup's four waves),
+// 32x32x16 bf16 or 32x32x64 fp8 MFMA, fp32 accumulation.  The ReLU * w head
+// sum runs on the accumulators: the row order inside a 32-row tile is chosen
+// so that each lane holds all heads of its query for its key column.
+//
+// Exact selection without writing the score rows (1-4 GiB at long context):
+//  * a workgroup owns 32 consecutive queries (h = 8; fewer for more heads)
+//    and one of S key splits; blocks are numbered so that all workgroups of
+//    one split land on the same XCD and share its L2;
+//  * it first scores a strided 512-key sample of its split and sets, per
+//    query, a threshold tau at the sample's (2.5 k/n)-quantile;
+//  * the full pass appends every score >= tau of a key inside the query's
+//    prefix to the (query, split) candidate segment (wave ballots give the
+//    positions; each segment has a single writer wave);
+//  * the select kernel takes the top-k of a query's candidates.  That is the
+//    true top-k iff at least k candidates score >= max over splits of tau
+//    (every non-candidate is below its split's tau); otherwise, or when a
+//    segment overflowed, the query is queued and the repair kernel scores its
+//    whole prefix into a scratch row and selects from that.
+#include "common.hpp"
+#include "launch.hpp"
+#include "mfma.hpp"
+#include "row_scorer.hpp"
+#include "topk.hpp"
+
+namespace misa {
+
+namespace {
+
+constexpr int kPThreads = 256;
+constexpr int kPWaves = 4;
+constexpr int kRT = 2;             // 32-row tiles per wave
+constexpr int kTileKeys = 64;      // keys per LDS tile (two 32-key column tiles)
+constexpr int kSamples = 512;      // sample keys per (workgroup, split)
+constexpr float kSampleMargin = 2.5f;
+constexpr int kRepairSlots = 64;   // repair workgroups (one scratch row each)
+constexpr int kRepThreads = 512;
+constexpr int kTopkThreadsSel = 1024;
+
+template <int DT>
+constexpr int lds_row_bytes() { return DT == kBF16 ? kD * 2 + 16 : kD + 16; }
+
+// Queries per wave for HPQ padded heads per query (rows of a 32-row tile).
+template <int HPQ>
+constexpr int qpw() { return HPQ == 8 ? 8 : (HPQ == 16 ? 4 : (HPQ == 32 ? 2 : 1)); }
+
+// Row r of row tile rt (A operand) -> (query within wave, head slot).
+template <int HPQ>
+__device__ __forceinline__ void row_map(int rt, int r, int& qw, int& hs) {
+  if constexpr (HPQ == 8) {
+    qw = rt * 4 + (r >> 4) + 2 * ((r >> 2) & 1);
+    hs = ((r >> 3) & 1) * 4 + (r & 3);
+  } else if constexpr (HPQ == 16) {
+    qw = rt * 2 + ((r >> 2) & 1);
+    hs = 4 * (r >> 3) + (r & 3);
+  } else if constexpr (HPQ == 32) {
+    qw = rt;
+    hs = r;
+  } else {
+    qw = 0;
+    hs = 32 * rt + r;
+  }
+}
+
+// Score slots per lane: how many (query) sums a lane forms per column tile.
+template <int HPQ>
+constexpr int nslots() { return HPQ == 8 ? 4 : (HPQ == 16 ? 2 : (HPQ == 32 ? 2 : 1)); }
+
+// Slot -> query within wave for a lane in half hf.
+template <int HPQ>
+__device__ __forceinline__ int slot_query(int slot, int hf) {
+  if constexpr (HPQ == 8) return (slot >> 1) * 4 + 2 * hf + (slot & 1);
+  else if constexpr (HPQ == 16) return slot * 2 + hf;
+  else if constexpr (HPQ == 32) return slot;
+  else return 0;
+}
+
+struct PrefillArgs {
+  const void* q;
+  const float* q_scale;
+  const float* w;
+  const void* k;
+  const float* k_scale;
+  const int32_t* heads;  // [batch*T, nh] or nullptr (all heads)
+  int32_t nh;            // heads scored per query
+  int32_t L, T, H, k_top;
+  int32_t S;             // key splits
+  int64_t chunk;         // keys per split
+  int32_t cap;           // candidate slots per (query, split)
+  int32_t nqt;           // query tiles per sequence
+  int32_t batch;
+  uint2* cand;           // [rows*S*cap] (score bits, token)
+  int32_t* cnt;          // [rows*S]
+  float* tau;            // [rows*S]
+};
+
+template <int DT, int HPQ>
+__global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs a) {
+  constexpr int QPW = qpw<HPQ>();
+  constexpr int QWG = QPW * kPWaves;
+  constexpr int NS = nslots<HPQ>();
+  constexpr int RB = lds_row_bytes<DT>();
+  constexpr int TILE_BYTES = kTileKeys * RB;
+  constexpr int SAMPLE_BYTES = kPWaves * QPW * kSamples * 4;
+  constexpr int STAGE_BYTES = 32 * RB;  // one 32-key sample tile, after the sample area
+  constexpr int LDS_BYTES = (2 * TILE_BYTES > SAMPLE_BYTES + STAGE_BYTES) ? 2 * TILE_BYTES
+                                                                          : SAMPLE_BYTES + STAGE_BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+  __shared__ float sk_tile[3][kTileKeys];  // fp8 key scales: tile buffers 0, 1 and the sample stage
+
+  // XCD-aware numbering: workgroups of one split share an XCD (id % 8).
+  const int id = blockIdx.x;
+  const int xcd = id & 7;
+  const int split = xcd % a.S;
+  const int64_t qt_global = static_cast<int64_t>(id >> 3) * (8 / a.S) + xcd / a.S;
+  if (qt_global >= static_cast<int64_t>(a.nqt) * a.batch) return;
+  const int64_t seq = qt_global / a.nqt;
+  const int t0 = static_cast<int>(qt_global % a.nqt) * QWG;
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int hf = lane >> 5;
+  const int colr = lane & 31;
+  const int tw0 = t0 + wave * QPW;  // first query of this wave
+
+  // Key range of this workgroup: its split of [0, pos_last].
+  const int t_last = min(t0 + QWG - 1, a.T - 1);
+  const int64_t pos_last = static_cast<int64_t>(a.L) - a.T + t_last;
+  const int64_t s_begin = split * a.chunk;
+  const int64_t s_end = min<int64_t>(s_begin + a.chunk, pos_last + 1);
+  const int64_t s_safe = s_end > s_begin ? s_begin : 0;  // a row every load may touch
+
+  // ---- A operand: this wave's gathered head rows, and per-lane weights.
+  bf16x8 a16[kRT][8];
+  i32x8 a8[kRT][2];
+  float wl[kRT][16];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    int qw, hs;
+    row_map<HPQ>(rt, colr, qw, hs);
+    const int t = tw0 + qw;
+    int j = -1;
+    if (t < a.T && hs < a.nh) {
+      const int64_t r = seq * a.T + t;
+      j = a.heads ? a.heads[r * a.nh + hs] : hs;
+      if (j < 0 || j >= a.H) j = -1;
+    }
+    const int64_t qrow = (seq * a.T + (t < a.T ? t : 0)) * a.H + (j < 0 ? 0 : j);
+    if constexpr (DT == kBF16) {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + qrow * kD + 64 * hf);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) a16[rt][ks] = as_bf16x8(j < 0 ? make_uint4(0, 0, 0, 0) : src[ks]);
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.q) + qrow * kD + 64 * hf);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint4 lo = j < 0 ? make_uint4(0, 0, 0, 0) : src[2 * ks];
+        const uint4 hi = j < 0 ? make_uint4(0, 0, 0, 0) : src[2 * ks + 1];
+        a8[rt][ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+    }
+    // Weights of the accumulator rows this lane holds (rows 8*(i/4)+4hf+i%4).
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      int qw2, hs2;
+      row_map<HPQ>(rt, 8 * (i / 4) + 4 * hf + (i % 4), qw2, hs2);
+      const int t2 = tw0 + qw2;
+      float wv = 0.f;
+      if (t2 < a.T && hs2 < a.nh) {
+        const int64_t r2 = seq * a.T + t2;
+        const int j2 = a.heads ? a.heads[r2 * a.nh + hs2] : hs2;
+        if (j2 >= 0 && j2 < a.H) {
+          wv = a.w[r2 * a.H + j2];
+          if constexpr (DT == kFP8) wv *= a.q_scale[r2];
+        }
+      }
+      wl[rt][i] = wv;
+    }
+  }
+
+  // Scores of one staged 32-key column tile: out[slot] for this lane's column.
+  auto score_tile = [&](const uint8_t* tile, int c, float (&out)[NS]) {
+    f32x16 acc[kRT];
+    const uint8_t* brow = tile + (32 * c + colr) * RB;
+    if constexpr (DT == kBF16) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4*>(brow + 128 * hf + 16 * ks));
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt)
+          acc[rt] = mfma32_bf16(a16[rt][ks], b, ks == 0 ? f32x16{} : acc[rt]);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(brow + 64 * hf + 32 * ks);
+        const uint4 hi = *reinterpret_cast<const uint4*>(brow + 64 * hf + 32 * ks + 16);
+        const i32x8 b{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt)
+          acc[rt] = mfma32_fp8(a8[rt][ks], b, ks == 0 ? f32x16{} : acc[rt]);
+      }
+    }
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) out[sl] = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float v = wl[rt][i] * relu(acc[rt][i]);
+        if constexpr (HPQ == 8) out[rt * 2 + (i >> 3)] += v;
+        else if constexpr (HPQ == 16) out[rt] += v;
+        else if constexpr (HPQ == 32) out[rt] += v;
+        else out[0] += v;
+      }
+    if constexpr (HPQ >= 32) {
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) out[sl] += __shfl_xor(out[sl], 32, kWave);
+    }
+  };
+
+  // Stage keys into an LDS tile: 64 keys, thread t takes key t/4, quarter t%4.
+  // key_of(i) gives the key index of tile row i (or -1: zero row).
+  // Rows past the range load a clamped (valid) row: their scores are masked.
+  auto load_tile_regs = [&](auto key_of, uint4 (&reg)[DT == kBF16 ? 4 : 2], float& skr) {
+    const int kr = threadIdx.x >> 2;
+    const int qd = threadIdx.x & 3;
+    const int64_t key = key_of(kr);
+    const int64_t row = seq * a.L + (key < 0 ? s_safe : key);
+    if constexpr (DT == kBF16) {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + row * kD + 32 * qd);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) reg[u] = src[u];
+      skr = 1.f;
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.k) + row * kD + 32 * qd);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) reg[u] = src[u];
+      skr = a.k_scale[row];
+    }
+  };
+  auto store_tile = [&](uint8_t* tile, int buf, const uint4 (&reg)[DT == kBF16 ? 4 : 2], float skr) {
+    const int kr = threadIdx.x >> 2;
+    const int qd = threadIdx.x & 3;
+    uint4* dst = reinterpret_cast<uint4*>(tile + kr * RB + (DT == kBF16 ? 64 : 32) * qd);
+#pragma unroll
+    for (int u = 0; u < (DT == kBF16 ? 4 : 2); ++u) dst[u] = reg[u];
+    if constexpr (DT == kFP8) {
+      if (qd == 0) sk_tile[buf][kr] = skr;
+    }
+  };
+
+  // Query positions of this lane's slots (and of the wave's queries).
+  int64_t pos_slot[NS];
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) {
+    const int t = tw0 + slot_query<HPQ>(sl, hf);
+    pos_slot[sl] = t < a.T ? static_cast<int64_t>(a.L) - a.T + t : -1;
+  }
+
+  // ---- 1. sample pass: thresholds per (query, split).
+  const int64_t len = s_end - s_begin;
+  float* smp = reinterpret_cast<float*>(lds) + wave * QPW * kSamples;  // [QPW][kSamples]
+  float tau_slot[NS];
+  // Sample tiles (32 keys) are staged after the sample area; each tile's
+  // scores go straight to the sample area (sample m of query qw at
+  // smp[qw][m]).  The main pass later reuses all of it for its tile buffers.
+  {
+    uint8_t* stage = lds + SAMPLE_BYTES;
+    const int kr = threadIdx.x >> 3;  // 8 threads per key row
+    const int part = threadIdx.x & 7;
+    for (int st = 0; st < kSamples / 32; ++st) {
+      const int m_ld = st * 32 + kr;
+      const int64_t key_ld = len > 0 ? s_begin + (static_cast<int64_t>(m_ld) * len) / kSamples : -1;
+      if constexpr (DT == kBF16) {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) +
+                                                          (seq * a.L + (key_ld < 0 ? 0 : key_ld)) * kD + 16 * part);
+        const uint4 v0 = key_ld < 0 ? make_uint4(0, 0, 0, 0) : src[0];
+        const uint4 v1 = key_ld < 0 ? make_uint4(0, 0, 0, 0) : src[1];
+        __syncthreads();
+        uint4* dst = reinterpret_cast<uint4*>(stage + kr * RB + 32 * part);
+        dst[0] = v0;
+        dst[1] = v1;
+      } else {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.k) +
+                                                          (seq * a.L + (key_ld < 0 ? 0 : key_ld)) * kD + 16 * part);
+        const uint4 v0 = key_ld < 0 ? make_uint4(0, 0, 0, 0) : src[0];
+        const float skr = (key_ld >= 0 && part == 0) ? a.k_scale[seq * a.L + key_ld] : 1.f;
+        __syncthreads();
+        *reinterpret_cast<uint4*>(stage + kr * RB + 16 * part) = v0;
+        if (part == 0) sk_tile[2][kr] = skr;
+      }
+      __syncthreads();
+      float out[NS];
+      score_tile(stage, 0, out);
+      const int m = st * 32 + colr;
+      const int64_t key = len > 0 ? s_begin + (static_cast<int64_t>(m) * len) / kSamples : -1;
+      float skv = 1.f;
+      if constexpr (DT == kFP8) skv = sk_tile[2][colr];
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) {
+        const bool ok = key >= 0 && key <= pos_slot[sl];
+        const int qw = slot_query<HPQ>(sl, hf);
+        if (HPQ < 32 || hf == 0) smp[qw * kSamples + m] = ok ? out[sl] * skv : -__builtin_inff();
+      }
+    }
+    __syncthreads();
+  }
+  {
+    // Lanes [g*LPQ, (g+1)*LPQ) find the j-th largest sample of query g:
+    // bitwise search for the largest key v with #{samples >= v} >= j.
+    constexpr int LPQ = kWave / QPW;
+    constexpr int VPL = kSamples / LPQ;
+    const int g = lane / LPQ;
+    const int lg = lane % LPQ;
+    uint32_t kv[VPL];
+    int nvs = 0;
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) {
+      const float v = smp[g * kSamples + lg * VPL + e];
+      kv[e] = float_key(v);
+      nvs += (v != -__builtin_inff()) ? 1 : 0;
+    }
+#pragma unroll
+    for (int o = LPQ / 2; o >= 1; o >>= 1) nvs += __shfl_xor(nvs, o, kWave);
+    const int t = tw0 + g;
+    const int64_t nq = static_cast<int64_t>(a.L) - a.T + t + 1;
+    // j = ceil(margin * k * nvs / n_q)
+    const double jd = static_cast<double>(kSampleMargin) * a.k_top * nvs / static_cast<double>(nq > 0 ? nq : 1);
+    const int j = static_cast<int>(jd) + 1;
+    // Padding queries (t >= T) never pass; a query whose split holds fewer
+    // sampled keys than j keeps every key of the split (tau = -inf).
+    float tq = t < a.T ? -__builtin_inff() : __builtin_inff();
+    if (t < a.T && nvs > 0 && j < nvs) {
+      uint32_t v = 0;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = v | (1u << bit);
+        int c = 0;
+#pragma unroll
+        for (int e = 0; e < VPL; ++e) c += kv[e] >= cand ? 1 : 0;
+#pragma unroll
+        for (int o = LPQ / 2; o >= 1; o >>= 1) c += __shfl_xor(c, o, kWave);
+        if (c >= j) v = cand;
+      }
+      // Back from key to float (inverse of float_key; v is a sample's key).
+      const uint32_t u = (v & 0x80000000u) ? (v & 0x7FFFFFFFu) : ~v;
+      tq = __uint_as_float(u);
+    }
+    // Broadcast: every lane needs the tau of its slots' queries.
+    float tau_q[QPW];
+#pragma unroll
+    for (int qq = 0; qq < QPW; ++qq) tau_q[qq] = __shfl(tq, qq * LPQ, kWave);
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl) {
+      const int qw0 = slot_query<HPQ>(sl, 0), qw1 = slot_query<HPQ>(sl, 1);
+      tau_slot[sl] = hf ? tau_q[qw1] : tau_q[qw0];
+    }
+    if (lg == 0 && t < a.T) a.tau[(seq * a.T + t) * a.S + split] = tq;
+  }
+  __syncthreads();  // sample area is reused as tile buffers below
+
+  // ---- 2. full pass over [s_begin, s_end): append scores >= tau.
+  // Candidate counts per (slot, half): (sl, h) is query slot_query(sl, h) --
+  // a bijection onto the wave's queries for h = 8, 16 (only h = 0 is used
+  // for 32, 64).  Wave-uniform values; a lane picks its half with one select.
+  int ctr2[NS][2];
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) ctr2[sl][0] = ctr2[sl][1] = 0;
+  // This lane's candidate segment per slot (its half's query).
+  uint2* segp[NS];
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) {
+    const int t = tw0 + slot_query<HPQ>(sl, hf);
+    segp[sl] = a.cand + ((seq * a.T + (t < a.T ? t : 0)) * a.S + split) * a.cap;
+  }
+  // Keys below the wave's first query position are in every slot's prefix.
+  const int64_t pos_wave_min = static_cast<int64_t>(a.L) - a.T + tw0;
+  const uint64_t half_mask = hf ? 0xFFFFFFFF00000000ull : 0x00000000FFFFFFFFull;
+  const int64_t ntiles = len > 0 ? (len + kTileKeys - 1) / kTileKeys : 0;
+  uint4 reg[DT == kBF16 ? 4 : 2];
+  float skr = 1.f;
+  auto key_at = [&](int64_t tile_idx) {
+    return [=](int i) -> int64_t {
+      const int64_t key = s_begin + tile_idx * kTileKeys + i;
+      return key < s_end ? key : -1;
+    };
+  };
+  if (ntiles > 0) {
+    load_tile_regs(key_at(0), reg, skr);
+    store_tile(lds, 0, reg, skr);
+  }
+  __syncthreads();
+  for (int64_t ti = 0; ti < ntiles; ++ti) {
+    const int buf = static_cast<int>(ti & 1);
+    uint8_t* tile = lds + buf * TILE_BYTES;
+    if (ti + 1 < ntiles) load_tile_regs(key_at(ti + 1), reg, skr);
+    const int64_t tbase = s_begin + ti * kTileKeys;
+    // Wave-uniform: no causal / range check needed inside this tile.
+    const bool interior = tbase + kTileKeys <= s_end && tbase + kTileKeys - 1 <= pos_wave_min;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float out[NS];
+      score_tile(tile, c, out);
+      const int64_t key = tbase + 32 * c + colr;
+      float skv = 1.f;
+      if constexpr (DT == kFP8) skv = sk_tile[buf][32 * c + colr];
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) {
+        const float v = out[sl] * skv;
+        const bool owner = HPQ < 32 || hf == 0;
+        bool pass = owner && v >= tau_slot[sl];
+        if (!interior) pass = pass && key < s_end && key <= pos_slot[sl];
+        const uint64_t m = __ballot(pass);
+        if (m == 0) continue;
+        if (pass) {
+          const int p = (hf ? ctr2[sl][1] : ctr2[sl][0]) + lanes_below(m & half_mask);
+          if (p < a.cap) segp[sl][p] = make_uint2(__float_as_uint(v), static_cast<uint32_t>(key));
+        }
+        ctr2[sl][0] += __popcll(m & 0x00000000FFFFFFFFull);
+        ctr2[sl][1] += __popcll(m >> 32);
+      }
+    }
+    if (ti + 1 < ntiles) store_tile(lds + (buf ^ 1) * TILE_BYTES, buf ^ 1, reg, skr);
+    __syncthreads();
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (HPQ >= 32 && h == 1) continue;
+        const int t = tw0 + slot_query<HPQ>(sl, h);
+        if (t < a.T) a.cnt[(seq * a.T + t) * a.S + split] = ctr2[sl][h];
+      }
+  }
+}
+
+__global__ void prefill_clear_kernel(int32_t* fail_count) {
+  if (threadIdx.x == 0) *fail_count = 0;
+}
+
+// Top-k of query r's candidates; queues the query for repair when the
+// candidates cannot be shown to hold the true top-k.  The S segments are
+// viewed as one compact list: entry c lies in segment s with
+// pre[s] <= c < pre[s+1] (S <= 8 compares, no division).
+__global__ __launch_bounds__(kTopkThreadsSel) void prefill_select_kernel(
+    const uint2* __restrict__ cand, const int32_t* __restrict__ cnt, const float* __restrict__ tau,
+    int32_t S, int32_t cap, int32_t L, int32_t T, int32_t k, int32_t* __restrict__ idx,
+    float* __restrict__ scores_out, int32_t* __restrict__ fail_count,
+    int32_t* __restrict__ fail_list) {
+  __shared__ TopkFastSmem sm;
+  __shared__ int s_pre[9];
+  __shared__ float s_tau_max;
+  __shared__ int s_flag;
+  const int64_t r = blockIdx.x;
+  if (threadIdx.x == 0) {
+    int bad = 0, total = 0;
+    float tm = -__builtin_inff();
+    for (int s = 0; s < 8; ++s) {
+      s_pre[s] = total;
+      if (s < S) {
+        const int c = cnt[r * S + s];
+        bad |= c > cap;
+        total += c < cap ? c : cap;
+        tm = fmaxf(tm, tau[r * S + s]);
+      }
+    }
+    s_pre[8] = total;
+    s_tau_max = tm;
+    // Fewer than k candidates is fine only when nothing was filtered out.
+    s_flag = bad ? 1 : ((total < k && tm != -__builtin_inff()) ? 1 : 0);
+  }
+  __syncthreads();
+  const uint2* cr = cand + r * S * cap;
+  int pre[9];
+#pragma unroll
+  for (int u = 0; u < 9; ++u) pre[u] = s_pre[u];
+  const int C = pre[8];
+  auto addr = [=](int64_t c) -> int64_t {
+    const int ci = static_cast<int>(c);
+    int sg = 0, base = 0;
+#pragma unroll
+    for (int u = 1; u < 8; ++u) {
+      const bool ge = ci >= pre[u] && u < S;
+      sg = ge ? u : sg;
+      base = ge ? pre[u] : base;
+    }
+    return static_cast<int64_t>(sg) * cap + (ci - base);
+  };
+  if (s_flag) {
+    if (threadIdx.x == 0) fail_list[atomicAdd(fail_count, 1)] = static_cast<int32_t>(r);
+    return;
+  }
+  // Certificate: at least k candidates score >= max tau (gate); else repair.
+  const bool ok = block_topk_fast<kTopkThreadsSel>(
+      C, k, [](int64_t) { return true; }, [=](int64_t c) { return __uint_as_float(cr[addr(c)].x); },
+      [=](int64_t c) { return static_cast<int32_t>(cr[addr(c)].y); }, idx + r * k,
+      scores_out ? scores_out + r * k : nullptr, sm, s_tau_max);
+  if (!ok && threadIdx.x == 0) fail_list[atomicAdd(fail_count, 1)] = static_cast<int32_t>(r);
+}
+
+// Repair: queries whose candidates could not be certified are scored over
+// their whole prefix (16x16 MFMA key streaming) into this workgroup's scratch
+// row and selected from it.  The grid is fixed; each workgroup walks the
+// queue with stride gridDim.x and exits when it is exhausted.
+template <int DT, int NRT>
+__global__ __launch_bounds__(kRepThreads) void prefill_repair_kernel(
+    const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const void* __restrict__ k, const float* __restrict__ k_scale,
+    const int32_t* __restrict__ heads, int32_t nh, int32_t L, int32_t T, int32_t H, int32_t k_top,
+    const int32_t* __restrict__ fail_count, const int32_t* __restrict__ fail_list,
+    float* __restrict__ scratch, int32_t* __restrict__ idx, float* __restrict__ scores_out) {
+  __shared__ TopkFastSmem sm;
+  constexpr int NW = kRepThreads / kWave;
+  const int nfail = *fail_count;
+  float* row = scratch + static_cast<int64_t>(blockIdx.x) * L;
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  for (int f = blockIdx.x; f < nfail; f += gridDim.x) {
+    const int64_t r = fail_list[f];
+    const int64_t seq = r / T;
+    const int64_t n = static_cast<int64_t>(L) - T + (r % T) + 1;
+    RowScorer<DT, NRT> sc;
+    sc.init(q, q_scale, w, heads, nh, r, H);
+    const void* krows = (DT == kBF16) ? static_cast<const void*>(static_cast<const uint16_t*>(k) + seq * L * kD)
+                                      : static_cast<const void*>(static_cast<const uint8_t*>(k) + seq * L * kD);
+    for (int64_t s0 = static_cast<int64_t>(wave) * 64; s0 < n; s0 += NW * 64) {
+      const float res = sc.score64(krows, s0, n, 0);
+      const int64_t s = s0 + lane;
+      if (s < n) {
+        float v = res;
+        if constexpr (DT == kFP8) v *= k_scale[seq * L + s];
+        row[s] = v;
+      }
+    }
+    __syncthreads();
+    block_topk_fast<kRepThreads>(
+        n, k_top, [](int64_t) { return true; }, [=](int64_t i) { return row[i]; },
+        [](int64_t i) { return static_cast<int32_t>(i); }, idx + r * k_top,
+        scores_out ? scores_out + r * k_top : nullptr, sm);
+    __syncthreads();
+  }
+}
+
+struct PrefillPlan {
+  int32_t S, cap, nqt, qwg;
+  int64_t chunk;
+  size_t off_cnt, off_tau, off_fail, off_list, off_scratch, total;
+};
+
+int32_t qwg_for(int32_t nh) {
+  const int hpq = nh <= 8 ? 8 : (nh <= 16 ? 16 : (nh <= 32 ? 32 : 64));
+  return (hpq == 8 ? 8 : hpq == 16 ? 4 : hpq == 32 ? 2 : 1) * kPWaves;
+}
+
+PrefillPlan plan_prefill(const Shape& s, int32_t nh, int32_t k) {
+  PrefillPlan p{};
+  p.qwg = qwg_for(nh);
+  p.nqt = (s.T + p.qwg - 1) / p.qwg;
+  const int64_t tiles = static_cast<int64_t>(p.nqt) * s.batch;
+  int S = 1;
+  while (S < 8 && tiles * S < 512 && s.L / (2 * S) >= 2048) S *= 2;
+  p.S = S;
+  p.chunk = ((static_cast<int64_t>(s.L) + S - 1) / S + kTileKeys - 1) / kTileKeys * kTileKeys;
+  // Expected survivors per segment ~ 2.5k/S with a relative spread of about
+  // 1/sqrt(j) (j ~ 20 at the smallest sample quantile): 8k/S + 1024 leaves
+  // >10 sigma before a segment overflows.
+  const int64_t want = (8LL * k + S - 1) / S + 1024;
+  int64_t cap = want < p.chunk ? want : p.chunk;
+  cap = (cap + 63) / 64 * 64;
+  p.cap = static_cast<int32_t>(cap);
+  const int64_t rows = static_cast<int64_t>(s.batch) * s.T;
+  size_t off = align_up(static_cast<size_t>(rows) * S * cap * sizeof(uint2));
+  p.off_cnt = off;
+  off += align_up(static_cast<size_t>(rows) * S * sizeof(int32_t));
+  p.off_tau = off;
+  off += align_up(static_cast<size_t>(rows) * S * sizeof(float));
+  p.off_fail = off;
+  off += 256;
+  p.off_list = off;
+  off += align_up(static_cast<size_t>(rows) * sizeof(int32_t));
+  p.off_scratch = off;
+  off += align_up(static_cast<size_t>(kRepairSlots) * s.L * sizeof(float));
+  p.total = off;
+  return p;
+}
+
+template <int DT, int HPQ>
+void launch_prefill_dt(const Shape& s, const PrefillPlan& pl, PrefillArgs args, hipStream_t st) {
+  const int64_t tiles = static_cast<int64_t>(pl.nqt) * s.batch;
+  const int per8 = 8 / pl.S;
+  const int64_t nblocks = (tiles + per8 - 1) / per8 * 8;
+  prefill_score_kernel<DT, HPQ><<<static_cast<unsigned>(nblocks), kPThreads, 0, st>>>(args);
+}
+
+}  // namespace
+
+bool prefill_supported(const Shape& s) { return s.T > 1 && s.dtype != kF32; }
+
+size_t prefill_ws_bytes(const Shape& s, int32_t nh, int32_t k) {
+  return plan_prefill(s, nh, k).total;
+}
+
+hipError_t launch_prefill_score_topk(const Shape& s, int32_t nh, const int32_t* heads, int32_t k,
+                                     const void* q, const float* q_scale, const float* w,
+                                     const void* kk, const float* k_scale, int32_t* idx,
+                                     float* scores_out, void* ws, hipStream_t st) {
+  const PrefillPlan pl = plan_prefill(s, nh, k);
+  char* base = static_cast<char*>(ws);
+  PrefillArgs args{q, q_scale, w, kk, k_scale, heads, nh, s.L, s.T, s.H, k, pl.S, pl.chunk,
+                   pl.cap, pl.nqt, s.batch, reinterpret_cast<uint2*>(base),
+                   reinterpret_cast<int32_t*>(base + pl.off_cnt),
+                   reinterpret_cast<float*>(base + pl.off_tau)};
+  int32_t* fail_count = reinterpret_cast<int32_t*>(base + pl.off_fail);
+  int32_t* fail_list = reinterpret_cast<int32_t*>(base + pl.off_list);
+  float* scratch = reinterpret_cast<float*>(base + pl.off_scratch);
+  prefill_clear_kernel<<<1, 64, 0, st>>>(fail_count);
+  const int hpq = nh <= 8 ? 8 : (nh <= 16 ? 16 : (nh <= 32 ? 32 : 64));
+#define PF(DT) \
+  if (hpq == 8) launch_prefill_dt<DT, 8>(s, pl, args, st); \
+  else if (hpq == 16) launch_prefill_dt<DT, 16>(s, pl, args, st); \
+  else if (hpq == 32) launch_prefill_dt<DT, 32>(s, pl, args, st); \
+  else launch_prefill_dt<DT, 64>(s, pl, args, st);
+  if (s.dtype == kBF16) { PF(kBF16) } else { PF(kFP8) }
+#undef PF
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows = static_cast<int64_t>(s.batch) * s.T;
+  prefill_select_kernel<<<static_cast<unsigned>(rows), kTopkThreadsSel, 0, st>>>(
+      args.cand, args.cnt, args.tau, pl.S, pl.cap, s.L, s.T, k, idx, scores_out, fail_count,
+      fail_list);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nrt = nh <= 16 ? 1 : (nh <= 32 ? 2 : 4);
+#define RP(DT, NRT) prefill_repair_kernel<DT, NRT><<<kRepairSlots, kRepThreads, 0, st>>>(q, q_scale, w, kk, k_scale, heads, nh, s.L, s.T, s.H, k, fail_count, fail_list, scratch, idx, scores_out)
+  if (s.dtype == kBF16) {
+    if (nrt == 1) RP(kBF16, 1); else if (nrt == 2) RP(kBF16, 2); else RP(kBF16, 4);
+  } else {
+    if (nrt == 1) RP(kFP8, 1); else if (nrt == 2) RP(kFP8, 2); else RP(kFP8, 4);
+  }
+#undef RP
+  return hipGetLastError();
+}
+
+}  // namespace misa

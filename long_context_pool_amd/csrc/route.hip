@@ -110,7 +110,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 
 }  // namespace
 
-size_t route_ws_bytes(const Shape& s) { return s.T == 1 ? route_decode_ws_bytes(s) : 0; }
+size_t route_ws_bytes(const Shape& s) {
+  if (s.T == 1) return route_decode_ws_bytes(s);
+  return route_mfma_supported(s) ? route_mfma_ws_bytes(s) : 0;
+}
 
 hipError_t launch_route(const Shape& s, int32_t h, const void* q, const float* q_scale,
                         const float* w, const float* pooled, const void* k, const float* k_scale,
@@ -118,7 +121,7 @@ hipError_t launch_route(const Shape& s, int32_t h, const void* q, const float* q
   if (s.T == 1)
     return launch_route_decode(s, h, q, q_scale, w, pooled, k, k_scale, heads, E_out, ws, st);
   if (route_mfma_supported(s))
-    return launch_route_mfma(s, h, q, q_scale, w, pooled, k, k_scale, heads, E_out, st);
+    return launch_route_mfma(s, h, q, q_scale, w, pooled, k, k_scale, heads, E_out, ws, st);
   dim3 grid(s.T, s.batch);
   switch (s.dtype) {
     case kF32:

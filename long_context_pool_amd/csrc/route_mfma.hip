@@ -85,25 +85,6 @@ __device__ __forceinline__ void split_bf16(float4 x, uint32_t& h0, uint32_t& h1,
        (f32_to_bf16_bits(x.w - __uint_as_float(d << 16)) << 16);
 }
 
-// B operand of pooled block `b` (fp32 row -> bf16 hi [+ lo]), elements
-// [64hf, 64hf+64).
-template <bool SPLIT>
-__device__ __forceinline__ void load_pooled_b(const float* prow, bool ok, bf16x8 (&bh)[8],
-                                              bf16x8 (&bl)[8]) {
-  const int hf = lane_id() >> 5;
-  const float4* src = reinterpret_cast<const float4*>(prow + 64 * hf);
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    const float4 x0 = ok ? src[2 * ks] : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 x1 = ok ? src[2 * ks + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
-    uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
-    split_bf16(x0, h0, h1, l0, l1);
-    split_bf16(x1, h2, h3, l2, l3);
-    bh[ks] = as_bf16x8(make_uint4(h0, h1, h2, h3));
-    if constexpr (SPLIT) bl[ks] = as_bf16x8(make_uint4(l0, l1, l2, l3));
-  }
-}
-
 // acc (rows x 32 blocks) = A . (B_hi [+ B_lo]); rs += ReLU(acc) when col_ok.
 // The hi and lo products of every row tile go to separate accumulators so the
 // MFMA chains are independent.
@@ -128,7 +109,7 @@ __device__ __forceinline__ void accumulate_tile(const bf16x8 (&a)[RT][8], const 
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) rs[rt][i] += fmaxf(SPLIT ? acc[rt][i] + acl[rt][i] : acc[rt][i], 0.f);
+      for (int i = 0; i < 16; ++i) rs[rt][i] += relu(SPLIT ? acc[rt][i] + acl[rt][i] : acc[rt][i]);
   }
 }
 
@@ -152,12 +133,27 @@ __device__ __forceinline__ void reduce_rows(f32x16 (&rs)[RT], float* rowsum) {
     }
 }
 
+// Pooled keys -> bf16 hi and lo (bf16 rounding of the remainder) planes,
+// [batch*M, 128] each; one thread per 4 elements.
+__global__ void pooled_split_kernel(const float* __restrict__ pooled, uint32_t* __restrict__ hi,
+                                    uint32_t* __restrict__ lo, int64_t n4) {
+  const int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (i >= n4) return;
+  const float4 x = reinterpret_cast<const float4*>(pooled)[i];
+  uint32_t h0, h1, l0, l1;
+  split_bf16(x, h0, h1, l0, l1);
+  hi[2 * i] = h0;
+  hi[2 * i + 1] = h1;
+  lo[2 * i] = l0;
+  lo[2 * i + 1] = l1;
+}
+
 template <int DT, int RT>
 __global__ __launch_bounds__(kRThreads) void route_prefill_kernel(
     const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
-    const float* __restrict__ pooled, const void* __restrict__ k, const float* __restrict__ k_scale,
-    int32_t* __restrict__ heads, float* __restrict__ E_out, int32_t L, int32_t T, int32_t H,
-    int32_t B, int64_t M, int32_t h) {
+    const uint16_t* __restrict__ phi, const uint16_t* __restrict__ plo, const void* __restrict__ k,
+    const float* __restrict__ k_scale, int32_t* __restrict__ heads, float* __restrict__ E_out,
+    int32_t L, int32_t T, int32_t H, int32_t B, int64_t M, int32_t h) {
   constexpr bool SPLIT = DT == kBF16;
   __shared__ __attribute__((aligned(16))) uint8_t tile[SPLIT ? 2 : 1][32 * kLdsRow];
   __shared__ float rowsum[kRWaves][64];
@@ -185,27 +181,31 @@ __global__ __launch_bounds__(kRThreads) void route_prefill_kernel(
   for (int rt = 0; rt < RT; ++rt) rs[rt] = f32x16{};
 
   const int64_t ntiles = (full_max + 31) / 32;
-  const int ld_row = threadIdx.x >> 3;        // 32 rows x 8 chunks of 16 floats
+  const int ld_row = threadIdx.x >> 3;  // 32 rows x 8 chunks of 32 bytes
   const int ld_chunk = threadIdx.x & 7;
   for (int64_t bt = 0; bt < ntiles; ++bt) {
     {
       const int64_t b = bt * 32 + ld_row;
       const bool ok = b < full_max;
-      const float4* src = reinterpret_cast<const float4*>(pooled + (seq * M + (ok ? b : 0)) * kD +
-                                                          16 * ld_chunk);
-      uint32_t o[8], lo[8];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float4 x = ok ? src[u] : make_float4(0.f, 0.f, 0.f, 0.f);
-        split_bf16(x, o[2 * u], o[2 * u + 1], lo[2 * u], lo[2 * u + 1]);
+      const int64_t off = (seq * M + (ok ? b : 0)) * kD + 16 * ld_chunk;
+      const uint4* sh = reinterpret_cast<const uint4*>(phi + off);
+      const uint4 h0 = ok ? sh[0] : make_uint4(0, 0, 0, 0);
+      const uint4 h1 = ok ? sh[1] : make_uint4(0, 0, 0, 0);
+      uint4 l0 = make_uint4(0, 0, 0, 0), l1 = make_uint4(0, 0, 0, 0);
+      if constexpr (SPLIT) {
+        if (ok) {
+          const uint4* sl = reinterpret_cast<const uint4*>(plo + off);
+          l0 = sl[0];
+          l1 = sl[1];
+        }
       }
       uint4* dst = reinterpret_cast<uint4*>(tile[0] + ld_row * kLdsRow + 32 * ld_chunk);
-      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+      dst[0] = h0;
+      dst[1] = h1;
       if constexpr (SPLIT) {
         uint4* dl = reinterpret_cast<uint4*>(tile[SPLIT ? 1 : 0] + ld_row * kLdsRow + 32 * ld_chunk);
-        dl[0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-        dl[1] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+        dl[0] = l0;
+        dl[1] = l1;
       }
     }
     __syncthreads();
@@ -256,12 +256,23 @@ __global__ __launch_bounds__(kRThreads) void route_prefill_kernel(
 
 bool route_mfma_supported(const Shape& s) { return s.dtype != kF32 && s.H <= 64 && s.T > 1; }
 
+size_t route_mfma_ws_bytes(const Shape& s) {
+  return 2 * align_up(static_cast<size_t>(s.batch) * s.M() * kD * sizeof(uint16_t));
+}
+
 hipError_t launch_route_mfma(const Shape& s, int32_t h, const void* q, const float* q_scale,
                              const float* w, const float* pooled, const void* k,
-                             const float* k_scale, int32_t* heads, float* E_out, hipStream_t st) {
+                             const float* k_scale, int32_t* heads, float* E_out, void* ws,
+                             hipStream_t st) {
+  const size_t plane = align_up(static_cast<size_t>(s.batch) * s.M() * kD * sizeof(uint16_t));
+  uint16_t* phi = static_cast<uint16_t*>(ws);
+  uint16_t* plo = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + plane);
+  const int64_t n4 = static_cast<int64_t>(s.batch) * s.M() * kD / 4;
+  pooled_split_kernel<<<static_cast<unsigned>((n4 + 255) / 256), 256, 0, st>>>(
+      pooled, reinterpret_cast<uint32_t*>(phi), reinterpret_cast<uint32_t*>(plo), n4);
   const bool two = s.H > 32;
   dim3 grid((s.T + kRWaves - 1) / kRWaves, s.batch);
-#define RP(DT, RT) route_prefill_kernel<DT, RT><<<grid, kRThreads, 0, st>>>(q, q_scale, w, pooled, k, k_scale, heads, E_out, s.L, s.T, s.H, s.B, s.M(), h)
+#define RP(DT, RT) route_prefill_kernel<DT, RT><<<grid, kRThreads, 0, st>>>(q, q_scale, w, phi, plo, k, k_scale, heads, E_out, s.L, s.T, s.H, s.B, s.M(), h)
   if (s.dtype == kBF16) { if (two) RP(kBF16, 2); else RP(kBF16, 1); }
   else { if (two) RP(kFP8, 2); else RP(kFP8, 1); }
 #undef RP

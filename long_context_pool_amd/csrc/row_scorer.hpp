@@ -1,0 +1,107 @@
+// Scoring one query against a stream of keys on 16x16 MFMA tiles, Eq. (9) /
+// Eq. (1) of the MISA summary page: I_s = sum_j w_j * ReLU(q_j . k_s).
+//
+// The query's scored head rows are the A operand (16-row tiles, rows past the
+// head count are zero); 16 keys form one output tile; lane l loads bytes of
+// key l%16 covering head-dim elements [32*(l/16), +32) (one contiguous run per
+// lane, the same split for A and B).  The ReLU * w head sum is taken on the
+// accumulators and finished with a 4-lane reduction.
+#pragma once
+
+#include "common.hpp"
+#include "mfma.hpp"
+
+namespace misa {
+
+template <int DT, int NRT>
+struct RowScorer {
+  bf16x8 a16[NRT][4];
+  i32x8 a8[NRT];
+  float wl[NRT][4];
+
+  // Query row r (= seq*T + t) with nh scored heads: heads[r*nh + i] (or i).
+  __device__ __forceinline__ void init(const void* q, const float* q_scale, const float* w,
+                                       const int32_t* heads, int nh, int64_t r, int H) {
+    const int lane = lane_id();
+    const int col = lane & 15;
+    const int qq = lane >> 4;
+    const float sq = (DT == kFP8) ? q_scale[r] : 1.f;
+    auto head_of = [&](int row) -> int {
+      if (row >= nh) return -1;
+      const int j = heads ? heads[r * nh + row] : row;
+      return (j >= 0 && j < H) ? j : -1;
+    };
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = head_of(rt * 16 + 4 * qq + i);
+        wl[rt][i] = (j >= 0) ? w[r * H + j] * sq : 0.f;
+      }
+      const int j = head_of(rt * 16 + col);
+      const int64_t qoff = (r * H + (j < 0 ? 0 : j)) * kD;
+      if constexpr (DT == kBF16) {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + qoff + 32 * qq);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) a16[rt][ks] = as_bf16x8(j < 0 ? make_uint4(0, 0, 0, 0) : src[ks]);
+      } else {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(q) + qoff + 32 * qq);
+        const uint4 lo = j < 0 ? make_uint4(0, 0, 0, 0) : src[0];
+        const uint4 hi = j < 0 ? make_uint4(0, 0, 0, 0) : src[1];
+        a8[rt] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+    }
+  }
+
+  // Scores of keys [s0, s0+64) of `krows` (row s at krows + s*kD elements),
+  // valid below s_end; returns the score of key s0 + lane (unscaled by the
+  // fp8 key scale).  Invalid keys score 0.
+  __device__ __forceinline__ float score64(const void* krows, int64_t s0, int64_t s_end,
+                                           int64_t s_safe) const {
+    const int lane = lane_id();
+    const int col = lane & 15;
+    const int qq = lane >> 4;
+    uint4 kb[4][DT == kBF16 ? 4 : 2];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int64_t s = s0 + 16 * g + col;
+      const bool ok = s < s_end;
+      const int64_t row = (ok ? s : s_safe) * kD;
+      if constexpr (DT == kBF16) {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(krows) + row + 32 * qq);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kb[g][ks] = ok ? src[ks] : make_uint4(0, 0, 0, 0);
+      } else {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(krows) + row + 32 * qq);
+        kb[g][0] = ok ? src[0] : make_uint4(0, 0, 0, 0);
+        kb[g][1] = ok ? src[1] : make_uint4(0, 0, 0, 0);
+      }
+    }
+    float res = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float part = 0.f;
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (DT == kBF16) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) acc = mfma16_bf16(a16[rt][ks], as_bf16x8(kb[g][ks]), acc);
+        } else {
+          const i32x8 b8{(int)kb[g][0].x, (int)kb[g][0].y, (int)kb[g][0].z, (int)kb[g][0].w,
+                         (int)kb[g][1].x, (int)kb[g][1].y, (int)kb[g][1].z, (int)kb[g][1].w};
+          acc = mfma16_fp8(a8[rt], b8, acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part += wl[rt][i] * relu(acc[i]);
+      }
+      // Sum the four lane groups holding rows 0-3, 4-7, 8-11, 12-15.
+      part += __shfl_xor(part, 16, kWave);
+      part += __shfl_xor(part, 32, kWave);
+      if (qq == g) res = part;  // lane group g keeps key group g: lane l <-> key s0 + l
+    }
+    return res;
+  }
+};
+
+}  // namespace misa

@@ -78,8 +78,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
 
 }  // namespace
 
-size_t score_ws_bytes(const Shape& s, int32_t, int32_t) {
+size_t score_ws_bytes(const Shape& s, int32_t nh, int32_t k) {
   if (s.T == 1 && s.dtype != kF32) return decode_ws_bytes(s);
+  if (prefill_supported(s)) return prefill_ws_bytes(s, nh, k);
   return align_up(static_cast<size_t>(s.batch) * s.T * s.L * sizeof(float));
 }
 
@@ -90,6 +91,9 @@ hipError_t launch_score_topk(const Shape& s, int32_t nh, const int32_t* heads, i
   if (s.T == 1 && s.dtype != kF32)
     return launch_decode_score_topk(s, nh, heads, k, q, q_scale, w, kk, k_scale, idx, scores_out,
                                     ws, st);
+  if (prefill_supported(s))
+    return launch_prefill_score_topk(s, nh, heads, k, q, q_scale, w, kk, k_scale, idx, scores_out,
+                                     ws, st);
   float* rows = static_cast<float*>(ws);
   dim3 g1((s.L + kScoreThreads - 1) / kScoreThreads, s.T, s.batch);
   switch (s.dtype) {

@@ -154,8 +154,9 @@ __device__ __forceinline__ void block_topk(int64_t n, int k, Valid valid, Key ke
 //      log-spaced in value, so a few large outliers cannot crowd all scores
 //      into a few bins.  A suffix scan gives the bin b* holding the k-th best
 //      and `above`, the count in higher bins;
-//   3. one ordered compaction (wave ballots + a scan over the waves): elements
-//      of bins above b* go straight to the output, those of b* to an LDS list;
+//   3. one compaction pass (wave ballots + LDS counters; set semantics):
+//      elements of bins above b* go straight to the output, those of b* to an
+//      LDS list;
 //   4. the b* list is resolved exactly: by pairwise rank when it is short,
 //      else by block_topk.
 // When the range is degenerate or b* holds more than kLinCap elements the
@@ -174,6 +175,7 @@ struct TopkFastSmem {
   float red[2][32];
   int wtot[2][32];
   int sel_bin, sel_above, sel_count;
+  int cnt_hi, cnt_at;
 };
 
 __device__ __forceinline__ int lin_bin(float s, uint32_t kmin, int shift) {
@@ -183,9 +185,10 @@ __device__ __forceinline__ int lin_bin(float s, uint32_t kmin, int shift) {
 }
 
 template <int NT, class Valid, class Score, class Idx>
-__device__ __forceinline__ void block_topk_fast(int64_t n, int k, Valid valid, Score score, Idx idx,
+__device__ __forceinline__ bool block_topk_fast(int64_t n, int k, Valid valid, Score score, Idx idx,
                                                 int32_t* out_idx, float* out_score,
-                                                TopkFastSmem& sm) {
+                                                TopkFastSmem& sm,
+                                                float gate = -__builtin_inff()) {
   constexpr int NW = NT / kWave;
   const int lane = lane_id();
   const int wid = threadIdx.x / kWave;
@@ -193,23 +196,31 @@ __device__ __forceinline__ void block_topk_fast(int64_t n, int k, Valid valid, S
   const int J = static_cast<int>(CW / kWave);
   const int64_t wbase = static_cast<int64_t>(wid) * CW + lane;
   const bool cached = J <= kRegCache;
-  // Register cache of this lane's elements; ok bit j marks a valid element.
+  // Register cache of this lane's elements (score, token); ok bit j marks a
+  // valid element.  Steps j >= J are skipped with wave-uniform branches.
   float rc[kRegCache];
+  int32_t ri[kRegCache];
   uint32_t okm = 0;
-  // 1. count, min, max.
-  int cnt = 0;
+  // 1. count, min, max, and the count of scores >= gate.
+  int cnt = 0, cge = 0;
   float mn = __builtin_inff(), mx = -__builtin_inff();
   if (cached) {
 #pragma unroll
     for (int j = 0; j < kRegCache; ++j) {
-      const int64_t i = wbase + 64 * j;
-      const bool ok = j < J && i < n && valid(i);
-      const float v = ok ? score(i) : 0.f;
-      rc[j] = v;
-      okm |= ok ? (1u << j) : 0u;
-      cnt += ok ? 1 : 0;
-      mn = ok ? fminf(mn, v) : mn;
-      mx = ok ? fmaxf(mx, v) : mx;
+      rc[j] = 0.f;
+      ri[j] = -1;
+      if (j < J) {
+        const int64_t i = wbase + 64 * j;
+        const bool ok = i < n && valid(i);
+        const float v = ok ? score(i) : 0.f;
+        rc[j] = v;
+        ri[j] = ok ? idx(i) : -1;
+        okm |= ok ? (1u << j) : 0u;
+        cnt += ok ? 1 : 0;
+        cge += (ok && v >= gate) ? 1 : 0;
+        mn = ok ? fminf(mn, v) : mn;
+        mx = ok ? fmaxf(mx, v) : mx;
+      }
     }
   } else {
     for (int j = 0; j < J; ++j) {
@@ -217,6 +228,7 @@ __device__ __forceinline__ void block_topk_fast(int64_t n, int k, Valid valid, S
       if (i >= n || !valid(i)) continue;
       const float v = score(i);
       ++cnt;
+      cge += v >= gate ? 1 : 0;
       mn = fminf(mn, v);
       mx = fmaxf(mx, v);
     }
@@ -224,26 +236,32 @@ __device__ __forceinline__ void block_topk_fast(int64_t n, int k, Valid valid, S
 #pragma unroll
   for (int o = kWave / 2; o >= 1; o >>= 1) {
     cnt += __shfl_xor(cnt, o, kWave);
+    cge += __shfl_xor(cge, o, kWave);
     mn = fminf(mn, __shfl_xor(mn, o, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
   }
   if (lane == 0) {
     sm.base.scan_tmp[wid] = cnt;
+    sm.wtot[0][wid] = cge;
     sm.red[0][wid] = mn;
     sm.red[1][wid] = mx;
   }
   for (int b = threadIdx.x; b < kLinBins; b += NT) sm.hist[b] = 0;
   __syncthreads();
-  int nvalid = 0;
+  int nvalid = 0, nge = 0;
   mn = __builtin_inff();
   mx = -__builtin_inff();
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
     nvalid += sm.base.scan_tmp[i];
+    nge += sm.wtot[0][i];
     mn = fminf(mn, sm.red[0][i]);
     mx = fmaxf(mx, sm.red[1][i]);
   }
   __syncthreads();
+  // Gate: the caller needs at least k valid scores >= gate (else nothing is
+  // written and false is returned).
+  if (gate != -__builtin_inff() && nge < k) return false;
   const uint32_t kmin = float_key(mn);
   const uint32_t kspan = float_key(mx) - kmin;
   // Smallest shift with (kspan >> shift) < kLinBins.
@@ -252,13 +270,13 @@ __device__ __forceinline__ void block_topk_fast(int64_t n, int k, Valid valid, S
   if (nvalid <= k || degenerate) {
     block_topk<NT>(n, k, valid, [=](int64_t i) { return float_key(score(i)); }, idx, score,
                    out_idx, out_score, sm.base);
-    return;
+    return true;
   }
-  // 2. histogram of the linear bins, then the bin holding the k-th best.
+  // 2. histogram of the key bins, then the bin holding the k-th best.
   if (cached) {
 #pragma unroll
     for (int j = 0; j < kRegCache; ++j)
-      if (okm & (1u << j)) atomicAdd(&sm.hist[lin_bin(rc[j], kmin, shift)], 1u);
+      if (j < J && (okm & (1u << j))) atomicAdd(&sm.hist[lin_bin(rc[j], kmin, shift)], 1u);
   } else {
     for (int j = 0; j < J; ++j) {
       const int64_t i = wbase + 64 * j;
@@ -286,78 +304,62 @@ __device__ __forceinline__ void block_topk_fast(int64_t n, int k, Valid valid, S
       }
       run += local[c];
     }
+    if (threadIdx.x == 0) {
+      sm.cnt_hi = 0;
+      sm.cnt_at = 0;
+    }
     __syncthreads();
   }
   const int bstar = sm.sel_bin;
   const int above = sm.sel_above;
   const int bcount = sm.sel_count;
-  __syncthreads();
   if (bcount > kLinCap) {
+    __syncthreads();
     block_topk<NT>(n, k, valid, [=](int64_t i) { return float_key(score(i)); }, idx, score,
                    out_idx, out_score, sm.base);
-    return;
+    return true;
   }
-  // 3. ordered compaction: wave totals, a scan over the waves, then per-step
-  //    ballots place each element at its index-order position.
-  int na = 0, nc = 0;
-  if (cached) {
-#pragma unroll
-    for (int j = 0; j < kRegCache; ++j) {
-      const bool ok = okm & (1u << j);
-      const int b = lin_bin(rc[j], kmin, shift);
-      na += __popcll(__ballot(ok && b > bstar));
-      nc += __popcll(__ballot(ok && b == bstar));
-    }
-  } else {
-    for (int j = 0; j < J; ++j) {
-      const int64_t i = wbase + 64 * j;
-      const bool ok = i < n && valid(i);
-      const int b = ok ? lin_bin(score(i), kmin, shift) : -1;
-      na += __popcll(__ballot(ok && b > bstar));
-      nc += __popcll(__ballot(ok && b == bstar));
-    }
-  }
-  if (lane == 0) {
-    sm.wtot[0][wid] = na;
-    sm.wtot[1][wid] = nc;
-  }
-  __syncthreads();
-  int pa = 0, pc = 0;
-  for (int u = 0; u < wid; ++u) {
-    pa += sm.wtot[0][u];
-    pc += sm.wtot[1][u];
-  }
-  auto emit = [&](int64_t i, bool ok, float v) {
+  // 3. compaction: bins above b* -> output, bin b* -> LDS list.  Positions
+  //    come from wave ballots and two LDS counters (set semantics).
+  auto emit = [&](bool ok, float v, int32_t id) {
     const int b = ok ? lin_bin(v, kmin, shift) : -1;
-    const uint64_t mh = __ballot(b > bstar);
-    const uint64_t mc = __ballot(b == bstar);
-    if (b > bstar) {
-      const int p = pa + lanes_below(mh);
-      if (p < k) {
-        out_idx[p] = idx(i);
-        if (out_score) out_score[p] = v;
-      }
-    } else if (b == bstar) {
-      const int p = pc + lanes_below(mc);
-      if (p < kLinCap) {
-        sm.cand_score[p] = v;
-        sm.cand_idx[p] = idx(i);
+    const bool hi = b > bstar, at = b == bstar;
+    const uint64_t mh = __ballot(hi);
+    const uint64_t ma = __ballot(at);
+    if (mh) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&sm.cnt_hi, __popcll(mh));
+      base = __shfl(base, 0, kWave);
+      if (hi) {
+        const int p = base + lanes_below(mh);
+        if (p < k) {
+          out_idx[p] = id;
+          if (out_score) out_score[p] = v;
+        }
       }
     }
-    pa += __popcll(mh);
-    pc += __popcll(mc);
+    if (ma) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&sm.cnt_at, __popcll(ma));
+      base = __shfl(base, 0, kWave);
+      if (at) {
+        const int p = base + lanes_below(ma);
+        if (p < kLinCap) {
+          sm.cand_score[p] = v;
+          sm.cand_idx[p] = id;
+        }
+      }
+    }
   };
   if (cached) {
 #pragma unroll
-    for (int j = 0; j < kRegCache; ++j) {
-      const bool ok = okm & (1u << j);
-      emit(wbase + 64 * j, ok, rc[j]);
-    }
+    for (int j = 0; j < kRegCache; ++j)
+      if (j < J) emit((okm >> j) & 1u, rc[j], ri[j]);
   } else {
     for (int j = 0; j < J; ++j) {
       const int64_t i = wbase + 64 * j;
       const bool ok = i < n && valid(i);
-      emit(i, ok, ok ? score(i) : 0.f);
+      emit(ok, ok ? score(i) : 0.f, ok ? idx(i) : -1);
     }
   }
   __syncthreads();
@@ -381,7 +383,7 @@ __device__ __forceinline__ void block_topk_fast(int64_t n, int k, Valid valid, S
         if (out_score) out_score[above + rank] = sm.cand_score[threadIdx.x];
       }
     }
-    return;
+    return true;
   }
   const float* cs = sm.cand_score;
   const int32_t* ci = sm.cand_idx;
@@ -389,6 +391,7 @@ __device__ __forceinline__ void block_topk_fast(int64_t n, int k, Valid valid, S
       bcount, need, [](int64_t) { return true; }, [=](int64_t j) { return float_key(cs[j]); },
       [=](int64_t j) { return ci[j]; }, [=](int64_t j) { return cs[j]; }, out_idx + above,
       out_score ? out_score + above : nullptr, sm.base);
+  return true;
 }
 
 }  // namespace misa

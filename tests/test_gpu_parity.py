@@ -149,11 +149,16 @@ def test_repeat_runs_are_bit_identical():
     x = synth.generate(p)
     a = parity.run_gpu(x)
     b = parity.run_gpu(x)
-    for key in a:
-        if key in ("idx", "d_idx", "cand", "r_idx"):
-            assert (np.sort(a[key], axis=-1) == np.sort(b[key], axis=-1)).all(), key
-        else:
-            np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+    # Selections are sets: the slot order may differ, the (token, score) pairs may not.
+    pairs = {"idx": "scores", "d_idx": "d_scores", "cand": "cand_scores", "r_idx": "r_scores"}
+    for key, skey in pairs.items():
+        oa, ob = np.argsort(a[key], axis=-1), np.argsort(b[key], axis=-1)
+        np.testing.assert_array_equal(np.take_along_axis(a[key], oa, -1),
+                                      np.take_along_axis(b[key], ob, -1), err_msg=key)
+        np.testing.assert_array_equal(np.take_along_axis(a[skey], oa, -1),
+                                      np.take_along_axis(b[skey], ob, -1), err_msg=skey)
+    for key in ("pooled", "heads", "E"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
 
 
 def test_pool_range_updates_only_its_blocks():
