@@ -3,8 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
 
 A step is one pass of the hot path over one batch of synthetic input:
-  decode (T = 1): refresh the pooled key of the block holding the newest token
-                  (the pooled-key cache update) -> route -> routed score + top-k
+  decode (T = 1): misa_decode_step -- refresh the pooled key of the block
+                  holding the newest token (the pooled-key cache update),
+                  route, routed score + top-k in two kernels
                   [-> rerank when the workload has k'];
   prefill:        pool all keys -> route -> routed score + top-k [-> rerank].
 The dense DSA indexer (all heads, same library) is timed the same way for the
@@ -52,8 +53,10 @@ def parse():
     ap.add_argument("--workload", default="c2", help="c1..c5 (default c2, the decode workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="approximate CPU work budget of the oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate wall time of the oracle baseline")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="after timing, copy BYTES device-to-device (profiler counter calibration)")
     return ap.parse_args()
 
 
@@ -94,21 +97,27 @@ class Runner:
 
     def misa_step(self, i, ev=None):
         """One MISA pass on input set i; ev = (before, after) events around the
-        routed score + top-k call."""
+        dominant call (decode: misa_decode_step; prefill: the routed score +
+        top-k)."""
         m, p, s, st = self.misa, self.p, self.sets[i % len(self.sets)], self.stream
+        out = self.cand if p.kprime else self.idx
         if self.decode:
-            m.misa_pool_keys_range(self.shp, p.M - 1, 1, s["k"], s["ks"], s["pooled"], st)
+            if ev:
+                ev[0].record(st)
+            m.misa_decode_step(self.shp, p.h, p.kprime or p.k, s["q"], s["qs"], s["w"], s["pooled"],
+                               s["k"], s["ks"], self.heads, None, out, None, self.ws, st)
+            if ev:
+                ev[1].record(st)
         else:
             m.misa_pool_keys(self.shp, s["k"], s["ks"], s["pooled"], st)
-        m.misa_route(self.shp, p.h, s["q"], s["qs"], s["w"], s["pooled"], s["k"], s["ks"],
-                     self.heads, None, self.ws, st)
-        out = self.cand if p.kprime else self.idx
-        if ev:
-            ev[0].record(st)
-        m.misa_score_topk(self.shp, p.h, p.kprime or p.k, s["q"], s["qs"], s["w"], s["k"], s["ks"],
-                          self.heads, out, None, self.ws, st)
-        if ev:
-            ev[1].record(st)
+            m.misa_route(self.shp, p.h, s["q"], s["qs"], s["w"], s["pooled"], s["k"], s["ks"],
+                         self.heads, None, self.ws, st)
+            if ev:
+                ev[0].record(st)
+            m.misa_score_topk(self.shp, p.h, p.kprime or p.k, s["q"], s["qs"], s["w"], s["k"],
+                              s["ks"], self.heads, out, None, self.ws, st)
+            if ev:
+                ev[1].record(st)
         if p.kprime:
             m.misa_rerank(self.shp, p.kprime, p.k, s["q"], s["qs"], s["w"], s["k"], s["ks"],
                           self.cand, self.idx, None, self.ws, st)
@@ -149,7 +158,9 @@ def time_steps(fn, steps, warmup, stream):
 
 def cpu_baseline(x, budget_s):
     """The oracle as it stands, on a bounded sample of the same workload,
-    over a thread pool of host cores (ctypes releases the GIL)."""
+    over a thread pool of host cores (ctypes releases the GIL).  The sample
+    (every sequence of a decode batch, or 32 evenly spaced queries of a
+    prefill) is run in whole passes until about budget_s seconds have gone."""
     import concurrent.futures
 
     import numpy as np
@@ -164,12 +175,6 @@ def cpu_baseline(x, budget_s):
         sample = [(b, 0) for b in range(p.batch)]
     else:
         sample = [(0, int(t)) for t in np.linspace(0, p.T - 1, 32).round()]
-    # Per-query cost model to bound the sample at about budget_s of CPU work.
-    n_avg = p.L
-    mac_per_q = p.h * p.d * n_avg + p.H * p.d * p.M
-    est_s_per_q = mac_per_q / 1.5e8
-    max_q = max(cores, int(budget_s * cores / max(est_s_per_q, 1e-6)))
-    sample = sample[:max_q]
     seqs = {}
     qraw = x.raw_numpy("q")
     for b in sorted({b for b, _ in sample}):
@@ -193,11 +198,18 @@ def cpu_baseline(x, budget_s):
             oracle.rerank(seqs[b].K, q, w, r["idx"], p.k)
         return pos + 1
 
+    pairs, passes = 0, 0
     with concurrent.futures.ThreadPoolExecutor(cores) as ex:
         t0 = time.perf_counter()
-        pairs = sum(ex.map(one, sample))
-        dt = time.perf_counter() - t0
-    desc = f"{len(sample)} queries ({'all sequences' if p.T == 1 else 'evenly spaced'}) of the workload"
+        while True:
+            pairs += sum(ex.map(one, sample))
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= budget_s:
+                break
+    desc = (f"{passes} pass(es) over {len(sample)} queries "
+            f"({'every sequence' if p.T == 1 else 'evenly spaced'}) of the workload: "
+            f"route + routed score + top-k{' + rerank' if p.kprime else ''}")
     return {"value": pairs / dt, "unit": "pairs/s", "cores": cores, "kind": "oracle",
             "sample": desc, "seconds": round(dt, 3)}
 
@@ -259,22 +271,37 @@ def main():
     sha = source_sha()
     kp = p.kprime or p.k
     if p.T == 1:
-        # Decode: the routed score + top-k call streams every key once.
-        alg_bytes = p.batch * p.L * p.d * e + p.batch * p.h * p.d * e + p.batch * p.H * 4 \
-            + p.batch * kp * 4
+        # Decode step: every key (and fp8 key scale), the pooled-key cache, the
+        # query heads and w are read once; the k' (or k) indices are written.
+        per_seq = (p.L * p.d * e + (p.L * 4 if e == 1 else 0) + p.M * p.d * 4 + p.H * p.d * e
+                   + p.H * 4 + kp * 4)
+        alg_bytes = p.batch * per_seq
         achieved = alg_bytes / (m_call * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "kernel": "misa_score_topk",
+                "frac": achieved / HBM_PEAK_GBS,
+                "kernel": "misa_decode_step (step_route_kernel + decode_score_kernel)",
                 "algorithmic_bytes": alg_bytes,
-                "traffic": traffic_from_profile("misa_score_topk", args.workload, sha)}
+                "traffic": traffic_from_profile("misa_decode_step", args.workload, sha)}
     else:
         flops = 2 * p.h * p.d * pairs
         achieved = flops / (m_call * 1e-3) / 1e12
         peak = MFMA_PEAK_TFLOPS[dtype]
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                "frac": achieved / peak, "kernel": "misa_score_topk", "algorithmic_flops": flops,
+                "frac": achieved / peak,
+                "kernel": "misa_score_topk (prefill_clear + prefill_score + prefill_select + prefill_repair)",
+                "algorithmic_flops": flops,
                 "traffic": traffic_from_profile("misa_score_topk", args.workload, sha)}
     roof["call_ms"] = m_call
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy // 16 * 16
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -135,6 +135,24 @@ misa_status misa_rerank(const misa_shape* shape, int32_t kprime, int32_t k, cons
                         const int32_t* cand, int32_t* idx, float* scores_out, void* ws,
                         size_t ws_bytes, hipStream_t stream);
 
+/* One decode step of MISA (T = 1; bf16 or fp8 only): Eq. (4) for the block
+ * holding the newest key, then Eq. (7)-(8) and Eq. (9)-(10) -- the results of
+ *   misa_pool_keys_range(shape, M-1, 1, ...); misa_route(...); misa_score_topk(...)
+ * in two kernel launches.
+ *   pooled   [batch, M, d]  fp32, read and written: blocks 0 .. M-2 must hold
+ *            their Eq. (4) means (the cache kept by misa_pool_keys); block
+ *            M-1 (keys (M-1)*B .. L-1, possibly partial) is recomputed from k
+ *            and written.
+ *   heads    [batch, h]     int32, written (ascending)
+ *   E_out    [batch, H]     fp32, written if non-NULL
+ *   idx, scores_out [batch, k] as misa_score_topk.
+ * Other arguments and layouts as misa_route and misa_score_topk.  T != 1 or
+ * fp32 inputs return MISA_ERR_UNSUPPORTED. */
+misa_status misa_decode_step(const misa_shape* shape, int32_t h, int32_t k, const void* q,
+                             const float* q_scale, const float* w, float* pooled, const void* kk,
+                             const float* k_scale, int32_t* heads, float* E_out, int32_t* idx,
+                             float* scores_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Eq. (1)-(2), the dense DSA indexer baseline: Eq. (9)-(10) with every head
  * j < H, no router.  Layouts as misa_score_topk. */
 misa_status dsa_index_dense(const misa_shape* shape, int32_t k, const void* q,

@@ -29,7 +29,8 @@ MISA_F32, MISA_BF16, MISA_FP8_E4M3 = 0, 1, 2
 
 EXPORTED = (
     "misa_workspace_bytes", "misa_pool_keys", "misa_pool_keys_range", "misa_route",
-    "misa_score_topk", "misa_rerank", "dsa_index_dense", "misa_status_string",
+    "misa_score_topk", "misa_decode_step", "misa_rerank", "dsa_index_dense",
+    "misa_status_string",
 )
 
 
@@ -61,10 +62,11 @@ _lib.misa_pool_keys.argtypes = [_SHP, _P, _P, _P, _P]
 _lib.misa_pool_keys_range.argtypes = [_SHP, _I32, _I32, _P, _P, _P, _P]
 _lib.misa_route.argtypes = [_SHP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.misa_score_topk.argtypes = [_SHP, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.misa_decode_step.argtypes = [_SHP, _I32, _I32] + [_P] * 11 + [_SZ, _P]
 _lib.misa_rerank.argtypes = [_SHP, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.dsa_index_dense.argtypes = [_SHP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
 for _f in ("misa_pool_keys", "misa_pool_keys_range", "misa_route", "misa_score_topk",
-           "misa_rerank", "dsa_index_dense"):
+           "misa_decode_step", "misa_rerank", "dsa_index_dense"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.misa_status_string.argtypes = [ctypes.c_int]
 _lib.misa_status_string.restype = ctypes.c_char_p
@@ -138,6 +140,14 @@ def misa_score_topk(shp, h, k, q, q_scale, w, kk, k_scale, heads, idx, scores_ou
                                 _ptr(kk), _ptr(k_scale), _ptr(heads), _ptr(idx),
                                 _ptr(scores_out), _ptr(ws), _nbytes(ws), _stream(stream)),
            "misa_score_topk")
+
+
+def misa_decode_step(shp, h, k, q, q_scale, w, pooled, kk, k_scale, heads, E_out, idx,
+                     scores_out, ws, stream=None):
+    _check(_lib.misa_decode_step(ctypes.byref(shp), h, k, _ptr(q), _ptr(q_scale), _ptr(w),
+                                 _ptr(pooled), _ptr(kk), _ptr(k_scale), _ptr(heads), _ptr(E_out),
+                                 _ptr(idx), _ptr(scores_out), _ptr(ws), _nbytes(ws),
+                                 _stream(stream)), "misa_decode_step")
 
 
 def misa_rerank(shp, kprime, k, q, q_scale, w, kk, k_scale, cand, idx, scores_out, ws,

@@ -82,6 +82,7 @@ size_t misa_workspace_bytes(const misa_shape* shape, int32_t h, int32_t k, int32
   need = std::max(need, misa::score_ws_bytes(s, std::max<int32_t>(h, 1), kp));
   need = std::max(need, misa::score_ws_bytes(s, s.H, kp));
   need = std::max(need, misa::rerank_ws_bytes(s, kp));
+  if (s.T == 1 && s.dtype != MISA_F32) need = std::max(need, misa::decode_ws_bytes(s));
   return need;
 }
 
@@ -142,6 +143,27 @@ misa_status misa_score_topk(const misa_shape* shape, int32_t h, int32_t k, const
   if (s.batch > 65535 || s.T > 65535) return MISA_ERR_UNSUPPORTED;
   return from_hip(misa::launch_score_topk(s, h, heads, k, q, q_scale, w, kk, k_scale, idx,
                                           scores_out, ws, stream));
+}
+
+misa_status misa_decode_step(const misa_shape* shape, int32_t h, int32_t k, const void* q,
+                             const float* q_scale, const float* w, float* pooled, const void* kk,
+                             const float* k_scale, int32_t* heads, float* E_out, int32_t* idx,
+                             float* scores_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  MISA_TRY(check_shape(shape, s));
+  if (h < 1 || h > s.H) return MISA_ERR_INVALID_ARG;
+  if (h > kMaxRouted || s.T != 1 || s.dtype == MISA_F32) return MISA_ERR_UNSUPPORTED;
+  MISA_TRY(check_topk(k));
+  MISA_TRY(check_inputs(s, q, q_scale, w, kk, k_scale));
+  MISA_TRY(check_out(pooled, true));
+  MISA_TRY(check_out(heads, true));
+  MISA_TRY(check_out(E_out, false));
+  MISA_TRY(check_out(idx, true));
+  MISA_TRY(check_out(scores_out, false));
+  MISA_TRY(check_ws(ws, ws_bytes, misa::decode_ws_bytes(s)));
+  if (s.batch > 65535) return MISA_ERR_UNSUPPORTED;
+  return from_hip(misa::launch_decode_step(s, h, k, q, q_scale, w, pooled, kk, k_scale, heads,
+                                           E_out, idx, scores_out, ws, stream));
 }
 
 misa_status dsa_index_dense(const misa_shape* shape, int32_t k, const void* q,

@@ -54,6 +54,14 @@ hipError_t launch_decode_score_topk(const Shape& s, int32_t nh, const int32_t* h
                                     const void* kk, const float* k_scale, int32_t* idx,
                                     float* scores_out, void* ws, hipStream_t st);
 
+// Fused decode step (T == 1, bf16/fp8): refresh the pooled key of the block
+// holding key L-1, route (E, top-h) and score + top-k; two kernels.  ws must
+// hold decode_ws_bytes(s).
+hipError_t launch_decode_step(const Shape& s, int32_t h, int32_t k, const void* q,
+                              const float* q_scale, const float* w, float* pooled, const void* kk,
+                              const float* k_scale, int32_t* heads, float* E_out, int32_t* idx,
+                              float* scores_out, void* ws, hipStream_t st);
+
 // Prefill (T > 1, bf16/fp8) token scoring + top-k on 32x32 MFMA tiles with
 // sampled thresholds, certified candidate selection and a repair path.
 bool prefill_supported(const Shape& s);

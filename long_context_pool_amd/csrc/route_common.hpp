@@ -5,6 +5,57 @@
 
 namespace misa {
 
+// One head row of q (kD elements from element offset `off`) widened to fp32
+// in registers with 16-byte loads; fp8 codes are not scaled.
+template <int DT>
+__device__ __forceinline__ void load_head_row(const void* q, int64_t off, float (&qr)[kD]) {
+  if constexpr (DT == kF32) {
+    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(q) + off);
+#pragma unroll
+    for (int u = 0; u < kD / 4; ++u) {
+      const float4 v = src[u];
+      qr[4 * u] = v.x; qr[4 * u + 1] = v.y; qr[4 * u + 2] = v.z; qr[4 * u + 3] = v.w;
+    }
+  } else if constexpr (DT == kBF16) {
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + off);
+#pragma unroll
+    for (int u = 0; u < kD / 8; ++u) {
+      const uint4 v = src[u];
+      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qr[8 * u + 2 * e] = __uint_as_float(wd[e] << 16);
+        qr[8 * u + 2 * e + 1] = __uint_as_float(wd[e] & 0xFFFF0000u);
+      }
+    }
+  } else {
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(q) + off);
+#pragma unroll
+    for (int u = 0; u < kD / 16; ++u) {
+      const uint4 v = src[u];
+      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) qr[16 * u + e] = fp8_to_f32((wd[e / 4] >> (8 * (e % 4))) & 0xFF);
+    }
+  }
+}
+
+// q . p for a register row qr and an LDS row p (kD floats, broadcast reads),
+// in four interleaved partial sums so the FMAs do not form one serial chain.
+__device__ __forceinline__ float dot_lds_row(const float (&qr)[kD], const float* p) {
+  const float4* pb = reinterpret_cast<const float4*>(p);
+  float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+#pragma unroll
+  for (int i = 0; i < kD / 4; ++i) {
+    const float4 v = pb[i];
+    d0 = fmaf(qr[4 * i], v.x, d0);
+    d1 = fmaf(qr[4 * i + 1], v.y, d1);
+    d2 = fmaf(qr[4 * i + 2], v.z, d2);
+    d3 = fmaf(qr[4 * i + 3], v.w, d3);
+  }
+  return (d0 + d1) + (d2 + d3);
+}
+
 // Top-h of Eq. (8) by one wave: lane j < H holds E_j (>= 0); h rounds of a
 // wave arg-max (ties to the lower head) mark the winners, which are written
 // to heads[0..h) in ascending head order.

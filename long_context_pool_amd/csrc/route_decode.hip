@@ -43,51 +43,10 @@ __global__ __launch_bounds__(kRDThreads) void route_decode_partial_kernel(
   }
   // This thread's head row in registers (vector loads, widened to fp32).
   float qr[kD];
-  const int jj = j < H ? j : 0;
-  if constexpr (DT == kF32) {
-    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(q) + (seq * H + jj) * kD);
-#pragma unroll
-    for (int u = 0; u < kD / 4; ++u) {
-      const float4 v = src[u];
-      qr[4 * u] = v.x; qr[4 * u + 1] = v.y; qr[4 * u + 2] = v.z; qr[4 * u + 3] = v.w;
-    }
-  } else if constexpr (DT == kBF16) {
-    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + (seq * H + jj) * kD);
-#pragma unroll
-    for (int u = 0; u < kD / 8; ++u) {
-      const uint4 v = src[u];
-      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qr[8 * u + 2 * e] = __uint_as_float(wd[e] << 16);
-        qr[8 * u + 2 * e + 1] = __uint_as_float(wd[e] & 0xFFFF0000u);
-      }
-    }
-  } else {
-    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(q) + (seq * H + jj) * kD);
-#pragma unroll
-    for (int u = 0; u < kD / 16; ++u) {
-      const uint4 v = src[u];
-      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 16; ++e) qr[16 * u + e] = fp8_to_f32((wd[e / 4] >> (8 * (e % 4))) & 0xFF);
-    }
-  }
+  load_head_row<DT>(q, (seq * H + (j < H ? j : 0)) * kD, qr);
   __syncthreads();
   float acc = 0.f;
-  for (int b = sub; b < nb; b += kRDThreads / kMaxH) {
-    const float4* pb = reinterpret_cast<const float4*>(&ps[b][0]);
-    float dot = 0.f;
-#pragma unroll
-    for (int i = 0; i < kD / 4; ++i) {
-      const float4 v = pb[i];
-      dot = fmaf(qr[4 * i], v.x, dot);
-      dot = fmaf(qr[4 * i + 1], v.y, dot);
-      dot = fmaf(qr[4 * i + 2], v.z, dot);
-      dot = fmaf(qr[4 * i + 3], v.w, dot);
-    }
-    acc += fmaxf(dot, 0.f);
-  }
+  for (int b = sub; b < nb; b += kRDThreads / kMaxH) acc += relu(dot_lds_row(qr, &ps[b][0]));
   red[sub][j] = acc;
   __syncthreads();
   if (threadIdx.x < kMaxH) {

@@ -2,10 +2,14 @@
 // Eq. (1) of the MISA summary page: I_s = sum_j w_j * ReLU(q_j . k_s).
 //
 // The query's scored head rows are the A operand (16-row tiles, rows past the
-// head count are zero); 16 keys form one output tile; lane l loads bytes of
-// key l%16 covering head-dim elements [32*(l/16), +32) (one contiguous run per
-// lane, the same split for A and B).  The ReLU * w head sum is taken on the
-// accumulators and finished with a 4-lane reduction.
+// head count are zero); 16 keys form one output tile.  A row (d = 128) is cut
+// into 16-byte pieces; in load step i, lane group g = l/16 of lane l takes
+// piece 4*i + g of key l%16, so each load instruction reads 64 contiguous
+// bytes of each of 16 keys (measured faster than one contiguous 64-byte run
+// per lane).  The MFMA k index is therefore a permutation of the head
+// dimension, the same for A and B, which leaves every dot product unchanged.
+// The ReLU * w head sum is taken on the accumulators and finished with a
+// 4-lane reduction.
 #pragma once
 
 #include "common.hpp"
@@ -19,16 +23,19 @@ struct RowScorer {
   i32x8 a8[NRT];
   float wl[NRT][4];
 
-  // Query row r (= seq*T + t) with nh scored heads: heads[r*nh + i] (or i).
+  // Query row r (= seq*T + t) with nh scored heads: heads[hr*nh + i] (or i
+  // when heads is null); hr < 0 means hr = r.
   __device__ __forceinline__ void init(const void* q, const float* q_scale, const float* w,
-                                       const int32_t* heads, int nh, int64_t r, int H) {
+                                       const int32_t* heads, int nh, int64_t r, int H,
+                                       int64_t hr = -1) {
+    if (hr < 0) hr = r;
     const int lane = lane_id();
     const int col = lane & 15;
     const int qq = lane >> 4;
     const float sq = (DT == kFP8) ? q_scale[r] : 1.f;
     auto head_of = [&](int row) -> int {
       if (row >= nh) return -1;
-      const int j = heads ? heads[r * nh + row] : row;
+      const int j = heads ? heads[hr * nh + row] : row;
       return (j >= 0 && j < H) ? j : -1;
     };
 #pragma unroll
@@ -41,13 +48,13 @@ struct RowScorer {
       const int j = head_of(rt * 16 + col);
       const int64_t qoff = (r * H + (j < 0 ? 0 : j)) * kD;
       if constexpr (DT == kBF16) {
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + qoff + 32 * qq);
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + qoff);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) a16[rt][ks] = as_bf16x8(j < 0 ? make_uint4(0, 0, 0, 0) : src[ks]);
+        for (int ks = 0; ks < 4; ++ks) a16[rt][ks] = as_bf16x8(j < 0 ? make_uint4(0, 0, 0, 0) : src[4 * ks + qq]);
       } else {
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(q) + qoff + 32 * qq);
-        const uint4 lo = j < 0 ? make_uint4(0, 0, 0, 0) : src[0];
-        const uint4 hi = j < 0 ? make_uint4(0, 0, 0, 0) : src[1];
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(q) + qoff);
+        const uint4 lo = j < 0 ? make_uint4(0, 0, 0, 0) : src[qq];
+        const uint4 hi = j < 0 ? make_uint4(0, 0, 0, 0) : src[4 + qq];
         a8[rt] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
     }
@@ -68,13 +75,13 @@ struct RowScorer {
       const bool ok = s < s_end;
       const int64_t row = (ok ? s : s_safe) * kD;
       if constexpr (DT == kBF16) {
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(krows) + row + 32 * qq);
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(krows) + row);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kb[g][ks] = ok ? src[ks] : make_uint4(0, 0, 0, 0);
+        for (int ks = 0; ks < 4; ++ks) kb[g][ks] = ok ? src[4 * ks + qq] : make_uint4(0, 0, 0, 0);
       } else {
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(krows) + row + 32 * qq);
-        kb[g][0] = ok ? src[0] : make_uint4(0, 0, 0, 0);
-        kb[g][1] = ok ? src[1] : make_uint4(0, 0, 0, 0);
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(krows) + row);
+        kb[g][0] = ok ? src[qq] : make_uint4(0, 0, 0, 0);
+        kb[g][1] = ok ? src[4 + qq] : make_uint4(0, 0, 0, 0);
       }
     }
     float res = 0.f;

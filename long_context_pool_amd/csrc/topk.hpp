@@ -139,6 +139,141 @@ __device__ __forceinline__ void block_topk(int64_t n, int k, Valid valid, Key ke
   }
 }
 
+// ---------------------------------------------------------------- list resolve
+//
+// The `need` best of a short LDS list (score, token), written to out[0..need)
+// in any order (ties: lower token first).  Up to kDirectRank entries are ranked
+// pairwise; a longer list is cut once more by a 2048-bin histogram over its
+// own key range (the bin is monotone in the score): entries of bins above the
+// threshold bin are written directly, the threshold bin is ranked pairwise.
+// Returns false (nothing written) when even that bin exceeds kRankMax; the
+// caller then falls back to block_topk.  All threads must call.
+
+constexpr int kRankMax = 256;
+constexpr int kDirectRank = 64;  // longer lists take the histogram cut first
+constexpr int kResolveBins = 2048;
+
+struct ResolveSmem {
+  uint32_t hist[kResolveBins];
+  alignas(16) float s2[kRankMax];
+  alignas(16) int32_t i2[kRankMax];
+  int scan_tmp[32];
+  int bin, above, count, n_hi, n_at;
+  uint32_t kmin, kmax;
+};
+
+// Entry t of the list is ranked by how many entries beat it: larger key, or
+// equal key and lower token (one 64-bit compare of key:~token).  The list is
+// read four entries at a time (cs and ci 16-byte aligned, with capacity a
+// multiple of 4; entries past n are masked).
+__device__ __forceinline__ uint64_t rank_key(float s, int32_t id) {
+  return (static_cast<uint64_t>(float_key(s)) << 32) | static_cast<uint32_t>(~id);
+}
+
+template <int NT>
+__device__ __forceinline__ void rank_write(const float* cs, const int32_t* ci, int n, int need,
+                                           int32_t* out_idx, float* out_score) {
+  const float4* cs4 = reinterpret_cast<const float4*>(cs);
+  const int4* ci4 = reinterpret_cast<const int4*>(ci);
+  for (int t = threadIdx.x; t < n; t += NT) {
+    const uint64_t me = rank_key(cs[t], ci[t]);
+    int rank = 0;
+    for (int j0 = 0; j0 < n; j0 += 4) {
+      const float4 c = cs4[j0 / 4];
+      const int4 d = ci4[j0 / 4];
+      rank += (j0 + 0 < n && rank_key(c.x, d.x) > me) ? 1 : 0;
+      rank += (j0 + 1 < n && rank_key(c.y, d.y) > me) ? 1 : 0;
+      rank += (j0 + 2 < n && rank_key(c.z, d.z) > me) ? 1 : 0;
+      rank += (j0 + 3 < n && rank_key(c.w, d.w) > me) ? 1 : 0;
+    }
+    if (rank < need) {
+      out_idx[rank] = ci[t];
+      if (out_score) out_score[rank] = cs[t];
+    }
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ bool resolve_list(const float* cs, const int32_t* ci, int n, int need,
+                                             int32_t* out_idx, float* out_score, ResolveSmem& rs) {
+  // Every slot gets one rank when the tokens are distinct; -1 guards the rest.
+  for (int p = threadIdx.x; p < need; p += NT) out_idx[p] = -1;
+  if (n <= kDirectRank) {
+    __syncthreads();
+    rank_write<NT>(cs, ci, n, need, out_idx, out_score);
+    return true;
+  }
+  if (threadIdx.x == 0) {
+    rs.kmin = 0xFFFFFFFFu;
+    rs.kmax = 0;
+    rs.n_hi = 0;
+    rs.n_at = 0;
+  }
+  for (int b = threadIdx.x; b < kResolveBins; b += NT) rs.hist[b] = 0;
+  __syncthreads();
+  uint32_t lo = 0xFFFFFFFFu, hi = 0;
+  for (int t = threadIdx.x; t < n; t += NT) {
+    const uint32_t key = float_key(cs[t]);
+    lo = min(lo, key);
+    hi = max(hi, key);
+  }
+  atomicMin(&rs.kmin, lo);
+  atomicMax(&rs.kmax, hi);
+  __syncthreads();
+  const uint32_t kmin = rs.kmin, span = rs.kmax - rs.kmin;
+  const int shift = span < static_cast<uint32_t>(kResolveBins) ? 0 : 32 - __clz(span) - 11;
+  for (int t = threadIdx.x; t < n; t += NT)
+    atomicAdd(&rs.hist[(float_key(cs[t]) - kmin) >> shift], 1u);
+  __syncthreads();
+  {
+    constexpr int BPT = (kResolveBins + NT - 1) / NT;
+    int local[BPT];
+    int lsum = 0;
+#pragma unroll
+    for (int c = 0; c < BPT; ++c) {
+      const int bin = kResolveBins - 1 - (threadIdx.x * BPT + c);
+      local[c] = bin >= 0 ? static_cast<int>(rs.hist[bin]) : 0;
+      lsum += local[c];
+    }
+    int total;
+    int run = block_exclusive_sum<NT>(lsum, rs.scan_tmp, total);
+#pragma unroll
+    for (int c = 0; c < BPT; ++c) {
+      const int bin = kResolveBins - 1 - (threadIdx.x * BPT + c);
+      if (bin >= 0 && run < need && run + local[c] >= need) {
+        rs.bin = bin;
+        rs.above = run;
+        rs.count = local[c];
+      }
+      run += local[c];
+    }
+    __syncthreads();
+  }
+  const uint32_t b2 = static_cast<uint32_t>(rs.bin);
+  const int above = rs.above, cnt2 = rs.count;
+  if (cnt2 > kRankMax) return false;
+  for (int t = threadIdx.x; t < n; t += NT) {
+    const uint32_t bin = (float_key(cs[t]) - kmin) >> shift;
+    if (bin > b2) {
+      const int p = atomicAdd(&rs.n_hi, 1);
+      if (p < above) {
+        out_idx[p] = ci[t];
+        if (out_score) out_score[p] = cs[t];
+      }
+    } else if (bin == b2) {
+      const int p = atomicAdd(&rs.n_at, 1);
+      if (p < kRankMax) {
+        rs.s2[p] = cs[t];
+        rs.i2[p] = ci[t];
+      }
+    }
+  }
+  __syncthreads();
+  rank_write<NT>(rs.s2, rs.i2, cnt2, need - above, out_idx + above,
+                 out_score ? out_score + above : nullptr);
+  return true;
+}
+
 // ---------------------------------------------------------------- fast path
 //
 // Same contract as block_topk, for scores held as fp32.  Wave w owns the
@@ -165,13 +300,13 @@ __device__ __forceinline__ void block_topk(int64_t n, int k, Valid valid, Key ke
 constexpr int kLinBins = 4096;
 constexpr int kLinCap = 4096;
 constexpr int kRegCache = 32;
-constexpr int kRankMax = 256;
 
 struct TopkFastSmem {
   TopkSmem base;
+  ResolveSmem rs;
   uint32_t hist[kLinBins];
-  float cand_score[kLinCap];
-  int32_t cand_idx[kLinCap];
+  alignas(16) float cand_score[kLinCap];
+  alignas(16) int32_t cand_idx[kLinCap];
   float red[2][32];
   int wtot[2][32];
   int sel_bin, sel_above, sel_count;
@@ -365,28 +500,12 @@ __device__ __forceinline__ bool block_topk_fast(int64_t n, int k, Valid valid, S
   __syncthreads();
   // 4. the (k - above) best of the b* list, written after the `above` slots.
   const int need = k - above;
-  if (bcount <= kRankMax) {
-    // Every slot of [above, k) receives exactly one rank (ranks are distinct
-    // for distinct token ids); prefill guards against duplicated ids.
-    for (int p = above + threadIdx.x; p < k; p += NT) out_idx[p] = -1;
-    __syncthreads();
-    if (threadIdx.x < bcount) {
-      const uint32_t key = float_key(sm.cand_score[threadIdx.x]);
-      const int32_t id = sm.cand_idx[threadIdx.x];
-      int rank = 0;
-      for (int j = 0; j < bcount; ++j) {
-        const uint32_t kj = float_key(sm.cand_score[j]);
-        rank += (kj > key || (kj == key && sm.cand_idx[j] < id)) ? 1 : 0;
-      }
-      if (rank < need) {
-        out_idx[above + rank] = id;
-        if (out_score) out_score[above + rank] = sm.cand_score[threadIdx.x];
-      }
-    }
-    return true;
-  }
   const float* cs = sm.cand_score;
   const int32_t* ci = sm.cand_idx;
+  if (resolve_list<NT>(cs, ci, bcount, need, out_idx + above,
+                       out_score ? out_score + above : nullptr, sm.rs))
+    return true;
+  __syncthreads();
   block_topk<NT>(
       bcount, need, [](int64_t) { return true; }, [=](int64_t j) { return float_key(cs[j]); },
       [=](int64_t j) { return ci[j]; }, [=](int64_t j) { return cs[j]; }, out_idx + above,

@@ -1,0 +1,132 @@
+"""Summarise rocprofv3 CSV output into the short text files kept under profiles/.
+
+    python -m long_context_pool_amd.profsum stats  <rocprof_dir> <out.md> --cmd "<command>"
+    python -m long_context_pool_amd.profsum traffic <fetch_dir> <write_dir> <kernel_regex> \
+        <copy_bytes> <workload> <out.json> --cmd "<command>"
+
+`stats` lists every kernel of a --kernel-trace --stats run (calls, average
+and median duration).  `traffic` turns two --pmc runs (FETCH_SIZE, then
+WRITE_SIZE; KiB per dispatch) into HBM bytes per launch of the matching
+kernel, each scaled by what the same counter reads for a device copy of
+`copy_bytes` bytes (the __amd_rocclr_copyBuffer dispatch of the same run),
+and records the source hash of the kernels it was measured on.
+
+This module only reads profiler output; it needs neither a GPU nor the
+HIP library.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import statistics
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "long_context_pool_amd", "csrc")
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _find(d: str, suffix: str) -> str:
+    hits = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return max(hits, key=os.path.getmtime)  # the newest run
+
+
+def short_name(name: str) -> str:
+    name = name.replace("misa::(anonymous namespace)::", "").replace("void ", "")
+    name = re.sub(r"\(.*", "", name)
+    return name.strip()
+
+
+def stats(d: str, out: str, cmd: str) -> None:
+    rows = list(csv.DictReader(open(_find(d, "kernel_trace.csv"))))
+    per = {}
+    for r in rows:
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        per.setdefault(short_name(r["Kernel_Name"]), []).append(dur)
+    lines = ["# rocprofv3 kernel statistics", "", f"Command: `{cmd}`", "",
+             f"Kernels measured on the source tree with hash `{source_sha()}`.", "",
+             "| kernel | calls | average us | median us | min us |", "|---|---|---|---|---|"]
+    for k, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{k}` | {len(v)} | {statistics.mean(v):.1f} | {statistics.median(v):.1f} | "
+                     f"{min(v):.1f} |")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def _counter(d: str, counter: str):
+    rows = list(csv.DictReader(open(_find(d, "counter_collection.csv"))))
+    out = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def traffic(fetch_dir: str, write_dir: str, regex: str, copy_bytes: int, workload: str, out: str,
+            cmd: str) -> None:
+    res = {"workload": workload, "kernel_regex": regex, "source_sha": source_sha(), "command": cmd,
+           "copy_bytes": copy_bytes}
+    total = 0.0
+    for name, counter, d in (("fetch", "FETCH_SIZE", fetch_dir), ("write", "WRITE_SIZE", write_dir)):
+        vals = _counter(d, counter)
+        # The calibration copy is the largest copyBuffer dispatch of the run.
+        copies = [v for k, vs in vals.items() if "copyBuffer" in k for v in vs]
+        kerns = {short_name(k): vs for k, vs in vals.items() if re.search(regex, k)}
+        if not copies or not kerns:
+            raise RuntimeError(f"{counter}: missing copy ({len(copies)}) or kernel ({len(kerns)}) dispatches")
+        copy = max(copies)
+        # A copy of copy_bytes reads and writes copy_bytes: counter KiB -> bytes factor.
+        factor = copy_bytes / (copy * 1024.0)
+        # One launch of the timed call = one dispatch of each matching kernel.
+        kib = sum(statistics.median(v) for v in kerns.values())
+        per_launch = kib * 1024.0 * factor
+        res[name] = {"kernels": {k: statistics.median(v) for k, v in kerns.items()},
+                     "counter_kib_per_launch": kib, "copy_counter_kib": copy, "scale": factor,
+                     "bytes_per_launch": per_launch}
+        total += per_launch
+    res["bytes_per_launch"] = total
+    with open(out, "w") as fh:
+        json.dump(res, fh, indent=1)
+        fh.write("\n")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd_name", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("dir")
+    a.add_argument("out")
+    a.add_argument("--cmd", required=True)
+    b = sub.add_parser("traffic")
+    b.add_argument("fetch_dir")
+    b.add_argument("write_dir")
+    b.add_argument("regex")
+    b.add_argument("copy_bytes", type=int)
+    b.add_argument("workload")
+    b.add_argument("out")
+    b.add_argument("--cmd", required=True)
+    args = ap.parse_args()
+    if args.cmd_name == "stats":
+        stats(args.dir, args.out, args.cmd)
+    else:
+        traffic(args.fetch_dir, args.write_dir, args.regex, args.copy_bytes, args.workload, args.out,
+                args.cmd)
+
+
+if __name__ == "__main__":
+    main()

@@ -69,9 +69,13 @@ class OracleProblem:
 # ------------------------------------------------------------------ GPU run
 
 
-def run_gpu(x: synth.Inputs, stages=("pool", "route", "score", "dense", "dagger"), h=None, k=None,
-            kprime=None, device="cuda:0"):
-    """Run the requested stages through the C ABI; returns numpy outputs."""
+def run_gpu(x: synth.Inputs, stages=("pool", "route", "score", "dense", "dagger", "step"), h=None,
+            k=None, kprime=None, device="cuda:0"):
+    """Run the requested stages through the C ABI; returns numpy outputs.
+
+    "step" (decode problems with bf16/fp8 inputs only) runs misa_decode_step
+    on a copy of the pooled cache whose last block was overwritten, so the
+    step must rebuild it; its outputs carry the prefix "s_"."""
     import torch
 
     import long_context_pool_amd as misa
@@ -115,8 +119,24 @@ def run_gpu(x: synth.Inputs, stages=("pool", "route", "score", "dense", "dagger"
         sc = torch.empty((p.batch, p.T, k), dtype=torch.float32, device=dev)
         misa.misa_rerank(shp, kprime, k, q, qs, w, kk, ks, cand, idx, sc, ws)
         out["cand"], out["cand_scores"], out["r_idx"], out["r_scores"] = cand, csc, idx, sc
+    if "step" in stages and p.T == 1 and p.dtype != synth.F32:
+        sp = pooled.clone()
+        sp[:, p.M - 1].fill_(7.0)
+        heads = torch.empty((p.batch, 1, h), dtype=torch.int32, device=dev)
+        E = torch.empty((p.batch, 1, p.H), dtype=torch.float32, device=dev)
+        idx = torch.empty((p.batch, 1, k), dtype=torch.int32, device=dev)
+        sc = torch.empty((p.batch, 1, k), dtype=torch.float32, device=dev)
+        misa.misa_decode_step(shp, h, k, q, qs, w, sp, kk, ks, heads, E, idx, sc, ws)
+        out["s_pooled"], out["s_heads"], out["s_E"], out["s_idx"], out["s_scores"] = (
+            sp, heads, E, idx, sc)
     torch.cuda.synchronize()
     return {name: v.cpu().numpy() for name, v in out.items()}
+
+
+def step_view(gpu: dict) -> dict:
+    """The misa_decode_step outputs under the names check_query_misa reads."""
+    return {"E": gpu["s_E"], "heads": gpu["s_heads"], "idx": gpu["s_idx"],
+            "scores": gpu["s_scores"]}
 
 
 # ------------------------------------------------------------------ comparators

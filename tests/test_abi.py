@@ -101,3 +101,31 @@ def test_fp8_requires_scales_and_rerank_requires_kprime_ge_k():
     assert st == misa.MISA_ERR_INVALID_ARG
     st = lib.misa_pool_keys_range(ctypes.byref(shp), 10, 7, FAKE, None, FAKE, None)  # 17 > M=16
     assert st == misa.MISA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("ok-shape, ws too small", -3), ("T=2", -2), ("fp32", -2), ("null pooled", -1),
+    ("h>16", -2), ("fp8 without scales", -1),
+])
+def test_decode_step_argument_checks(case, expect):
+    import long_context_pool_amd as misa
+
+    lib = misa.lib()
+    shp = misa.shape(4, 4096, 1, 64, 128, 64, misa.MISA_BF16)
+    h, k, pooled, ws_bytes, qs = 8, 64, FAKE, 1 << 40, None
+    if case == "ok-shape, ws too small":
+        ws_bytes = misa.misa_workspace_bytes(shp, h, k, k) - 1
+        assert ws_bytes > 0
+    elif case == "T=2":
+        shp = misa.shape(4, 4096, 2, 64, 128, 64, misa.MISA_BF16)
+    elif case == "fp32":
+        shp = misa.shape(4, 4096, 1, 64, 128, 64, misa.MISA_F32)
+    elif case == "null pooled":
+        pooled = None
+    elif case == "h>16":
+        h = 17
+    elif case == "fp8 without scales":
+        shp = misa.shape(4, 4096, 1, 64, 128, 64, misa.MISA_FP8_E4M3)
+    st = lib.misa_decode_step(ctypes.byref(shp), h, k, FAKE, qs, FAKE, pooled, FAKE, None, FAKE,
+                              None, FAKE, None, FAKE, ws_bytes, None)
+    assert st == expect

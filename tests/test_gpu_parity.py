@@ -32,6 +32,8 @@ SMALL = {
                               kprime=600, dtype=synth.FP8_E4M3, needles=8, seed=22),
     "h32_decode": synth.small("h32_decode", batch=4, L=5000, T=1, H=32, h=8, B=128, k=512,
                               kprime=1024, dtype=synth.BF16, needles=16, seed=23),
+    "fp8_decode": synth.small("fp8_decode", batch=3, L=4100, T=1, H=64, h=8, B=64, k=400,
+                              kprime=900, dtype=synth.FP8_E4M3, needles=12, seed=26),
     "t_eq_l": synth.small("t_eq_l", batch=1, L=200, T=200, H=64, h=8, B=64, k=64, kprime=96,
                           dtype=synth.BF16, needles=0, seed=24),
     "b1_h16": synth.small("b1_h16", batch=1, L=700, T=9, H=64, h=16, B=1, k=100, kprime=200,
@@ -70,6 +72,30 @@ def test_small_route_and_score(small_case):
     hs = sum(r["head_swaps"] for r in res)
     ts = sum(r["tok_swaps"] for r in res)
     _log(f"[gpu] {name}: {len(res)} queries, head swaps in band {hs}, token swaps in band {ts}")
+
+
+def _check_step(op, gpu, qs, tol, name):
+    """misa_decode_step against the oracle: the rebuilt last pooled block,
+    then route and routed top-k of each query in qs."""
+    p = op.p
+    for b in {b for b, _ in qs}:
+        ref = op.seq(b).pooled
+        got = gpu["s_pooled"][b]
+        np.testing.assert_allclose(got[p.M - 1], ref[p.M - 1], rtol=1e-5, atol=1e-6 * np.abs(ref).max(),
+                                   err_msg=f"{name}: decode step pooled block {p.M - 1} of seq {b}")
+        np.testing.assert_array_equal(got[: p.M - 1], gpu["pooled"][b, : p.M - 1])
+    view = parity.step_view(gpu)
+    res = parity.pmap(lambda bt: parity.check_query_misa(op, view, *bt, tol), qs)
+    _log(f"[gpu] {name}: decode step ok on {len(qs)} queries; head swaps "
+         f"{sum(r['head_swaps'] for r in res)}, token swaps {sum(r['tok_swaps'] for r in res)}")
+
+
+def test_small_decode_step(small_case):
+    name, x, gpu, op = small_case
+    p = x.problem
+    if "s_idx" not in gpu:
+        pytest.skip("misa_decode_step covers decode (T = 1) with bf16/fp8 inputs")
+    _check_step(op, gpu, _all_queries(p), parity.TOL[p.dtype], name)
 
 
 def test_small_dense(small_case):
@@ -287,6 +313,9 @@ def test_full_size_sampled(full_case):
             row = gpu["idx"][b, t]
             assert row.min() >= 0 and row.max() <= pos
             assert len(np.unique(row)) == k_
+    if "s_idx" in gpu:
+        _check_step(op, gpu, qs, tol, name)
+        assert (gpu["s_idx"].min(axis=2) >= 0).all()
     rec = np.mean([len(set(gpu["idx"][b, t].tolist()) & set(gpu["d_idx"][b, t].tolist())) / p.k
                    for b in range(p.batch) for t in range(p.T)])
     _log(f"[gpu] {name}: sampled {len(qs)} queries ok; head swaps {sum(r['head_swaps'] for r in res)}, "
