@@ -52,9 +52,10 @@ constexpr int kCandCap = 2048;                    // LDS list of the threshold d
 constexpr int kChunk = 32;                        // pooled blocks per router workgroup
 constexpr int kMaxH = 64;
 
-// Histogram digit of a score: a monotone (non-decreasing) map of fp32 values
-// to [0, kDigits) that spends its bins where top-k thresholds live.  Bin 0
-// holds every negative value, bin 1 zero (and subnormals); positive values
+// Histogram digit of a score: a monotone (non-decreasing) map of the
+// order-preserving key to [0, kDigits) that spends its bins where top-k
+// thresholds live.  Bin 0 holds every negative value, bin 1 zero (either
+// sign) and positive subnormals; positive values
 // with binary exponent in a 63-binade window get 128 bins per binade (7
 // mantissa bits: bins 0.8% wide), values below or above the window share the
 // window's first or last bin.  A 13-bit prefix of the order-preserving key
@@ -63,47 +64,73 @@ constexpr int kMaxH = 64;
 constexpr int kExpLo = 127 - 31;  // window: values in [2^-31, 2^32)
 constexpr int kExpBins = 63;
 __device__ __forceinline__ uint32_t key_digit(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const int e = static_cast<int>((u >> 23) & 0xFFu);
-  if (u >> 31) return 0u;
+  const uint32_t key = float_key(v);  // -0 has the key of +0
+  if (key < 0x80000000u) return 0u;
+  const uint32_t u = key & 0x7FFFFFFFu;
+  const int e = static_cast<int>(u >> 23);
   if (e == 0) return 1u;
   if (e < kExpLo) return 2u;
   if (e >= kExpLo + kExpBins) return 2u + ((kExpBins - 1) << 7) + 127u;
   return 2u + (static_cast<uint32_t>(e - kExpLo) << 7) + ((u >> 16) & 0x7Fu);
 }
 static_assert(2 + (kExpBins << 7) <= kDigits, "digit range");
+constexpr uint32_t kTopDigit = 2u + ((kExpBins - 1) << 7) + 127u;
 
-// The digit b* of the k-th largest score of a row from its digit histogram
-// gh[kDigits] (total n > k): *digit, *above = count in higher digits, *count =
-// count at b*.  All threads call; the results are in LDS on return.
+// The smallest order-preserving key (float_key) whose score has digit d, for
+// 0 <= d <= kTopDigit: key_digit(v) >= d  <=>  float_key(v) >= digit_lo_key(d).
+__device__ __forceinline__ uint32_t digit_lo_key(uint32_t d) {
+  if (d == 0) return 0u;
+  if (d == 1) return 0x80000000u;  // +0
+  if (d == 2) return 0x80800000u;  // smallest positive normal
+  const uint32_t b = d - 2;
+  return 0x80000000u | ((kExpLo + (b >> 7)) << 23) | ((b & 127u) << 16);
+}
+// The largest key with digit d.
+__device__ __forceinline__ uint32_t digit_hi_key(uint32_t d) {
+  return d >= kTopDigit ? 0xFFFFFFFFu : digit_lo_key(d + 1) - 1u;
+}
+
+// Per-row histogram record: kDigits fine bins, then kCoarse coarse bins
+// (coarse bin c = fine bins [32c, 32c + 32)).
+constexpr int kCoarse = 256;
+constexpr int kFinePerCoarse = kDigits / kCoarse;
+constexpr int kHistWords = kDigits + kCoarse;
+
+// Coarse bin count owned by thread t (< kCoarse): coarse bin kCoarse-1-t, so
+// threads run from the highest scores down.  Issued before the caller's other
+// loads so that it is not queued behind them.
+__device__ __forceinline__ int load_coarse(const uint32_t* gh) {
+  return threadIdx.x < kCoarse ? static_cast<int>(gh[kDigits + kCoarse - 1 - threadIdx.x]) : 0;
+}
+
+// The digit b* of the k-th largest score of a row (n > k scores) from its
+// histogram record gh: *digit, *above = count in higher digits, *count =
+// count at b*.  c = load_coarse(gh).  All threads call; results are in LDS on
+// return.
 template <int NT>
-__device__ __forceinline__ void find_digit(const uint32_t* gh, int k, int* scan_tmp, int* digit,
-                                           int* above, int* count) {
-  constexpr int BPT = kDigits / NT;
-  int local[BPT];
-  int lsum = 0;
-  // Thread t owns digits kDigits-1-t*BPT downwards (highest digits first).
-  const uint4* src = reinterpret_cast<const uint4*>(gh + kDigits - (threadIdx.x + 1) * BPT);
-#pragma unroll
-  for (int c = 0; c < BPT / 4; ++c) {
-    const uint4 v = src[BPT / 4 - 1 - c];
-    local[4 * c] = static_cast<int>(v.w);
-    local[4 * c + 1] = static_cast<int>(v.z);
-    local[4 * c + 2] = static_cast<int>(v.y);
-    local[4 * c + 3] = static_cast<int>(v.x);
-  }
-#pragma unroll
-  for (int c = 0; c < BPT; ++c) lsum += local[c];
+__device__ __forceinline__ void find_digit(const uint32_t* gh, int c, int k, int* scan_tmp,
+                                           int* sel_coarse, int* digit, int* above, int* count) {
+  static_assert(NT >= kCoarse, "one coarse bin per thread");
   int total;
-  int run = block_exclusive_sum<NT>(lsum, scan_tmp, total);
-#pragma unroll
-  for (int c = 0; c < BPT; ++c) {
-    if (run < k && run + local[c] >= k) {
-      *digit = kDigits - 1 - (threadIdx.x * BPT + c);
-      *above = run;
-      *count = local[c];
+  const int run = block_exclusive_sum<NT>(c, scan_tmp, total);  // count in higher coarse bins
+  if (threadIdx.x < kCoarse && run < k && run + c >= k) {
+    sel_coarse[0] = kCoarse - 1 - static_cast<int>(threadIdx.x);
+    sel_coarse[1] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int cb = sel_coarse[0];
+    const int base = sel_coarse[1];
+    const int lane = threadIdx.x;
+    // Lane l < 32 owns fine bin 32cb + 31 - l.
+    const int f = lane < kFinePerCoarse ? static_cast<int>(gh[cb * kFinePerCoarse + kFinePerCoarse - 1 - lane]) : 0;
+    const int inc = wave_inclusive_sum(f);
+    const int ex = inc - f;
+    if (lane < kFinePerCoarse && base + ex < k && base + inc >= k) {
+      *digit = cb * kFinePerCoarse + kFinePerCoarse - 1 - lane;
+      *above = base + ex;
+      *count = f;
     }
-    run += local[c];
   }
   __syncthreads();
 }
@@ -123,7 +150,7 @@ struct DecodeArgs {
   int32_t* heads_out;
   float* E_out;
   int64_t Mt;
-  // Score rows [batch, L] and digit histograms [batch, kDigits].
+  // Score rows [batch, L] and histogram records [batch, kHistWords].
   float* rows;
   uint32_t* ghist;
   int32_t L, H, keys_per_wave;
@@ -136,44 +163,84 @@ __global__ __launch_bounds__(kDecThreads) void decode_score_kernel(DecodeArgs a)
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
   const int64_t r = blockIdx.y;  // sequence (T == 1)
-  for (int b = threadIdx.x; b < kDigits; b += kDecThreads) hist[b] = 0;
-  const int32_t* heads = a.heads;
-  int64_t hrow = r;
+  const void* krows = (DT == kBF16) ? static_cast<const void*>(static_cast<const uint16_t*>(a.k) + r * a.L * kD)
+                                    : static_cast<const void*>(static_cast<const uint8_t*>(a.k) + r * a.L * kD);
+  const int64_t s_begin = (static_cast<int64_t>(blockIdx.x) * kDecWaves + wave) * a.keys_per_wave;
+  const int64_t s_end = min<int64_t>(s_begin + a.keys_per_wave, a.L);
+  // The first 64 keys are loaded before the prologue (histogram clear,
+  // router finish, query rows) so that their latency overlaps it.
+  typename RowScorer<DT, NRT>::Keys kb;
+  if (s_begin < s_end) RowScorer<DT, NRT>::load64(krows, s_begin, s_end, s_begin, kb);
+  RowScorer<DT, NRT> sc;
   if constexpr (FUSED) {
-    // Finish the router for this sequence: E_j and the top-h heads.
+    // Finish the router for this sequence (E_j and the top-h heads, Eq. (7)-
+    // (8)) while the keys load.  Every load of the prologue is issued at
+    // once: the query's head rows and weights are staged in LDS (in the
+    // histogram area, cleared afterwards), so the scorer's operands do not
+    // wait for the head choice to be fetched from HBM.
+    constexpr int EB = (DT == kBF16) ? 2 : 1;
+    constexpr int QPIECES = kMaxH * kD * EB / 16;  // 16-byte pieces of all head rows
+    static_assert(QPIECES * 16 + kMaxH * 4 <= kDigits * 4, "staging fits the histogram area");
+    uint8_t* q_lds = reinterpret_cast<uint8_t*>(hist);
+    float* w_lds = reinterpret_cast<float*>(q_lds + QPIECES * 16);
+    const uint4* qsrc = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.q) + r * a.H * kD * EB);
+    const int qpieces = a.H * kD * EB / 16;
+    uint4 qv[(QPIECES + kDecThreads - 1) / kDecThreads];
+#pragma unroll
+    for (int u = 0; u < (QPIECES + kDecThreads - 1) / kDecThreads; ++u) {
+      const int pc = u * kDecThreads + threadIdx.x;
+      qv[u] = pc < qpieces ? qsrc[pc] : make_uint4(0, 0, 0, 0);
+    }
+    const int hd = threadIdx.x & (kMaxH - 1);
+    const int grp = threadIdx.x / kMaxH;
+    constexpr int NG = kDecThreads / kMaxH;
+    const float wv = (threadIdx.x < kMaxH && hd < a.H) ? a.w[r * a.H + hd] : 0.f;
+    const float sq = (DT == kFP8) ? a.q_scale[r] : 1.f;
+    // Chunk partials: group g sums chunks g, g + NG, ... (all loads at once).
+    constexpr int kMaxPer = 16;
+    float pv[kMaxPer];
+#pragma unroll
+    for (int u = 0; u < kMaxPer; ++u) {
+      const int c = grp + NG * u;
+      pv[u] = c < a.nchunks ? a.route_part[(r * a.nchunks + c) * kMaxH + hd] : 0.f;
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int u = 0; u < kMaxPer; ++u) psum += pv[u];
+    for (int c = grp + NG * kMaxPer; c < a.nchunks; c += NG) psum += a.route_part[(r * a.nchunks + c) * kMaxH + hd];
+    __shared__ float red[NG][kMaxH];
+    red[grp][hd] = psum;
+#pragma unroll
+    for (int u = 0; u < (QPIECES + kDecThreads - 1) / kDecThreads; ++u) {
+      const int pc = u * kDecThreads + threadIdx.x;
+      if (pc < QPIECES) reinterpret_cast<uint4*>(q_lds)[pc] = qv[u];
+    }
+    if (threadIdx.x < kMaxH) w_lds[threadIdx.x] = wv;
+    __syncthreads();
     if (wave == 0) {
       float sum = 0.f;
-      for (int c0 = 0; c0 < a.nchunks; c0 += 8) {
-        float v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          v[u] = c0 + u < a.nchunks ? a.route_part[(r * a.nchunks + c0 + u) * kMaxH + lane] : 0.f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) sum += v[u];
-      }
+      for (int g = 0; g < NG; ++g) sum += red[g][lane];
       float e = -2.f;
       if (lane < a.H) {
-        const float sq = (DT == kFP8) ? a.q_scale[r] : 1.f;
-        e = fabsf(a.w[r * a.H + lane]) * sq * sum / static_cast<float>(a.Mt);
+        e = fabsf(wv) * sq * sum / static_cast<float>(a.Mt);
         if (blockIdx.x == 0 && a.E_out) a.E_out[r * a.H + lane] = e;
       }
       wave_top_heads(e, a.H, a.h, sh_heads);
     }
     __syncthreads();
     if (blockIdx.x == 0 && threadIdx.x < a.h) a.heads_out[r * a.h + threadIdx.x] = sh_heads[threadIdx.x];
-    heads = sh_heads;
-    hrow = 0;
+    sc.init_rows(q_lds, w_lds, sq, sh_heads, a.nh, a.H);
+    __syncthreads();  // the staging area becomes the histogram
+  } else {
+    sc.init(a.q, a.q_scale, a.w, a.heads, a.nh, r, a.H);
   }
+  for (int b = threadIdx.x; b < kDigits; b += kDecThreads) hist[b] = 0;
   __syncthreads();
-  RowScorer<DT, NRT> sc;
-  sc.init(a.q, a.q_scale, a.w, heads, a.nh, r, a.H, hrow);
-  const void* krows = (DT == kBF16) ? static_cast<const void*>(static_cast<const uint16_t*>(a.k) + r * a.L * kD)
-                                    : static_cast<const void*>(static_cast<const uint8_t*>(a.k) + r * a.L * kD);
-  const int64_t s_begin = (static_cast<int64_t>(blockIdx.x) * kDecWaves + wave) * a.keys_per_wave;
-  const int64_t s_end = min<int64_t>(s_begin + a.keys_per_wave, a.L);
   float* row = a.rows + r * a.L;
   for (int64_t s0 = s_begin; s0 < s_end; s0 += 64) {
-    const float res = sc.score64(krows, s0, s_end, s_begin);
+    if (s0 != s_begin) RowScorer<DT, NRT>::load64(krows, s0, s_end, s_begin, kb);
+    const float res = sc.compute64(kb);
     const int64_t s = s0 + lane;
     if (s < s_end) {
       float v = res;
@@ -183,105 +250,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_score_kernel(DecodeArgs a)
     }
   }
   __syncthreads();
-  uint32_t* gh = a.ghist + r * kDigits;
+  uint32_t* gh = a.ghist + r * kHistWords;
   for (int b = threadIdx.x; b < kDigits; b += kDecThreads) {
     const uint32_t c = hist[b];
     if (c) atomicAdd(&gh[b], c);
   }
-}
-
-// Top-k of one row in one workgroup (rows of at most PER * kSelThreads
-// scores): the row is read once into registers (PER scores per thread,
-// coalesced) together with the histogram, tokens of digits above b* go
-// straight to the output and those of digit b* to an LDS list (positions
-// from one block scan), and the list is resolved exactly.  Everything is a
-// short chain of dependent steps: this kernel is latency-bound.
-constexpr int kSelThreads = 1024;
-
-struct SelectSmem {
-  alignas(16) float cand_score[kCandCap];
-  alignas(16) int32_t cand_idx[kCandCap];
-  ResolveSmem rs;
-  TopkSmem base;
-  int scan_tmp[32];
-  int digit, above, count;
-};
-
-template <int PER>
-__global__ __launch_bounds__(kSelThreads) void decode_select_kernel(
-    const float* __restrict__ rows, const uint32_t* __restrict__ ghist, int32_t* __restrict__ idx,
-    float* __restrict__ scores_out, int32_t L, int32_t k) {
-  __shared__ SelectSmem sm;
-  const int64_t r = blockIdx.x;
-  const float* row = rows + r * L;
-  int32_t* out = idx + r * k;
-  float* out_s = scores_out ? scores_out + r * k : nullptr;
-  if (L <= k) {
-    for (int i = threadIdx.x; i < k; i += kSelThreads) {
-      out[i] = i < L ? i : -1;
-      if (out_s) out_s[i] = i < L ? row[i] : -__builtin_inff();
-    }
-    return;
-  }
-  // Loads are clamped to the row (L >= 1) and masked below, so the register
-  // array is written without branches.
-  float v[PER];
+  for (int cb = threadIdx.x; cb < kCoarse; cb += kDecThreads) {
+    uint32_t c = 0;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) v[j] = row[min(j * kSelThreads + static_cast<int>(threadIdx.x), L - 1)];
-  find_digit<kSelThreads>(ghist + r * kDigits, k, sm.scan_tmp, &sm.digit, &sm.above, &sm.count);
-  const uint32_t bstar = static_cast<uint32_t>(sm.digit);
-  const int above = sm.above;
-  const int bcount = sm.count;
-  if (bcount > kCandCap) {
-    block_topk<kSelThreads>(
-        L, k, [](int64_t) { return true; }, [=](int64_t i) { return float_key(row[i]); },
-        [](int64_t i) { return static_cast<int32_t>(i); }, [=](int64_t i) { return row[i]; }, out,
-        out_s, sm.base);
-    return;
+    for (int u = 0; u < kFinePerCoarse; ++u) c += hist[cb * kFinePerCoarse + (u + cb) % kFinePerCoarse];
+    if (c) atomicAdd(&gh[kDigits + cb], c);
   }
-  uint64_t mh = 0, ma = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int i = j * kSelThreads + threadIdx.x;
-    const uint32_t dg = key_digit(v[j]);
-    mh |= (i < L && dg > bstar) ? (uint64_t{1} << j) : 0u;
-    ma |= (i < L && dg == bstar) ? (uint64_t{1} << j) : 0u;
-  }
-  // Packed counts: above-b* in the low 16 bits (row total < k <= 8192),
-  // at-b* in the high 16 bits (row total <= kCandCap).
-  int total;
-  const int off = block_exclusive_sum<kSelThreads>(__popcll(mh) | (__popcll(ma) << 16), sm.scan_tmp,
-                                                   total);
-  int ph = off & 0xFFFF;
-  int pa = off >> 16;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int i = j * kSelThreads + threadIdx.x;
-    if ((mh >> j) & 1u) {
-      if (ph < k) {
-        out[ph] = i;
-        if (out_s) out_s[ph] = v[j];
-      }
-      ++ph;
-    } else if ((ma >> j) & 1u) {
-      if (pa < kCandCap) {
-        sm.cand_score[pa] = v[j];
-        sm.cand_idx[pa] = i;
-      }
-      ++pa;
-    }
-  }
-  __syncthreads();
-  if (resolve_list<kSelThreads>(sm.cand_score, sm.cand_idx, bcount, k - above, out + above,
-                                out_s ? out_s + above : nullptr, sm.rs))
-    return;
-  __syncthreads();
-  const float* cs = sm.cand_score;
-  const int32_t* ci = sm.cand_idx;
-  block_topk<kSelThreads>(
-      bcount, k - above, [](int64_t) { return true; }, [=](int64_t j) { return float_key(cs[j]); },
-      [=](int64_t j) { return ci[j]; }, [=](int64_t j) { return cs[j]; }, out + above,
-      out_s ? out_s + above : nullptr, sm.base);
 }
 
 // Top-k step 1: tokens of digits above b* -> output, digit b* -> the list.
@@ -299,29 +278,33 @@ __global__ __launch_bounds__(kCompactThreads) void decode_compact_kernel(
     SelState* __restrict__ sel, float* __restrict__ cand_s, int32_t* __restrict__ cand_i,
     int32_t* __restrict__ idx, float* __restrict__ scores_out, int32_t L, int32_t k) {
   __shared__ int scan_tmp[32];
+  __shared__ int s_coarse[2];
   __shared__ int s_digit, s_above, s_count;
   __shared__ uint32_t s_base;
   if (L <= k) return;
   const int64_t r = blockIdx.y;
   const float* row = rows + r * L;
   const int c0 = blockIdx.x * kCompactChunk;
+  const uint32_t* gh = ghist + r * kHistWords;
+  const int coarse = load_coarse(gh);
   // Scores first (independent of b*), so their loads overlap the scan.
   float v[kCompactPer];  // clamped loads; tokens past L are masked below
 #pragma unroll
   for (int j = 0; j < kCompactPer; ++j)
     v[j] = row[min(c0 + j * kCompactThreads + static_cast<int>(threadIdx.x), L - 1)];
-  find_digit<kCompactThreads>(ghist + r * kDigits, k, scan_tmp, &s_digit, &s_above, &s_count);
+  find_digit<kCompactThreads>(gh, coarse, k, scan_tmp, s_coarse, &s_digit, &s_above, &s_count);
   const uint32_t bstar = static_cast<uint32_t>(s_digit);
   const int count = s_count;
   if (blockIdx.x == 0 && threadIdx.x == 0) sel[r] = SelState{s_digit, s_above, count, 0};
   if (count > kCandCap) return;  // the resolve kernel selects from the whole row
+  const uint32_t lo = digit_lo_key(bstar), hi = digit_hi_key(bstar);
   uint32_t mh = 0, ma = 0;
 #pragma unroll
   for (int j = 0; j < kCompactPer; ++j) {
     const int i = c0 + j * kCompactThreads + threadIdx.x;
-    const uint32_t dg = key_digit(v[j]);
-    mh |= (i < L && dg > bstar) ? (1u << j) : 0u;
-    ma |= (i < L && dg == bstar) ? (1u << j) : 0u;
+    const uint32_t key = float_key(v[j]);
+    mh |= (i < L && key > hi) ? (1u << j) : 0u;
+    ma |= (i < L && key >= lo && key <= hi) ? (1u << j) : 0u;
   }
   // Packed counts: above-b* in the low 16 bits (their row total is below
   // k <= 8192), at-b* in the high 16 bits (row total <= kCandCap).
@@ -359,6 +342,7 @@ __global__ __launch_bounds__(kCompactThreads) void decode_compact_kernel(
 // Top-k step 2, one workgroup per sequence: the (k - above) best of the b*
 // list (or, when b* holds more than kCandCap tokens, the whole row).
 constexpr int kResolveThreads = 256;
+static_assert(kResolveThreads <= kCandCap, "speculative list loads stay inside the list");
 
 struct ResolveAll {
   alignas(16) float cand_score[kCandCap];
@@ -383,6 +367,11 @@ __global__ __launch_bounds__(kResolveThreads) void decode_resolve_kernel(
     }
     return;
   }
+  // The first kResolveThreads list entries are loaded together with the
+  // selection state (the list area always exists; entries past the count
+  // are ignored), saving a dependent round trip for short lists.
+  const float s0 = cand_s[r * kCandCap + threadIdx.x];
+  const int32_t i0 = cand_i[r * kCandCap + threadIdx.x];
   const SelState st = sel[r];
   const int above = st.above;
   const int bcount = st.count;
@@ -393,7 +382,11 @@ __global__ __launch_bounds__(kResolveThreads) void decode_resolve_kernel(
         out_s, sm.base);
     return;
   }
-  for (int t = threadIdx.x; t < bcount; t += kResolveThreads) {
+  if (static_cast<int>(threadIdx.x) < bcount) {
+    sm.cand_score[threadIdx.x] = s0;
+    sm.cand_idx[threadIdx.x] = i0;
+  }
+  for (int t = threadIdx.x + kResolveThreads; t < bcount; t += kResolveThreads) {
     sm.cand_score[t] = cand_s[r * kCandCap + t];
     sm.cand_idx[t] = cand_i[r * kCandCap + t];
   }
@@ -416,17 +409,19 @@ __global__ void clear_kernel(uint32_t* __restrict__ p, int64_t n) {
     p[i] = 0;
 }
 
-// Fused step, kernel 1: router partial sums over 32 pooled blocks per
-// workgroup; the workgroup holding the newest key's block recomputes that
-// block's mean from the keys and writes it to the cache.  Also zeroes the
-// digit histograms and compaction counters of the top-k kernels.
+// Fused step, kernel 1: router partial sums.  Workgroup (c, sequence) with
+// c < nmain sums ReLU(q_j . p_b) over pooled blocks [32c, 32c+32) of the
+// cached blocks 0 .. M-2; workgroup (nmain, sequence) recomputes the mean of
+// the newest block M-1 (keys (M-1)B .. L-1) from the keys, writes it to the
+// cache and forms its ReLU(q_j . p) term.  Partial j of slot c goes to
+// part[(seq*(nmain+1) + c)*64 + j].  Every workgroup also zeroes a share of
+// the digit histograms and compaction counters of the top-k kernels.
 template <int DT>
 __global__ __launch_bounds__(256) void step_route_kernel(
     const void* __restrict__ q, float* __restrict__ pooled, const void* __restrict__ k,
     const float* __restrict__ k_scale, float* __restrict__ part, uint32_t* __restrict__ zero,
-    int64_t nzero, int32_t L, int32_t H, int32_t B, int64_t M, int32_t nchunks) {
-  __shared__ __attribute__((aligned(16))) float ps[kChunk][kD];
-  __shared__ float red[4][kMaxH];
+    int64_t nzero, int32_t L, int32_t H, int32_t B, int64_t M, int32_t nmain) {
+  __shared__ __attribute__((aligned(16))) float ps[kD];
   __shared__ float lastp[32][kD];
   {
     const int64_t g = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
@@ -435,20 +430,9 @@ __global__ __launch_bounds__(256) void step_route_kernel(
   }
   const int c = blockIdx.x;
   const int64_t seq = blockIdx.y;
-  const int j = threadIdx.x & (kMaxH - 1);
-  const int sub = threadIdx.x / kMaxH;
-  const int64_t b0 = static_cast<int64_t>(c) * kChunk;
-  const int nb = static_cast<int>(min<int64_t>(kChunk, M - b0));
-  const int64_t blast = M - 1;  // the block holding key L-1
-  for (int e = threadIdx.x; e < kChunk * kD / 4; e += 256) {
-    const int b = e / (kD / 4);
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (b < nb && b0 + b != blast)
-      v = reinterpret_cast<const float4*>(pooled + (seq * M + b0 + b) * kD)[e % (kD / 4)];
-    reinterpret_cast<float4*>(&ps[b][0])[e % (kD / 4)] = v;
-  }
-  if (blast >= b0 && blast < b0 + nb) {
-    // Mean of keys [blast*B, L): thread t takes 16-byte piece t % P of key
+  float* out = part + (seq * (nmain + 1) + c) * kMaxH;
+  if (c == nmain) {
+    // Mean of keys [(M-1)B, L): thread t takes 16-byte piece t % P of key
     // rows t / P + KPR * u; a round's loads are all in flight together and
     // the per-dimension partial sums of the KPR key slots meet in LDS.
     constexpr int EB = (DT == kBF16) ? 2 : 1;  // bytes per element
@@ -458,7 +442,7 @@ __global__ __launch_bounds__(256) void step_route_kernel(
     constexpr int U = 4;
     const int piece = threadIdx.x % P;
     const int slot = threadIdx.x / P;
-    const int64_t s0 = blast * B;
+    const int64_t s0 = (M - 1) * B;
     const int nl = static_cast<int>(L - s0);
     const uint8_t* kb = static_cast<const uint8_t*>(k) + (seq * L + s0) * kD * EB;
     float acc[EPP];
@@ -492,6 +476,10 @@ __global__ __launch_bounds__(256) void step_route_kernel(
         }
       }
     }
+    // This thread's query head row (loads overlap the reduction below).
+    const int j = threadIdx.x & (kMaxH - 1);
+    float qr[kD];
+    load_head_row<DT>(q, (seq * H + (j < H ? j : 0)) * kD, qr);
 #pragma unroll
     for (int e = 0; e < EPP; ++e) lastp[slot][piece * EPP + e] = acc[e];
     __syncthreads();
@@ -500,20 +488,78 @@ __global__ __launch_bounds__(256) void step_route_kernel(
 #pragma unroll
       for (int sl = 0; sl < KPR; ++sl) sum += lastp[sl][threadIdx.x];
       const float m = sum / static_cast<float>(nl);
-      ps[blast - b0][threadIdx.x] = m;
-      pooled[(seq * M + blast) * kD + threadIdx.x] = m;
+      ps[threadIdx.x] = m;
+      pooled[(seq * M + M - 1) * kD + threadIdx.x] = m;
+    }
+    __syncthreads();
+    if (threadIdx.x < kMaxH) out[threadIdx.x] = relu(dot_lds_row(qr, ps));
+    return;
+  }
+  // Cached blocks [b0, b0 + nb) on 16x16x32 bf16 MFMA: wave w takes heads
+  // [16w, 16w + 16) as A (q codes are exact in bf16: bf16 inputs, or e4m3
+  // widened), 16 blocks per column tile as B, each pooled key split into a
+  // bf16 hi part and the bf16 rounding of its remainder (two MFMAs), so the
+  // products carry ~16 mantissa bits of the fp32 pooled keys.  The head-dim
+  // pieces follow the key scorer's permutation (piece 4*ks + lane/16).
+  const int64_t b0 = static_cast<int64_t>(c) * kChunk;
+  const int nb = static_cast<int>(min<int64_t>(kChunk, (M - 1) - b0));
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int col = lane & 15;
+  const int qq = lane >> 4;
+  const int jh = 16 * wave + col;  // head of this lane's A row
+  bf16x8 qa[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (jh < H) {
+      if constexpr (DT == kBF16) {
+        v = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + (seq * H + jh) * kD)[4 * ks + qq];
+      } else {
+        const uint2 c8 = reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(q) + (seq * H + jh) * kD)[4 * ks + qq];
+        uint32_t b16[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          b16[e] = __float_as_uint(fp8_to_f32(((e < 4 ? c8.x : c8.y) >> (8 * (e & 3))) & 0xFF)) >> 16;
+        v = make_uint4(b16[0] | (b16[1] << 16), b16[2] | (b16[3] << 16), b16[4] | (b16[5] << 16),
+                       b16[6] | (b16[7] << 16));
+      }
+    }
+    qa[ks] = as_bf16x8(v);
+  }
+  f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int bl = 16 * ct + col;
+    const bool ok = bl < nb;
+    const float4* src = reinterpret_cast<const float4*>(pooled + (seq * M + b0 + (ok ? bl : 0)) * kD);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      // dims 8*(4ks+qq) .. +8: float4s 2*(4ks+qq) and 2*(4ks+qq)+1
+      float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
+      if (ok) {
+        x0 = src[2 * (4 * ks + qq)];
+        x1 = src[2 * (4 * ks + qq) + 1];
+      }
+      uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+      split_bf16(x0, h0, h1, l0, l1);
+      split_bf16(x1, h2, h3, l2, l3);
+      acc[ct] = mfma16_bf16(qa[ks], as_bf16x8(make_uint4(h0, h1, h2, h3)), acc[ct]);
+      acc[ct] = mfma16_bf16(qa[ks], as_bf16x8(make_uint4(l0, l1, l2, l3)), acc[ct]);
     }
   }
-  float qr[kD];
-  load_head_row<DT>(q, (seq * H + (j < H ? j : 0)) * kD, qr);
-  __syncthreads();
-  float acc = 0.f;
-  for (int b = sub; b < nb; b += 4) acc += relu(dot_lds_row(qr, &ps[b][0]));
-  red[sub][j] = acc;
-  __syncthreads();
-  if (threadIdx.x < kMaxH)
-    part[(seq * nchunks + c) * kMaxH + threadIdx.x] =
-        red[0][threadIdx.x] + red[1][threadIdx.x] + red[2][threadIdx.x] + red[3][threadIdx.x];
+  // C layout: lane holds heads 16w + 4qq + i (i < 4) for blocks col and 16 + col.
+  float rs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rs[i] = relu(acc[0][i]) + relu(acc[1][i]);
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rs[i] += __shfl_xor(rs[i], o, kWave);
+  if (col == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[16 * wave + 4 * qq + i] = rs[i];
+  }
 }
 
 template <int DT, bool FUSED>
@@ -526,7 +572,7 @@ void launch_score(const Shape& s, const DecodeArgs& a, hipStream_t st) {
 
 struct DecodeWs {
   float* rows;
-  uint32_t* ghist;  // [batch, kDigits], followed by
+  uint32_t* ghist;  // [batch, kHistWords], followed by
   uint32_t* cnt;    // [batch] packed compaction counters (zeroed together)
   SelState* sel;
   float* cand_s;
@@ -534,6 +580,12 @@ struct DecodeWs {
   float* part;
   size_t total;
 };
+
+// Router chunks of the cached blocks 0 .. M-2 (the newest block has its own
+// workgroup).
+int32_t step_main_chunks(const Shape& s) {
+  return static_cast<int32_t>((s.M() - 1 + kChunk - 1) / kChunk);
+}
 
 DecodeWs decode_layout(const Shape& s, void* ws) {
   const uintptr_t base = reinterpret_cast<uintptr_t>(ws);
@@ -543,8 +595,8 @@ DecodeWs decode_layout(const Shape& s, void* ws) {
   d.rows = reinterpret_cast<float*>(base + off);
   off += align_up(nb * s.L * sizeof(float));
   d.ghist = reinterpret_cast<uint32_t*>(base + off);
-  d.cnt = reinterpret_cast<uint32_t*>(base + off) + nb * kDigits;
-  off += align_up((nb * kDigits + nb) * sizeof(uint32_t));
+  d.cnt = reinterpret_cast<uint32_t*>(base + off) + nb * kHistWords;
+  off += align_up((nb * kHistWords + nb) * sizeof(uint32_t));
   d.sel = reinterpret_cast<SelState*>(base + off);
   off += align_up(nb * sizeof(SelState));
   d.cand_s = reinterpret_cast<float*>(base + off);
@@ -552,20 +604,13 @@ DecodeWs decode_layout(const Shape& s, void* ws) {
   d.cand_i = reinterpret_cast<int32_t*>(base + off);
   off += align_up(nb * kCandCap * sizeof(int32_t));
   d.part = reinterpret_cast<float*>(base + off);
-  const int64_t nch = (s.M() + kChunk - 1) / kChunk;
-  off += align_up(nb * nch * kMaxH * sizeof(float));
+  off += align_up(nb * (step_main_chunks(s) + 1) * kMaxH * sizeof(float));
   d.total = off;
   return d;
 }
 
 void launch_select(const Shape& s, const DecodeWs& d, int32_t k, int32_t* idx, float* scores_out,
                    hipStream_t st) {
-#ifndef MISA_DECODE_SELECT_SPLIT
-  if (s.L <= 32 * kSelThreads) {
-    decode_select_kernel<32><<<s.batch, kSelThreads, 0, st>>>(d.rows, d.ghist, idx, scores_out, s.L, k);
-    return;
-  }
-#endif
   dim3 g((s.L + kCompactChunk - 1) / kCompactChunk, s.batch);
   decode_compact_kernel<<<g, kCompactThreads, 0, st>>>(d.rows, d.ghist, d.cnt, d.sel, d.cand_s,
                                                        d.cand_i, idx, scores_out, s.L, k);
@@ -582,7 +627,7 @@ hipError_t launch_decode_score_topk(const Shape& s, int32_t nh, const int32_t* h
                                     const void* kk, const float* k_scale, int32_t* idx,
                                     float* scores_out, void* ws, hipStream_t st) {
   const DecodeWs d = decode_layout(s, ws);
-  const int64_t nz = static_cast<int64_t>(s.batch) * kDigits + s.batch;
+  const int64_t nz = static_cast<int64_t>(s.batch) * kHistWords + s.batch;
   clear_kernel<<<static_cast<unsigned>((nz + 1023) / 1024), 256, 0, st>>>(d.ghist, nz);
   DecodeArgs a{q, q_scale, w, kk, k_scale, heads, nh, nullptr, 0, 0, nullptr, nullptr, 0,
                d.rows, d.ghist, s.L, s.H, MISA_DECODE_KEYS_PER_WAVE};
@@ -598,15 +643,16 @@ hipError_t launch_decode_step(const Shape& s, int32_t h, int32_t k, const void* 
                               float* scores_out, void* ws, hipStream_t st) {
   const DecodeWs d = decode_layout(s, ws);
   const int64_t M = s.M();
-  const int32_t nch = static_cast<int32_t>((M + kChunk - 1) / kChunk);
-  const int64_t nz = static_cast<int64_t>(s.batch) * kDigits + s.batch;
+  const int32_t nmain = step_main_chunks(s);
+  const int32_t nch = nmain + 1;
+  const int64_t nz = static_cast<int64_t>(s.batch) * kHistWords + s.batch;
   dim3 g1(nch, s.batch);
   if (s.dtype == kBF16)
     step_route_kernel<kBF16><<<g1, 256, 0, st>>>(q, pooled, kk, k_scale, d.part, d.ghist, nz, s.L,
-                                                 s.H, s.B, M, nch);
+                                                 s.H, s.B, M, nmain);
   else
     step_route_kernel<kFP8><<<g1, 256, 0, st>>>(q, pooled, kk, k_scale, d.part, d.ghist, nz, s.L,
-                                                s.H, s.B, M, nch);
+                                                s.H, s.B, M, nmain);
   DecodeArgs a{q, q_scale, w, kk, k_scale, nullptr, h, d.part, nch, h, heads, E_out, M,
                d.rows, d.ghist, s.L, s.H, MISA_DECODE_KEYS_PER_WAVE};
   if (s.dtype == kBF16) launch_score<kBF16, true>(s, a, st);

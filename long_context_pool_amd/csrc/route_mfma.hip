@@ -72,19 +72,6 @@ __device__ __forceinline__ void load_q_rows(const void* q, int64_t r, int H, bf1
   }
 }
 
-// Split an fp32 quad into bf16 hi (RNE) and lo (RNE of the remainder) pairs.
-__device__ __forceinline__ void split_bf16(float4 x, uint32_t& h0, uint32_t& h1, uint32_t& l0,
-                                           uint32_t& l1) {
-  const uint32_t a = f32_to_bf16_bits(x.x), b = f32_to_bf16_bits(x.y);
-  const uint32_t c = f32_to_bf16_bits(x.z), d = f32_to_bf16_bits(x.w);
-  h0 = a | (b << 16);
-  h1 = c | (d << 16);
-  l0 = f32_to_bf16_bits(x.x - __uint_as_float(a << 16)) |
-       (f32_to_bf16_bits(x.y - __uint_as_float(b << 16)) << 16);
-  l1 = f32_to_bf16_bits(x.z - __uint_as_float(c << 16)) |
-       (f32_to_bf16_bits(x.w - __uint_as_float(d << 16)) << 16);
-}
-
 // acc (rows x 32 blocks) = A . (B_hi [+ B_lo]); rs += ReLU(acc) when col_ok.
 // The hi and lo products of every row tile go to separate accumulators so the
 // MFMA chains are independent.

@@ -170,6 +170,26 @@ def test_h_equals_H_matches_dense_on_gpu():
         assert set(gpu["idx"][0, t].tolist()) == set(gpu["d_idx"][0, t].tolist())
 
 
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.FP8_E4M3])
+def test_negative_weights_decode_and_prefill(dtype):
+    """Eq. (7) takes |w| for the router; Eq. (9) keeps the sign, so scores can
+    be negative or -0.  Every other head's weight is negated."""
+    for T in (1, 40):
+        p = synth.small(f"negw_T{T}", batch=2, L=2600, T=T, H=64, h=8, B=64, k=300, kprime=None,
+                        dtype=dtype, needles=8, seed=40 + T)
+        x = synth.generate(p)
+        x.w[..., ::2] *= -1.0
+        _log(f"[gpu] negative weights {p}")
+        gpu = parity.run_gpu(x, stages=("pool", "route", "score", "dense", "step"))
+        op = parity.OracleProblem(x)
+        tol = parity.TOL[p.dtype]
+        qs = _all_queries(p)
+        parity.pmap(lambda bt: parity.check_query_misa(op, gpu, *bt, tol), qs)
+        parity.pmap(lambda bt: parity.check_query_dense(op, gpu, *bt, tol), qs)
+        if "s_idx" in gpu:
+            _check_step(op, gpu, qs, tol, p.name)
+
+
 def test_repeat_runs_are_bit_identical():
     p = SMALL["bf16_ragged"]
     x = synth.generate(p)
