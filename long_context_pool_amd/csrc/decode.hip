@@ -47,48 +47,9 @@ namespace {
 #endif
 constexpr int kDecThreads = MISA_DECODE_THREADS;
 constexpr int kDecWaves = kDecThreads / kWave;
-constexpr int kDigits = 8192;
-constexpr int kCandCap = 2048;                    // LDS list of the threshold digit
-constexpr int kChunk = 32;                        // pooled blocks per router workgroup
+constexpr int kCandCap = 2048;  // LDS list of the threshold digit
+constexpr int kChunk = 32;      // pooled blocks per router workgroup
 constexpr int kMaxH = 64;
-
-// Histogram digit of a score: a monotone (non-decreasing) map of the
-// order-preserving key to [0, kDigits) that spends its bins where top-k
-// thresholds live.  Bin 0 holds every negative value, bin 1 zero (either
-// sign) and positive subnormals; positive values
-// with binary exponent in a 63-binade window get 128 bins per binade (7
-// mantissa bits: bins 0.8% wide), values below or above the window share the
-// window's first or last bin.  A 13-bit prefix of the order-preserving key
-// would spend 7/8 of its bins on exponents that scores never reach and leave
-// bins 6% wide.
-constexpr int kExpLo = 127 - 31;  // window: values in [2^-31, 2^32)
-constexpr int kExpBins = 63;
-__device__ __forceinline__ uint32_t key_digit(float v) {
-  const uint32_t key = float_key(v);  // -0 has the key of +0
-  if (key < 0x80000000u) return 0u;
-  const uint32_t u = key & 0x7FFFFFFFu;
-  const int e = static_cast<int>(u >> 23);
-  if (e == 0) return 1u;
-  if (e < kExpLo) return 2u;
-  if (e >= kExpLo + kExpBins) return 2u + ((kExpBins - 1) << 7) + 127u;
-  return 2u + (static_cast<uint32_t>(e - kExpLo) << 7) + ((u >> 16) & 0x7Fu);
-}
-static_assert(2 + (kExpBins << 7) <= kDigits, "digit range");
-constexpr uint32_t kTopDigit = 2u + ((kExpBins - 1) << 7) + 127u;
-
-// The smallest order-preserving key (float_key) whose score has digit d, for
-// 0 <= d <= kTopDigit: key_digit(v) >= d  <=>  float_key(v) >= digit_lo_key(d).
-__device__ __forceinline__ uint32_t digit_lo_key(uint32_t d) {
-  if (d == 0) return 0u;
-  if (d == 1) return 0x80000000u;  // +0
-  if (d == 2) return 0x80800000u;  // smallest positive normal
-  const uint32_t b = d - 2;
-  return 0x80000000u | ((kExpLo + (b >> 7)) << 23) | ((b & 127u) << 16);
-}
-// The largest key with digit d.
-__device__ __forceinline__ uint32_t digit_hi_key(uint32_t d) {
-  return d >= kTopDigit ? 0xFFFFFFFFu : digit_lo_key(d + 1) - 1u;
-}
 
 // Per-row histogram record: kDigits fine bins, then kCoarse coarse bins
 // (coarse bin c = fine bins [32c, 32c + 32)).

@@ -17,7 +17,8 @@
 //    query, a threshold tau at the sample's (2.5 k/n)-quantile;
 //  * the full pass appends every score >= tau of a key inside the query's
 //    prefix to the (query, split) candidate segment (wave ballots give the
-//    positions; each segment has a single writer wave);
+//    positions, so each store writes consecutive entries; each segment has a
+//    single writer wave);
 //  * the select kernel takes the top-k of a query's candidates.  That is the
 //    true top-k iff at least k candidates score >= max over splits of tau
 //    (every non-candidate is below its split's tau); otherwise, or when a
@@ -95,8 +96,8 @@ struct PrefillArgs {
   int32_t cap;           // candidate slots per (query, split)
   int32_t nqt;           // query tiles per sequence
   int32_t batch;
-  uint2* cand;           // [rows*S*cap] (score bits, token)
-  int32_t* cnt;          // [rows*S]
+  uint2* cand;           // [rows, S, cap] (score bits, token)
+  int32_t* cnt;          // [rows, S]
   float* tau;            // [rows*S]
 };
 
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
   constexpr int NS = nslots<HPQ>();
   constexpr int RB = lds_row_bytes<DT>();
   constexpr int TILE_BYTES = kTileKeys * RB;
-  constexpr int SAMPLE_BYTES = kPWaves * QPW * kSamples * 4;
+  constexpr int SAMPLE_BYTES = kPWaves * QPW * kSamples * 2;  // top 16 bits of each sample's key
   constexpr int STAGE_BYTES = 32 * RB;  // one 32-key sample tile, after the sample area
   constexpr int LDS_BYTES = (2 * TILE_BYTES > SAMPLE_BYTES + STAGE_BYTES) ? 2 * TILE_BYTES
                                                                           : SAMPLE_BYTES + STAGE_BYTES;
@@ -226,47 +227,60 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
   };
 
   // Stage keys into an LDS tile: 64 keys, thread t takes key t/4, quarter t%4.
-  // key_of(i) gives the key index of tile row i (or -1: zero row).
-  // Rows past the range load a clamped (valid) row: their scores are masked.
-  auto load_tile_regs = [&](auto key_of, uint4 (&reg)[DT == kBF16 ? 4 : 2], float& skr) {
+  // Keys past the split's range load a clamped (valid) row; their scores are
+  // masked.  The staging values are named fields, not an array, so they stay
+  // in registers across the tile's compute.
+  struct TileRegs {
+    uint4 v0, v1, v2, v3;
+    float sk;
+  };
+  auto load_tile = [&](int64_t tile_idx) -> TileRegs {
     const int kr = threadIdx.x >> 2;
     const int qd = threadIdx.x & 3;
-    const int64_t key = key_of(kr);
-    const int64_t row = seq * a.L + (key < 0 ? s_safe : key);
+    const int64_t key = s_begin + tile_idx * kTileKeys + kr;
+    const int64_t row = seq * a.L + (key < s_end ? key : s_safe);
+    TileRegs t;
     if constexpr (DT == kBF16) {
       const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + row * kD + 32 * qd);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) reg[u] = src[u];
-      skr = 1.f;
+      t.v0 = src[0];
+      t.v1 = src[1];
+      t.v2 = src[2];
+      t.v3 = src[3];
+      t.sk = 1.f;
     } else {
       const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.k) + row * kD + 32 * qd);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) reg[u] = src[u];
-      skr = a.k_scale[row];
+      t.v0 = src[0];
+      t.v1 = src[1];
+      t.v2 = t.v3 = make_uint4(0, 0, 0, 0);
+      t.sk = a.k_scale[row];
     }
+    return t;
   };
-  auto store_tile = [&](uint8_t* tile, int buf, const uint4 (&reg)[DT == kBF16 ? 4 : 2], float skr) {
+  auto store_tile = [&](uint8_t* tile, int buf, const TileRegs& t) {
     const int kr = threadIdx.x >> 2;
     const int qd = threadIdx.x & 3;
     uint4* dst = reinterpret_cast<uint4*>(tile + kr * RB + (DT == kBF16 ? 64 : 32) * qd);
-#pragma unroll
-    for (int u = 0; u < (DT == kBF16 ? 4 : 2); ++u) dst[u] = reg[u];
-    if constexpr (DT == kFP8) {
-      if (qd == 0) sk_tile[buf][kr] = skr;
+    dst[0] = t.v0;
+    dst[1] = t.v1;
+    if constexpr (DT == kBF16) {
+      dst[2] = t.v2;
+      dst[3] = t.v3;
+    } else {
+      if (qd == 0) sk_tile[buf][kr] = t.sk;
     }
   };
 
   // Query positions of this lane's slots (and of the wave's queries).
-  int64_t pos_slot[NS];
+  int pos_slot[NS];  // L < 2^31
 #pragma unroll
   for (int sl = 0; sl < NS; ++sl) {
     const int t = tw0 + slot_query<HPQ>(sl, hf);
-    pos_slot[sl] = t < a.T ? static_cast<int64_t>(a.L) - a.T + t : -1;
+    pos_slot[sl] = t < a.T ? a.L - a.T + t : -1;
   }
 
   // ---- 1. sample pass: thresholds per (query, split).
   const int64_t len = s_end - s_begin;
-  float* smp = reinterpret_cast<float*>(lds) + wave * QPW * kSamples;  // [QPW][kSamples]
+  uint16_t* smp = reinterpret_cast<uint16_t*>(lds) + wave * QPW * kSamples;  // [QPW][kSamples]
   float tau_slot[NS];
   // Sample tiles (32 keys) are staged after the sample area; each tile's
   // scores go straight to the sample area (sample m of query qw at
@@ -307,7 +321,9 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
       for (int sl = 0; sl < NS; ++sl) {
         const bool ok = key >= 0 && key <= pos_slot[sl];
         const int qw = slot_query<HPQ>(sl, hf);
-        if (HPQ < 32 || hf == 0) smp[qw * kSamples + m] = ok ? out[sl] * skv : -__builtin_inff();
+        // 0 marks a missing sample (no score has a key below 2^16).
+        if (HPQ < 32 || hf == 0)
+          smp[qw * kSamples + m] = ok ? static_cast<uint16_t>(float_key(out[sl] * skv) >> 16) : 0;
       }
     }
     __syncthreads();
@@ -319,14 +335,21 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
     constexpr int VPL = kSamples / LPQ;
     const int g = lane / LPQ;
     const int lg = lane % LPQ;
-    uint32_t kv[VPL];
+    // This lane's VPL 16-bit sample keys, two per register.
+    static_assert(VPL % 8 == 0, "samples are read 8 at a time");
+    uint32_t kv[VPL / 2];
     int nvs = 0;
 #pragma unroll
-    for (int e = 0; e < VPL; ++e) {
-      const float v = smp[g * kSamples + lg * VPL + e];
-      kv[e] = float_key(v);
-      nvs += (v != -__builtin_inff()) ? 1 : 0;
+    for (int e = 0; e < VPL / 8; ++e) {
+      const uint4 w4 = reinterpret_cast<const uint4*>(smp + g * kSamples + lg * VPL)[e];
+      kv[4 * e] = w4.x;
+      kv[4 * e + 1] = w4.y;
+      kv[4 * e + 2] = w4.z;
+      kv[4 * e + 3] = w4.w;
     }
+#pragma unroll
+    for (int e = 0; e < VPL / 2; ++e)
+      nvs += ((kv[e] & 0xFFFFu) != 0 ? 1 : 0) + ((kv[e] >> 16) != 0 ? 1 : 0);
 #pragma unroll
     for (int o = LPQ / 2; o >= 1; o >>= 1) nvs += __shfl_xor(nvs, o, kWave);
     const int t = tw0 + g;
@@ -339,17 +362,20 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
     float tq = t < a.T ? -__builtin_inff() : __builtin_inff();
     if (t < a.T && nvs > 0 && j < nvs) {
       uint32_t v = 0;
-      for (int bit = 31; bit >= 0; --bit) {
+      for (int bit = 15; bit >= 0; --bit) {
         const uint32_t cand = v | (1u << bit);
         int c = 0;
 #pragma unroll
-        for (int e = 0; e < VPL; ++e) c += kv[e] >= cand ? 1 : 0;
+        for (int e = 0; e < VPL / 2; ++e)
+          c += ((kv[e] & 0xFFFFu) >= cand ? 1 : 0) + ((kv[e] >> 16) >= cand ? 1 : 0);
 #pragma unroll
         for (int o = LPQ / 2; o >= 1; o >>= 1) c += __shfl_xor(c, o, kWave);
         if (c >= j) v = cand;
       }
-      // Back from key to float (inverse of float_key; v is a sample's key).
-      const uint32_t u = (v & 0x80000000u) ? (v & 0x7FFFFFFFu) : ~v;
+      // The smallest float whose key has top bits v: every sample counted
+      // above scores at least this.
+      const uint32_t key = v << 16;
+      const uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
       tq = __uint_as_float(u);
     }
     // Broadcast: every lane needs the tau of its slots' queries.
@@ -369,6 +395,9 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
   // Candidate counts per (slot, half): (sl, h) is query slot_query(sl, h) --
   // a bijection onto the wave's queries for h = 8, 16 (only h = 0 is used
   // for 32, 64).  Wave-uniform values; a lane picks its half with one select.
+  // The counts go to cnt at the end (they may exceed the capacity: the
+  // select kernel then queues the query for repair).
+  const bool owner = HPQ < 32 || hf == 0;
   int ctr2[NS][2];
 #pragma unroll
   for (int sl = 0; sl < NS; ++sl) ctr2[sl][0] = ctr2[sl][1] = 0;
@@ -379,27 +408,19 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
     const int t = tw0 + slot_query<HPQ>(sl, hf);
     segp[sl] = a.cand + ((seq * a.T + (t < a.T ? t : 0)) * a.S + split) * a.cap;
   }
+  const uint64_t half_mask = hf ? 0xFFFFFFFF00000000ull : 0x00000000FFFFFFFFull;
   // Keys below the wave's first query position are in every slot's prefix.
   const int64_t pos_wave_min = static_cast<int64_t>(a.L) - a.T + tw0;
-  const uint64_t half_mask = hf ? 0xFFFFFFFF00000000ull : 0x00000000FFFFFFFFull;
   const int64_t ntiles = len > 0 ? (len + kTileKeys - 1) / kTileKeys : 0;
-  uint4 reg[DT == kBF16 ? 4 : 2];
-  float skr = 1.f;
-  auto key_at = [&](int64_t tile_idx) {
-    return [=](int i) -> int64_t {
-      const int64_t key = s_begin + tile_idx * kTileKeys + i;
-      return key < s_end ? key : -1;
-    };
-  };
-  if (ntiles > 0) {
-    load_tile_regs(key_at(0), reg, skr);
-    store_tile(lds, 0, reg, skr);
-  }
+  TileRegs reg = load_tile(0);  // unconditional (clamped rows when empty)
+  store_tile(lds, 0, reg);
   __syncthreads();
   for (int64_t ti = 0; ti < ntiles; ++ti) {
     const int buf = static_cast<int>(ti & 1);
     uint8_t* tile = lds + buf * TILE_BYTES;
-    if (ti + 1 < ntiles) load_tile_regs(key_at(ti + 1), reg, skr);
+    // The next tile's keys (past the end: clamped rows, never read), loaded
+    // and stored unconditionally so the staging registers stay registers.
+    reg = load_tile(ti + 1);
     const int64_t tbase = s_begin + ti * kTileKeys;
     // Wave-uniform: no causal / range check needed inside this tile.
     const bool interior = tbase + kTileKeys <= s_end && tbase + kTileKeys - 1 <= pos_wave_min;
@@ -407,13 +428,12 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
     for (int c = 0; c < 2; ++c) {
       float out[NS];
       score_tile(tile, c, out);
-      const int64_t key = tbase + 32 * c + colr;
+      const int key = static_cast<int>(tbase) + 32 * c + colr;
       float skv = 1.f;
       if constexpr (DT == kFP8) skv = sk_tile[buf][32 * c + colr];
 #pragma unroll
       for (int sl = 0; sl < NS; ++sl) {
         const float v = out[sl] * skv;
-        const bool owner = HPQ < 32 || hf == 0;
         bool pass = owner && v >= tau_slot[sl];
         if (!interior) pass = pass && key < s_end && key <= pos_slot[sl];
         const uint64_t m = __ballot(pass);
@@ -426,7 +446,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
         ctr2[sl][1] += __popcll(m >> 32);
       }
     }
-    if (ti + 1 < ntiles) store_tile(lds + (buf ^ 1) * TILE_BYTES, buf ^ 1, reg, skr);
+    store_tile(lds + (buf ^ 1) * TILE_BYTES, buf ^ 1, reg);
     __syncthreads();
   }
   if (lane == 0) {
@@ -445,65 +465,233 @@ __global__ void prefill_clear_kernel(int32_t* fail_count) {
   if (threadIdx.x == 0) *fail_count = 0;
 }
 
-// Top-k of query r's candidates; queues the query for repair when the
-// candidates cannot be shown to hold the true top-k.  The S segments are
-// viewed as one compact list: entry c lies in segment s with
-// pre[s] <= c < pre[s+1] (S <= 8 compares, no division).
+// Top-k of query r's candidates, or a place in the repair queue when the
+// candidates cannot be shown to hold the true top-k.  Certificate: no
+// segment overflowed and at least k candidates score >= tau_max = max over
+// splits of tau (every non-candidate of split s scores below tau_s).  Then:
+//  1. one pass over the candidates (the S segments viewed as one list: entry
+//     c lies in segment s with pre[s] <= c < pre[s+1]) keeps the first
+//     kPCache of them in LDS, builds an LDS histogram of their digits
+//     relative to the digit of tau_min (every candidate is >= tau_min) and
+//     counts the candidates >= tau_max;
+//  2. the digit b* holding the k-th best comes from a block scan of the
+//     histogram;
+//  3. a second pass (LDS, then global beyond the cache) writes candidates
+//     above b* straight to the output and gathers those at b* into an LDS
+//     list (wave ballots + LDS counters);
+//  4. the list is resolved exactly (ties: lower token).
+constexpr int kPCandCap = 1024;
+constexpr int kPCache = 6144;
+constexpr int kRelBins = 2048;
+
+struct PSelSmem {
+  alignas(16) float cache_s[kPCache];
+  alignas(16) int32_t cache_i[kPCache];
+  uint32_t hist[kRelBins];
+  alignas(16) float cand_score[kPCandCap];
+  alignas(16) int32_t cand_idx[kPCandCap];
+  ResolveSmem rs;
+  int pre[9];
+  int scan_tmp[32];
+  int digit, above, count, nge, bad;
+  uint32_t cnt_hi, cnt_at;
+  float tau_max, tau_min;
+};
+
 __global__ __launch_bounds__(kTopkThreadsSel) void prefill_select_kernel(
     const uint2* __restrict__ cand, const int32_t* __restrict__ cnt, const float* __restrict__ tau,
-    int32_t S, int32_t cap, int32_t L, int32_t T, int32_t k, int32_t* __restrict__ idx,
-    float* __restrict__ scores_out, int32_t* __restrict__ fail_count,
-    int32_t* __restrict__ fail_list) {
-  __shared__ TopkFastSmem sm;
-  __shared__ int s_pre[9];
-  __shared__ float s_tau_max;
-  __shared__ int s_flag;
+    int32_t S, int32_t cap, int32_t k, int32_t* __restrict__ idx, float* __restrict__ scores_out,
+    int32_t* __restrict__ fail_count, int32_t* __restrict__ fail_list) {
+  constexpr int NT = kTopkThreadsSel;
+  __shared__ PSelSmem sm;
   const int64_t r = blockIdx.x;
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  int32_t* out = idx + r * k;
+  float* out_s = scores_out ? scores_out + r * k : nullptr;
+  const uint2* base = cand + r * S * static_cast<int64_t>(cap);
+  for (int b = threadIdx.x; b < kRelBins; b += NT) sm.hist[b] = 0;
   if (threadIdx.x == 0) {
-    int bad = 0, total = 0;
-    float tm = -__builtin_inff();
-    for (int s = 0; s < 8; ++s) {
-      s_pre[s] = total;
-      if (s < S) {
-        const int c = cnt[r * S + s];
+    int total = 0, bad = 0;
+    float tmax = -__builtin_inff(), tmin = __builtin_inff();
+    for (int sp = 0; sp < 8; ++sp) {
+      sm.pre[sp] = total;
+      if (sp < S) {
+        const int c = cnt[r * S + sp];
         bad |= c > cap;
         total += c < cap ? c : cap;
-        tm = fmaxf(tm, tau[r * S + s]);
+        const float t = tau[r * S + sp];
+        tmax = fmaxf(tmax, t);
+        tmin = fminf(tmin, t);
       }
     }
-    s_pre[8] = total;
-    s_tau_max = tm;
-    // Fewer than k candidates is fine only when nothing was filtered out.
-    s_flag = bad ? 1 : ((total < k && tm != -__builtin_inff()) ? 1 : 0);
+    sm.pre[8] = total;
+    sm.tau_max = tmax;
+    sm.tau_min = tmin;
+    sm.bad = bad;
+    sm.nge = 0;
+    sm.cnt_hi = 0;
+    sm.cnt_at = 0;
   }
   __syncthreads();
-  const uint2* cr = cand + r * S * cap;
   int pre[9];
 #pragma unroll
-  for (int u = 0; u < 9; ++u) pre[u] = s_pre[u];
-  const int C = pre[8];
-  auto addr = [=](int64_t c) -> int64_t {
-    const int ci = static_cast<int>(c);
-    int sg = 0, base = 0;
+  for (int u = 0; u < 9; ++u) pre[u] = sm.pre[u];
+  const int total = pre[8];
+  const float tm = sm.tau_max;
+  auto entry = [=](int c) -> uint2 {
+    int sg = 0, b = 0;
 #pragma unroll
     for (int u = 1; u < 8; ++u) {
-      const bool ge = ci >= pre[u] && u < S;
+      const bool ge = c >= pre[u] && u < S;
       sg = ge ? u : sg;
-      base = ge ? pre[u] : base;
+      b = ge ? pre[u] : b;
     }
-    return static_cast<int64_t>(sg) * cap + (ci - base);
+    return base[static_cast<int64_t>(sg) * cap + (c - b)];
   };
-  if (s_flag) {
+  // Fewer than k candidates is fine only when nothing was filtered out.
+  if (sm.bad || (total < k && tm != -__builtin_inff())) {
     if (threadIdx.x == 0) fail_list[atomicAdd(fail_count, 1)] = static_cast<int32_t>(r);
     return;
   }
-  // Certificate: at least k candidates score >= max tau (gate); else repair.
-  const bool ok = block_topk_fast<kTopkThreadsSel>(
-      C, k, [](int64_t) { return true; }, [=](int64_t c) { return __uint_as_float(cr[addr(c)].x); },
-      [=](int64_t c) { return static_cast<int32_t>(cr[addr(c)].y); }, idx + r * k,
-      scores_out ? scores_out + r * k : nullptr, sm, s_tau_max);
-  if (!ok && threadIdx.x == 0) fail_list[atomicAdd(fail_count, 1)] = static_cast<int32_t>(r);
+  if (total <= k) {
+    // Every key of the prefix is a candidate: take them all, pad with -1.
+    for (int c = threadIdx.x; c < total; c += NT) {
+      const uint2 e = entry(c);
+      out[c] = static_cast<int32_t>(e.y);
+      if (out_s) out_s[c] = __uint_as_float(e.x);
+    }
+    for (int p = total + threadIdx.x; p < k; p += NT) {
+      out[p] = -1;
+      if (out_s) out_s[p] = -__builtin_inff();
+    }
+    return;
+  }
+  // Relative digit: every candidate is >= tau_min, so its digit is >= d0
+  // (d0 = 0 when some split kept every key).
+  const float tmin = sm.tau_min;
+  const uint32_t d0 = tmin == -__builtin_inff() ? 0u : key_digit(tmin);
+  auto rel = [=](float v) -> uint32_t {
+    const uint32_t d = key_digit(v) - d0;  // >= 0 for candidates
+    return d < static_cast<uint32_t>(kRelBins) ? d : static_cast<uint32_t>(kRelBins - 1);
+  };
+  // 1. cache, histogram, certificate count.
+  // Four loads in flight per thread (clamped to the list, masked after).
+  int nge = 0;
+  for (int c0 = 0; c0 < total; c0 += 4 * NT) {
+    uint2 e[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) e[u] = entry(min(c0 + u * NT + static_cast<int>(threadIdx.x), total - 1));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = c0 + u * NT + threadIdx.x;
+      if (c < total) {
+        const float v = __uint_as_float(e[u].x);
+        if (c < kPCache) {
+          sm.cache_s[c] = v;
+          sm.cache_i[c] = static_cast<int32_t>(e[u].y);
+        }
+        atomicAdd(&sm.hist[rel(v)], 1u);
+        nge += v >= tm ? 1 : 0;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) nge += __shfl_xor(nge, o, kWave);
+  if (lane == 0) atomicAdd(&sm.nge, nge);
+  __syncthreads();
+  if (sm.nge < k) {
+    if (threadIdx.x == 0) fail_list[atomicAdd(fail_count, 1)] = static_cast<int32_t>(r);
+    return;
+  }
+  // 2. b*: thread t owns relative digits kRelBins-1-t*BPT downwards.
+  {
+    constexpr int BPT = kRelBins / NT;
+    int local[BPT];
+    int lsum = 0;
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      local[u] = static_cast<int>(sm.hist[kRelBins - 1 - (threadIdx.x * BPT + u)]);
+      lsum += local[u];
+    }
+    int tot;
+    int run = block_exclusive_sum<NT>(lsum, sm.scan_tmp, tot);
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      if (run < k && run + local[u] >= k) {
+        sm.digit = kRelBins - 1 - (threadIdx.x * BPT + u);
+        sm.above = run;
+        sm.count = local[u];
+      }
+      run += local[u];
+    }
+    __syncthreads();
+  }
+  const uint32_t bstar = static_cast<uint32_t>(sm.digit);
+  const int above = sm.above;
+  const int bcount = sm.count;
+  if (bcount > kPCandCap) {
+    if (threadIdx.x == 0) fail_list[atomicAdd(fail_count, 1)] = static_cast<int32_t>(r);
+    return;
+  }
+  // 3. compaction by relative digit (64 consecutive entries per wave step,
+  // so the loop bound is wave-uniform for the ballots).
+  for (int c0 = wave * kWave; c0 < total; c0 += NT) {
+    const int c = c0 + lane;
+    const bool ok = c < total;
+    float v = 0.f;
+    int32_t id = 0;
+    if (ok) {
+      if (c < kPCache) {
+        v = sm.cache_s[c];
+        id = sm.cache_i[c];
+      } else {
+        const uint2 e = entry(c);
+        v = __uint_as_float(e.x);
+        id = static_cast<int32_t>(e.y);
+      }
+    }
+    const uint32_t d = rel(v);
+    const bool h = ok && d > bstar;
+    const bool at = ok && d == bstar;
+    const uint64_t mh = __ballot(h);
+    const uint64_t ma = __ballot(at);
+    if (mh) {
+      uint32_t pos = 0;
+      if (lane == 0) pos = atomicAdd(&sm.cnt_hi, static_cast<uint32_t>(__popcll(mh)));
+      pos = __shfl(pos, 0, kWave) + lanes_below(mh);
+      if (h && pos < static_cast<uint32_t>(k)) {
+        out[pos] = id;
+        if (out_s) out_s[pos] = v;
+      }
+    }
+    if (ma) {
+      uint32_t pos = 0;
+      if (lane == 0) pos = atomicAdd(&sm.cnt_at, static_cast<uint32_t>(__popcll(ma)));
+      pos = __shfl(pos, 0, kWave) + lanes_below(ma);
+      if (at && pos < static_cast<uint32_t>(kPCandCap)) {
+        sm.cand_score[pos] = v;
+        sm.cand_idx[pos] = id;
+      }
+    }
+  }
+  __syncthreads();
+  // 4. the (k - above) best of the b* list.
+  if (resolve_list<NT>(sm.cand_score, sm.cand_idx, bcount, k - above, out + above,
+                       out_s ? out_s + above : nullptr, sm.rs))
+    return;
+  // A bin of more than kRankMax equal-digit entries: exact fallback, reusing
+  // the cache area (no longer needed) for the radix select.
+  __syncthreads();
+  TopkSmem& tsm = *reinterpret_cast<TopkSmem*>(sm.cache_s);
+  const float* cs = sm.cand_score;
+  const int32_t* ci = sm.cand_idx;
+  block_topk<NT>(
+      bcount, k - above, [](int64_t) { return true; }, [=](int64_t j) { return float_key(cs[j]); },
+      [=](int64_t j) { return ci[j]; }, [=](int64_t j) { return cs[j]; }, out + above,
+      out_s ? out_s + above : nullptr, tsm);
 }
+static_assert(sizeof(TopkSmem) <= sizeof(float) * kPCache, "fallback fits the cache area");
 
 // Repair: queries whose candidates could not be certified are scored over
 // their whole prefix (16x16 MFMA key streaming) into this workgroup's scratch
@@ -568,17 +756,23 @@ PrefillPlan plan_prefill(const Shape& s, int32_t nh, int32_t k) {
   while (S < 8 && tiles * S < 512 && s.L / (2 * S) >= 2048) S *= 2;
   p.S = S;
   p.chunk = ((static_cast<int64_t>(s.L) + S - 1) / S + kTileKeys - 1) / kTileKeys * kTileKeys;
-  // Expected survivors per segment ~ 2.5k/S with a relative spread of about
-  // 1/sqrt(j) (j ~ 20 at the smallest sample quantile): 8k/S + 1024 leaves
-  // >10 sigma before a segment overflows.
-  const int64_t want = (8LL * k + S - 1) / S + 1024;
-  int64_t cap = want < p.chunk ? want : p.chunk;
+  // Candidates per (query, split): about margin * k * (split keys in the
+  // prefix) / n_q, at most margin * k * chunk / (L - T + 1).  The threshold
+  // comes from a sample quantile with relative spread ~1/sqrt(j) (j >= ~20);
+  // at j ~ 20 the count can run ~2x its mean in a few of thousands of
+  // queries: 2.5x + 16 sigma + 512 leaves overflow (then repair) very rare.
+  const double nmin = static_cast<double>(s.L - s.T + 1);
+  const double share = static_cast<double>(p.chunk) / nmin < 1.0 ? static_cast<double>(p.chunk) / nmin : 1.0;
+  const double mean = kSampleMargin * k * share;
+  int64_t cap = static_cast<int64_t>(2.5 * mean + 16.0 * __builtin_sqrt(mean) + 512.0);
+  cap = cap < p.chunk ? cap : p.chunk;
   cap = (cap + 63) / 64 * 64;
   p.cap = static_cast<int32_t>(cap);
   const int64_t rows = static_cast<int64_t>(s.batch) * s.T;
-  size_t off = align_up(static_cast<size_t>(rows) * S * cap * sizeof(uint2));
+  const size_t segs = static_cast<size_t>(rows) * S;
+  size_t off = align_up(segs * cap * sizeof(uint2));
   p.off_cnt = off;
-  off += align_up(static_cast<size_t>(rows) * S * sizeof(int32_t));
+  off += align_up(segs * sizeof(int32_t));
   p.off_tau = off;
   off += align_up(static_cast<size_t>(rows) * S * sizeof(float));
   p.off_fail = off;
@@ -633,8 +827,7 @@ hipError_t launch_prefill_score_topk(const Shape& s, int32_t nh, const int32_t* 
   if (e != hipSuccess) return e;
   const int64_t rows = static_cast<int64_t>(s.batch) * s.T;
   prefill_select_kernel<<<static_cast<unsigned>(rows), kTopkThreadsSel, 0, st>>>(
-      args.cand, args.cnt, args.tau, pl.S, pl.cap, s.L, s.T, k, idx, scores_out, fail_count,
-      fail_list);
+      args.cand, args.cnt, args.tau, pl.S, pl.cap, k, idx, scores_out, fail_count, fail_list);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nrt = nh <= 16 ? 1 : (nh <= 32 ? 2 : 4);

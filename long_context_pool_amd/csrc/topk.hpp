@@ -139,6 +139,48 @@ __device__ __forceinline__ void block_topk(int64_t n, int k, Valid valid, Key ke
   }
 }
 
+// ---------------------------------------------------------------- score digits
+
+constexpr int kDigits = 8192;  // histogram bins of key_digit
+
+// Histogram digit of a score: a monotone (non-decreasing) map of the
+// order-preserving key to [0, kDigits) that spends its bins where top-k
+// thresholds live.  Bin 0 holds every negative value, bin 1 zero (either
+// sign) and positive subnormals; positive values with binary exponent in a
+// 63-binade window get 128 bins per binade (7 mantissa bits: bins 0.8%
+// wide), values below or above the window share the window's first or last
+// bin.  A 13-bit prefix of the order-preserving key
+// would spend 7/8 of its bins on exponents that scores never reach and leave
+// bins 6% wide.
+constexpr int kExpLo = 127 - 31;  // window: values in [2^-31, 2^32)
+constexpr int kExpBins = 63;
+__device__ __forceinline__ uint32_t key_digit(float v) {
+  const uint32_t key = float_key(v);  // -0 has the key of +0
+  if (key < 0x80000000u) return 0u;
+  const uint32_t u = key & 0x7FFFFFFFu;
+  const int e = static_cast<int>(u >> 23);
+  if (e == 0) return 1u;
+  if (e < kExpLo) return 2u;
+  if (e >= kExpLo + kExpBins) return 2u + ((kExpBins - 1) << 7) + 127u;
+  return 2u + (static_cast<uint32_t>(e - kExpLo) << 7) + ((u >> 16) & 0x7Fu);
+}
+static_assert(2 + (kExpBins << 7) <= kDigits, "digit range");
+constexpr uint32_t kTopDigit = 2u + ((kExpBins - 1) << 7) + 127u;
+
+// The smallest order-preserving key (float_key) whose score has digit d, for
+// 0 <= d <= kTopDigit: key_digit(v) >= d  <=>  float_key(v) >= digit_lo_key(d).
+__device__ __forceinline__ uint32_t digit_lo_key(uint32_t d) {
+  if (d == 0) return 0u;
+  if (d == 1) return 0x80000000u;  // +0
+  if (d == 2) return 0x80800000u;  // smallest positive normal
+  const uint32_t b = d - 2;
+  return 0x80000000u | ((kExpLo + (b >> 7)) << 23) | ((b & 127u) << 16);
+}
+// The largest key with digit d.
+__device__ __forceinline__ uint32_t digit_hi_key(uint32_t d) {
+  return d >= kTopDigit ? 0xFFFFFFFFu : digit_lo_key(d + 1) - 1u;
+}
+
 // ---------------------------------------------------------------- list resolve
 //
 // The `need` best of a short LDS list (score, token), written to out[0..need)
@@ -150,7 +192,7 @@ __device__ __forceinline__ void block_topk(int64_t n, int k, Valid valid, Key ke
 // caller then falls back to block_topk.  All threads must call.
 
 constexpr int kRankMax = 256;
-constexpr int kDirectRank = 64;  // longer lists take the histogram cut first
+constexpr int kDirectRank = 128;  // longer lists take the histogram cut first
 constexpr int kResolveBins = 2048;
 
 struct ResolveSmem {
@@ -217,8 +259,16 @@ __device__ __forceinline__ bool resolve_list(const float* cs, const int32_t* ci,
     lo = min(lo, key);
     hi = max(hi, key);
   }
-  atomicMin(&rs.kmin, lo);
-  atomicMax(&rs.kmax, hi);
+  // One LDS atomic per wave: same-address atomics from every thread serialize.
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) {
+    lo = min(lo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), o, kWave)));
+    hi = max(hi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), o, kWave)));
+  }
+  if ((threadIdx.x & (kWave - 1)) == 0 && lo <= hi) {
+    atomicMin(&rs.kmin, lo);
+    atomicMax(&rs.kmax, hi);
+  }
   __syncthreads();
   const uint32_t kmin = rs.kmin, span = rs.kmax - rs.kmin;
   const int shift = span < static_cast<uint32_t>(kResolveBins) ? 0 : 32 - __clz(span) - 11;
@@ -252,17 +302,31 @@ __device__ __forceinline__ bool resolve_list(const float* cs, const int32_t* ci,
   const uint32_t b2 = static_cast<uint32_t>(rs.bin);
   const int above = rs.above, cnt2 = rs.count;
   if (cnt2 > kRankMax) return false;
-  for (int t = threadIdx.x; t < n; t += NT) {
-    const uint32_t bin = (float_key(cs[t]) - kmin) >> shift;
-    if (bin > b2) {
-      const int p = atomicAdd(&rs.n_hi, 1);
-      if (p < above) {
+  // Positions from wave ballots and one LDS atomic per wave and list (the
+  // loop bound is wave-uniform).
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int t0 = threadIdx.x - lane; t0 < n; t0 += NT) {
+    const int t = t0 + lane;
+    const bool ok = t < n;
+    const uint32_t bin = ok ? (float_key(cs[t]) - kmin) >> shift : 0u;
+    const bool h = ok && bin > b2;
+    const bool at = ok && bin == b2;
+    const uint64_t mh = __ballot(h);
+    const uint64_t ma = __ballot(at);
+    if (mh) {
+      int p = 0;
+      if (lane == 0) p = atomicAdd(&rs.n_hi, __popcll(mh));
+      p = __shfl(p, 0, kWave) + lanes_below(mh);
+      if (h && p < above) {
         out_idx[p] = ci[t];
         if (out_score) out_score[p] = cs[t];
       }
-    } else if (bin == b2) {
-      const int p = atomicAdd(&rs.n_at, 1);
-      if (p < kRankMax) {
+    }
+    if (ma) {
+      int p = 0;
+      if (lane == 0) p = atomicAdd(&rs.n_at, __popcll(ma));
+      p = __shfl(p, 0, kWave) + lanes_below(ma);
+      if (at && p < kRankMax) {
         rs.s2[p] = cs[t];
         rs.i2[p] = ci[t];
       }
