@@ -279,7 +279,8 @@ def main():
         achieved = alg_bytes / (m_call * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS,
-                "kernel": "misa_decode_step (step_route_kernel + decode_score_kernel)",
+                "kernel": "misa_decode_step call: step_route_kernel + decode_score_kernel + "
+                          "decode_compact_kernel + decode_resolve_kernel",
                 "algorithmic_bytes": alg_bytes,
                 "traffic": traffic_from_profile("misa_decode_step", args.workload, sha)}
     else:
@@ -288,7 +289,8 @@ def main():
         peak = MFMA_PEAK_TFLOPS[dtype]
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                 "frac": achieved / peak,
-                "kernel": "misa_score_topk (prefill_clear + prefill_score + prefill_select + prefill_repair)",
+                "kernel": "misa_score_topk call: prefill_clear_kernel + prefill_score_kernel + "
+                          "prefill_select_kernel + prefill_repair_kernel",
                 "algorithmic_flops": flops,
                 "traffic": traffic_from_profile("misa_score_topk", args.workload, sha)}
     roof["call_ms"] = m_call
