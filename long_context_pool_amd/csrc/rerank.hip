@@ -6,11 +6,14 @@
 // (held in registers); each 32-candidate column tile gathers its key rows
 // straight into B registers (lane l: candidate l%32, head-dim elements
 // [64*(l/32), +64) -- one contiguous run per lane).  The ReLU * w head sum is
-// taken on the accumulators.  With many query rows, one workgroup per query
-// keeps its k' scores in LDS and selects in place; with few rows (decode) the
-// candidates of a query are spread over many workgroups, scores go to the
-// workspace and a select kernel per query follows.
-// fp32: one thread per candidate (query rows staged in LDS), then the select.
+// taken on the accumulators.  Workgroup (chunk, query) scores 128 (fp8) or 64
+// (bf16) candidates per wave with every gather of the wave in flight before
+// its first MFMA, and writes the scores to the workspace; the gathers are
+// the cost, so the kernel keeps many of them in flight and no LDS.
+// fp32: one thread per candidate (query rows staged in LDS).
+// Then one workgroup per query selects the k best of its k' scores in
+// registers: a digit histogram in LDS, the threshold digit from a block scan,
+// a block-scan compaction, and an exact resolve of the threshold digit.
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma.hpp"
@@ -21,7 +24,6 @@ namespace misa {
 namespace {
 
 constexpr int kRerankThreads = 256;
-constexpr int kTopkThreads = 1024;
 constexpr int kMaxHeads = 64;
 
 template <int DT>
@@ -60,23 +62,6 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_score_kernel(
     acc += wsh[j] * fmaxf(dot, 0.f);
   }
   out[r * kprime + c] = acc;
-}
-
-__global__ __launch_bounds__(kTopkThreads) void topk_list_kernel(const float* __restrict__ sc,
-                                                                 const int32_t* __restrict__ cand,
-                                                                 int32_t kprime, int32_t L,
-                                                                 int32_t T, int32_t k,
-                                                                 int32_t* __restrict__ idx,
-                                                                 float* __restrict__ scores_out) {
-  __shared__ TopkFastSmem sm;
-  const int64_t r = static_cast<int64_t>(blockIdx.y) * T + blockIdx.x;
-  const int64_t pos = static_cast<int64_t>(L) - T + blockIdx.x;
-  const float* srow = sc + r * kprime;
-  const int32_t* crow = cand + r * kprime;
-  block_topk_fast<kTopkThreads>(
-      kprime, k, [=](int64_t i) { return crow[i] >= 0 && crow[i] <= pos; },
-      [=](int64_t i) { return srow[i]; }, [=](int64_t i) { return crow[i]; }, idx + r * k,
-      scores_out ? scores_out + r * k : nullptr, sm);
 }
 
 constexpr int kRRThreads = 256;
@@ -120,26 +105,38 @@ struct CandScorer {
     }
   }
 
-  // Score of this lane's column candidate whose key row starts at krow
-  // (always a valid row; the caller masks invalid candidates).
-  __device__ __forceinline__ float score(const void* krow) const {
+  // This lane's half of a key row (krow always a valid row; the caller
+  // masks invalid candidates).
+  struct KeyB {
+    uint4 b[DT == kBF16 ? 8 : 4];
+  };
+  __device__ __forceinline__ static KeyB load(const void* krow) {
     const int hf = lane_id() >> 5;
-    f32x16 acc[RT];
+    KeyB kb;
     if constexpr (DT == kBF16) {
       const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(krow) + 64 * hf);
-      uint4 b[8];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) b[ks] = src[ks];
+      for (int ks = 0; ks < 8; ++ks) kb.b[ks] = src[ks];
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(krow) + 64 * hf);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kb.b[u] = src[u];
+    }
+    return kb;
+  }
+
+  // Score of this lane's column candidate from its loaded key half.
+  __device__ __forceinline__ float compute(const KeyB& kb) const {
+    f32x16 acc[RT];
+    if constexpr (DT == kBF16) {
+      const uint4* b = kb.b;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
           acc[rt] = mfma32_bf16(a16[rt][ks], as_bf16x8(b[ks]), ks == 0 ? f32x16{} : acc[rt]);
     } else {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(krow) + 64 * hf);
-      uint4 b[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) b[u] = src[u];
+      const uint4* b = kb.b;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const i32x8 bb{(int)b[2 * ks].x, (int)b[2 * ks].y, (int)b[2 * ks].z, (int)b[2 * ks].w,
@@ -155,6 +152,8 @@ struct CandScorer {
       for (int i = 0; i < 16; ++i) part += wl[rt][i] * relu(acc[rt][i]);
     return part + __shfl_xor(part, 32, kWave);  // rows 4hf..: the other half-wave
   }
+
+  __device__ __forceinline__ float score(const void* krow) const { return compute(load(krow)); }
 };
 
 template <int DT>
@@ -163,45 +162,10 @@ __device__ __forceinline__ const void* key_row(const void* k, int64_t row) {
   else return static_cast<const uint8_t*>(k) + row * kD;
 }
 
-// One workgroup per query row: scores of all k' candidates in LDS, then the
-// top-k among the valid ones.
-template <int DT, int RT>
-__global__ __launch_bounds__(kRRThreads) void rerank_fused_kernel(
-    const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
-    const void* __restrict__ k, const float* __restrict__ k_scale,
-    const int32_t* __restrict__ cand, int32_t kprime, int32_t k_top, int32_t L, int32_t T,
-    int32_t H, int32_t* __restrict__ idx, float* __restrict__ scores_out) {
-  __shared__ float sc[kMaxKprime];
-  __shared__ TopkFastSmem sm;
-  const int64_t r = blockIdx.x;
-  const int64_t seq = r / T;
-  const int64_t pos = static_cast<int64_t>(L) - T + (r % T);
-  const int wave = threadIdx.x / kWave;
-  const int lane = lane_id();
-  const int32_t* crow = cand + r * kprime;
-  CandScorer<DT, RT> cs;
-  cs.init(q, q_scale, w, r, H);
-  const int ntile = (kprime + 31) / 32;
-  for (int ct = wave; ct < ntile; ct += kRRWaves) {
-    const int c = ct * 32 + (lane & 31);
-    const int32_t s = c < kprime ? crow[c] : -1;
-    const bool ok = s >= 0 && s <= pos;
-    const int64_t row = seq * L + (ok ? s : 0);
-    float v = cs.score(key_row<DT>(k, row));
-    if constexpr (DT == kFP8) v *= k_scale[row];
-    if (lane < 32 && c < kprime) sc[c] = v;
-  }
-  __syncthreads();
-  block_topk_fast<kRRThreads>(
-      kprime, k_top, [=](int64_t c) { return crow[c] >= 0 && crow[c] <= pos; },
-      [=](int64_t c) { return sc[c]; }, [=](int64_t c) { return crow[c]; }, idx + r * k_top,
-      scores_out ? scores_out + r * k_top : nullptr, sm);
-}
-
-// Few query rows: workgroup (chunk, row) scores 32 candidates per wave and
-// writes them to the workspace; topk_list_kernel selects afterwards.
-template <int DT, int RT>
-__global__ __launch_bounds__(kRRThreads) void rerank_split_kernel(
+// Workgroup (chunk, row): wave w scores NTW tiles of 32 candidates, issuing
+// every tile's key gathers (and fp8 key scales) before the first MFMA.
+template <int DT, int RT, int NTW>
+__global__ __launch_bounds__(kRRThreads) void rerank_gather_kernel(
     const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const void* __restrict__ k, const float* __restrict__ k_scale,
     const int32_t* __restrict__ cand, int32_t kprime, int32_t L, int32_t T, int32_t H,
@@ -211,15 +175,158 @@ __global__ __launch_bounds__(kRRThreads) void rerank_split_kernel(
   const int64_t pos = static_cast<int64_t>(L) - T + (r % T);
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
+  const int cbase = (blockIdx.x * kRRWaves + wave) * 32 * NTW + (lane & 31);
+  typename CandScorer<DT, RT>::KeyB kb[NTW];
+  bool okv[NTW];
+  float skv[NTW];
+#pragma unroll
+  for (int u = 0; u < NTW; ++u) {
+    const int c = cbase + 32 * u;
+    const int32_t s = c < kprime ? cand[r * kprime + c] : -1;
+    okv[u] = s >= 0 && s <= pos;
+    const int64_t row = seq * L + (okv[u] ? s : 0);
+    kb[u] = CandScorer<DT, RT>::load(key_row<DT>(k, row));
+    skv[u] = (DT == kFP8) ? k_scale[row] : 1.f;
+  }
   CandScorer<DT, RT> cs;
   cs.init(q, q_scale, w, r, H);
-  const int c = (blockIdx.x * kRRWaves + wave) * 32 + (lane & 31);
-  const int32_t s = c < kprime ? cand[r * kprime + c] : -1;
-  const bool ok = s >= 0 && s <= pos;
-  const int64_t row = seq * L + (ok ? s : 0);
-  float v = cs.score(key_row<DT>(k, row));
-  if constexpr (DT == kFP8) v *= k_scale[row];
-  if (lane < 32 && c < kprime) out[r * kprime + c] = ok ? v : -__builtin_inff();
+#pragma unroll
+  for (int u = 0; u < NTW; ++u) {
+    const int c = cbase + 32 * u;
+    const float v = cs.compute(kb[u]) * skv[u];
+    if (lane < 32 && c < kprime) out[r * kprime + c] = okv[u] ? v : -__builtin_inff();
+  }
+}
+
+// Top-k of one query's k' (score, candidate) list, in one 1024-thread
+// workgroup: the list is read once into registers, a digit histogram (LDS)
+// gives the threshold digit b*, a block scan places the entries above b* in
+// the output and those at b* in an LDS list, which is resolved exactly.
+// Invalid candidates carry score -inf and a distinct negative id (so ties
+// among them resolve), printed as -1 at the end.
+constexpr int kLSThreads = 1024;
+constexpr int kLSPer = kMaxKprime / kLSThreads;
+constexpr int kLSCap = 2048;
+
+struct LSelSmem {
+  uint32_t hist[kDigits];
+  alignas(16) float cand_score[kLSCap];
+  alignas(16) int32_t cand_idx[kLSCap];
+  ResolveSmem rs;
+  TopkSmem base;
+  int scan_tmp[32];
+  int digit, above, count;
+};
+
+__global__ __launch_bounds__(kLSThreads) void list_select_kernel(
+    const float* __restrict__ sc, const int32_t* __restrict__ cand, int32_t kprime, int32_t L,
+    int32_t T, int32_t k, int32_t* __restrict__ idx, float* __restrict__ scores_out) {
+  __shared__ LSelSmem sm;
+  const int64_t r = static_cast<int64_t>(blockIdx.y) * T + blockIdx.x;
+  const int64_t pos = static_cast<int64_t>(L) - T + blockIdx.x;
+  const float* srow = sc + r * kprime;
+  const int32_t* crow = cand + r * kprime;
+  int32_t* out = idx + r * k;
+  float* out_s = scores_out ? scores_out + r * k : nullptr;
+  for (int b = threadIdx.x; b < kDigits; b += kLSThreads) sm.hist[b] = 0;
+  float v[kLSPer];
+  int32_t id[kLSPer];
+#pragma unroll
+  for (int j = 0; j < kLSPer; ++j) {
+    const int i = j * kLSThreads + threadIdx.x;
+    const int ic = min(i, kprime - 1);
+    const float x = srow[ic];
+    const int32_t c = crow[ic];
+    const bool ok = c >= 0 && c <= pos;
+    v[j] = ok ? x : -__builtin_inff();
+    id[j] = ok ? c : -1 - i;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kLSPer; ++j)
+    if (j * kLSThreads + static_cast<int>(threadIdx.x) < kprime) atomicAdd(&sm.hist[key_digit(v[j])], 1u);
+  __syncthreads();
+  {
+    constexpr int BPT = kDigits / kLSThreads;
+    int local[BPT];
+    int lsum = 0;
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      local[u] = static_cast<int>(sm.hist[kDigits - 1 - (threadIdx.x * BPT + u)]);
+      lsum += local[u];
+    }
+    int tot;
+    int run = block_exclusive_sum<kLSThreads>(lsum, sm.scan_tmp, tot);
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+      if (run < k && run + local[u] >= k) {
+        sm.digit = kDigits - 1 - (threadIdx.x * BPT + u);
+        sm.above = run;
+        sm.count = local[u];
+      }
+      run += local[u];
+    }
+    __syncthreads();
+  }
+  const uint32_t bstar = static_cast<uint32_t>(sm.digit);
+  const int above = sm.above;
+  const int bcount = sm.count;
+  if (bcount > kLSCap) {
+    // Exact fallback over the whole list (e.g. fewer than k valid candidates
+    // with thousands of -inf ties).
+    block_topk<kLSThreads>(
+        kprime, k, [](int64_t) { return true; },
+        [=](int64_t i) { const int32_t c = crow[i]; return float_key(c >= 0 && c <= pos ? srow[i] : -__builtin_inff()); },
+        [=](int64_t i) { const int32_t c = crow[i]; return c >= 0 && c <= pos ? c : static_cast<int32_t>(-1 - i); },
+        [=](int64_t i) { const int32_t c = crow[i]; return c >= 0 && c <= pos ? srow[i] : -__builtin_inff(); },
+        out, out_s, sm.base);
+  } else {
+    const uint32_t lo = digit_lo_key(bstar), hi = digit_hi_key(bstar);
+    uint32_t mh = 0, ma = 0;
+#pragma unroll
+    for (int j = 0; j < kLSPer; ++j) {
+      const bool in = j * kLSThreads + static_cast<int>(threadIdx.x) < kprime;
+      const uint32_t key = float_key(v[j]);
+      mh |= (in && key > hi) ? (1u << j) : 0u;
+      ma |= (in && key >= lo && key <= hi) ? (1u << j) : 0u;
+    }
+    // Packed counts: above-b* in the low 16 bits (< k <= 8192), at-b* high.
+    int total;
+    const int off = block_exclusive_sum<kLSThreads>(__popc(mh) | (__popc(ma) << 16), sm.scan_tmp,
+                                                    total);
+    int ph = off & 0xFFFF;
+    int pa = off >> 16;
+#pragma unroll
+    for (int j = 0; j < kLSPer; ++j) {
+      if ((mh >> j) & 1u) {
+        if (ph < k) {
+          out[ph] = id[j];
+          if (out_s) out_s[ph] = v[j];
+        }
+        ++ph;
+      } else if ((ma >> j) & 1u) {
+        if (pa < kLSCap) {
+          sm.cand_score[pa] = v[j];
+          sm.cand_idx[pa] = id[j];
+        }
+        ++pa;
+      }
+    }
+    __syncthreads();
+    if (!resolve_list<kLSThreads>(sm.cand_score, sm.cand_idx, bcount, k - above, out + above,
+                                  out_s ? out_s + above : nullptr, sm.rs)) {
+      __syncthreads();
+      const float* cs = sm.cand_score;
+      const int32_t* ci = sm.cand_idx;
+      block_topk<kLSThreads>(
+          bcount, k - above, [](int64_t) { return true; }, [=](int64_t j) { return float_key(cs[j]); },
+          [=](int64_t j) { return ci[j]; }, [=](int64_t j) { return cs[j]; }, out + above,
+          out_s ? out_s + above : nullptr, sm.base);
+    }
+  }
+  __syncthreads();
+  for (int p = threadIdx.x; p < k; p += kLSThreads)
+    if (out[p] < 0) out[p] = -1;
 }
 
 }  // namespace
@@ -236,18 +343,15 @@ hipError_t launch_rerank(const Shape& s, int32_t kprime, int32_t k, const void* 
   float* sc = static_cast<float*>(ws);
   if (s.dtype != kF32) {
     const bool two = s.H > 32;
-    if (rows >= 64) {
-#define RF(DT, RT) rerank_fused_kernel<DT, RT><<<static_cast<unsigned>(rows), kRRThreads, 0, st>>>(q, q_scale, w, kk, k_scale, cand, kprime, k, s.L, s.T, s.H, idx, scores_out)
-      if (s.dtype == kBF16) { if (two) RF(kBF16, 2); else RF(kBF16, 1); }
-      else { if (two) RF(kFP8, 2); else RF(kFP8, 1); }
-#undef RF
-      return hipGetLastError();
-    }
-    dim3 g((kprime + kRRWaves * 32 - 1) / (kRRWaves * 32), static_cast<unsigned>(rows));
-#define RS(DT, RT) rerank_split_kernel<DT, RT><<<g, kRRThreads, 0, st>>>(q, q_scale, w, kk, k_scale, cand, kprime, s.L, s.T, s.H, sc)
-    if (s.dtype == kBF16) { if (two) RS(kBF16, 2); else RS(kBF16, 1); }
-    else { if (two) RS(kFP8, 2); else RS(kFP8, 1); }
-#undef RS
+    // Gathers in flight per wave: 4 tiles (fp8: 64 B per lane each) or 2
+    // (bf16: 128 B per lane each).
+    constexpr int kNtwF8 = 4, kNtwB16 = 2;
+    const int ntw = s.dtype == kBF16 ? kNtwB16 : kNtwF8;
+    dim3 g((kprime + kRRWaves * 32 * ntw - 1) / (kRRWaves * 32 * ntw), static_cast<unsigned>(rows));
+#define RG(DT, RT, NTW) rerank_gather_kernel<DT, RT, NTW><<<g, kRRThreads, 0, st>>>(q, q_scale, w, kk, k_scale, cand, kprime, s.L, s.T, s.H, sc)
+    if (s.dtype == kBF16) { if (two) RG(kBF16, 2, kNtwB16); else RG(kBF16, 1, kNtwB16); }
+    else { if (two) RG(kFP8, 2, kNtwF8); else RG(kFP8, 1, kNtwF8); }
+#undef RG
   } else {
     dim3 g1((kprime + kRerankThreads - 1) / kRerankThreads, s.T, s.batch);
     rerank_score_kernel<kF32><<<g1, kRerankThreads, 0, st>>>(q, q_scale, w, kk, k_scale, cand,
@@ -256,7 +360,7 @@ hipError_t launch_rerank(const Shape& s, int32_t kprime, int32_t k, const void* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(s.T, s.batch);
-  topk_list_kernel<<<g2, kTopkThreads, 0, st>>>(sc, cand, kprime, s.L, s.T, k, idx, scores_out);
+  list_select_kernel<<<g2, kLSThreads, 0, st>>>(sc, cand, kprime, s.L, s.T, k, idx, scores_out);
   return hipGetLastError();
 }
 
