@@ -101,6 +101,48 @@ struct PrefillArgs {
   float* tau;            // [rows*S]
 };
 
+// Buffer resource over [base, base + bytes): loads past the end read zero,
+// stores past it are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+// Direct buffer-to-LDS loads: lane l's 16 (4) bytes at voff land at
+// lds + 16 l (4 l); lds is wave-uniform.
+__device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void load4_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void buffer_store_u32x2(uint32_t lo, uint32_t hi, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, r, off, 0, 0);
+}
+// Wait until at most N vector-memory operations of this wave are
+// outstanding, then a workgroup barrier; the signal fences keep the
+// compiler from moving memory operations across.
+template <int N>
+__device__ __forceinline__ void vmcnt_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate in the low field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ void vmcnt_zero() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+
+// A pointer the compiler cannot prove wave-uniform but that is: pinned to
+// scalar registers (a buffer resource built from it then needs no per-lane
+// loop).
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 template <int DT, int HPQ>
 __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs a) {
   constexpr int QPW = qpw<HPQ>();
@@ -109,11 +151,23 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
   constexpr int RB = lds_row_bytes<DT>();
   constexpr int TILE_BYTES = kTileKeys * RB;
   constexpr int SAMPLE_BYTES = kPWaves * QPW * kSamples * 2;  // top 16 bits of each sample's key
-  constexpr int STAGE_BYTES = 32 * RB;  // one 32-key sample tile, after the sample area
-  constexpr int LDS_BYTES = (2 * TILE_BYTES > SAMPLE_BYTES + STAGE_BYTES) ? 2 * TILE_BYTES
-                                                                          : SAMPLE_BYTES + STAGE_BYTES;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
-  __shared__ float sk_tile[3][kTileKeys];  // fp8 key scales: tile buffers 0, 1 and the sample stage
+  constexpr int STAGE_BYTES = 32 * RB;                        // one 32-key sample tile
+  constexpr int NDMA = (TILE_BYTES + 4 * 1024 - 1) / (4 * 1024);  // 1 KiB direct loads per thread per tile
+  // Three main-pass tile buffers, separate objects so that the compiler can
+  // tell a buffer being filled by direct loads from the one being read.  The
+  // sample pass borrows them first: the samples of waves 0-1 in buffer 0,
+  // of waves 2-3 in buffer 1, its key stage in buffer 2.
+  constexpr int BUF_DMA = kPWaves * NDMA * 1024;
+  constexpr int BUF_BYTES = BUF_DMA > SAMPLE_BYTES / 2 ? BUF_DMA : SAMPLE_BYTES / 2;
+  static_assert(STAGE_BYTES <= BUF_BYTES, "sample stage fits a tile buffer");
+  __shared__ __attribute__((aligned(16))) uint8_t tb0[BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t tb1[BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t tb2[BUF_BYTES];
+  __shared__ float sk_tile[kTileKeys];  // fp8 key scales of the sample stage
+  // fp8 key scales of the tile in buffer 0, 1, 2 (one copy per wave).
+  __shared__ float sk0[DT == kFP8 ? kPWaves : 1][kTileKeys];
+  __shared__ float sk1[DT == kFP8 ? kPWaves : 1][kTileKeys];
+  __shared__ float sk2[DT == kFP8 ? kPWaves : 1][kTileKeys];
 
   // XCD-aware numbering: workgroups of one split share an XCD (id % 8).
   const int id = blockIdx.x;
@@ -125,7 +179,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
   const int t0 = static_cast<int>(qt_global % a.nqt) * QWG;
 
   const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int hf = lane >> 5;
   const int colr = lane & 31;
   const int tw0 = t0 + wave * QPW;  // first query of this wave
@@ -226,50 +280,6 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
     }
   };
 
-  // Stage keys into an LDS tile: 64 keys, thread t takes key t/4, quarter t%4.
-  // Keys past the split's range load a clamped (valid) row; their scores are
-  // masked.  The staging values are named fields, not an array, so they stay
-  // in registers across the tile's compute.
-  struct TileRegs {
-    uint4 v0, v1, v2, v3;
-    float sk;
-  };
-  auto load_tile = [&](int64_t tile_idx) -> TileRegs {
-    const int kr = threadIdx.x >> 2;
-    const int qd = threadIdx.x & 3;
-    const int64_t key = s_begin + tile_idx * kTileKeys + kr;
-    const int64_t row = seq * a.L + (key < s_end ? key : s_safe);
-    TileRegs t;
-    if constexpr (DT == kBF16) {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + row * kD + 32 * qd);
-      t.v0 = src[0];
-      t.v1 = src[1];
-      t.v2 = src[2];
-      t.v3 = src[3];
-      t.sk = 1.f;
-    } else {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.k) + row * kD + 32 * qd);
-      t.v0 = src[0];
-      t.v1 = src[1];
-      t.v2 = t.v3 = make_uint4(0, 0, 0, 0);
-      t.sk = a.k_scale[row];
-    }
-    return t;
-  };
-  auto store_tile = [&](uint8_t* tile, int buf, const TileRegs& t) {
-    const int kr = threadIdx.x >> 2;
-    const int qd = threadIdx.x & 3;
-    uint4* dst = reinterpret_cast<uint4*>(tile + kr * RB + (DT == kBF16 ? 64 : 32) * qd);
-    dst[0] = t.v0;
-    dst[1] = t.v1;
-    if constexpr (DT == kBF16) {
-      dst[2] = t.v2;
-      dst[3] = t.v3;
-    } else {
-      if (qd == 0) sk_tile[buf][kr] = t.sk;
-    }
-  };
-
   // Query positions of this lane's slots (and of the wave's queries).
   int pos_slot[NS];  // L < 2^31
 #pragma unroll
@@ -280,13 +290,12 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
 
   // ---- 1. sample pass: thresholds per (query, split).
   const int64_t len = s_end - s_begin;
-  uint16_t* smp = reinterpret_cast<uint16_t*>(lds) + wave * QPW * kSamples;  // [QPW][kSamples]
+  uint16_t* smp = reinterpret_cast<uint16_t*>(wave < 2 ? tb0 : tb1) + (wave & 1) * QPW * kSamples;  // [QPW][kSamples]
   float tau_slot[NS];
-  // Sample tiles (32 keys) are staged after the sample area; each tile's
-  // scores go straight to the sample area (sample m of query qw at
-  // smp[qw][m]).  The main pass later reuses all of it for its tile buffers.
+  // Sample tiles (32 keys) are staged in buffer 2; each tile's scores go
+  // straight to the sample area (sample m of query qw at smp[qw][m]).
   {
-    uint8_t* stage = lds + SAMPLE_BYTES;
+    uint8_t* stage = tb2;
     const int kr = threadIdx.x >> 3;  // 8 threads per key row
     const int part = threadIdx.x & 7;
     for (int st = 0; st < kSamples / 32; ++st) {
@@ -308,7 +317,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
         const float skr = (key_ld >= 0 && part == 0) ? a.k_scale[seq * a.L + key_ld] : 1.f;
         __syncthreads();
         *reinterpret_cast<uint4*>(stage + kr * RB + 16 * part) = v0;
-        if (part == 0) sk_tile[2][kr] = skr;
+        if (part == 0) sk_tile[kr] = skr;
       }
       __syncthreads();
       float out[NS];
@@ -316,7 +325,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
       const int m = st * 32 + colr;
       const int64_t key = len > 0 ? s_begin + (static_cast<int64_t>(m) * len) / kSamples : -1;
       float skv = 1.f;
-      if constexpr (DT == kFP8) skv = sk_tile[2][colr];
+      if constexpr (DT == kFP8) skv = sk_tile[colr];
 #pragma unroll
       for (int sl = 0; sl < NS; ++sl) {
         const bool ok = key >= 0 && key <= pos_slot[sl];
@@ -392,63 +401,211 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
   __syncthreads();  // sample area is reused as tile buffers below
 
   // ---- 2. full pass over [s_begin, s_end): append scores >= tau.
-  // Candidate counts per (slot, half): (sl, h) is query slot_query(sl, h) --
-  // a bijection onto the wave's queries for h = 8, 16 (only h = 0 is used
-  // for 32, 64).  Wave-uniform values; a lane picks its half with one select.
-  // The counts go to cnt at the end (they may exceed the capacity: the
-  // select kernel then queues the query for repair).
+  //
+  // Key tiles (64 keys) reach LDS by direct buffer-to-LDS loads (no VGPR
+  // staging, no LDS store instructions) into three buffers: tile ti+2 is in
+  // flight while tile ti is multiplied.  Every thread issues the same number
+  // of vector-memory operations per tile (NL loads, NSTEP candidate stores
+  // per column tile), so a fixed vmcnt wait before each barrier proves that
+  // the next tile has landed.  The column tiles are software-pipelined: the
+  // MFMAs of column tile j run while the epilogue (ReLU * w head sum,
+  // threshold test, candidate append) of column tile j-1 executes, with no
+  // branch in either, so the two interleave.
+  //
+  // Candidate append: per slot, the wave ballot of passing lanes gives each
+  // lane its position in its half's (query's) segment; the entry is written
+  // by a buffer store whose offset is pushed out of range for lanes that do
+  // not pass, and positions past the capacity are clamped onto the last
+  // slot (the count still grows, which sends the query to repair).
+  constexpr int ROWB = kD * (DT == kBF16 ? 2 : 1);  // key row bytes in HBM
+  constexpr int NL = NDMA + (DT == kFP8 ? 1 : 0);
+  // This thread's byte offset inside a tile's key rows for each of its DMA
+  // slots (LDS row pitch RB keeps the MFMA operand reads conflict-free; the
+  // 16-byte pads and the spare tail load row 0, never read).
+  uint32_t dma_off[NDMA];
+#pragma unroll
+  for (int j = 0; j < NDMA; ++j) {
+    const int o = 1024 * (NDMA * wave + j) + 16 * lane;
+    const int r = o / RB, c = (o % RB) / 16;
+    dma_off[j] = (r < kTileKeys && c < ROWB / 16) ? static_cast<uint32_t>(r * ROWB + 16 * c) : 0u;
+  }
+  const uint8_t* kseq = static_cast<const uint8_t*>(a.k) + seq * a.L * static_cast<int64_t>(ROWB);
+  const float* kscale_seq = (DT == kFP8) ? a.k_scale + seq * a.L : nullptr;
+  // Tile ti -> LDS buffer tb (key scales: sk); rows at or past s_end read as
+  // zero.
+  auto issue = [&](int64_t ti, uint8_t* tb, float (*sk)[kTileKeys]) __attribute__((always_inline)) {
+    const int64_t key0 = s_begin + ti * kTileKeys;
+    const int64_t nrows = s_end - key0;
+    const int32_t nb = nrows <= 0 ? 0 : static_cast<int32_t>(nrows < kTileKeys ? nrows : kTileKeys);
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kseq + (nrows <= 0 ? 0 : key0 * ROWB), nb * ROWB);
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) load16_to_lds(rk, tb + 1024 * (NDMA * wave + j), dma_off[j]);
+    if constexpr (DT == kFP8) {
+      const __amdgpu_buffer_rsrc_t rsk = buffer_rsrc(kscale_seq + (nrows <= 0 ? 0 : key0), nb * 4);
+      load4_to_lds(rsk, &sk[wave][0], 4u * lane);
+    }
+  };
+  // Per-slot constants: the last key a slot may take (split end and causal
+  // bound), and the byte offset of the slot's segment from the wave's first.
   const bool owner = HPQ < 32 || hf == 0;
+  int lim_slot[NS];
+  uint32_t seg_off[NS];
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) {
+    const int64_t lim = min<int64_t>(s_end - 1, pos_slot[sl]);
+    lim_slot[sl] = owner ? static_cast<int>(lim) : -1;
+    seg_off[sl] = static_cast<uint32_t>(slot_query<HPQ>(sl, hf)) * static_cast<uint32_t>(a.S) *
+                  static_cast<uint32_t>(a.cap) * 8u;
+  }
+  const __amdgpu_buffer_rsrc_t rcand =
+      buffer_rsrc(uniform_ptr(a.cand + ((seq * a.T + tw0) * a.S + split) * static_cast<int64_t>(a.cap)),
+                  __builtin_amdgcn_readfirstlane(QPW * a.S * a.cap * 8));
+  const uint32_t cap_last = static_cast<uint32_t>(a.cap - 1);
+  // Candidate counts per (slot, half): scalar; (sl, h) is query
+  // slot_query(sl, h).  They go to cnt at the end and may exceed the
+  // capacity (the select kernel then queues the query for repair).
   int ctr2[NS][2];
 #pragma unroll
   for (int sl = 0; sl < NS; ++sl) ctr2[sl][0] = ctr2[sl][1] = 0;
-  // This lane's candidate segment per slot (its half's query).
-  uint2* segp[NS];
+
+  // Epilogue, in parts: part 2*sl sums slot sl's heads (ReLU * w), part
+  // 2*sl+1 tests and appends it.  live = false marks a placeholder column
+  // tile that stores nothing but issues the same instructions.
+  auto epi_part = [&](int p, const f32x16 (&acc)[kRT], int key0, bool live, float sk, float (&out)[NS])
+      __attribute__((always_inline)) {
+    const int sl = p >> 1;
+    if ((p & 1) == 0) {
+      float sum = 0.f;
+      if constexpr (HPQ == 8) {
 #pragma unroll
-  for (int sl = 0; sl < NS; ++sl) {
-    const int t = tw0 + slot_query<HPQ>(sl, hf);
-    segp[sl] = a.cand + ((seq * a.T + (t < a.T ? t : 0)) * a.S + split) * a.cap;
-  }
-  const uint64_t half_mask = hf ? 0xFFFFFFFF00000000ull : 0x00000000FFFFFFFFull;
-  // Keys below the wave's first query position are in every slot's prefix.
-  const int64_t pos_wave_min = static_cast<int64_t>(a.L) - a.T + tw0;
-  const int64_t ntiles = len > 0 ? (len + kTileKeys - 1) / kTileKeys : 0;
-  TileRegs reg = load_tile(0);  // unconditional (clamped rows when empty)
-  store_tile(lds, 0, reg);
-  __syncthreads();
-  for (int64_t ti = 0; ti < ntiles; ++ti) {
-    const int buf = static_cast<int>(ti & 1);
-    uint8_t* tile = lds + buf * TILE_BYTES;
-    // The next tile's keys (past the end: clamped rows, never read), loaded
-    // and stored unconditionally so the staging registers stay registers.
-    reg = load_tile(ti + 1);
-    const int64_t tbase = s_begin + ti * kTileKeys;
-    // Wave-uniform: no causal / range check needed inside this tile.
-    const bool interior = tbase + kTileKeys <= s_end && tbase + kTileKeys - 1 <= pos_wave_min;
+        for (int i = 0; i < 8; ++i) sum += wl[sl >> 1][8 * (sl & 1) + i] * relu(acc[sl >> 1][8 * (sl & 1) + i]);
+      } else if constexpr (HPQ == 16 || HPQ == 32) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float out[NS];
-      score_tile(tile, c, out);
-      const int key = static_cast<int>(tbase) + 32 * c + colr;
-      float skv = 1.f;
-      if constexpr (DT == kFP8) skv = sk_tile[buf][32 * c + colr];
+        for (int i = 0; i < 16; ++i) sum += wl[sl][i] * relu(acc[sl][i]);
+      } else {
 #pragma unroll
-      for (int sl = 0; sl < NS; ++sl) {
-        const float v = out[sl] * skv;
-        bool pass = owner && v >= tau_slot[sl];
-        if (!interior) pass = pass && key < s_end && key <= pos_slot[sl];
-        const uint64_t m = __ballot(pass);
-        if (m == 0) continue;
-        if (pass) {
-          const int p = (hf ? ctr2[sl][1] : ctr2[sl][0]) + lanes_below(m & half_mask);
-          if (p < a.cap) segp[sl][p] = make_uint2(__float_as_uint(v), static_cast<uint32_t>(key));
+        for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sum += wl[rt][i] * relu(acc[rt][i]);
+      }
+      if constexpr (HPQ >= 32) sum += __shfl_xor(sum, 32, kWave);
+      out[sl] = (DT == kFP8) ? sum * sk : sum;
+      return;
+    }
+    const int key = key0 + colr;
+    const float v = out[sl];
+    const uint64_t m = __builtin_amdgcn_ballot_w64(v >= tau_slot[sl]) &
+                       __builtin_amdgcn_ballot_w64(key <= lim_slot[sl]) & (live ? ~0ull : 0ull);
+    const uint32_t mlo = static_cast<uint32_t>(m), mhi = static_cast<uint32_t>(m >> 32);
+    // Position in this lane's half: lower half ctr_lo + passing lanes below
+    // it; upper half ctr_hi + passing upper lanes below it, which is the
+    // 64-lane count plus (ctr_hi - popcount(mlo)).
+    const uint32_t base = hf ? static_cast<uint32_t>(ctr2[sl][1]) - __builtin_popcount(mlo)
+                             : static_cast<uint32_t>(ctr2[sl][0]);
+    uint32_t pos = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, base));
+    pos = pos < cap_last ? pos : cap_last;
+    // Out of range (dropped) for lanes that do not pass; no select on the
+    // offset itself, so the step stays one basic block.
+    const uint32_t oob = __builtin_amdgcn_inverse_ballot_w64(m) ? 0u : 0x80000000u;
+    const uint32_t off = (seg_off[sl] + 8u * pos) | oob;
+    buffer_store_u32x2(__float_as_uint(v), static_cast<uint32_t>(key), rcand, off);
+    ctr2[sl][0] += __builtin_popcount(mlo);
+    ctr2[sl][1] += __builtin_popcount(mhi);
+  };
+
+  // One step: acc = this wave's rows x column tile c of buffer tb (skv = the
+  // fp8 scale of this lane's key column), with the epilogue of the previous
+  // column tile (pacc, its first key pkey0) spread between the k-steps.  The
+  // B operands are read two k-steps ahead; scheduling barriers keep the
+  // order, so the VALU work runs while the MFMAs execute.
+  constexpr int NKS = DT == kBF16 ? 8 : 2;
+  constexpr int NP = 2 * NS;
+  auto step = [&](const uint8_t* tb, const float (*sk)[kTileKeys], int c, f32x16 (&acc)[kRT], float& skv,
+                  const f32x16 (&pacc)[kRT], int pkey0, bool plive, float pskv) __attribute__((always_inline)) {
+    const uint8_t* brow = tb + (32 * c + colr) * RB;
+    float out[NS];
+    if constexpr (DT == kBF16) {
+      uint4 bv[3];
+      bv[0] = *reinterpret_cast<const uint4*>(brow + 128 * hf);
+      bv[1] = *reinterpret_cast<const uint4*>(brow + 128 * hf + 16);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (ks + 2 < NKS) bv[(ks + 2) % 3] = *reinterpret_cast<const uint4*>(brow + 128 * hf + 16 * (ks + 2));
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt)
+          acc[rt] = mfma32_bf16(a16[rt][ks], as_bf16x8(bv[ks % 3]), ks == 0 ? f32x16{} : acc[rt]);
+#pragma unroll
+        for (int p = ks * NP / NKS; p < (ks + 1) * NP / NKS; ++p) epi_part(p, pacc, pkey0, plive, pskv, out);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      skv = 1.f;
+    } else {
+      i32x8 bv[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(brow + 64 * hf + 32 * ks);
+        const uint4 hi = *reinterpret_cast<const uint4*>(brow + 64 * hf + 32 * ks + 16);
+        bv[ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+      skv = sk[wave][32 * c + colr];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) {
+          acc[rt] = mfma32_fp8(a8[rt][ks], bv[ks], ks == 0 ? f32x16{} : acc[rt]);
+          constexpr int PPM = NP / (NKS * kRT) > 0 ? NP / (NKS * kRT) : 1;  // parts per MFMA
+          const int m = ks * kRT + rt;
+#pragma unroll
+          for (int p = m * PPM; p < (m + 1) * PPM && p < NP; ++p) epi_part(p, pacc, pkey0, plive, pskv, out);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        ctr2[sl][0] += __popcll(m & 0x00000000FFFFFFFFull);
-        ctr2[sl][1] += __popcll(m >> 32);
       }
     }
-    store_tile(lds + (buf ^ 1) * TILE_BYTES, buf ^ 1, reg);
-    __syncthreads();
+  };
+  // Epilogue only (the last column tile).
+  auto epi_all = [&](const f32x16 (&pacc)[kRT], int pkey0, float pskv) __attribute__((always_inline)) {
+    float out[NS];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) epi_part(p, pacc, pkey0, true, pskv, out);
+  };
+
+  const int64_t ntiles = len > 0 ? (len + kTileKeys - 1) / kTileKeys : 0;
+  // vmcnt(N) with N = the operations issued after the tile that must have
+  // landed: the next tile's loads and one step's stores.
+  constexpr int kWaitCnt = NL + NS;
+  if (ntiles > 0) {
+    issue(0, tb0, sk0);
+    issue(1, tb1, sk1);
+    vmcnt_barrier<NL>();  // tile 0 landed (tile 1 may be in flight)
+    f32x16 acc_a[kRT], acc_b[kRT];
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) acc_b[rt] = f32x16{};
+    float sk_a = 1.f, sk_b = 1.f;
+    // Column tile 0 beside a placeholder epilogue.
+    step(tb0, sk0, 0, acc_a, sk_a, acc_b, 0, false, 1.f);
+    // Tile ti sits in buffer ti % 3: the loop is unrolled by three so that
+    // every buffer reference is static.
+    auto tile_iter = [&](int64_t ti, uint8_t* tcur, float (*scur)[kTileKeys], uint8_t* tnext,
+                         float (*snext)[kTileKeys], uint8_t* tfill, float (*sfill)[kTileKeys])
+        __attribute__((always_inline)) {
+      const int key0 = static_cast<int>(s_begin + ti * kTileKeys);
+      issue(ti + 2, tfill, sfill);
+      compiler_fence();
+      step(tcur, scur, 1, acc_b, sk_b, acc_a, key0, true, sk_a);
+      vmcnt_barrier<kWaitCnt>();
+      if (ti + 1 < ntiles) step(tnext, snext, 0, acc_a, sk_a, acc_b, key0 + 32, true, sk_b);
+      else epi_all(acc_b, key0 + 32, sk_b);
+    };
+    for (int64_t ti = 0; ti < ntiles; ti += 3) {
+      tile_iter(ti, tb0, sk0, tb1, sk1, tb2, sk2);
+      if (ti + 1 >= ntiles) break;
+      tile_iter(ti + 1, tb1, sk1, tb2, sk2, tb0, sk0);
+      if (ti + 2 >= ntiles) break;
+      tile_iter(ti + 2, tb2, sk2, tb0, sk0, tb1, sk1);
+    }
   }
+  // No load may still be writing LDS when the wave ends.
+  vmcnt_zero();
   if (lane == 0) {
 #pragma unroll
     for (int sl = 0; sl < NS; ++sl)
@@ -795,7 +952,9 @@ void launch_prefill_dt(const Shape& s, const PrefillPlan& pl, PrefillArgs args, 
 
 }  // namespace
 
-bool prefill_supported(const Shape& s) { return s.T > 1 && s.dtype != kF32; }
+// The candidate stores address a wave's segments through a buffer resource
+// with 32-bit offsets (at most ~64 L bytes): L up to 2^24 keeps them below 2^31.
+bool prefill_supported(const Shape& s) { return s.T > 1 && s.dtype != kF32 && s.L <= (1 << 24); }
 
 size_t prefill_ws_bytes(const Shape& s, int32_t nh, int32_t k) {
   return plan_prefill(s, nh, k).total;

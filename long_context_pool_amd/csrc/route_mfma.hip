@@ -9,8 +9,8 @@
 // rounding of p costs ~1e-3 relative in E on short prefixes), 32x32x16 MFMA
 // tiles, ReLU and a masked
 // running sum on the accumulators, then one cross-lane reduction per row.
-// The partial last block (B not dividing n_t) is averaged from the raw keys
-// and dotted in fp32.  Then E_{t,j} = |w_{t,j}| * s_t * (S + partial) / M_t
+// The partial last block (B not dividing n_t) uses ReLU(mean_s q . k_s): the
+// per-key dots come from the same MFMA tiles on the raw keys.  Then E_{t,j} = |w_{t,j}| * s_t * (S + partial) / M_t
 // (s_t = the fp8 query scale, else 1) and the h best heads are picked by h
 // rounds of a wave arg-max (ties to the lower head) and written ascending.
 //
@@ -72,31 +72,35 @@ __device__ __forceinline__ void load_q_rows(const void* q, int64_t r, int H, bf1
   }
 }
 
-// acc (rows x 32 blocks) = A . (B_hi [+ B_lo]); rs += ReLU(acc) when col_ok.
-// The hi and lo products of every row tile go to separate accumulators so the
-// MFMA chains are independent.
+// acc (rows x 32 blocks) = A . B_hi [+ A . B_lo]; rs += ReLU(acc) when
+// col_ok.  B comes from the LDS tile (rows of kLdsRow bytes: this lane's
+// block row, its 64-element half); the hi and lo products share one
+// accumulator per row tile, the RT row tiles giving independent chains.
 template <int RT, bool SPLIT>
-__device__ __forceinline__ void accumulate_tile(const bf16x8 (&a)[RT][8], const bf16x8 (&bh)[8],
-                                                const bf16x8 (&bl)[8], bool col_ok,
+__device__ __forceinline__ void accumulate_tile(const bf16x8 (&a)[RT][8], const uint8_t* bhi,
+                                                const uint8_t* blo, bool col_ok,
                                                 f32x16 (&rs)[RT]) {
-  f32x16 acc[RT], acl[RT];
+  const uint4* ph = reinterpret_cast<const uint4*>(bhi);
+  const uint4* pl = reinterpret_cast<const uint4*>(blo);
+  f32x16 acc[RT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    acc[rt] = f32x16{};
-    acl[rt] = f32x16{};
-  }
+  for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks)
+  for (int ks = 0; ks < 8; ++ks) {
+    const bf16x8 bh = as_bf16x8(ph[ks]);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      acc[rt] = mfma32_bf16(a[rt][ks], bh[ks], acc[rt]);
-      if constexpr (SPLIT) acl[rt] = mfma32_bf16(a[rt][ks], bl[ks], acl[rt]);
+    for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_bf16(a[rt][ks], bh, acc[rt]);
+    if constexpr (SPLIT) {
+      const bf16x8 bl = as_bf16x8(pl[ks]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_bf16(a[rt][ks], bl, acc[rt]);
     }
+  }
   if (col_ok) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) rs[rt][i] += relu(SPLIT ? acc[rt][i] + acl[rt][i] : acc[rt][i]);
+      for (int i = 0; i < 16; ++i) rs[rt][i] += relu(acc[rt][i]);
   }
 }
 
@@ -142,9 +146,8 @@ __global__ __launch_bounds__(kRThreads) void route_prefill_kernel(
     const float* __restrict__ k_scale, int32_t* __restrict__ heads, float* __restrict__ E_out,
     int32_t L, int32_t T, int32_t H, int32_t B, int64_t M, int32_t h) {
   constexpr bool SPLIT = DT == kBF16;
-  __shared__ __attribute__((aligned(16))) uint8_t tile[SPLIT ? 2 : 1][32 * kLdsRow];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[2][SPLIT ? 2 : 1][32 * kLdsRow];
   __shared__ float rowsum[kRWaves][64];
-  __shared__ float kp[kRWaves][kD];
   __shared__ float partial[kRWaves][64];
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
@@ -167,68 +170,109 @@ __global__ __launch_bounds__(kRThreads) void route_prefill_kernel(
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) rs[rt] = f32x16{};
 
+  // Pooled tiles of 32 blocks go through two LDS buffers: the global loads
+  // of tile bt+1 are in flight while tile bt is multiplied, and one barrier
+  // per tile separates the store of a buffer from its last readers.
   const int64_t ntiles = (full_max + 31) / 32;
   const int ld_row = threadIdx.x >> 3;  // 32 rows x 8 chunks of 32 bytes
   const int ld_chunk = threadIdx.x & 7;
-  for (int64_t bt = 0; bt < ntiles; ++bt) {
-    {
-      const int64_t b = bt * 32 + ld_row;
-      const bool ok = b < full_max;
-      const int64_t off = (seq * M + (ok ? b : 0)) * kD + 16 * ld_chunk;
-      const uint4* sh = reinterpret_cast<const uint4*>(phi + off);
-      const uint4 h0 = ok ? sh[0] : make_uint4(0, 0, 0, 0);
-      const uint4 h1 = ok ? sh[1] : make_uint4(0, 0, 0, 0);
-      uint4 l0 = make_uint4(0, 0, 0, 0), l1 = make_uint4(0, 0, 0, 0);
-      if constexpr (SPLIT) {
-        if (ok) {
-          const uint4* sl = reinterpret_cast<const uint4*>(plo + off);
-          l0 = sl[0];
-          l1 = sl[1];
-        }
-      }
-      uint4* dst = reinterpret_cast<uint4*>(tile[0] + ld_row * kLdsRow + 32 * ld_chunk);
-      dst[0] = h0;
-      dst[1] = h1;
-      if constexpr (SPLIT) {
-        uint4* dl = reinterpret_cast<uint4*>(tile[SPLIT ? 1 : 0] + ld_row * kLdsRow + 32 * ld_chunk);
-        dl[0] = l0;
-        dl[1] = l1;
-      }
-    }
-    __syncthreads();
-    bf16x8 bh[8], bl[8];
-    const int boff = (lane & 31) * kLdsRow + 128 * (lane >> 5);
-    const uint4* brow = reinterpret_cast<const uint4*>(tile[0] + boff);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) bh[ks] = as_bf16x8(brow[ks]);
+  uint4 st[SPLIT ? 4 : 2];
+  auto fetch = [&](int64_t bt) {
+    const int64_t b = bt * 32 + ld_row;
+    const bool ok = b < full_max;
+    const int64_t off = (seq * M + (ok ? b : 0)) * kD + 16 * ld_chunk;
+    const uint4* sh = reinterpret_cast<const uint4*>(phi + off);
+    st[0] = ok ? sh[0] : make_uint4(0, 0, 0, 0);
+    st[1] = ok ? sh[1] : make_uint4(0, 0, 0, 0);
     if constexpr (SPLIT) {
-      const uint4* blow = reinterpret_cast<const uint4*>(tile[SPLIT ? 1 : 0] + boff);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) bl[ks] = as_bf16x8(blow[ks]);
+      const uint4* sl = reinterpret_cast<const uint4*>(plo + off);
+      st[2] = ok ? sl[0] : make_uint4(0, 0, 0, 0);
+      st[3] = ok ? sl[1] : make_uint4(0, 0, 0, 0);
     }
+  };
+  auto stash = [&](int buf) {
+    uint4* dst = reinterpret_cast<uint4*>(tile[buf][0] + ld_row * kLdsRow + 32 * ld_chunk);
+    dst[0] = st[0];
+    dst[1] = st[1];
+    if constexpr (SPLIT) {
+      uint4* dl = reinterpret_cast<uint4*>(tile[buf][SPLIT ? 1 : 0] + ld_row * kLdsRow + 32 * ld_chunk);
+      dl[0] = st[2];
+      dl[1] = st[3];
+    }
+  };
+  // Unconditional, so that every path into the loop has drained the A-operand
+  // loads (the stash waits for all of this thread's loads): the prefetch
+  // inside the loop then never waits on anything but itself.
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  const int boff = (lane & 31) * kLdsRow + 128 * (lane >> 5);
+  for (int64_t bt = 0; bt < ntiles; ++bt) {
+    const int buf = static_cast<int>(bt & 1);
+    const bool more = bt + 1 < ntiles;
+    if (more) fetch(bt + 1);
     const bool ok = bt * 32 + (lane & 31) < full;
-    accumulate_tile<RT, SPLIT>(a, bh, bl, ok, rs);
+    accumulate_tile<RT, SPLIT>(a, tile[buf][0] + boff, tile[buf][SPLIT ? 1 : 0] + boff, ok, rs);
+    if (more) stash(buf ^ 1);
     __syncthreads();
   }
   reduce_rows<RT>(rs, rowsum[wave]);
   const bool has_partial = Mt > full;
   if (has_partial) {
-    // Partial mean of keys [full*B, pos] by this wave (two dims per lane).
-    for (int c = 0; c < 2; ++c) {
-      const int dim = lane + 64 * c;
-      float acc = 0.f;
-      for (int64_t s = full * B; s <= pos; ++s) {
-        float x = load_elem<DT>(k, (seq * L + s) * kD + dim);
-        if constexpr (DT == kFP8) x *= k_scale[seq * L + s];
-        acc += x;
+    // Partial block [full*B, pos]: ReLU(q . mean of its keys) = ReLU(mean of
+    // q . k_s), so the per-key dots come from the same MFMA tiles (raw keys
+    // as B, 32 per column tile, fp8 codes widened to bf16 exactly and the
+    // key scale applied per column), summed over the block and divided.
+    f32x16 ps[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) ps[rt] = f32x16{};
+    const int64_t s_lo = full * B;
+    const int hf = lane >> 5;
+    for (int64_t s0 = s_lo; s0 <= pos; s0 += 32) {
+      const int64_t sk_i = s0 + (lane & 31);
+      const bool ok = sk_i <= pos;
+      const int64_t row = seq * L + (ok ? sk_i : s_lo);
+      bf16x8 b[8];
+      if constexpr (DT == kBF16) {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(k) + row * kD + 64 * hf);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) b[ks] = as_bf16x8(src[ks]);
+      } else {
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(k) + row * kD + 64 * hf);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint4 v = src[c];
+          const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+          uint32_t o[8];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float f0 = fp8_to_f32(wds[u] & 0xFF), f1 = fp8_to_f32((wds[u] >> 8) & 0xFF);
+            const float f2 = fp8_to_f32((wds[u] >> 16) & 0xFF), f3 = fp8_to_f32(wds[u] >> 24);
+            o[2 * u] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+            o[2 * u + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u);
+          }
+          b[2 * c] = as_bf16x8(make_uint4(o[0], o[1], o[2], o[3]));
+          b[2 * c + 1] = as_bf16x8(make_uint4(o[4], o[5], o[6], o[7]));
+        }
       }
-      kp[wave][dim] = acc / static_cast<float>(pos - full * B + 1);
+      const float skv = ok ? ((DT == kFP8) ? k_scale[row] : 1.f) : 0.f;
+      f32x16 acc[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_bf16(a[rt][ks], b[ks], acc[rt]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ps[rt][i] += acc[rt][i] * skv;
     }
+    reduce_rows<RT>(ps, partial[wave]);
     __builtin_amdgcn_wave_barrier();
-    if (lane < H) {
-      float dot = 0.f;
-      for (int i = 0; i < kD; ++i) dot += load_elem<DT>(q, (r * H + lane) * kD + i) * kp[wave][i];
-      partial[wave][lane] = fmaxf(dot, 0.f);
+    if (lane < 64) {
+      const float cnt = static_cast<float>(pos - s_lo + 1);
+      partial[wave][lane] = fmaxf(partial[wave][lane] / cnt, 0.f);
     }
   }
   __syncthreads();
