@@ -45,9 +45,22 @@ namespace {
 #ifndef MISA_DECODE_KEYS_PER_WAVE
 #define MISA_DECODE_KEYS_PER_WAVE 256
 #endif
+#ifndef MISA_DECODE_PREFETCH
+#define MISA_DECODE_PREFETCH 1
+#endif
 constexpr int kDecThreads = MISA_DECODE_THREADS;
+constexpr int kDecPrefetch = MISA_DECODE_PREFETCH;  // 64-key groups in flight per wave
 constexpr int kDecWaves = kDecThreads / kWave;
 constexpr int kCandCap = 2048;  // LDS list of the threshold digit
+constexpr uint64_t kSyncMagic = 0x4D4953415354ull;  // 48-bit tag of a re-armed router arrival word
+
+// Wait until this wave's vector-memory operations have completed.
+__device__ __forceinline__ void vmcnt_zero_wait() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 constexpr int kChunk = 32;      // pooled blocks per router workgroup
 constexpr int kMaxH = 64;
 
@@ -58,19 +71,35 @@ constexpr int kFinePerCoarse = kDigits / kCoarse;
 constexpr int kHistWords = kDigits + kCoarse;
 
 // Coarse bin count owned by thread t (< kCoarse): coarse bin kCoarse-1-t, so
-// threads run from the highest scores down.  Issued before the caller's other
+// threads run from the highest scores down; summed over the row's G
+// histogram records (kHistWords apart).  Issued before the caller's other
 // loads so that it is not queued behind them.
-__device__ __forceinline__ int load_coarse(const uint32_t* gh) {
-  return threadIdx.x < kCoarse ? static_cast<int>(gh[kDigits + kCoarse - 1 - threadIdx.x]) : 0;
+// Sum of word p[g * kHistWords] over g < G, eight loads in flight at a time.
+__device__ __forceinline__ int sum_records(const uint32_t* p, int G) {
+  int c = 0, g = 0;
+  for (; g + 8 <= G; g += 8) {
+    uint32_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[static_cast<int64_t>(g + u) * kHistWords];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c += static_cast<int>(v[u]);
+  }
+  for (; g < G; ++g) c += static_cast<int>(p[static_cast<int64_t>(g) * kHistWords]);
+  return c;
 }
 
-// The digit b* of the k-th largest score of a row (n > k scores) from its
-// histogram record gh: *digit, *above = count in higher digits, *count =
-// count at b*.  c = load_coarse(gh).  All threads call; results are in LDS on
-// return.
+__device__ __forceinline__ int load_coarse(const uint32_t* gh, int G = 1) {
+  return threadIdx.x < kCoarse ? sum_records(gh + kDigits + kCoarse - 1 - threadIdx.x, G) : 0;
+}
+
+// The digit b* of the k-th largest score of a row (n > k scores) from its G
+// histogram records at gh: *digit, *above = count in higher digits, *count =
+// count at b*.  c = load_coarse(gh, G).  All threads call; results are in LDS
+// on return.
 template <int NT>
 __device__ __forceinline__ void find_digit(const uint32_t* gh, int c, int k, int* scan_tmp,
-                                           int* sel_coarse, int* digit, int* above, int* count) {
+                                           int* sel_coarse, int* digit, int* above, int* count,
+                                           int G = 1) {
   static_assert(NT >= kCoarse, "one coarse bin per thread");
   int total;
   const int run = block_exclusive_sum<NT>(c, scan_tmp, total);  // count in higher coarse bins
@@ -84,7 +113,7 @@ __device__ __forceinline__ void find_digit(const uint32_t* gh, int c, int k, int
     const int base = sel_coarse[1];
     const int lane = threadIdx.x;
     // Lane l < 32 owns fine bin 32cb + 31 - l.
-    const int f = lane < kFinePerCoarse ? static_cast<int>(gh[cb * kFinePerCoarse + kFinePerCoarse - 1 - lane]) : 0;
+    const int f = lane < kFinePerCoarse ? sum_records(gh + cb * kFinePerCoarse + kFinePerCoarse - 1 - lane, G) : 0;
     const int inc = wave_inclusive_sum(f);
     const int ex = inc - f;
     if (lane < kFinePerCoarse && base + ex < k && base + inc >= k) {
@@ -199,15 +228,33 @@ __global__ __launch_bounds__(kDecThreads) void decode_score_kernel(DecodeArgs a)
   for (int b = threadIdx.x; b < kDigits; b += kDecThreads) hist[b] = 0;
   __syncthreads();
   float* row = a.rows + r * a.L;
-  for (int64_t s0 = s_begin; s0 < s_end; s0 += 64) {
-    if (s0 != s_begin) RowScorer<DT, NRT>::load64(krows, s0, s_end, s_begin, kb);
-    const float res = sc.compute64(kb);
+  auto emit = [&](float res, int64_t s0) {
     const int64_t s = s0 + lane;
     if (s < s_end) {
       float v = res;
       if constexpr (DT == kFP8) v *= a.k_scale[r * a.L + s];
       row[s] = v;
       atomicAdd(&hist[key_digit(v)], 1u);
+    }
+  };
+  if constexpr (kDecPrefetch == 1) {
+    for (int64_t s0 = s_begin; s0 < s_end; s0 += 64) {
+      if (s0 != s_begin) RowScorer<DT, NRT>::load64(krows, s0, s_end, s_begin, kb);
+      emit(sc.compute64(kb), s0);
+    }
+  } else {
+    // Two 64-key groups per wave: one is scored while the other loads.
+    typename RowScorer<DT, NRT>::Keys kb1;
+    if (s_begin + 64 < s_end) RowScorer<DT, NRT>::load64(krows, s_begin + 64, s_end, s_begin, kb1);
+    for (int64_t s0 = s_begin; s0 < s_end; s0 += 128) {
+      const float r0 = sc.compute64(kb);
+      if (s0 + 128 < s_end) RowScorer<DT, NRT>::load64(krows, s0 + 128, s_end, s_begin, kb);
+      emit(r0, s0);
+      if (s0 + 64 < s_end) {
+        const float r1 = sc.compute64(kb1);
+        if (s0 + 192 < s_end) RowScorer<DT, NRT>::load64(krows, s0 + 192, s_end, s_begin, kb1);
+        emit(r1, s0 + 64);
+      }
     }
   }
   __syncthreads();
@@ -224,40 +271,74 @@ __global__ __launch_bounds__(kDecThreads) void decode_score_kernel(DecodeArgs a)
   }
 }
 
-// Top-k step 1: tokens of digits above b* -> output, digit b* -> the list.
-// Workgroup (chunk, sequence) takes kCompactChunk consecutive scores.
+// Top-k after scoring, one kernel: workgroup (chunk, sequence) takes
+// kCompactChunk consecutive scores, finds b* from the histogram records,
+// writes its tokens of digits above b* straight to the output and appends
+// those of digit b* to a short list (one packed atomic counter per sequence
+// reserves both ranges).  The last workgroup of the sequence to finish (an
+// arrival counter, zeroed by the kernel before) then takes the (k - above)
+// best of the list, exactly.  The list is written and read with
+// device-coherent accesses, and each workgroup's writes are complete before
+// it is counted.  When b* holds more than kCandCap tokens, workgroup 0 alone
+// selects from the whole row.
 constexpr int kCompactThreads = 256;
 constexpr int kCompactPer = 16;  // scores per thread
 constexpr int kCompactChunk = kCompactThreads * kCompactPer;
+static_assert(kCompactThreads <= kCandCap, "speculative list loads stay inside the list");
 
-struct SelState {
-  int digit, above, count, pad;
+struct SelectSmem {
+  alignas(16) float cand_score[kCandCap];
+  alignas(16) int32_t cand_idx[kCandCap];
+  ResolveSmem rs;
+  TopkSmem base;
+  int scan_tmp[32];
+  int s_coarse[2];
+  int s_digit, s_above, s_count, s_last;
+  uint32_t s_base;
 };
 
-__global__ __launch_bounds__(kCompactThreads) void decode_compact_kernel(
+__global__ __launch_bounds__(kCompactThreads) void decode_select_kernel(
     const float* __restrict__ rows, const uint32_t* __restrict__ ghist, uint32_t* __restrict__ cnt,
-    SelState* __restrict__ sel, float* __restrict__ cand_s, int32_t* __restrict__ cand_i,
-    int32_t* __restrict__ idx, float* __restrict__ scores_out, int32_t L, int32_t k) {
-  __shared__ int scan_tmp[32];
-  __shared__ int s_coarse[2];
-  __shared__ int s_digit, s_above, s_count;
-  __shared__ uint32_t s_base;
-  if (L <= k) return;
+    uint32_t* __restrict__ done, float* __restrict__ cand_s, int32_t* __restrict__ cand_i,
+    int32_t* __restrict__ idx, float* __restrict__ scores_out, int32_t L, int32_t k, int32_t G,
+    uint64_t* __restrict__ rsync) {
+  __shared__ SelectSmem sm;
   const int64_t r = blockIdx.y;
+  // Re-arm the next step's router exchange (this kernel follows the step
+  // kernel, so every arrival of this call has been counted).
+  if (rsync && blockIdx.x == 0 && threadIdx.x == 0) rsync[r] = kSyncMagic << 16;
   const float* row = rows + r * L;
+  int32_t* out = idx + r * k;
+  float* out_s = scores_out ? scores_out + r * k : nullptr;
+  if (L <= k) {
+    if (blockIdx.x == 0)
+      for (int i = threadIdx.x; i < k; i += kCompactThreads) {
+        out[i] = i < L ? i : -1;
+        if (out_s) out_s[i] = i < L ? row[i] : -__builtin_inff();
+      }
+    return;
+  }
   const int c0 = blockIdx.x * kCompactChunk;
-  const uint32_t* gh = ghist + r * kHistWords;
-  const int coarse = load_coarse(gh);
+  const uint32_t* gh = ghist + r * G * kHistWords;
+  const int coarse = load_coarse(gh, G);
   // Scores first (independent of b*), so their loads overlap the scan.
   float v[kCompactPer];  // clamped loads; tokens past L are masked below
 #pragma unroll
   for (int j = 0; j < kCompactPer; ++j)
     v[j] = row[min(c0 + j * kCompactThreads + static_cast<int>(threadIdx.x), L - 1)];
-  find_digit<kCompactThreads>(gh, coarse, k, scan_tmp, s_coarse, &s_digit, &s_above, &s_count);
-  const uint32_t bstar = static_cast<uint32_t>(s_digit);
-  const int count = s_count;
-  if (blockIdx.x == 0 && threadIdx.x == 0) sel[r] = SelState{s_digit, s_above, count, 0};
-  if (count > kCandCap) return;  // the resolve kernel selects from the whole row
+  find_digit<kCompactThreads>(gh, coarse, k, sm.scan_tmp, sm.s_coarse, &sm.s_digit, &sm.s_above,
+                              &sm.s_count, G);
+  const uint32_t bstar = static_cast<uint32_t>(sm.s_digit);
+  const int count = sm.s_count;
+  const int above = sm.s_above;
+  if (count > kCandCap) {
+    if (blockIdx.x == 0)
+      block_topk<kCompactThreads>(
+          L, k, [](int64_t) { return true; }, [=](int64_t i) { return float_key(row[i]); },
+          [](int64_t i) { return static_cast<int32_t>(i); }, [=](int64_t i) { return row[i]; }, out,
+          out_s, sm.base);
+    return;
+  }
   const uint32_t lo = digit_lo_key(bstar), hi = digit_hi_key(bstar);
   uint32_t mh = 0, ma = 0;
 #pragma unroll
@@ -271,14 +352,12 @@ __global__ __launch_bounds__(kCompactThreads) void decode_compact_kernel(
   // k <= 8192), at-b* in the high 16 bits (row total <= kCandCap).
   const int packed = __popc(mh) | (__popc(ma) << 16);
   int total;
-  const int off = block_exclusive_sum<kCompactThreads>(packed, scan_tmp, total);
-  if (threadIdx.x == 0) s_base = atomicAdd(&cnt[r], static_cast<uint32_t>(total));
+  const int off = block_exclusive_sum<kCompactThreads>(packed, sm.scan_tmp, total);
+  if (threadIdx.x == 0) sm.s_base = atomicAdd(&cnt[r], static_cast<uint32_t>(total));
   __syncthreads();
-  const uint32_t base = s_base + static_cast<uint32_t>(off);
+  const uint32_t base = sm.s_base + static_cast<uint32_t>(off);
   int ph = static_cast<int>(base & 0xFFFFu);
   int pa = static_cast<int>(base >> 16);
-  int32_t* out = idx + r * k;
-  float* out_s = scores_out ? scores_out + r * k : nullptr;
   float* ls = cand_s + r * kCandCap;
   int32_t* li = cand_i + r * kCandCap;
 #pragma unroll
@@ -292,74 +371,51 @@ __global__ __launch_bounds__(kCompactThreads) void decode_compact_kernel(
       ++ph;
     } else if ((ma >> j) & 1u) {
       if (pa < kCandCap) {
-        ls[pa] = v[j];
-        li[pa] = i;
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(ls + pa), __float_as_uint(v[j]), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(li + pa, i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       ++pa;
     }
   }
-}
-
-// Top-k step 2, one workgroup per sequence: the (k - above) best of the b*
-// list (or, when b* holds more than kCandCap tokens, the whole row).
-constexpr int kResolveThreads = 256;
-static_assert(kResolveThreads <= kCandCap, "speculative list loads stay inside the list");
-
-struct ResolveAll {
-  alignas(16) float cand_score[kCandCap];
-  alignas(16) int32_t cand_idx[kCandCap];
-  ResolveSmem rs;
-  TopkSmem base;
-};
-
-__global__ __launch_bounds__(kResolveThreads) void decode_resolve_kernel(
-    const float* __restrict__ rows, const SelState* __restrict__ sel,
-    const float* __restrict__ cand_s, const int32_t* __restrict__ cand_i,
-    int32_t* __restrict__ idx, float* __restrict__ scores_out, int32_t L, int32_t k) {
-  __shared__ ResolveAll sm;
-  const int64_t r = blockIdx.x;
-  const float* row = rows + r * L;
-  int32_t* out = idx + r * k;
-  float* out_s = scores_out ? scores_out + r * k : nullptr;
-  if (L <= k) {
-    for (int i = threadIdx.x; i < k; i += kResolveThreads) {
-      out[i] = i < L ? i : -1;
-      if (out_s) out_s[i] = i < L ? row[i] : -__builtin_inff();
+  // Arrival: this workgroup's list entries are complete before it counts.
+  vmcnt_zero_wait();
+  __syncthreads();
+  if (threadIdx.x == 0) sm.s_last = atomicAdd(&done[r], 1u) == gridDim.x - 1 ? 1 : 0;
+  __syncthreads();
+  if (!sm.s_last) return;
+  // The last workgroup: the (k - above) best of the list (all of its loads
+  // in flight at once).
+  {
+    constexpr int PER = kCandCap / kCompactThreads;
+    uint32_t vs[PER];
+    int32_t vi[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int t = static_cast<int>(threadIdx.x) + u * kCompactThreads;
+      vs[u] = t < count ? __hip_atomic_load(reinterpret_cast<const uint32_t*>(ls + t), __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT)
+                        : 0u;
+      vi[u] = t < count ? __hip_atomic_load(li + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
     }
-    return;
-  }
-  // The first kResolveThreads list entries are loaded together with the
-  // selection state (the list area always exists; entries past the count
-  // are ignored), saving a dependent round trip for short lists.
-  const float s0 = cand_s[r * kCandCap + threadIdx.x];
-  const int32_t i0 = cand_i[r * kCandCap + threadIdx.x];
-  const SelState st = sel[r];
-  const int above = st.above;
-  const int bcount = st.count;
-  if (bcount > kCandCap) {
-    block_topk<kResolveThreads>(
-        L, k, [](int64_t) { return true; }, [=](int64_t i) { return float_key(row[i]); },
-        [](int64_t i) { return static_cast<int32_t>(i); }, [=](int64_t i) { return row[i]; }, out,
-        out_s, sm.base);
-    return;
-  }
-  if (static_cast<int>(threadIdx.x) < bcount) {
-    sm.cand_score[threadIdx.x] = s0;
-    sm.cand_idx[threadIdx.x] = i0;
-  }
-  for (int t = threadIdx.x + kResolveThreads; t < bcount; t += kResolveThreads) {
-    sm.cand_score[t] = cand_s[r * kCandCap + t];
-    sm.cand_idx[t] = cand_i[r * kCandCap + t];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int t = static_cast<int>(threadIdx.x) + u * kCompactThreads;
+      if (t < count) {
+        sm.cand_score[t] = __uint_as_float(vs[u]);
+        sm.cand_idx[t] = vi[u];
+      }
+    }
   }
   __syncthreads();
-  if (resolve_list<kResolveThreads>(sm.cand_score, sm.cand_idx, bcount, k - above, out + above,
+  if (resolve_list<kCompactThreads>(sm.cand_score, sm.cand_idx, count, k - above, out + above,
                                     out_s ? out_s + above : nullptr, sm.rs))
     return;
   __syncthreads();
   const float* cs = sm.cand_score;
   const int32_t* ci = sm.cand_idx;
-  block_topk<kResolveThreads>(
-      bcount, k - above, [](int64_t) { return true; }, [=](int64_t j) { return float_key(cs[j]); },
+  block_topk<kCompactThreads>(
+      count, k - above, [](int64_t) { return true; }, [=](int64_t j) { return float_key(cs[j]); },
       [=](int64_t j) { return ci[j]; }, [=](int64_t j) { return cs[j]; }, out + above,
       out_s ? out_s + above : nullptr, sm.base);
 }
@@ -523,6 +579,360 @@ __global__ __launch_bounds__(256) void step_route_kernel(
   }
 }
 
+// Single-kernel decode step (router + scoring) for batches that fill the
+// chip: G = ceil(256 / batch) workgroups per sequence, all on one XCD (the
+// workgroup id's residue mod 8 is the sequence's), so that the sequence's
+// pooled keys are read from HBM once and then from that XCD's L2.  Every
+// workgroup
+//  1. stages the query's head rows (padded LDS rows) and weights;
+//  2. recomputes the mean of the newest block M-1 from its keys (Eq. (4));
+//     workgroup 0 writes it back to the pooled cache;
+//  3. forms S_j = sum over the M blocks of ReLU(q_j . p_m) on 16x16x32 bf16
+//     MFMA (16-block column tiles dealt round-robin to the waves; pooled keys
+//     split into bf16 hi + lo, fp8 query codes widened exactly), then E_j and the top-h heads
+//     (Eq. (7)-(8)); workgroup 0 writes them;
+//  4. scores its key range with the routed heads (two 64-key groups in
+//     flight per wave), writes the scores and its own digit histogram (no
+//     atomics, so nothing needs clearing first) and, in workgroup 0, clears
+//     the sequence's compaction counter for the select kernels.
+constexpr int kStepThreads = 512;
+constexpr int kSyncSpin = 1 << 16;  // bounded wait for the peers' router partials
+constexpr int kStepMaxG = 32;       // workgroups per sequence (batch >= 8)
+
+
+constexpr int kStepWaves = kStepThreads / kWave;
+
+struct StepArgs {
+  const void* q;
+  const float* q_scale;
+  const float* w;
+  float* pooled;
+  const void* k;
+  const float* k_scale;
+  int32_t* heads_out;
+  float* E_out;
+  float* rows;
+  uint32_t* ghist;  // [batch, G, kHistWords]
+  uint32_t* cnt;    // [batch]
+  uint32_t* done;   // [batch]
+  uint32_t* rpart;  // [batch, G, 64] published router partials (fp32 bits)
+  uint64_t* rsync;  // [batch] (magic << 16) | arrivals; reset by the compact kernel
+  int64_t M;
+  int32_t L, H, B, h, G, batch, keys_per_wave;
+};
+
+template <int DT>
+__global__ __launch_bounds__(kStepThreads) void decode_step_kernel(StepArgs a) {
+  constexpr int EB = (DT == kBF16) ? 2 : 1;
+  constexpr int QP = kD * 2 + 16;  // router staging pitch (bf16 rows + pad), bytes
+  constexpr int SP = kD * EB + 16;  // scorer staging pitch, bytes
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kDigits];  // also the newest-block partial sums
+  __shared__ __attribute__((aligned(16))) uint8_t qr_lds[kMaxH * QP];  // bf16 head rows (router)
+  __shared__ __attribute__((aligned(16))) uint8_t qs_lds[DT == kBF16 ? 16 : kMaxH * SP];  // fp8 codes (scorer)
+  __shared__ __attribute__((aligned(16))) float meanv[kD];
+  __shared__ float w_lds[kMaxH];
+  __shared__ float red[kStepWaves][kMaxH];
+  __shared__ int32_t sh_heads[16];
+  __shared__ int sh_flag;
+  __shared__ float xpart[kStepMaxG * kMaxH];  // the sequence's published router partials
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t seq = blockIdx.x % a.batch;
+  const int g = blockIdx.x / a.batch;
+  const int64_t M = a.M;
+  const int H = a.H;
+
+  // The first pooled tile of this workgroup's router chunk (section 3) is
+  // requested before the staging and newest-block loads below, so the three
+  // round trips overlap.
+  const int col = lane & 15;
+  const int qq = lane >> 4;
+  struct PTile {
+    float4 x[8];
+  };
+  auto load_tile = [&](int64_t c0, PTile& t) {
+    const int64_t b = c0 + col;
+    const bool cached = b < M - 1;
+    const float4* src = reinterpret_cast<const float4*>(a.pooled + (seq * M + (cached ? b : 0)) * kD);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      t.x[2 * ks] = src[(32 * ks + 8 * qq) / 4];
+      t.x[2 * ks + 1] = src[(32 * ks + 8 * qq) / 4 + 1];
+    }
+  };
+  const int G = a.G;
+  const int64_t own_cb = static_cast<int64_t>(g) * M / G, own_ce = static_cast<int64_t>(g + 1) * M / G;
+  PTile t_first;
+  if (own_cb + 16 * wave < own_ce) load_tile(own_cb + 16 * wave, t_first);
+
+  // 1. Head rows -> LDS (router copy widened to bf16; fp8 codes kept for the
+  // scorer), weights.
+  {
+    constexpr int PPR = kD * EB / 16;  // 16-byte pieces per head row
+    const uint4* qsrc = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.q) + seq * H * kD * EB);
+    for (int pc = threadIdx.x; pc < kMaxH * PPR; pc += kStepThreads) {
+      const int row = pc / PPR, c = pc % PPR;
+      const uint4 v = row < H ? qsrc[pc] : make_uint4(0, 0, 0, 0);
+      if constexpr (DT == kBF16) {
+        *reinterpret_cast<uint4*>(qr_lds + row * QP + 16 * c) = v;
+      } else {
+        *reinterpret_cast<uint4*>(qs_lds + row * SP + 16 * c) = v;
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          // e4m3 -> fp32 is exact and bf16 holds the 4-bit significand exactly.
+          const float f0 = fp8_to_f32(wd[u] & 0xFF), f1 = fp8_to_f32((wd[u] >> 8) & 0xFF);
+          const float f2 = fp8_to_f32((wd[u] >> 16) & 0xFF), f3 = fp8_to_f32(wd[u] >> 24);
+          o[2 * u] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+          o[2 * u + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u);
+        }
+        uint4* dst = reinterpret_cast<uint4*>(qr_lds + row * QP + 32 * c);
+        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+      }
+    }
+    if (threadIdx.x < kMaxH) w_lds[threadIdx.x] = threadIdx.x < H ? a.w[seq * H + threadIdx.x] : 0.f;
+  }
+  // 2. Mean of keys [(M-1)B, L): thread t takes 16-byte piece t % P of key
+  // slots t / P + NSL * u; the slots' sums meet in LDS.
+  {
+    constexpr int P = kD * EB / 16;
+    constexpr int EPP = 16 / EB;
+    constexpr int NSL = kStepThreads / P;
+    static_assert(NSL * kD <= kDigits, "slot sums fit the histogram area");
+    float* part = reinterpret_cast<float*>(hist);  // [NSL][kD]
+    const int piece = threadIdx.x % P;
+    const int slot = threadIdx.x / P;
+    const int64_t s0 = (M - 1) * a.B;
+    const int nl = static_cast<int>(a.L - s0);
+    const uint8_t* kb = static_cast<const uint8_t*>(a.k) + (seq * a.L + s0) * kD * EB;
+    float acc[EPP];
+#pragma unroll
+    for (int e = 0; e < EPP; ++e) acc[e] = 0.f;
+    for (int key = slot; key < nl; key += NSL) {
+      const uint4 v = reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(key) * kD * EB)[piece];
+      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+      if constexpr (DT == kBF16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += __uint_as_float(wd[e] << 16);
+          acc[2 * e + 1] += __uint_as_float(wd[e] & 0xFFFF0000u);
+        }
+      } else {
+        const float sc = a.k_scale[seq * a.L + s0 + key];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] += fp8_to_f32((wd[e / 4] >> (8 * (e % 4))) & 0xFF) * sc;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPP; ++e) part[slot * kD + piece * EPP + e] = acc[e];
+    __syncthreads();
+    if (threadIdx.x < kD) {
+      float sum = 0.f;
+      for (int sl = 0; sl < NSL; ++sl) sum += part[sl * kD + threadIdx.x];
+      const float m = sum / static_cast<float>(nl);
+      meanv[threadIdx.x] = m;
+      if (g == 0) a.pooled[(seq * M + M - 1) * kD + threadIdx.x] = m;
+    }
+    __syncthreads();
+  }
+
+  // 3. Router.  The M blocks are cut into G chunks; workgroup g computes
+  // chunk g's partial P_g[j] = sum over its blocks of ReLU(q_j . p_m) and
+  // publishes it, then S_j = P_0[j] + ... + P_{G-1}[j] in that order from
+  // the published partials.  When the exchange cannot be trusted (first call
+  // on a workspace, or a peer missing for too long) the workgroup computes
+  // every chunk itself with the same code and summation order, so S is the
+  // same bits either way.
+  //
+  // A chunk's 16-block column tiles are dealt to the waves (tile i to wave
+  // i % 8); lane l supplies block c0 + l%16, head-dim elements
+  // 32 ks + 8 (l/16) .. + 8 (A and B alike).
+  float rs[4][4];
+  auto mul_tile = [&](int64_t c0, int64_t ce, const PTile& t) {
+    const int64_t b = c0 + col;
+    f32x4 acc[4];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int e0 = 32 * ks + 8 * qq;
+      float4 x0 = t.x[2 * ks], x1 = t.x[2 * ks + 1];
+      if (b == M - 1) {  // the newest block: its mean, just recomputed
+        x0 = *reinterpret_cast<const float4*>(meanv + e0);
+        x1 = *reinterpret_cast<const float4*>(meanv + e0 + 4);
+      }
+      uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+      split_bf16(x0, h0, h1, l0, l1);
+      split_bf16(x1, h2, h3, l2, l3);
+      const bf16x8 bh = as_bf16x8(make_uint4(h0, h1, h2, h3));
+      const bf16x8 bl = as_bf16x8(make_uint4(l0, l1, l2, l3));
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) {
+        const bf16x8 qa = as_bf16x8(*reinterpret_cast<const uint4*>(qr_lds + (16 * ht + col) * QP + 2 * e0));
+        acc[ht] = mfma16_bf16(qa, bh, acc[ht]);
+        acc[ht] = mfma16_bf16(qa, bl, acc[ht]);
+      }
+    }
+    // C layout: lane holds heads 16 ht + 4 qq + i for block column col.
+    const bool ok = b < ce;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rs[ht][i] += ok ? relu(acc[ht][i]) : 0.f;
+  };
+  constexpr int64_t kTileStep = 16 * kStepWaves;
+  // Chunk [cb, ce): every wave writes its per-head sums to red[wave][.];
+  // callers synchronise, then add red[0..7][j] in wave order.  One tile is
+  // multiplied while the next loads; the loop body is kept single because
+  // this code runs from a cold instruction cache, where size costs more than
+  // a register copy.
+  auto chunk_sums = [&](int64_t cb, int64_t ce, const PTile* first) {
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rs[ht][i] = 0.f;
+    const int64_t c_first = cb + 16 * wave;
+    PTile tc, tn;
+    if (c_first < ce) {
+      if (first) tc = *first;
+      else load_tile(c_first, tc);
+    }
+#pragma unroll 1
+    for (int64_t c0 = c_first; c0 < ce; c0 += kTileStep) {
+      if (c0 + kTileStep < ce) load_tile(c0 + kTileStep, tn);
+      mul_tile(c0, ce, tc);
+      tc = tn;
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rs[ht][i] += __shfl_xor(rs[ht][i], o, kWave);
+    if (col == 0) {
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][16 * ht + 4 * qq + i] = rs[ht][i];
+    }
+  };
+  auto red_sum = [&]() {  // wave 0, lane j: the chunk partial of head j
+    float p = 0.f;
+#pragma unroll
+    for (int w8 = 0; w8 < kStepWaves; ++w8) p += red[w8][lane];
+    return p;
+  };
+  chunk_sums(own_cb, own_ce, &t_first);
+  __syncthreads();
+  float S = 0.f;  // wave 0, lane j: S_j
+  if (wave == 0) {
+    const float mine = red_sum();
+    uint32_t* pub = a.rpart + (seq * G + g) * kMaxH;
+    __hip_atomic_store(pub + lane, __float_as_uint(mine), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    vmcnt_zero_wait();  // the partial is globally visible before it is counted
+    int ok = 0;
+    if (lane == 0) {
+      const uint64_t old = __hip_atomic_fetch_add(a.rsync + seq, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok = ((old >> 16) == kSyncMagic && (old & 0xFFFF) < static_cast<uint64_t>(G)) ? 1 : 0;
+      for (int it = 0; ok && it < kSyncSpin; ++it) {
+        const uint64_t v = __hip_atomic_load(a.rsync + seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((v & 0xFFFF) >= static_cast<uint64_t>(G)) break;
+        if (it + 1 == kSyncSpin) ok = 0;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    ok = __shfl(ok, 0, kWave);
+    if (lane == 0) sh_flag = ok;
+  }
+  __syncthreads();
+  if (sh_flag) {
+    // All G partials of the sequence, fetched by the whole workgroup at once
+    // (coherent loads), then added by wave 0 in chunk order.
+    for (int i = threadIdx.x; i < G * kMaxH; i += kStepThreads)
+      xpart[i] = __uint_as_float(__hip_atomic_load(a.rpart + seq * G * kMaxH + i, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT));
+    __syncthreads();
+    if (wave == 0)
+      for (int c = 0; c < G; ++c) S += xpart[c * kMaxH + lane];
+  }
+  if (!sh_flag) {
+    S = 0.f;
+    for (int c = 0; c < G; ++c) {
+      chunk_sums(static_cast<int64_t>(c) * M / G, static_cast<int64_t>(c + 1) * M / G, nullptr);
+      __syncthreads();
+      if (wave == 0) S += red_sum();
+      __syncthreads();
+    }
+  }
+
+  // Key range of this wave; its first group loads while the heads are
+  // chosen.  (Requested earlier, the key stream would delay the router's own
+  // round trips more than it gains.)
+  const void* krows = static_cast<const void*>(static_cast<const uint8_t*>(a.k) + seq * a.L * kD * EB);
+  const int64_t s_begin = (static_cast<int64_t>(g) * kStepWaves + wave) * a.keys_per_wave;
+  const int64_t s_end = min<int64_t>(s_begin + a.keys_per_wave, a.L);
+  typename RowScorer<DT, 1>::Keys kb0;
+  if (s_begin < s_end) RowScorer<DT, 1>::load64(krows, s_begin, s_end, s_begin, kb0);
+
+  const float sq = (DT == kFP8) ? a.q_scale[seq] : 1.f;
+  if (wave == 0) {
+    float e = -2.f;
+    if (lane < H) {
+      e = fabsf(w_lds[lane]) * sq * S / static_cast<float>(M);
+      if (g == 0 && a.E_out) a.E_out[seq * H + lane] = e;
+    }
+    wave_top_heads_rank(e, H, a.h, sh_heads);
+  }
+  for (int b = threadIdx.x; b < kDigits; b += kStepThreads) hist[b] = 0;
+  __syncthreads();
+  if (g == 0 && threadIdx.x < a.h) a.heads_out[seq * a.h + threadIdx.x] = sh_heads[threadIdx.x];
+  if (g == 0 && threadIdx.x == 0) {
+    a.cnt[seq] = 0;
+    a.done[seq] = 0;
+  }
+  RowScorer<DT, 1> sc;
+  if constexpr (DT == kBF16) sc.init_rows(qr_lds, w_lds, sq, sh_heads, a.h, H, QP / 2);
+  else sc.init_rows(qs_lds, w_lds, sq, sh_heads, a.h, H, SP);
+
+  // 4. Scores, two groups in flight per wave.
+  float* row = a.rows + seq * a.L;
+  auto emit = [&](float res, int64_t s0) {
+    const int64_t s = s0 + lane;
+    if (s < s_end) {
+      float v = res;
+      if constexpr (DT == kFP8) v *= a.k_scale[seq * a.L + s];
+      row[s] = v;
+      atomicAdd(&hist[key_digit(v)], 1u);
+    }
+  };
+  {
+    typename RowScorer<DT, 1>::Keys kb1;
+    if (s_begin + 64 < s_end) RowScorer<DT, 1>::load64(krows, s_begin + 64, s_end, s_begin, kb1);
+    for (int64_t s0 = s_begin; s0 < s_end; s0 += 128) {
+      const float r0 = sc.compute64(kb0);
+      if (s0 + 128 < s_end) RowScorer<DT, 1>::load64(krows, s0 + 128, s_end, s_begin, kb0);
+      emit(r0, s0);
+      if (s0 + 64 < s_end) {
+        const float r1 = sc.compute64(kb1);
+        if (s0 + 192 < s_end) RowScorer<DT, 1>::load64(krows, s0 + 192, s_end, s_begin, kb1);
+        emit(r1, s0 + 64);
+      }
+    }
+  }
+  __syncthreads();
+  // This workgroup's histogram record (fine bins, then coarse sums).
+  uint32_t* gh = a.ghist + (seq * a.G + g) * kHistWords;
+  for (int b = threadIdx.x; b < kDigits; b += kStepThreads) gh[b] = hist[b];
+  for (int cb = threadIdx.x; cb < kCoarse; cb += kStepThreads) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int u = 0; u < kFinePerCoarse; ++u) c += hist[cb * kFinePerCoarse + (u + cb) % kFinePerCoarse];
+    gh[kDigits + cb] = c;
+  }
+}
+
 template <int DT, bool FUSED>
 void launch_score(const Shape& s, const DecodeArgs& a, hipStream_t st) {
   dim3 grid((s.L + kDecWaves * a.keys_per_wave - 1) / (kDecWaves * a.keys_per_wave), s.batch);
@@ -533,12 +943,15 @@ void launch_score(const Shape& s, const DecodeArgs& a, hipStream_t st) {
 
 struct DecodeWs {
   float* rows;
-  uint32_t* ghist;  // [batch, kHistWords], followed by
-  uint32_t* cnt;    // [batch] packed compaction counters (zeroed together)
-  SelState* sel;
+  uint32_t* cnt;    // [batch] packed compaction counters, then
+  uint32_t* done;   // [batch] select-kernel arrivals, followed by
+  uint32_t* ghist;  // [batch, kHistWords] (single-kernel step: [batch, G, kHistWords])
+  int64_t zero_words;  // counters + one record per sequence
   float* cand_s;
   int32_t* cand_i;
   float* part;
+  uint32_t* rpart;  // single-kernel step: [batch, G, 64] router partials
+  uint64_t* rsync;  // single-kernel step: [batch] arrival words
   size_t total;
 };
 
@@ -548,6 +961,15 @@ int32_t step_main_chunks(const Shape& s) {
   return static_cast<int32_t>((s.M() - 1 + kChunk - 1) / kChunk);
 }
 
+// Workgroups per sequence of the single-kernel step, or 0 when the batch is
+// too small to fill the chip that way and the step runs as router + score
+// kernels.
+int32_t step_groups(const Shape& s) {
+  if (s.batch < 8) return 0;
+  const int32_t G = (256 + s.batch - 1) / s.batch;
+  return G <= kStepMaxG ? G : 0;
+}
+
 DecodeWs decode_layout(const Shape& s, void* ws) {
   const uintptr_t base = reinterpret_cast<uintptr_t>(ws);
   const size_t nb = static_cast<size_t>(s.batch);
@@ -555,28 +977,34 @@ DecodeWs decode_layout(const Shape& s, void* ws) {
   size_t off = 0;
   d.rows = reinterpret_cast<float*>(base + off);
   off += align_up(nb * s.L * sizeof(float));
-  d.ghist = reinterpret_cast<uint32_t*>(base + off);
-  d.cnt = reinterpret_cast<uint32_t*>(base + off) + nb * kHistWords;
-  off += align_up((nb * kHistWords + nb) * sizeof(uint32_t));
-  d.sel = reinterpret_cast<SelState*>(base + off);
-  off += align_up(nb * sizeof(SelState));
+  // Counters first, then the histogram records: the kernels that need both
+  // zeroed clear one range [cnt, cnt + zero_words).
+  const size_t nrec = nb * static_cast<size_t>(s.T == 1 && step_groups(s) > 0 ? step_groups(s) : 1);
+  const size_t cnt_words = (2 * nb + 63) / 64 * 64;
+  d.cnt = reinterpret_cast<uint32_t*>(base + off);
+  d.done = d.cnt + nb;
+  d.ghist = d.cnt + cnt_words;
+  d.zero_words = static_cast<int64_t>(cnt_words + nb * kHistWords);
+  off += align_up((cnt_words + nrec * kHistWords) * sizeof(uint32_t));
   d.cand_s = reinterpret_cast<float*>(base + off);
   off += align_up(nb * kCandCap * sizeof(float));
   d.cand_i = reinterpret_cast<int32_t*>(base + off);
   off += align_up(nb * kCandCap * sizeof(int32_t));
   d.part = reinterpret_cast<float*>(base + off);
   off += align_up(nb * (step_main_chunks(s) + 1) * kMaxH * sizeof(float));
+  d.rpart = reinterpret_cast<uint32_t*>(base + off);
+  off += align_up(nrec * kMaxH * sizeof(uint32_t));
+  d.rsync = reinterpret_cast<uint64_t*>(base + off);
+  off += align_up(nb * sizeof(uint64_t));
   d.total = off;
   return d;
 }
 
 void launch_select(const Shape& s, const DecodeWs& d, int32_t k, int32_t* idx, float* scores_out,
-                   hipStream_t st) {
+                   hipStream_t st, int32_t G = 1) {
   dim3 g((s.L + kCompactChunk - 1) / kCompactChunk, s.batch);
-  decode_compact_kernel<<<g, kCompactThreads, 0, st>>>(d.rows, d.ghist, d.cnt, d.sel, d.cand_s,
-                                                       d.cand_i, idx, scores_out, s.L, k);
-  decode_resolve_kernel<<<s.batch, kResolveThreads, 0, st>>>(d.rows, d.sel, d.cand_s, d.cand_i, idx,
-                                                             scores_out, s.L, k);
+  decode_select_kernel<<<g, kCompactThreads, 0, st>>>(d.rows, d.ghist, d.cnt, d.done, d.cand_s,
+                                                      d.cand_i, idx, scores_out, s.L, k, G, d.rsync);
 }
 
 }  // namespace
@@ -588,8 +1016,8 @@ hipError_t launch_decode_score_topk(const Shape& s, int32_t nh, const int32_t* h
                                     const void* kk, const float* k_scale, int32_t* idx,
                                     float* scores_out, void* ws, hipStream_t st) {
   const DecodeWs d = decode_layout(s, ws);
-  const int64_t nz = static_cast<int64_t>(s.batch) * kHistWords + s.batch;
-  clear_kernel<<<static_cast<unsigned>((nz + 1023) / 1024), 256, 0, st>>>(d.ghist, nz);
+  const int64_t nz = d.zero_words;
+  clear_kernel<<<static_cast<unsigned>((nz + 1023) / 1024), 256, 0, st>>>(d.cnt, nz);
   DecodeArgs a{q, q_scale, w, kk, k_scale, heads, nh, nullptr, 0, 0, nullptr, nullptr, 0,
                d.rows, d.ghist, s.L, s.H, MISA_DECODE_KEYS_PER_WAVE};
   if (s.dtype == kBF16) launch_score<kBF16, false>(s, a, st);
@@ -604,15 +1032,26 @@ hipError_t launch_decode_step(const Shape& s, int32_t h, int32_t k, const void* 
                               float* scores_out, void* ws, hipStream_t st) {
   const DecodeWs d = decode_layout(s, ws);
   const int64_t M = s.M();
+  if (const int32_t G = step_groups(s)) {
+    const int32_t kpw = static_cast<int32_t>(
+        (((s.L + static_cast<int64_t>(G) * kStepWaves - 1) / (static_cast<int64_t>(G) * kStepWaves)) + 63) / 64 * 64);
+    StepArgs sa{q, q_scale, w, pooled, kk, k_scale, heads, E_out, d.rows, d.ghist, d.cnt, d.done,
+                d.rpart, d.rsync, M, s.L, s.H, s.B, h, G, s.batch, kpw};
+    const unsigned grid = static_cast<unsigned>(G) * static_cast<unsigned>(s.batch);
+    if (s.dtype == kBF16) decode_step_kernel<kBF16><<<grid, kStepThreads, 0, st>>>(sa);
+    else decode_step_kernel<kFP8><<<grid, kStepThreads, 0, st>>>(sa);
+    launch_select(s, d, k, idx, scores_out, st, G);
+    return hipGetLastError();
+  }
   const int32_t nmain = step_main_chunks(s);
   const int32_t nch = nmain + 1;
-  const int64_t nz = static_cast<int64_t>(s.batch) * kHistWords + s.batch;
+  const int64_t nz = d.zero_words;
   dim3 g1(nch, s.batch);
   if (s.dtype == kBF16)
-    step_route_kernel<kBF16><<<g1, 256, 0, st>>>(q, pooled, kk, k_scale, d.part, d.ghist, nz, s.L,
+    step_route_kernel<kBF16><<<g1, 256, 0, st>>>(q, pooled, kk, k_scale, d.part, d.cnt, nz, s.L,
                                                  s.H, s.B, M, nmain);
   else
-    step_route_kernel<kFP8><<<g1, 256, 0, st>>>(q, pooled, kk, k_scale, d.part, d.ghist, nz, s.L,
+    step_route_kernel<kFP8><<<g1, 256, 0, st>>>(q, pooled, kk, k_scale, d.part, d.cnt, nz, s.L,
                                                 s.H, s.B, M, nmain);
   DecodeArgs a{q, q_scale, w, kk, k_scale, nullptr, h, d.part, nch, h, heads, E_out, M,
                d.rows, d.ghist, s.L, s.H, MISA_DECODE_KEYS_PER_WAVE};

@@ -81,6 +81,24 @@ __device__ __forceinline__ void wave_top_heads(float e, int H, int h, int32_t* h
   if (taken) heads[lanes_below(mask)] = lane;
 }
 
+// The same selection as wave_top_heads by ranks: lane l counts the lanes
+// whose E beats its own (larger, or equal with a lower head) and is taken
+// when fewer than h do.  64 independent compares per lane instead of h
+// dependent arg-max rounds.
+__device__ __forceinline__ void wave_top_heads_rank(float e, int H, int h, int32_t* heads) {
+  const int lane = lane_id();
+  if (lane >= H) e = -2.f;
+  int rank = 0;
+#pragma unroll 8
+  for (int j = 0; j < kWave; ++j) {
+    const float ej = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), j));
+    rank += (ej > e || (ej == e && j < lane)) ? 1 : 0;
+  }
+  const bool taken = lane < H && rank < h;
+  const uint64_t mask = __ballot(taken);
+  if (taken) heads[lanes_below(mask)] = lane;
+}
+
 // One wave: E for its query from nparts row-sum slices (LDS, added in order)
 // plus the partial-block term, then top-h.
 __device__ __forceinline__ void finalize_query(const float (*rowsum)[64], int nparts,

@@ -23,12 +23,12 @@ struct RowScorer {
   i32x8 a8[NRT];
   float wl[NRT][4];
 
-  // One query: qrows = its H head rows (kD elements each, any address
-  // space), wrow = its H weights, sq = its fp8 scale (1 otherwise); the nh
-  // scored heads are hsel[0..nh) (or 0..nh-1 when hsel is null); ids
-  // outside [0, H) score nothing.
+  // One query: qrows = its H head rows (kD elements each, `pitch` elements
+  // apart, any address space), wrow = its H weights, sq = its fp8 scale (1
+  // otherwise); the nh scored heads are hsel[0..nh) (or 0..nh-1 when hsel is
+  // null); ids outside [0, H) score nothing.
   __device__ __forceinline__ void init_rows(const void* qrows, const float* wrow, float sq,
-                                            const int32_t* hsel, int nh, int H) {
+                                            const int32_t* hsel, int nh, int H, int pitch = kD) {
     const int lane = lane_id();
     const int col = lane & 15;
     const int qq = lane >> 4;
@@ -45,7 +45,7 @@ struct RowScorer {
         wl[rt][i] = (j >= 0) ? wrow[j] * sq : 0.f;
       }
       const int j = head_of(rt * 16 + col);
-      const int64_t qoff = static_cast<int64_t>(j < 0 ? 0 : j) * kD;
+      const int64_t qoff = static_cast<int64_t>(j < 0 ? 0 : j) * pitch;
       if constexpr (DT == kBF16) {
         const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(qrows) + qoff);
 #pragma unroll

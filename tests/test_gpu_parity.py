@@ -34,6 +34,13 @@ SMALL = {
                               kprime=1024, dtype=synth.BF16, needles=16, seed=23),
     "fp8_decode": synth.small("fp8_decode", batch=3, L=4100, T=1, H=64, h=8, B=64, k=400,
                               kprime=900, dtype=synth.FP8_E4M3, needles=12, seed=26),
+    # Decode batches of 8 and more take the single-kernel step (one
+    # workgroup per 256/batch of the chip per sequence); batch 12 leaves
+    # some waves with no keys.
+    "bf16_decode_b8": synth.small("bf16_decode_b8", batch=8, L=3000, T=1, H=64, h=8, B=64, k=300,
+                                  kprime=700, dtype=synth.BF16, needles=8, seed=27),
+    "fp8_decode_b12": synth.small("fp8_decode_b12", batch=12, L=2100, T=1, H=32, h=8, B=128, k=200,
+                                  kprime=500, dtype=synth.FP8_E4M3, needles=6, seed=28),
     "t_eq_l": synth.small("t_eq_l", batch=1, L=200, T=200, H=64, h=8, B=64, k=64, kprime=96,
                           dtype=synth.BF16, needles=0, seed=24),
     "b1_h16": synth.small("b1_h16", batch=1, L=700, T=9, H=64, h=16, B=1, k=100, kprime=200,
@@ -340,3 +347,46 @@ def test_full_size_sampled(full_case):
                    for b in range(p.batch) for t in range(p.T)])
     _log(f"[gpu] {name}: sampled {len(qs)} queries ok; head swaps {sum(r['head_swaps'] for r in res)}, "
          f"MISA recall of dense top-k over all queries = {rec:.4f}")
+
+
+def test_decode_step_exchange_paths():
+    """The single-kernel decode step (batch >= 8) shares router partials
+    between the workgroups of a sequence once its workspace has been armed by
+    a previous call; on a fresh (zeroed) workspace every workgroup computes
+    the whole router itself.  Both paths add the same partials in the same
+    order, so the two calls must agree bit for bit, and the second must match
+    the oracle."""
+    import torch
+
+    import long_context_pool_amd as misa
+
+    p = SMALL["bf16_decode_b8"]
+    x = synth.generate(p)
+    op = parity.OracleProblem(x)
+    dev = torch.device("cuda:0")
+    q, kk, w = x.q.to(dev), x.k.to(dev), x.w.to(dev)
+    shp = misa.shape(p.batch, p.L, p.T, p.H, p.d, p.B, p.dtype)
+    ws = torch.zeros(misa.misa_workspace_bytes(shp, p.h, p.k, p.k), dtype=torch.uint8, device=dev)
+    pooled = torch.empty((p.batch, p.M, p.d), dtype=torch.float32, device=dev)
+    misa.misa_pool_keys(shp, kk, None, pooled)
+    runs = []
+    for call in range(2):
+        sp = pooled.clone()
+        sp[:, p.M - 1].fill_(7.0)
+        heads = torch.empty((p.batch, 1, p.h), dtype=torch.int32, device=dev)
+        E = torch.empty((p.batch, 1, p.H), dtype=torch.float32, device=dev)
+        idx = torch.empty((p.batch, 1, p.k), dtype=torch.int32, device=dev)
+        sc = torch.empty((p.batch, 1, p.k), dtype=torch.float32, device=dev)
+        misa.misa_decode_step(shp, p.h, p.k, q, None, w, sp, kk, None, heads, E, idx, sc, ws)
+        torch.cuda.synchronize()
+        runs.append({"s_pooled": sp.cpu().numpy(), "s_heads": heads.cpu().numpy(), "s_E": E.cpu().numpy(),
+                     "s_idx": idx.cpu().numpy(), "s_scores": sc.cpu().numpy(), "pooled": pooled.cpu().numpy()})
+    a, b = runs
+    np.testing.assert_array_equal(a["s_E"].view(np.uint32), b["s_E"].view(np.uint32))
+    np.testing.assert_array_equal(a["s_heads"], b["s_heads"])
+    np.testing.assert_array_equal(a["s_pooled"], b["s_pooled"])
+    for r in range(p.batch):
+        oa, ob = np.argsort(a["s_idx"][r, 0]), np.argsort(b["s_idx"][r, 0])
+        np.testing.assert_array_equal(a["s_idx"][r, 0][oa], b["s_idx"][r, 0][ob])
+        np.testing.assert_array_equal(a["s_scores"][r, 0][oa].view(np.uint32), b["s_scores"][r, 0][ob].view(np.uint32))
+    _check_step(op, b, _all_queries(p), parity.TOL[p.dtype], "exchange")
