@@ -279,8 +279,10 @@ def main():
         achieved = alg_bytes / (m_call * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS,
-                "kernel": "misa_decode_step call: step_route_kernel + decode_score_kernel + "
-                          "decode_compact_kernel + decode_resolve_kernel",
+                "kernel": ("misa_decode_step call: decode_step_kernel + decode_select_kernel"
+                           if p.batch >= 8 else
+                           "misa_decode_step call: step_route_kernel + decode_score_kernel + "
+                           "decode_select_kernel"),
                 "algorithmic_bytes": alg_bytes,
                 "traffic": traffic_from_profile("misa_decode_step", args.workload, sha)}
     else:

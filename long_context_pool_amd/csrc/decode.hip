@@ -785,25 +785,30 @@ __global__ __launch_bounds__(kStepThreads) void decode_step_kernel(StepArgs a) {
   constexpr int64_t kTileStep = 16 * kStepWaves;
   // Chunk [cb, ce): every wave writes its per-head sums to red[wave][.];
   // callers synchronise, then add red[0..7][j] in wave order.  One tile is
-  // multiplied while the next loads; the loop body is kept single because
-  // this code runs from a cold instruction cache, where size costs more than
-  // a register copy.
+  // multiplied while the next loads; the loop is not unrolled further
+  // because this code runs once, from a cold instruction cache.
   auto chunk_sums = [&](int64_t cb, int64_t ce, const PTile* first) {
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
       for (int i = 0; i < 4; ++i) rs[ht][i] = 0.f;
     const int64_t c_first = cb + 16 * wave;
-    PTile tc, tn;
+    // Two tiles in fixed roles (ping-pong; a copy tc = tn would wait for the
+    // loads in flight).
+    PTile ta, tb;
     if (c_first < ce) {
-      if (first) tc = *first;
-      else load_tile(c_first, tc);
+      if (first) ta = *first;
+      else load_tile(c_first, ta);
     }
+    if (c_first + kTileStep < ce) load_tile(c_first + kTileStep, tb);
 #pragma unroll 1
-    for (int64_t c0 = c_first; c0 < ce; c0 += kTileStep) {
-      if (c0 + kTileStep < ce) load_tile(c0 + kTileStep, tn);
-      mul_tile(c0, ce, tc);
-      tc = tn;
+    for (int64_t c0 = c_first; c0 < ce; c0 += 2 * kTileStep) {
+      mul_tile(c0, ce, ta);
+      if (c0 + 2 * kTileStep < ce) load_tile(c0 + 2 * kTileStep, ta);
+      if (c0 + kTileStep < ce) {
+        mul_tile(c0 + kTileStep, ce, tb);
+        if (c0 + 3 * kTileStep < ce) load_tile(c0 + 3 * kTileStep, tb);
+      }
     }
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1)

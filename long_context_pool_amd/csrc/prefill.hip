@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
   __shared__ __attribute__((aligned(16))) uint8_t tb0[BUF_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t tb1[BUF_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t tb2[BUF_BYTES];
-  __shared__ float sk_tile[kTileKeys];  // fp8 key scales of the sample stage
+  __shared__ float sk_tile[2][32];  // fp8 key scales of the two sample stage slots
   // fp8 key scales of the tile in buffer 0, 1, 2 (one copy per wave).
   __shared__ float sk0[DT == kFP8 ? kPWaves : 1][kTileKeys];
   __shared__ float sk1[DT == kFP8 ? kPWaves : 1][kTileKeys];
@@ -292,32 +292,46 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
   const int64_t len = s_end - s_begin;
   uint16_t* smp = reinterpret_cast<uint16_t*>(wave < 2 ? tb0 : tb1) + (wave & 1) * QPW * kSamples;  // [QPW][kSamples]
   float tau_slot[NS];
-  // Sample tiles (32 keys) are staged in buffer 2; each tile's scores go
-  // straight to the sample area (sample m of query qw at smp[qw][m]).
+  // Sample tiles (32 keys) are staged in buffer 2 (two stage slots); each
+  // tile's scores go straight to the sample area (sample m of query qw at
+  // smp[qw][m]).  The strided sample rows are loaded four tiles ahead into
+  // registers, so their latency overlaps the scoring of earlier tiles.
   {
-    uint8_t* stage = tb2;
+    static_assert(2 * 32 * RB <= BUF_BYTES, "two sample stage slots fit buffer 2");
     const int kr = threadIdx.x >> 3;  // 8 threads per key row
     const int part = threadIdx.x & 7;
-    for (int st = 0; st < kSamples / 32; ++st) {
+    struct SReg {
+      uint4 v0, v1;
+      float sk;
+    };
+    auto sload = [&](int st) -> SReg {
+      SReg r;
       const int m_ld = st * 32 + kr;
-      const int64_t key_ld = len > 0 ? s_begin + (static_cast<int64_t>(m_ld) * len) / kSamples : -1;
+      const int64_t key_ld = (len > 0 && st < kSamples / 32) ? s_begin + (static_cast<int64_t>(m_ld) * len) / kSamples : -1;
+      const int64_t row = seq * a.L + (key_ld < 0 ? 0 : key_ld);
       if constexpr (DT == kBF16) {
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) +
-                                                          (seq * a.L + (key_ld < 0 ? 0 : key_ld)) * kD + 16 * part);
-        const uint4 v0 = key_ld < 0 ? make_uint4(0, 0, 0, 0) : src[0];
-        const uint4 v1 = key_ld < 0 ? make_uint4(0, 0, 0, 0) : src[1];
-        __syncthreads();
-        uint4* dst = reinterpret_cast<uint4*>(stage + kr * RB + 32 * part);
-        dst[0] = v0;
-        dst[1] = v1;
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + row * kD + 16 * part);
+        r.v0 = key_ld < 0 ? make_uint4(0, 0, 0, 0) : src[0];
+        r.v1 = key_ld < 0 ? make_uint4(0, 0, 0, 0) : src[1];
+        r.sk = 1.f;
       } else {
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.k) +
-                                                          (seq * a.L + (key_ld < 0 ? 0 : key_ld)) * kD + 16 * part);
-        const uint4 v0 = key_ld < 0 ? make_uint4(0, 0, 0, 0) : src[0];
-        const float skr = (key_ld >= 0 && part == 0) ? a.k_scale[seq * a.L + key_ld] : 1.f;
-        __syncthreads();
-        *reinterpret_cast<uint4*>(stage + kr * RB + 16 * part) = v0;
-        if (part == 0) sk_tile[kr] = skr;
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.k) + row * kD + 16 * part);
+        r.v0 = key_ld < 0 ? make_uint4(0, 0, 0, 0) : src[0];
+        r.v1 = make_uint4(0, 0, 0, 0);
+        r.sk = (key_ld >= 0 && part == 0) ? a.k_scale[row] : 1.f;
+      }
+      return r;
+    };
+    // One tile from the registers r: stage it, score it, store its keys.
+    auto sample_tile = [&](int st, const SReg& r) {
+      uint8_t* stage = tb2 + (st & 1) * 32 * RB;
+      if constexpr (DT == kBF16) {
+        uint4* dst = reinterpret_cast<uint4*>(stage + kr * RB + 32 * part);
+        dst[0] = r.v0;
+        dst[1] = r.v1;
+      } else {
+        *reinterpret_cast<uint4*>(stage + kr * RB + 16 * part) = r.v0;
+        if (part == 0) sk_tile[st & 1][kr] = r.sk;
       }
       __syncthreads();
       float out[NS];
@@ -325,7 +339,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
       const int m = st * 32 + colr;
       const int64_t key = len > 0 ? s_begin + (static_cast<int64_t>(m) * len) / kSamples : -1;
       float skv = 1.f;
-      if constexpr (DT == kFP8) skv = sk_tile[colr];
+      if constexpr (DT == kFP8) skv = sk_tile[st & 1][colr];
 #pragma unroll
       for (int sl = 0; sl < NS; ++sl) {
         const bool ok = key >= 0 && key <= pos_slot[sl];
@@ -334,6 +348,20 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
         if (HPQ < 32 || hf == 0)
           smp[qw * kSamples + m] = ok ? static_cast<uint16_t>(float_key(out[sl] * skv) >> 16) : 0;
       }
+    };
+    // Four register sets in fixed roles (a rotation by copies would wait
+    // for the loads being copied).
+    SReg r0 = sload(0), r1 = sload(1), r2 = sload(2), r3 = sload(3);
+    static_assert((kSamples / 32) % 4 == 0, "sample tiles come in fours");
+    for (int st = 0; st < kSamples / 32; st += 4) {
+      sample_tile(st, r0);
+      r0 = sload(st + 4);
+      sample_tile(st + 1, r1);
+      r1 = sload(st + 5);
+      sample_tile(st + 2, r2);
+      r2 = sload(st + 6);
+      sample_tile(st + 3, r3);
+      r3 = sload(st + 7);
     }
     __syncthreads();
   }
