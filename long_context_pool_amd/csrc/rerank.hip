@@ -198,6 +198,128 @@ __global__ __launch_bounds__(kRRThreads) void rerank_gather_kernel(
   }
 }
 
+// Gathers through LDS: a lane-per-candidate gather (lane l reads 16 bytes of
+// candidate l%32's row per instruction) touches 32 rows per instruction and
+// is limited by the address unit, not by memory.  Here each load instruction
+// instead covers whole rows -- 64 lanes = RPI rows of CPR 16-byte chunks --
+// and lands directly in LDS (buffer-to-LDS loads); the MFMA B operands are
+// then read from LDS.  Chunk c of tile row j sits at chunk position
+// c ^ (j % CPR), so the B reads (32 rows, one chunk each) hit distinct banks.
+// Workgroup (chunk, row): the query's head rows are staged once in LDS; wave
+// w scores NTW tiles of 32 candidates per round, all of a round's loads in
+// flight before its first MFMA, and its tiles are private (no barrier).
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rr_rsrc(const void* base, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void rr_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void rr_vmcnt0() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int DT, int RT, int NTW>
+__global__ __launch_bounds__(kRRThreads) void rerank_lds_kernel(
+    const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const void* __restrict__ k, const float* __restrict__ k_scale,
+    const int32_t* __restrict__ cand, int32_t kprime, int32_t L, int32_t T, int32_t H,
+    int32_t per_wg, float* __restrict__ out) {
+  constexpr int ROWB = kD * (DT == kBF16 ? 2 : 1);  // key row bytes
+  constexpr int CPR = ROWB / 16;                     // 16-byte chunks per row
+  constexpr int RPI = kWave / CPR;                   // rows per load instruction
+  constexpr int TILE = 32 * ROWB;                    // one 32-candidate tile
+  __shared__ __attribute__((aligned(16))) uint8_t keys[kRRWaves][NTW][TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t qst[kMaxHeads * ROWB];
+  __shared__ float wst[kMaxHeads];
+  const int64_t r = blockIdx.y;
+  const int64_t seq = r / T;
+  const int64_t pos = static_cast<int64_t>(L) - T + (r % T);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = lane_id();
+  const int hf = lane >> 5;
+  const int col = lane & 31;
+
+  // Query head rows and weights -> LDS.
+  const uint8_t* qrow = static_cast<const uint8_t*>(q) + r * H * ROWB;
+  for (int i = threadIdx.x; i < kMaxHeads * CPR; i += kRRThreads)
+    reinterpret_cast<uint4*>(qst)[i] = i < H * CPR ? reinterpret_cast<const uint4*>(qrow)[i] : make_uint4(0, 0, 0, 0);
+  const float sq = (DT == kFP8) ? q_scale[r] : 1.f;
+  if (threadIdx.x < kMaxHeads) wst[threadIdx.x] = threadIdx.x < H ? w[r * H + threadIdx.x] * sq : 0.f;
+  __syncthreads();
+  CandScorer<DT, RT> cs;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int j = rt * 32 + col;
+    const uint8_t* src = qst + j * ROWB;
+    if constexpr (DT == kBF16) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) cs.a16[rt][ks] = as_bf16x8(reinterpret_cast<const uint4*>(src + 128 * hf)[ks]);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint4 lo = reinterpret_cast<const uint4*>(src + 64 * hf)[2 * ks];
+        const uint4 hi = reinterpret_cast<const uint4*>(src + 64 * hf)[2 * ks + 1];
+        cs.a8[rt][ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cs.wl[rt][i] = wst[rt * 32 + 8 * (i / 4) + 4 * hf + (i % 4)];
+  }
+
+  const __amdgpu_buffer_rsrc_t rk =
+      rr_rsrc(static_cast<const uint8_t*>(k) + seq * static_cast<int64_t>(L) * ROWB, L * ROWB);
+  const int32_t* crow = cand + r * kprime;
+  float* orow = out + r * kprime;
+  const int c_wg = blockIdx.x * per_wg;
+  const int c_end = min(c_wg + per_wg, kprime);
+  for (int c_round = c_wg + wave * NTW * 32; c_round < c_end; c_round += kRRWaves * NTW * 32) {
+    int32_t sid[NTW];
+    float skv[NTW];
+    // This lane's candidate of each tile (lanes l and l+32 share one), then
+    // the tiles' rows into this wave's LDS slots.
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) {
+      const int c = c_round + 32 * u + col;
+      const int32_t sv = c < c_end ? crow[c] : -1;
+      sid[u] = (sv >= 0 && sv <= pos) ? sv : -1;
+      skv[u] = (DT == kFP8 && sid[u] >= 0) ? k_scale[seq * L + sid[u]] : 1.f;
+    }
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) {
+#pragma unroll
+      for (int i = 0; i < 32 / RPI; ++i) {
+        const int j = i * RPI + lane / CPR;        // tile row of this lane's chunk
+        const int pc = lane % CPR;                 // its chunk position in LDS
+        const int lc = pc ^ (j % CPR);             // the row chunk stored there
+        const int32_t sj = __shfl(sid[u], j, kWave);
+        const uint32_t voff = static_cast<uint32_t>(sj < 0 ? 0 : sj) * ROWB + 16u * lc;
+        rr_load16_lds(rk, &keys[wave][u][i * 1024], voff);
+      }
+    }
+    rr_vmcnt0();  // this wave's rows have landed (its LDS slots are private)
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) {
+      typename CandScorer<DT, RT>::KeyB kb;
+      const uint8_t* trow = &keys[wave][u][col * ROWB];
+      if constexpr (DT == kBF16) {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) kb.b[ks] = reinterpret_cast<const uint4*>(trow)[(8 * hf + ks) ^ (col % CPR)];
+      } else {
+#pragma unroll
+        for (int uu = 0; uu < 4; ++uu) kb.b[uu] = reinterpret_cast<const uint4*>(trow)[(4 * hf + uu) ^ (col % CPR)];
+      }
+      const float v = cs.compute(kb) * skv[u];
+      const int c = c_round + 32 * u + col;
+      if (lane < 32 && c < c_end) orow[c] = sid[u] >= 0 ? v : -__builtin_inff();
+    }
+    // The next round's loads overwrite these slots: reads must be done.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  }
+}
+
 // Top-k of one query's k' (score, candidate) list, in one 1024-thread
 // workgroup: the list is read once into registers, a digit histogram (LDS)
 // gives the threshold digit b*, a block scan places the entries above b* in
@@ -347,8 +469,9 @@ hipError_t launch_rerank(const Shape& s, int32_t kprime, int32_t k, const void* 
     // (bf16: 128 B per lane each).
     constexpr int kNtwF8 = 4, kNtwB16 = 2;
     const int ntw = s.dtype == kBF16 ? kNtwB16 : kNtwF8;
-    dim3 g((kprime + kRRWaves * 32 * ntw - 1) / (kRRWaves * 32 * ntw), static_cast<unsigned>(rows));
-#define RG(DT, RT, NTW) rerank_gather_kernel<DT, RT, NTW><<<g, kRRThreads, 0, st>>>(q, q_scale, w, kk, k_scale, cand, kprime, s.L, s.T, s.H, sc)
+    const int per_wg = kRRWaves * 32 * ntw * 2;  // two rounds per wave
+    dim3 g((kprime + per_wg - 1) / per_wg, static_cast<unsigned>(rows));
+#define RG(DT, RT, NTW) rerank_lds_kernel<DT, RT, NTW><<<g, kRRThreads, 0, st>>>(q, q_scale, w, kk, k_scale, cand, kprime, s.L, s.T, s.H, per_wg, sc)
     if (s.dtype == kBF16) { if (two) RG(kBF16, 2, kNtwB16); else RG(kBF16, 1, kNtwB16); }
     else { if (two) RG(kFP8, 2, kNtwF8); else RG(kFP8, 1, kNtwF8); }
 #undef RG
