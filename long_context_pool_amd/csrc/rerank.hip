@@ -170,9 +170,9 @@ __global__ __launch_bounds__(kRRThreads) void rerank_gather_kernel(
     const void* __restrict__ k, const float* __restrict__ k_scale,
     const int32_t* __restrict__ cand, int32_t kprime, int32_t L, int32_t T, int32_t H,
     float* __restrict__ out) {
-  const int64_t r = blockIdx.y;
-  const int64_t seq = r / T;
-  const int64_t pos = static_cast<int64_t>(L) - T + (r % T);
+  const int64_t seq = blockIdx.z;
+  const int64_t r = seq * T + blockIdx.y;
+  const int64_t pos = static_cast<int64_t>(L) - T + blockIdx.y;
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
   const int cbase = (blockIdx.x * kRRWaves + wave) * 32 * NTW + (lane & 31);
@@ -234,9 +234,9 @@ __global__ __launch_bounds__(kRRThreads) void rerank_lds_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t keys[kRRWaves][NTW][TILE];
   __shared__ __attribute__((aligned(16))) uint8_t qst[kMaxHeads * ROWB];
   __shared__ float wst[kMaxHeads];
-  const int64_t r = blockIdx.y;
-  const int64_t seq = r / T;
-  const int64_t pos = static_cast<int64_t>(L) - T + (r % T);
+  const int64_t seq = blockIdx.z;
+  const int64_t r = seq * T + blockIdx.y;
+  const int64_t pos = static_cast<int64_t>(L) - T + blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = lane_id();
   const int hf = lane >> 5;
@@ -465,16 +465,37 @@ hipError_t launch_rerank(const Shape& s, int32_t kprime, int32_t k, const void* 
   float* sc = static_cast<float*>(ws);
   if (s.dtype != kF32) {
     const bool two = s.H > 32;
-    // Gathers in flight per wave: 4 tiles (fp8: 64 B per lane each) or 2
-    // (bf16: 128 B per lane each).
-    constexpr int kNtwF8 = 4, kNtwB16 = 2;
-    const int ntw = s.dtype == kBF16 ? kNtwB16 : kNtwF8;
-    const int per_wg = kRRWaves * 32 * ntw * 2;  // two rounds per wave
-    dim3 g((kprime + per_wg - 1) / per_wg, static_cast<unsigned>(rows));
+    // Two tiles of 32 candidates in flight per wave (fp8: 64 B per lane
+    // each, bf16: 128 B).  Rounds per wave: as many as keep at least eight
+    // workgroups per CU, up to 32, so the query rows staged into LDS once
+    // per workgroup are reused over many candidate tiles on long prefill
+    // lists, while a short decode batch still spreads over the chip.
+    constexpr int kNtw = 2;
+    int rounds = 32;
+    while (rounds > 1) {
+      const int64_t per = static_cast<int64_t>(kRRWaves) * 32 * kNtw * rounds;
+      if (rows * ((kprime + per - 1) / per) >= 2048) break;
+      rounds >>= 1;
+    }
+    const int per_wg = kRRWaves * 32 * kNtw * rounds;
+    const int64_t seq_bytes = static_cast<int64_t>(s.L) * kD * (s.dtype == kBF16 ? 2 : 1);
+    if (seq_bytes < (int64_t{1} << 31)) {
+      dim3 g((kprime + per_wg - 1) / per_wg, s.T, s.batch);
 #define RG(DT, RT, NTW) rerank_lds_kernel<DT, RT, NTW><<<g, kRRThreads, 0, st>>>(q, q_scale, w, kk, k_scale, cand, kprime, s.L, s.T, s.H, per_wg, sc)
-    if (s.dtype == kBF16) { if (two) RG(kBF16, 2, kNtwB16); else RG(kBF16, 1, kNtwB16); }
-    else { if (two) RG(kFP8, 2, kNtwF8); else RG(kFP8, 1, kNtwF8); }
+      if (s.dtype == kBF16) { if (two) RG(kBF16, 2, kNtw); else RG(kBF16, 1, kNtw); }
+      else { if (two) RG(kFP8, 2, kNtw); else RG(kFP8, 1, kNtw); }
 #undef RG
+    } else {
+      // A sequence's keys beyond the 32-bit reach of a buffer descriptor:
+      // gather with flat addresses instead.
+      constexpr int kNtwF8 = 4, kNtwB16 = 2;
+      const int per = kRRWaves * 32 * (s.dtype == kBF16 ? kNtwB16 : kNtwF8);
+      dim3 g((kprime + per - 1) / per, s.T, s.batch);
+#define RG(DT, RT, NTW) rerank_gather_kernel<DT, RT, NTW><<<g, kRRThreads, 0, st>>>(q, q_scale, w, kk, k_scale, cand, kprime, s.L, s.T, s.H, sc)
+      if (s.dtype == kBF16) { if (two) RG(kBF16, 2, kNtwB16); else RG(kBF16, 1, kNtwB16); }
+      else { if (two) RG(kFP8, 2, kNtwF8); else RG(kFP8, 1, kNtwF8); }
+#undef RG
+    }
   } else {
     dim3 g1((kprime + kRerankThreads - 1) / kRerankThreads, s.T, s.batch);
     rerank_score_kernel<kF32><<<g1, kRerankThreads, 0, st>>>(q, q_scale, w, kk, k_scale, cand,
