@@ -3,31 +3,28 @@
 // step (router of Eq. (7)-(8) + scoring + top-k).
 //
 // Decode is HBM-bound: every key of the sequence is read once (d*e bytes per
-// key) whether h or H heads score it.  The score kernel streams keys with
-// 16-byte loads straight into MFMA B operands (RowScorer: the query's scored
-// head rows are the A operand, 16 keys per 16x16 output tile, ReLU * w head
-// sum on the accumulators) and writes the scores (L fp32 per sequence) to the
+// key) whether h or H heads score it.  The scorers stream keys with 16-byte
+// loads straight into MFMA B operands (RowScorer: the query's scored head
+// rows are the A operand, 16 keys per 16x16 output tile, ReLU * w head sum on
+// the accumulators) and write the scores (L fp32 per sequence) to the
 // workspace.  While scoring, each workgroup counts its scores by a histogram
-// digit (a monotone map of the score to 8192 bins; LDS histogram, flushed to
-// the sequence's global histogram with atomics), so after the score kernel
-// the digit b* holding the k-th best score of every sequence is known without
-// another pass:
-//   compact  (many workgroups per sequence): every workgroup finds b* from the
-//            histogram, writes its tokens of digits above b* straight to the
-//            output and appends those of digit b* to a short list (one packed
-//            atomic counter per sequence reserves both ranges);
-//   resolve  (one workgroup per sequence): the (k - above) best of the b*
-//            list, exactly.
-// Kernel boundaries order these steps: no workgroup waits for another inside
-// a kernel (a device-wide release fence per workgroup costs far more than a
-// launch here).
+// digit (a monotone map of the score to 8192 bins), so after scoring the
+// digit b* holding the k-th best score of every sequence is known without
+// another pass.  The select kernel (many workgroups per sequence) finds b*
+// from the histograms, writes its tokens of digits above b* straight to the
+// output and appends those of digit b* to a short list; the last workgroup
+// of the sequence to arrive takes the (k - above) best of that list.
 //
-// The fused step starts with a router kernel: workgroup (chunk, sequence)
-// sums ReLU(q_j . p_b) over 32 pooled blocks in fp32 (the last block's pooled
-// key -- the block holding the newest key -- is recomputed from the keys and
-// written back to the cache, the per-step pooling of Eq. (4)); every score
-// workgroup then finishes the router for its sequence (E and top-h, Eq. (7)-
-// (8)) before scoring, so no separate route launch is needed.
+// The fused step has two forms:
+//  - batch >= 8: one kernel (decode_step_kernel) with G workgroups per
+//    sequence; each computes one chunk of the router sums, the chunks are
+//    exchanged through the workspace (or recomputed locally, bit-identically,
+//    when a peer is late), then every workgroup picks the heads and scores
+//    its key range;
+//  - smaller batches: a router-partials kernel (step_route_kernel, which
+//    also re-pools the newest block) and the score kernel, which finishes
+//    the router (E and top-h) in its prologue.
+// Both are followed by the select kernel.
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma.hpp"

@@ -4,8 +4,11 @@
 // Every indexer head scores the same key, so for a tile of queries the scores
 // are one dense contraction: the gathered head rows of the tile (A operand,
 // held in registers for the whole pass) times K^T (B operand, 64-key tiles
-// staged through LDS, double-buffered, shared by the workgroup's four waves),
-// 32x32x16 bf16 or 32x32x64 fp8 MFMA, fp32 accumulation.  The ReLU * w head
+// loaded straight into LDS by buffer-to-LDS loads, three tile buffers so two
+// tiles are in flight while one is multiplied, shared by the workgroup's four
+// waves), 32x32x16 bf16 or 32x32x64 fp8 MFMA, fp32 accumulation.  The
+// epilogue of one tile (head sums, candidate selection and appends) is
+// interleaved with the next tile's MFMAs.  The ReLU * w head
 // sum runs on the accumulators: the row order inside a 32-row tile is chosen
 // so that each lane holds all heads of its query for its key column.
 //

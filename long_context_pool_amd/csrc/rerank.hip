@@ -3,13 +3,12 @@
 // H heads (the Eq. (1) score) and the k best candidates are kept.
 //
 // bf16 / fp8: the query's H head rows are the A operand of 32x32 MFMA tiles
-// (held in registers); each 32-candidate column tile gathers its key rows
-// straight into B registers (lane l: candidate l%32, head-dim elements
-// [64*(l/32), +64) -- one contiguous run per lane).  The ReLU * w head sum is
-// taken on the accumulators.  Workgroup (chunk, query) scores 128 (fp8) or 64
-// (bf16) candidates per wave with every gather of the wave in flight before
-// its first MFMA, and writes the scores to the workspace; the gathers are
-// the cost, so the kernel keeps many of them in flight and no LDS.
+// (held in registers); 32-candidate column tiles are the B operand.  The key
+// rows of a tile are gathered whole-row-coalesced into LDS (buffer-to-LDS
+// loads, rerank_lds_kernel); the ReLU * w head sum is taken on the
+// accumulators, and the scores go to the workspace.  A sequence whose keys
+// exceed a buffer descriptor's 32-bit reach is gathered with flat loads
+// straight into B registers instead (rerank_gather_kernel).
 // fp32: one thread per candidate (query rows staged in LDS).
 // Then one workgroup per query selects the k best of its k' scores in
 // registers: a digit histogram in LDS, the threshold digit from a block scan,
