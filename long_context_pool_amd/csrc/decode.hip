@@ -662,65 +662,96 @@ __global__ __launch_bounds__(kStepThreads) void decode_step_kernel(StepArgs a) {
   PTile t_first;
   if (own_cb + 16 * wave < own_ce) load_tile(own_cb + 16 * wave, t_first);
 
+  // 1-2. Loads of the head rows, weights and the newest block's first keys
+  // are all issued before any of them is used: one round trip (overlapping
+  // the pooled tile above) instead of one per loop iteration.
+  constexpr int PPR = kD * EB / 16;  // 16-byte pieces per head row / key row
+  constexpr int NPC = kMaxH * PPR / kStepThreads;  // staging pieces per thread
+  static_assert(NPC * kStepThreads == kMaxH * PPR, "staging pieces split evenly");
+  const uint4* qsrc = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.q) + seq * H * kD * EB);
+  uint4 qv[NPC];
+#pragma unroll
+  for (int u = 0; u < NPC; ++u) {
+    const int pc = threadIdx.x + u * kStepThreads;
+    qv[u] = pc / PPR < H ? qsrc[pc] : make_uint4(0, 0, 0, 0);
+  }
+  const float wv = threadIdx.x < H ? a.w[seq * H + threadIdx.x] : 0.f;
+  // Mean of keys [(M-1)B, L): thread t takes 16-byte piece t % PPR of key
+  // slots t / PPR + NSL * u, four keys per round; the slots' sums meet in
+  // LDS.
+  constexpr int NSL = kStepThreads / PPR;
+  constexpr int KR = 4;  // keys per slot per round
+  static_assert(NSL * kD <= kDigits, "slot sums fit the histogram area");
+  const int piece = threadIdx.x % PPR;
+  const int slot = threadIdx.x / PPR;
+  const int64_t s0 = (M - 1) * a.B;
+  const int nl = static_cast<int>(a.L - s0);
+  const uint8_t* kbm = static_cast<const uint8_t*>(a.k) + (seq * a.L + s0) * kD * EB;
+  uint4 mv[KR];
+  float msc[KR];
+  auto mean_load = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < KR; ++u) {
+      const int key = k0 + u * NSL;
+      const bool ok = key < nl;
+      mv[u] = ok ? reinterpret_cast<const uint4*>(kbm + static_cast<int64_t>(key) * kD * EB)[piece]
+                 : make_uint4(0, 0, 0, 0);
+      msc[u] = (DT == kFP8 && ok) ? a.k_scale[seq * a.L + s0 + key] : 0.f;
+    }
+  };
+  mean_load(slot);
+
   // 1. Head rows -> LDS (router copy widened to bf16; fp8 codes kept for the
   // scorer), weights.
-  {
-    constexpr int PPR = kD * EB / 16;  // 16-byte pieces per head row
-    const uint4* qsrc = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.q) + seq * H * kD * EB);
-    for (int pc = threadIdx.x; pc < kMaxH * PPR; pc += kStepThreads) {
-      const int row = pc / PPR, c = pc % PPR;
-      const uint4 v = row < H ? qsrc[pc] : make_uint4(0, 0, 0, 0);
-      if constexpr (DT == kBF16) {
-        *reinterpret_cast<uint4*>(qr_lds + row * QP + 16 * c) = v;
-      } else {
-        *reinterpret_cast<uint4*>(qs_lds + row * SP + 16 * c) = v;
-        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-        uint32_t o[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          // e4m3 -> fp32 is exact and bf16 holds the 4-bit significand exactly.
-          const float f0 = fp8_to_f32(wd[u] & 0xFF), f1 = fp8_to_f32((wd[u] >> 8) & 0xFF);
-          const float f2 = fp8_to_f32((wd[u] >> 16) & 0xFF), f3 = fp8_to_f32(wd[u] >> 24);
-          o[2 * u] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
-          o[2 * u + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u);
-        }
-        uint4* dst = reinterpret_cast<uint4*>(qr_lds + row * QP + 32 * c);
-        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  for (int u = 0; u < NPC; ++u) {
+    const int pc = threadIdx.x + u * kStepThreads;
+    const int row = pc / PPR, c = pc % PPR;
+    const uint4 v = qv[u];
+    if constexpr (DT == kBF16) {
+      *reinterpret_cast<uint4*>(qr_lds + row * QP + 16 * c) = v;
+    } else {
+      *reinterpret_cast<uint4*>(qs_lds + row * SP + 16 * c) = v;
+      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[8];
+#pragma unroll
+      for (int u2 = 0; u2 < 4; ++u2) {
+        // e4m3 -> fp32 is exact and bf16 holds the 4-bit significand exactly.
+        const float f0 = fp8_to_f32(wd[u2] & 0xFF), f1 = fp8_to_f32((wd[u2] >> 8) & 0xFF);
+        const float f2 = fp8_to_f32((wd[u2] >> 16) & 0xFF), f3 = fp8_to_f32(wd[u2] >> 24);
+        o[2 * u2] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+        o[2 * u2 + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u);
       }
+      uint4* dst = reinterpret_cast<uint4*>(qr_lds + row * QP + 32 * c);
+      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
     }
-    if (threadIdx.x < kMaxH) w_lds[threadIdx.x] = threadIdx.x < H ? a.w[seq * H + threadIdx.x] : 0.f;
   }
-  // 2. Mean of keys [(M-1)B, L): thread t takes 16-byte piece t % P of key
-  // slots t / P + NSL * u; the slots' sums meet in LDS.
+  if (threadIdx.x < kMaxH) w_lds[threadIdx.x] = wv;
+
+  // 2. The mean itself.
   {
-    constexpr int P = kD * EB / 16;
     constexpr int EPP = 16 / EB;
-    constexpr int NSL = kStepThreads / P;
-    static_assert(NSL * kD <= kDigits, "slot sums fit the histogram area");
     float* part = reinterpret_cast<float*>(hist);  // [NSL][kD]
-    const int piece = threadIdx.x % P;
-    const int slot = threadIdx.x / P;
-    const int64_t s0 = (M - 1) * a.B;
-    const int nl = static_cast<int>(a.L - s0);
-    const uint8_t* kb = static_cast<const uint8_t*>(a.k) + (seq * a.L + s0) * kD * EB;
     float acc[EPP];
 #pragma unroll
     for (int e = 0; e < EPP; ++e) acc[e] = 0.f;
-    for (int key = slot; key < nl; key += NSL) {
-      const uint4 v = reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(key) * kD * EB)[piece];
-      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
-      if constexpr (DT == kBF16) {
+    for (int k0 = slot; k0 < nl; k0 += KR * NSL) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += __uint_as_float(wd[e] << 16);
-          acc[2 * e + 1] += __uint_as_float(wd[e] & 0xFFFF0000u);
+      for (int u = 0; u < KR; ++u) {
+        const uint32_t wd[4] = {mv[u].x, mv[u].y, mv[u].z, mv[u].w};
+        if constexpr (DT == kBF16) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += __uint_as_float(wd[e] << 16);
+            acc[2 * e + 1] += __uint_as_float(wd[e] & 0xFFFF0000u);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[e] += fp8_to_f32((wd[e / 4] >> (8 * (e % 4))) & 0xFF) * msc[u];
         }
-      } else {
-        const float sc = a.k_scale[seq * a.L + s0 + key];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] += fp8_to_f32((wd[e / 4] >> (8 * (e % 4))) & 0xFF) * sc;
       }
+      if (k0 + KR * NSL < nl) mean_load(k0 + KR * NSL);
     }
 #pragma unroll
     for (int e = 0; e < EPP; ++e) part[slot * kD + piece * EPP + e] = acc[e];
@@ -852,9 +883,20 @@ __global__ __launch_bounds__(kStepThreads) void decode_step_kernel(StepArgs a) {
   if (sh_flag) {
     // All G partials of the sequence, fetched by the whole workgroup at once
     // (coherent loads), then added by wave 0 in chunk order.
-    for (int i = threadIdx.x; i < G * kMaxH; i += kStepThreads)
-      xpart[i] = __uint_as_float(__hip_atomic_load(a.rpart + seq * G * kMaxH + i, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT));
+    constexpr int NXP = kStepMaxG * kMaxH / kStepThreads;
+    uint32_t xv[NXP];
+#pragma unroll
+    for (int u = 0; u < NXP; ++u) {
+      const int i = threadIdx.x + u * kStepThreads;
+      xv[u] = i < G * kMaxH ? __hip_atomic_load(a.rpart + seq * G * kMaxH + i, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT)
+                            : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < NXP; ++u) {
+      const int i = threadIdx.x + u * kStepThreads;
+      if (i < G * kMaxH) xpart[i] = __uint_as_float(xv[u]);
+    }
     __syncthreads();
     if (wave == 0)
       for (int c = 0; c < G; ++c) S += xpart[c * kMaxH + lane];

@@ -41,6 +41,10 @@ SMALL = {
                                   kprime=700, dtype=synth.BF16, needles=8, seed=27),
     "fp8_decode_b12": synth.small("fp8_decode_b12", batch=12, L=2100, T=1, H=32, h=8, B=128, k=200,
                                   kprime=500, dtype=synth.FP8_E4M3, needles=6, seed=28),
+    # Long rows at batch 8: each select workgroup covers 4608 keys (two
+    # 4096-score chunks), and the last workgroup of a row has none.
+    "bf16_decode_b8_long": synth.small("bf16_decode_b8_long", batch=8, L=140000, T=1, H=16, h=4, B=128,
+                                       k=256, kprime=512, dtype=synth.BF16, needles=8, seed=29),
     "t_eq_l": synth.small("t_eq_l", batch=1, L=200, T=200, H=64, h=8, B=64, k=64, kprime=96,
                           dtype=synth.BF16, needles=0, seed=24),
     "b1_h16": synth.small("b1_h16", batch=1, L=700, T=9, H=64, h=16, B=1, k=100, kprime=200,
