@@ -117,6 +117,11 @@ __device__ __forceinline__ void load16_to_lds(__amdgpu_buffer_rsrc_t r, void* ld
 __device__ __forceinline__ void load4_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
 }
+__device__ __forceinline__ uint2 buffer_load_u32x2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_uint2(v.x, v.y);
+}
 __device__ __forceinline__ void buffer_store_u32x2(uint32_t lo, uint32_t hi, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, r, off, 0, 0);
@@ -192,7 +197,6 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
   const int64_t pos_last = static_cast<int64_t>(a.L) - a.T + t_last;
   const int64_t s_begin = split * a.chunk;
   const int64_t s_end = min<int64_t>(s_begin + a.chunk, pos_last + 1);
-  const int64_t s_safe = s_end > s_begin ? s_begin : 0;  // a row every load may touch
 
   // ---- A operand: this wave's gathered head rows, and per-lane weights.
   bf16x8 a16[kRT][8];
@@ -658,43 +662,52 @@ __global__ void prefill_clear_kernel(int32_t* fail_count) {
 // segment overflowed and at least k candidates score >= tau_max = max over
 // splits of tau (every non-candidate of split s scores below tau_s).  Then:
 //  1. one pass over the candidates (the S segments viewed as one list: entry
-//     c lies in segment s with pre[s] <= c < pre[s+1]) keeps the first
-//     kPCache of them in LDS, builds an LDS histogram of their digits
-//     relative to the digit of tau_min (every candidate is >= tau_min) and
-//     counts the candidates >= tau_max;
+//     c lies in segment s with pre[s] <= c < pre[s+1]; thread t holds
+//     entries t + NT u in registers, all of its loads in flight at once)
+//     builds an LDS histogram of their digits relative to the digit of
+//     tau_min (every candidate is >= tau_min) and counts the candidates
+//     >= tau_max;
 //  2. the digit b* holding the k-th best comes from a block scan of the
 //     histogram;
-//  3. a second pass (LDS, then global beyond the cache) writes candidates
-//     above b* straight to the output and gathers those at b* into an LDS
-//     list (wave ballots + LDS counters);
+//  3. per-wave counts (one barrier) and wave ballots place the entries
+//     above b* in the output and those at b* in an LDS list;
 //  4. the list is resolved exactly (ties: lower token).
+// Entries beyond the registers' NR * NT are read again from global memory,
+// 8 NT at a time.
 constexpr int kPCandCap = 1024;
-constexpr int kPCache = 6144;
+// Candidates held in registers per thread: kSelRegsSmall while the expected
+// count (about kSampleMargin k) fits comfortably, else kSelRegsLarge (more
+// registers, so one workgroup per CU).
+constexpr int kSelRegsSmall = 8;
+constexpr int kSelRegsLarge = 24;
 constexpr int kRelBins = 2048;
 
 struct PSelSmem {
-  alignas(16) float cache_s[kPCache];
-  alignas(16) int32_t cache_i[kPCache];
   uint32_t hist[kRelBins];
   alignas(16) float cand_score[kPCandCap];
   alignas(16) int32_t cand_idx[kPCandCap];
-  ResolveSmem rs;
+  union {
+    ResolveSmem rs;
+    TopkSmem ts;
+  };
   int pre[9];
   int scan_tmp[32];
   int digit, above, count, nge, bad;
-  uint32_t cnt_hi, cnt_at;
+  int wtot[kTopkThreadsSel / kWave];  // per-wave packed counts above / at b*
   float tau_max, tau_min;
 };
 
+template <int NR>
 __global__ __launch_bounds__(kTopkThreadsSel) void prefill_select_kernel(
     const uint2* __restrict__ cand, const int32_t* __restrict__ cnt, const float* __restrict__ tau,
     int32_t S, int32_t cap, int32_t k, int32_t* __restrict__ idx, float* __restrict__ scores_out,
     int32_t* __restrict__ fail_count, int32_t* __restrict__ fail_list) {
   constexpr int NT = kTopkThreadsSel;
+  static_assert(NR >= 1 && NR <= 32, "entry slots are bits of a 32-bit mask");
+  constexpr int NO = 8;  // entries per thread per round beyond the registers
   __shared__ PSelSmem sm;
   const int64_t r = blockIdx.x;
   const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
   int32_t* out = idx + r * k;
   float* out_s = scores_out ? scores_out + r * k : nullptr;
   const uint2* base = cand + r * S * static_cast<int64_t>(cap);
@@ -718,8 +731,6 @@ __global__ __launch_bounds__(kTopkThreadsSel) void prefill_select_kernel(
     sm.tau_min = tmin;
     sm.bad = bad;
     sm.nge = 0;
-    sm.cnt_hi = 0;
-    sm.cnt_at = 0;
   }
   __syncthreads();
   int pre[9];
@@ -727,6 +738,10 @@ __global__ __launch_bounds__(kTopkThreadsSel) void prefill_select_kernel(
   for (int u = 0; u < 9; ++u) pre[u] = sm.pre[u];
   const int total = pre[8];
   const float tm = sm.tau_max;
+  // The query's S segments through one buffer resource (32-bit offsets:
+  // S * cap * 8 bytes < 2^31 for L <= 2^24); entry c at byte offset
+  // 8 (s cap + c - pre[s]).
+  const __amdgpu_buffer_rsrc_t crs = buffer_rsrc(uniform_ptr(base), S * cap * 8);
   auto entry = [=](int c) -> uint2 {
     int sg = 0, b = 0;
 #pragma unroll
@@ -735,7 +750,7 @@ __global__ __launch_bounds__(kTopkThreadsSel) void prefill_select_kernel(
       sg = ge ? u : sg;
       b = ge ? pre[u] : b;
     }
-    return base[static_cast<int64_t>(sg) * cap + (c - b)];
+    return buffer_load_u32x2(crs, static_cast<uint32_t>(sg * cap + (c - b)) * 8u);
   };
   // Fewer than k candidates is fine only when nothing was filtered out.
   if (sm.bad || (total < k && tm != -__builtin_inff())) {
@@ -763,26 +778,34 @@ __global__ __launch_bounds__(kTopkThreadsSel) void prefill_select_kernel(
     const uint32_t d = key_digit(v) - d0;  // >= 0 for candidates
     return d < static_cast<uint32_t>(kRelBins) ? d : static_cast<uint32_t>(kRelBins - 1);
   };
-  // 1. cache, histogram, certificate count.
-  // Four loads in flight per thread (clamped to the list, masked after).
+  // 1. histogram and certificate count; entries t + NT u (u < NR) stay in
+  // registers.
+  uint2 e[NR];
+#pragma unroll
+  for (int u = 0; u < NR; ++u) {
+    const int c = u * NT + static_cast<int>(threadIdx.x);
+    e[u] = (u * NT < total && c < total) ? entry(c) : make_uint2(0u, 0u);
+  }
   int nge = 0;
-  for (int c0 = 0; c0 < total; c0 += 4 * NT) {
-    uint2 e[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) e[u] = entry(min(c0 + u * NT + static_cast<int>(threadIdx.x), total - 1));
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = c0 + u * NT + threadIdx.x;
-      if (c < total) {
-        const float v = __uint_as_float(e[u].x);
-        if (c < kPCache) {
-          sm.cache_s[c] = v;
-          sm.cache_i[c] = static_cast<int32_t>(e[u].y);
-        }
-        atomicAdd(&sm.hist[rel(v)], 1u);
-        nge += v >= tm ? 1 : 0;
-      }
+  auto count_entry = [&](int c, uint2 x) __attribute__((always_inline)) {
+    if (c < total) {
+      const float v = __uint_as_float(x.x);
+      atomicAdd(&sm.hist[rel(v)], 1u);
+      nge += v >= tm ? 1 : 0;
     }
+  };
+#pragma unroll
+  for (int u = 0; u < NR; ++u)
+    if (u * NT < total) count_entry(u * NT + static_cast<int>(threadIdx.x), e[u]);
+  for (int c0 = NR * NT; c0 < total; c0 += NO * NT) {  // beyond the registers
+    uint2 f[NO];
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+      const int c = c0 + u * NT + static_cast<int>(threadIdx.x);
+      f[u] = c < total ? entry(c) : make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < NO; ++u) count_entry(c0 + u * NT + static_cast<int>(threadIdx.x), f[u]);
   }
 #pragma unroll
   for (int o = kWave / 2; o >= 1; o >>= 1) nge += __shfl_xor(nge, o, kWave);
@@ -822,46 +845,89 @@ __global__ __launch_bounds__(kTopkThreadsSel) void prefill_select_kernel(
     if (threadIdx.x == 0) fail_list[atomicAdd(fail_count, 1)] = static_cast<int32_t>(r);
     return;
   }
-  // 3. compaction by relative digit (64 consecutive entries per wave step,
-  // so the loop bound is wave-uniform for the ballots).
-  for (int c0 = wave * kWave; c0 < total; c0 += NT) {
-    const int c = c0 + lane;
-    const bool ok = c < total;
-    float v = 0.f;
-    int32_t id = 0;
-    if (ok) {
-      if (c < kPCache) {
-        v = sm.cache_s[c];
-        id = sm.cache_i[c];
-      } else {
-        const uint2 e = entry(c);
-        v = __uint_as_float(e.x);
-        id = static_cast<int32_t>(e.y);
+  // 3. compaction by relative digit: per-thread counts above and at b*
+  // (packed: above in the low 16 bits, total < k <= 8192; at-b* high, total
+  // <= kPCandCap), one block scan for the positions.
+  // Positions: each wave's entries above b* (at b*) take one run of the
+  // output (list), after those of the lower waves; inside the run, entry
+  // slot by slot (ballots), so the stores of a slot coalesce.
+  // Relative digit b* as a key interval [blo, bhi] (the last relative bin
+  // holds every higher digit too).
+  const uint32_t blo = digit_lo_key(bstar + d0);
+  const uint32_t bhi = bstar == static_cast<uint32_t>(kRelBins - 1) ? 0xFFFFFFFFu : digit_hi_key(bstar + d0);
+  auto classify = [&](const uint2* ev, int n, int c0, uint32_t& mh, uint32_t& ma) __attribute__((always_inline)) {
+    mh = 0;
+    ma = 0;
+    const int nu = (total - c0 + NT - 1) / NT;  // slots holding entries (uniform)
+#pragma unroll
+    for (int u = 0; u < n; ++u) {
+      if (u < nu) {
+        const int c = c0 + u * NT + static_cast<int>(threadIdx.x);
+        const uint32_t key = float_key(__uint_as_float(ev[u].x));
+        mh |= (c < total && key > bhi) ? (1u << u) : 0u;
+        ma |= (c < total && key >= blo && key <= bhi) ? (1u << u) : 0u;
       }
     }
-    const uint32_t d = rel(v);
-    const bool h = ok && d > bstar;
-    const bool at = ok && d == bstar;
-    const uint64_t mh = __ballot(h);
-    const uint64_t ma = __ballot(at);
-    if (mh) {
-      uint32_t pos = 0;
-      if (lane == 0) pos = atomicAdd(&sm.cnt_hi, static_cast<uint32_t>(__popcll(mh)));
-      pos = __shfl(pos, 0, kWave) + lanes_below(mh);
-      if (h && pos < static_cast<uint32_t>(k)) {
-        out[pos] = id;
-        if (out_s) out_s[pos] = v;
-      }
+  };
+  const int wave = threadIdx.x / kWave;
+  int run_h = 0, run_a = 0;  // entries placed by earlier rounds (block totals)
+  auto place = [&](const uint2* ev, int n, int c0, uint32_t mh, uint32_t ma) __attribute__((always_inline)) {
+    int wt = __popc(mh) | (__popc(ma) << 16);
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) wt += __shfl_xor(wt, o, kWave);
+    if (lane == 0) sm.wtot[wave] = wt;
+    __syncthreads();
+    int base = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) {
+      const int v = sm.wtot[w];
+      base += w < wave ? v : 0;
+      all += v;
     }
-    if (ma) {
-      uint32_t pos = 0;
-      if (lane == 0) pos = atomicAdd(&sm.cnt_at, static_cast<uint32_t>(__popcll(ma)));
-      pos = __shfl(pos, 0, kWave) + lanes_below(ma);
-      if (at && pos < static_cast<uint32_t>(kPCandCap)) {
-        sm.cand_score[pos] = v;
-        sm.cand_idx[pos] = id;
+    int ph = run_h + (base & 0xFFFF), pa = run_a + (base >> 16);
+    const int nu = min(n, (total - c0 + NT - 1) / NT);  // slots holding entries (uniform)
+#pragma unroll
+    for (int u = 0; u < n; ++u) {
+      if (u >= nu) continue;
+      const bool h = (mh >> u) & 1u;
+      const bool at = (ma >> u) & 1u;
+      const uint64_t bh = __ballot(h);
+      const uint64_t ba = __ballot(at);
+      if (h) {
+        const int pos = ph + lanes_below(bh);
+        if (pos < k) {
+          out[pos] = static_cast<int32_t>(ev[u].y);
+          if (out_s) out_s[pos] = __uint_as_float(ev[u].x);
+        }
+      } else if (at) {
+        const int pos = pa + lanes_below(ba);
+        if (pos < kPCandCap) {
+          sm.cand_score[pos] = __uint_as_float(ev[u].x);
+          sm.cand_idx[pos] = static_cast<int32_t>(ev[u].y);
+        }
       }
+      ph += __popcll(bh);
+      pa += __popcll(ba);
     }
+    run_h += all & 0xFFFF;
+    run_a += all >> 16;
+    __syncthreads();  // wtot is reused
+  };
+  {
+    uint32_t mh, ma;
+    classify(e, NR, 0, mh, ma);
+    place(e, NR, 0, mh, ma);
+  }
+  for (int c0 = NR * NT; c0 < total; c0 += NO * NT) {  // beyond the registers
+    uint2 f[NO];
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+      const int c = c0 + u * NT + static_cast<int>(threadIdx.x);
+      f[u] = c < total ? entry(c) : make_uint2(0u, 0u);
+    }
+    uint32_t mh, ma;
+    classify(f, NO, c0, mh, ma);
+    place(f, NO, c0, mh, ma);
   }
   __syncthreads();
   // 4. the (k - above) best of the b* list.
@@ -869,9 +935,9 @@ __global__ __launch_bounds__(kTopkThreadsSel) void prefill_select_kernel(
                        out_s ? out_s + above : nullptr, sm.rs))
     return;
   // A bin of more than kRankMax equal-digit entries: exact fallback, reusing
-  // the cache area (no longer needed) for the radix select.
+  // the resolve area (no longer needed) for the radix select.
   __syncthreads();
-  TopkSmem& tsm = *reinterpret_cast<TopkSmem*>(sm.cache_s);
+  TopkSmem& tsm = sm.ts;
   const float* cs = sm.cand_score;
   const int32_t* ci = sm.cand_idx;
   block_topk<NT>(
@@ -879,7 +945,6 @@ __global__ __launch_bounds__(kTopkThreadsSel) void prefill_select_kernel(
       [=](int64_t j) { return ci[j]; }, [=](int64_t j) { return cs[j]; }, out + above,
       out_s ? out_s + above : nullptr, tsm);
 }
-static_assert(sizeof(TopkSmem) <= sizeof(float) * kPCache, "fallback fits the cache area");
 
 // Repair: queries whose candidates could not be certified are scored over
 // their whole prefix (16x16 MFMA key streaming) into this workgroup's scratch
@@ -1016,8 +1081,12 @@ hipError_t launch_prefill_score_topk(const Shape& s, int32_t nh, const int32_t* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = static_cast<int64_t>(s.batch) * s.T;
-  prefill_select_kernel<<<static_cast<unsigned>(rows), kTopkThreadsSel, 0, st>>>(
-      args.cand, args.cnt, args.tau, pl.S, pl.cap, k, idx, scores_out, fail_count, fail_list);
+  if (kSampleMargin * 1.25f * k <= static_cast<float>(kSelRegsSmall * kTopkThreadsSel))
+    prefill_select_kernel<kSelRegsSmall><<<static_cast<unsigned>(rows), kTopkThreadsSel, 0, st>>>(
+        args.cand, args.cnt, args.tau, pl.S, pl.cap, k, idx, scores_out, fail_count, fail_list);
+  else
+    prefill_select_kernel<kSelRegsLarge><<<static_cast<unsigned>(rows), kTopkThreadsSel, 0, st>>>(
+        args.cand, args.cnt, args.tau, pl.S, pl.cap, k, idx, scores_out, fail_count, fail_list);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nrt = nh <= 16 ? 1 : (nh <= 32 ? 2 : 4);
