@@ -321,10 +321,11 @@ __global__ __launch_bounds__(kRRThreads) void rerank_lds_kernel(
 
 // Top-k of one query's k' (score, candidate) list, in one 1024-thread
 // workgroup: the list is read once into registers, a digit histogram (LDS)
-// gives the threshold digit b*, a block scan places the entries above b* in
-// the output and those at b* in an LDS list, which is resolved exactly.
-// Invalid candidates carry score -inf and a distinct negative id (so ties
-// among them resolve), printed as -1 at the end.
+// gives the threshold digit b*; each wave's entries above b* take one run of
+// the output after those of the lower waves (slot by slot, wave ballots, so
+// the stores coalesce) and those at b* go to an LDS list, which is resolved
+// exactly.  Invalid candidates carry score -inf and a distinct negative id
+// (so ties among them resolve), written out as -1.
 constexpr int kLSThreads = 1024;
 constexpr int kLSPer = kMaxKprime / kLSThreads;
 constexpr int kLSCap = 2048;
@@ -336,6 +337,7 @@ struct LSelSmem {
   ResolveSmem rs;
   TopkSmem base;
   int scan_tmp[32];
+  int wtot[kLSThreads / kWave];
   int digit, above, count;
 };
 
@@ -401,6 +403,9 @@ __global__ __launch_bounds__(kLSThreads) void list_select_kernel(
         [=](int64_t i) { const int32_t c = crow[i]; return c >= 0 && c <= pos ? c : static_cast<int32_t>(-1 - i); },
         [=](int64_t i) { const int32_t c = crow[i]; return c >= 0 && c <= pos ? srow[i] : -__builtin_inff(); },
         out, out_s, sm.base);
+    __syncthreads();
+    for (int p = threadIdx.x; p < k; p += kLSThreads)
+      if (out[p] < 0) out[p] = -1;
   } else {
     const uint32_t lo = digit_lo_key(bstar), hi = digit_hi_key(bstar);
     uint32_t mh = 0, ma = 0;
@@ -411,27 +416,41 @@ __global__ __launch_bounds__(kLSThreads) void list_select_kernel(
       mh |= (in && key > hi) ? (1u << j) : 0u;
       ma |= (in && key >= lo && key <= hi) ? (1u << j) : 0u;
     }
-    // Packed counts: above-b* in the low 16 bits (< k <= 8192), at-b* high.
-    int total;
-    const int off = block_exclusive_sum<kLSThreads>(__popc(mh) | (__popc(ma) << 16), sm.scan_tmp,
-                                                    total);
-    int ph = off & 0xFFFF;
-    int pa = off >> 16;
+    // Per-wave packed counts (above-b* low 16 bits: < k <= 8192; at-b*
+    // high), then each wave's runs.
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    int wt = __popc(mh) | (__popc(ma) << 16);
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) wt += __shfl_xor(wt, o, kWave);
+    if (lane == 0) sm.wtot[wave] = wt;
+    __syncthreads();
+    int wb = 0;
+#pragma unroll
+    for (int w = 0; w < kLSThreads / kWave; ++w) wb += w < wave ? sm.wtot[w] : 0;
+    int ph = wb & 0xFFFF;
+    int pa = wb >> 16;
 #pragma unroll
     for (int j = 0; j < kLSPer; ++j) {
-      if ((mh >> j) & 1u) {
-        if (ph < k) {
-          out[ph] = id[j];
-          if (out_s) out_s[ph] = v[j];
+      const bool h = (mh >> j) & 1u;
+      const bool at = (ma >> j) & 1u;
+      const uint64_t bh = __ballot(h);
+      const uint64_t ba = __ballot(at);
+      if (h) {
+        const int pos = ph + lanes_below(bh);
+        if (pos < k) {
+          out[pos] = id[j];  // above b*: a valid candidate
+          if (out_s) out_s[pos] = v[j];
         }
-        ++ph;
-      } else if ((ma >> j) & 1u) {
-        if (pa < kLSCap) {
-          sm.cand_score[pa] = v[j];
-          sm.cand_idx[pa] = id[j];
+      } else if (at) {
+        const int pos = pa + lanes_below(ba);
+        if (pos < kLSCap) {
+          sm.cand_score[pos] = v[j];
+          sm.cand_idx[pos] = id[j];
         }
-        ++pa;
       }
+      ph += __popcll(bh);
+      pa += __popcll(ba);
     }
     __syncthreads();
     if (!resolve_list<kLSThreads>(sm.cand_score, sm.cand_idx, bcount, k - above, out + above,
@@ -443,11 +462,11 @@ __global__ __launch_bounds__(kLSThreads) void list_select_kernel(
           bcount, k - above, [](int64_t) { return true; }, [=](int64_t j) { return float_key(cs[j]); },
           [=](int64_t j) { return ci[j]; }, [=](int64_t j) { return cs[j]; }, out + above,
           out_s ? out_s + above : nullptr, sm.base);
+      __syncthreads();
+      for (int p = above + threadIdx.x; p < k; p += kLSThreads)
+        if (out[p] < 0) out[p] = -1;
     }
   }
-  __syncthreads();
-  for (int p = threadIdx.x; p < k; p += kLSThreads)
-    if (out[p] < 0) out[p] = -1;
 }
 
 }  // namespace

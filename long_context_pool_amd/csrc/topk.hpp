@@ -229,7 +229,7 @@ __device__ __forceinline__ void rank_write(const float* cs, const int32_t* ci, i
       rank += (j0 + 3 < n && rank_key(c.w, d.w) > me) ? 1 : 0;
     }
     if (rank < need) {
-      out_idx[rank] = ci[t];
+      out_idx[rank] = ci[t] < 0 ? -1 : ci[t];  // negative ids: distinct padding, printed as -1
       if (out_score) out_score[rank] = cs[t];
     }
   }
@@ -318,7 +318,7 @@ __device__ __forceinline__ bool resolve_list(const float* cs, const int32_t* ci,
       if (lane == 0) p = atomicAdd(&rs.n_hi, __popcll(mh));
       p = __shfl(p, 0, kWave) + lanes_below(mh);
       if (h && p < above) {
-        out_idx[p] = ci[t];
+        out_idx[p] = ci[t] < 0 ? -1 : ci[t];
         if (out_score) out_score[p] = cs[t];
       }
     }
