@@ -134,7 +134,8 @@ class Runner:
 
 def time_steps(fn, steps, warmup, stream):
     """Run warmup then exactly `steps` steps; returns (wall ms per step,
-    mean ms of the bracketed call measured with events on `stream`)."""
+    mean ms of the bracketed call measured with events on `stream`, host ms
+    per step, {10, 50, 90: percentile of the bracketed call's ms})."""
     import torch
 
     for i in range(warmup):
@@ -152,8 +153,10 @@ def time_steps(fn, steps, warmup, stream):
     torch.cuda.synchronize()
     host_ms = (time.perf_counter() - t0) * 1e3 / steps
     step_ms = start.elapsed_time(end) / steps
-    call_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
-    return step_ms, call_ms, host_ms
+    calls = sorted(a.elapsed_time(b) for a, b in evs)
+    call_ms = sum(calls) / steps
+    pct = {q: calls[min(len(calls) - 1, int(q / 100 * len(calls)))] for q in (10, 50, 90)}
+    return step_ms, call_ms, host_ms, pct
 
 
 def cpu_baseline(x, budget_s):
@@ -245,11 +248,11 @@ def main():
     r = Runner(x, n_sets, stream)
     torch.cuda.synchronize()
 
-    m_step, m_call, m_host = time_steps(r.misa_step, args.steps, args.warmup, stream)
+    m_step, m_call, m_host, m_pct = time_steps(r.misa_step, args.steps, args.warmup, stream)
     pairs = p.pairs
     res_dense = None
     if not args.no_dense:
-        d_step, d_call, _ = time_steps(r.dense_step, args.steps, args.warmup, stream)
+        d_step, d_call, _, _ = time_steps(r.dense_step, args.steps, args.warmup, stream)
         res_dense = {"value": pairs / (d_step / 1e3), "ms_per_step": d_step}
     torch.cuda.synchronize()
 
@@ -296,6 +299,7 @@ def main():
                 "algorithmic_flops": flops,
                 "traffic": traffic_from_profile("misa_score_topk", args.workload, sha)}
     roof["call_ms"] = m_call
+    roof["call_ms_p10_p50_p90"] = [m_pct[10], m_pct[50], m_pct[90]]
 
     if args.calibrate_copy:
         n = args.calibrate_copy // 16 * 16
