@@ -19,6 +19,7 @@ Prints one JSON line (metric/value = scored (query, token) pairs per second).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -51,6 +52,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", help="c1..c5 (default c2, the decode workload)")
+    ap.add_argument("--L", type=int, default=0,
+                    help="override the workload's context length (a sweep point, not a headline "
+                         "configuration: the line's workload name then carries _L<L>)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -240,6 +244,13 @@ def main():
     import synth
 
     p = synth.CONFIGS[args.workload]
+    wl_name = args.workload
+    if args.L:
+        if not p.T <= args.L:
+            print(f"--L {args.L} is shorter than the workload's {p.T} queries", file=sys.stderr)
+            sys.exit(2)
+        p = dataclasses.replace(p, L=args.L, name=f"{p.name}_L{args.L}")
+        wl_name = f"{args.workload}_L{args.L}"
     x = synth.generate(p)
     set_bytes = (x.q.numel() * x.q.element_size() + x.k.numel() * x.k.element_size() +
                  p.batch * p.M * p.d * 4)
@@ -287,7 +298,7 @@ def main():
                            "misa_decode_step call: step_route_kernel + decode_score_kernel + "
                            "decode_select_kernel"),
                 "algorithmic_bytes": alg_bytes,
-                "traffic": traffic_from_profile("misa_decode_step", args.workload, sha)}
+                "traffic": traffic_from_profile("misa_decode_step", wl_name, sha)}
     else:
         flops = 2 * p.h * p.d * pairs
         achieved = flops / (m_call * 1e-3) / 1e12
@@ -297,7 +308,7 @@ def main():
                 "kernel": "misa_score_topk call: prefill_clear_kernel + prefill_score_kernel + "
                           "prefill_select_kernel + prefill_repair_kernel",
                 "algorithmic_flops": flops,
-                "traffic": traffic_from_profile("misa_score_topk", args.workload, sha)}
+                "traffic": traffic_from_profile("misa_score_topk", wl_name, sha)}
     roof["call_ms"] = m_call
     roof["call_ms_p10_p50_p90"] = [m_pct[10], m_pct[50], m_pct[90]]
 

@@ -694,6 +694,7 @@ struct PSelSmem {
   int scan_tmp[32];
   int digit, above, count, nge, bad;
   int wtot[kTopkThreadsSel / kWave];  // per-wave packed counts above / at b*
+  uint32_t dmin, dmax;                 // candidate digit range (tau_min = -inf)
   float tau_max, tau_min;
 };
 
@@ -731,6 +732,8 @@ __global__ __launch_bounds__(kTopkThreadsSel) void prefill_select_kernel(
     sm.tau_min = tmin;
     sm.bad = bad;
     sm.nge = 0;
+    sm.dmin = 0xFFFFFFFFu;
+    sm.dmax = 0u;
   }
   __syncthreads();
   int pre[9];
@@ -770,22 +773,56 @@ __global__ __launch_bounds__(kTopkThreadsSel) void prefill_select_kernel(
     }
     return;
   }
-  // Relative digit: every candidate is >= tau_min, so its digit is >= d0
-  // (d0 = 0 when some split kept every key).
-  const float tmin = sm.tau_min;
-  const uint32_t d0 = tmin == -__builtin_inff() ? 0u : key_digit(tmin);
-  auto rel = [=](float v) -> uint32_t {
-    const uint32_t d = key_digit(v) - d0;  // >= 0 for candidates
-    return d < static_cast<uint32_t>(kRelBins) ? d : static_cast<uint32_t>(kRelBins - 1);
-  };
-  // 1. histogram and certificate count; entries t + NT u (u < NR) stay in
-  // registers.
+  // 1. entries t + NT u (u < NR) into registers.
   uint2 e[NR];
 #pragma unroll
   for (int u = 0; u < NR; ++u) {
     const int c = u * NT + static_cast<int>(threadIdx.x);
     e[u] = (u * NT < total && c < total) ? entry(c) : make_uint2(0u, 0u);
   }
+  // Relative digit (d - d0) >> shift.  Every candidate is >= tau_min, so
+  // with a finite tau_min, d0 = its digit (and digits more than kRelBins
+  // above it share the top bin).  When some split kept every key, the
+  // candidates' own digit range [dmin, dmax] sets d0 = dmin and the shift
+  // that fits the range in kRelBins bins.
+  const float tmin = sm.tau_min;
+  uint32_t d0 = 0, shift = 0;
+  if (tmin != -__builtin_inff()) {
+    d0 = key_digit(tmin);
+  } else {
+    uint32_t dmin = 0xFFFFFFFFu, dmax = 0u;
+    auto range_entry = [&](int c, uint2 x) __attribute__((always_inline)) {
+      if (c < total) {
+        const uint32_t d = key_digit(__uint_as_float(x.x));
+        dmin = min(dmin, d);
+        dmax = max(dmax, d);
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < NR; ++u)
+      if (u * NT < total) range_entry(u * NT + static_cast<int>(threadIdx.x), e[u]);
+    for (int c0 = NR * NT; c0 < total; c0 += NT)  // beyond the registers
+      range_entry(c0 + static_cast<int>(threadIdx.x),
+                  c0 + static_cast<int>(threadIdx.x) < total ? entry(c0 + threadIdx.x) : make_uint2(0u, 0u));
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) {
+      dmin = min(dmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(dmin), o, kWave)));
+      dmax = max(dmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(dmax), o, kWave)));
+    }
+    if (lane == 0) {
+      atomicMin(&sm.dmin, dmin);
+      atomicMax(&sm.dmax, dmax);
+    }
+    __syncthreads();
+    d0 = sm.dmin;
+    const uint32_t span = sm.dmax - sm.dmin;
+    shift = span < static_cast<uint32_t>(kRelBins) ? 0u : static_cast<uint32_t>(32 - __clz(static_cast<int>(span)) - 11);
+  }
+  auto rel = [=](float v) -> uint32_t {
+    const uint32_t d = (key_digit(v) - d0) >> shift;  // >= 0 for candidates
+    return d < static_cast<uint32_t>(kRelBins) ? d : static_cast<uint32_t>(kRelBins - 1);
+  };
+  // Histogram and certificate count.
   int nge = 0;
   auto count_entry = [&](int c, uint2 x) __attribute__((always_inline)) {
     if (c < total) {
@@ -851,10 +888,11 @@ __global__ __launch_bounds__(kTopkThreadsSel) void prefill_select_kernel(
   // Positions: each wave's entries above b* (at b*) take one run of the
   // output (list), after those of the lower waves; inside the run, entry
   // slot by slot (ballots), so the stores of a slot coalesce.
-  // Relative digit b* as a key interval [blo, bhi] (the last relative bin
+  // Relative bin b* as a key interval [blo, bhi] (the last relative bin
   // holds every higher digit too).
-  const uint32_t blo = digit_lo_key(bstar + d0);
-  const uint32_t bhi = bstar == static_cast<uint32_t>(kRelBins - 1) ? 0xFFFFFFFFu : digit_hi_key(bstar + d0);
+  const uint32_t dlo = d0 + (bstar << shift), dhi = d0 + ((bstar + 1) << shift) - 1u;
+  const uint32_t blo = digit_lo_key(dlo);
+  const uint32_t bhi = (bstar == static_cast<uint32_t>(kRelBins - 1) || dhi >= kTopDigit) ? 0xFFFFFFFFu : digit_hi_key(dhi);
   auto classify = [&](const uint2* ev, int n, int c0, uint32_t& mh, uint32_t& ma) __attribute__((always_inline)) {
     mh = 0;
     ma = 0;
