@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--L", type=int, default=0,
                     help="override the workload's context length (a sweep point, not a headline "
                          "configuration: the line's workload name then carries _L<L>)")
+    ap.add_argument("--T", type=int, default=0,
+                    help="override the workload's queries per sequence (likewise; _T<T>)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -245,12 +247,14 @@ def main():
 
     p = synth.CONFIGS[args.workload]
     wl_name = args.workload
-    if args.L:
-        if not p.T <= args.L:
-            print(f"--L {args.L} is shorter than the workload's {p.T} queries", file=sys.stderr)
+    if args.L or args.T:
+        L, T = args.L or p.L, args.T or p.T
+        if not 1 <= T <= L:
+            print(f"--L {L} / --T {T}: need 1 <= T <= L", file=sys.stderr)
             sys.exit(2)
-        p = dataclasses.replace(p, L=args.L, name=f"{p.name}_L{args.L}")
-        wl_name = f"{args.workload}_L{args.L}"
+        tag = (f"_L{L}" if args.L else "") + (f"_T{T}" if args.T else "")
+        p = dataclasses.replace(p, L=L, T=T, name=f"{p.name}{tag}")
+        wl_name = f"{args.workload}{tag}"
     x = synth.generate(p)
     set_bytes = (x.q.numel() * x.q.element_size() + x.k.numel() * x.k.element_size() +
                  p.batch * p.M * p.d * 4)

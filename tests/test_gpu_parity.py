@@ -45,6 +45,12 @@ SMALL = {
     # 4096-score chunks), and the last workgroup of a row has none.
     "bf16_decode_b8_long": synth.small("bf16_decode_b8_long", batch=8, L=140000, T=1, H=16, h=4, B=128,
                                        k=256, kprime=512, dtype=synth.BF16, needles=8, seed=29),
+    # Decode edge shapes: a context shorter than k (every key, -1 padding) in
+    # one partial block, and a two-block context with the newest block partial.
+    "decode_lt_k": synth.small("decode_lt_k", batch=3, L=50, T=1, H=64, h=8, B=64, k=64, kprime=96,
+                               dtype=synth.BF16, needles=2, seed=30),
+    "decode_two_blocks": synth.small("decode_two_blocks", batch=9, L=100, T=1, H=64, h=8, B=64, k=32,
+                                     kprime=48, dtype=synth.FP8_E4M3, needles=2, seed=31),
     "t_eq_l": synth.small("t_eq_l", batch=1, L=200, T=200, H=64, h=8, B=64, k=64, kprime=96,
                           dtype=synth.BF16, needles=0, seed=24),
     "b1_h16": synth.small("b1_h16", batch=1, L=700, T=9, H=64, h=16, B=1, k=100, kprime=200,
