@@ -115,7 +115,13 @@ class Runner:
             if ev:
                 ev[1].record(st)
         else:
-            m.misa_pool_keys(self.shp, s["k"], s["ks"], s["pooled"], st)
+            if p.T <= 8:
+                # Multi-query decode: the pooled cache only changes in the
+                # blocks holding the T newest keys.
+                b0 = (p.L - p.T) // p.B
+                m.misa_pool_keys_range(self.shp, b0, p.M - b0, s["k"], s["ks"], s["pooled"], st)
+            else:
+                m.misa_pool_keys(self.shp, s["k"], s["ks"], s["pooled"], st)
             m.misa_route(self.shp, p.h, s["q"], s["qs"], s["w"], s["pooled"], s["k"], s["ks"],
                          self.heads, None, self.ws, st)
             if ev:

@@ -298,20 +298,22 @@ __global__ __launch_bounds__(kCompactThreads) void decode_select_kernel(
     const float* __restrict__ rows, const uint32_t* __restrict__ ghist, uint32_t* __restrict__ cnt,
     uint32_t* __restrict__ done, float* __restrict__ cand_s, int32_t* __restrict__ cand_i,
     int32_t* __restrict__ idx, float* __restrict__ scores_out, int32_t L, int32_t k, int32_t G,
-    uint64_t* __restrict__ rsync) {
+    uint64_t* __restrict__ rsync, int32_t T) {
   __shared__ SelectSmem sm;
   const int64_t r = blockIdx.y;
   // Re-arm the next step's router exchange (this kernel follows the step
   // kernel, so every arrival of this call has been counted).
   if (rsync && blockIdx.x == 0 && threadIdx.x == 0) rsync[r] = kSyncMagic << 16;
   const float* row = rows + r * L;
+  // Row r = (sequence, query t < T): the query's prefix is keys [0, n).
+  const int32_t n = L - T + 1 + static_cast<int32_t>(r % T);
   int32_t* out = idx + r * k;
   float* out_s = scores_out ? scores_out + r * k : nullptr;
-  if (L <= k) {
+  if (n <= k) {
     if (blockIdx.x == 0)
       for (int i = threadIdx.x; i < k; i += kCompactThreads) {
-        out[i] = i < L ? i : -1;
-        if (out_s) out_s[i] = i < L ? row[i] : -__builtin_inff();
+        out[i] = i < n ? i : -1;
+        if (out_s) out_s[i] = i < n ? row[i] : -__builtin_inff();
       }
     return;
   }
@@ -319,10 +321,10 @@ __global__ __launch_bounds__(kCompactThreads) void decode_select_kernel(
   const uint32_t* gh = ghist + r * G * kHistWords;
   const int coarse = load_coarse(gh, G);
   // Scores first (independent of b*), so their loads overlap the scan.
-  float v[kCompactPer];  // clamped loads; tokens past L are masked below
+  float v[kCompactPer];  // clamped loads; tokens past n are masked below
 #pragma unroll
   for (int j = 0; j < kCompactPer; ++j)
-    v[j] = row[min(c0 + j * kCompactThreads + static_cast<int>(threadIdx.x), L - 1)];
+    v[j] = row[min(c0 + j * kCompactThreads + static_cast<int>(threadIdx.x), n - 1)];
   find_digit<kCompactThreads>(gh, coarse, k, sm.scan_tmp, sm.s_coarse, &sm.s_digit, &sm.s_above,
                               &sm.s_count, G);
   const uint32_t bstar = static_cast<uint32_t>(sm.s_digit);
@@ -331,7 +333,7 @@ __global__ __launch_bounds__(kCompactThreads) void decode_select_kernel(
   if (count > kCandCap) {
     if (blockIdx.x == 0)
       block_topk<kCompactThreads>(
-          L, k, [](int64_t) { return true; }, [=](int64_t i) { return float_key(row[i]); },
+          n, k, [](int64_t) { return true; }, [=](int64_t i) { return float_key(row[i]); },
           [](int64_t i) { return static_cast<int32_t>(i); }, [=](int64_t i) { return row[i]; }, out,
           out_s, sm.base);
     return;
@@ -342,8 +344,8 @@ __global__ __launch_bounds__(kCompactThreads) void decode_select_kernel(
   for (int j = 0; j < kCompactPer; ++j) {
     const int i = c0 + j * kCompactThreads + threadIdx.x;
     const uint32_t key = float_key(v[j]);
-    mh |= (i < L && key > hi) ? (1u << j) : 0u;
-    ma |= (i < L && key >= lo && key <= hi) ? (1u << j) : 0u;
+    mh |= (i < n && key > hi) ? (1u << j) : 0u;
+    ma |= (i < n && key >= lo && key <= hi) ? (1u << j) : 0u;
   }
   // Packed counts: above-b* in the low 16 bits (their row total is below
   // k <= 8192), at-b* in the high 16 bits (row total <= kCandCap).
@@ -1044,16 +1046,222 @@ DecodeWs decode_layout(const Shape& s, void* ws) {
   return d;
 }
 
+// Rows: s.batch of them, s.L scores apart; T consecutive rows per sequence
+// (row r's prefix holds s.L - T + 1 + r % T keys).
 void launch_select(const Shape& s, const DecodeWs& d, int32_t k, int32_t* idx, float* scores_out,
-                   hipStream_t st, int32_t G = 1) {
+                   hipStream_t st, int32_t G = 1, int32_t T = 1) {
   dim3 g((s.L + kCompactChunk - 1) / kCompactChunk, s.batch);
-  decode_select_kernel<<<g, kCompactThreads, 0, st>>>(d.rows, d.ghist, d.cnt, d.done, d.cand_s,
-                                                      d.cand_i, idx, scores_out, s.L, k, G, d.rsync);
+  decode_select_kernel<<<g, kCompactThreads, 0, st>>>(d.rows, d.ghist, d.cnt, d.done, d.cand_s, d.cand_i,
+                                                      idx, scores_out, s.L, k, G, d.rsync, T);
+}
+
+// ---------------------------------------------------------------------------
+// Multi-query decode: T (2 .. kMaxMQ) queries per sequence at the end of its
+// context (query t at position L - T + t, for instance draft tokens being
+// verified), scored in one pass over the keys.  The A operand of the 16x16
+// MFMA tiles holds every query's routed head rows: row rr of tile rt is head
+// slot rr % HP of query (16 rt + rr) / HP (HP = the head count rounded up to
+// 4, 8 or 16), so a query's rows share a 4-, 8- or 16-row band and its
+// ReLU * w head sum needs at most two cross-lane adds.  Each key is read once
+// for all T queries; the scores of query t go to row seq * T + t (keys past
+// its position are not written).  A row histogram kernel then records every
+// row's digit histogram, and the select kernel takes each row's top-k.
+constexpr int kMaxMQ = 8;
+
+struct MQArgs {
+  const void* q;
+  const float* q_scale;
+  const float* w;
+  const void* k;
+  const float* k_scale;
+  const int32_t* heads;  // [batch, T, nh] (nullptr: heads 0 .. nh-1)
+  int32_t nh;
+  float* rows;  // [batch * T, L]
+  int32_t L, T, H, keys_per_wave;
+};
+
+template <int DT, int HP, int NRT>
+__global__ __launch_bounds__(kDecThreads) void mq_score_kernel(MQArgs a) {
+  static_assert(HP == 4 || HP == 8 || HP == 16, "head band of 4, 8 or 16 rows");
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int col = lane & 15;
+  const int qq = lane >> 4;
+  const int64_t seq = blockIdx.y;
+  const int64_t L = a.L;
+  const void* krows = (DT == kBF16) ? static_cast<const void*>(static_cast<const uint16_t*>(a.k) + seq * L * kD)
+                                    : static_cast<const void*>(static_cast<const uint8_t*>(a.k) + seq * L * kD);
+  const int64_t s_begin = (static_cast<int64_t>(blockIdx.x) * kDecWaves + wave) * a.keys_per_wave;
+  const int64_t s_end = min<int64_t>(s_begin + a.keys_per_wave, L);
+  using Keys = typename RowScorer<DT, 1>::Keys;
+  Keys kb0, kb1;
+  if (s_begin < s_end) RowScorer<DT, 1>::load64(krows, s_begin, s_end, s_begin, kb0);
+  if (s_begin + 64 < s_end) RowScorer<DT, 1>::load64(krows, s_begin + 64, s_end, s_begin, kb1);
+
+  // A operands and per-row weights (times the query's fp8 scale).
+  auto head_of = [&](int rr) -> int {  // head of tile row rr, or -1
+    const int t = rr / HP, slot = rr % HP;
+    if (t >= a.T || slot >= a.nh) return -1;
+    const int j = a.heads ? a.heads[(seq * a.T + t) * a.nh + slot] : slot;
+    return (j >= 0 && j < a.H) ? j : -1;
+  };
+  bf16x8 a16[NRT][4];
+  i32x8 a8[NRT];
+  float wl[NRT][4];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = rt * 16 + 4 * qq + i;
+      const int j = head_of(rr);
+      const int64_t qr = seq * a.T + rr / HP;
+      wl[rt][i] = j >= 0 ? a.w[qr * a.H + j] * ((DT == kFP8) ? a.q_scale[qr] : 1.f) : 0.f;
+    }
+    const int rr = rt * 16 + col;
+    const int j = head_of(rr);
+    const int64_t qoff = ((seq * a.T + rr / HP) * a.H + (j < 0 ? 0 : j)) * kD;
+    if constexpr (DT == kBF16) {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + (j < 0 ? 0 : qoff));
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) a16[rt][ks] = as_bf16x8(j < 0 ? make_uint4(0, 0, 0, 0) : src[4 * ks + qq]);
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.q) + (j < 0 ? 0 : qoff));
+      const uint4 lo = j < 0 ? make_uint4(0, 0, 0, 0) : src[qq];
+      const uint4 hi = j < 0 ? make_uint4(0, 0, 0, 0) : src[4 + qq];
+      a8[rt] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+  }
+  // Lanes that write: the first lane group of each query's band.
+  const bool writer = HP == 4 || (HP == 8 && (qq & 1) == 0) || (HP == 16 && qq == 0);
+
+  auto score = [&](const Keys& kb, int64_t s0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int64_t s = s0 + 16 * g + col;
+      const float sk = (DT == kFP8 && s < s_end) ? a.k_scale[seq * L + s] : 1.f;
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (DT == kBF16) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) acc = mfma16_bf16(a16[rt][ks], as_bf16x8(kb[g][ks]), acc);
+        } else {
+          const i32x8 b8{(int)kb[g][0].x, (int)kb[g][0].y, (int)kb[g][0].z, (int)kb[g][0].w,
+                         (int)kb[g][1].x, (int)kb[g][1].y, (int)kb[g][1].z, (int)kb[g][1].w};
+          acc = mfma16_fp8(a8[rt], b8, acc);
+        }
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part += wl[rt][i] * relu(acc[i]);
+        if constexpr (HP >= 8) part += __shfl_xor(part, 16, kWave);
+        if constexpr (HP == 16) part += __shfl_xor(part, 32, kWave);
+        const int t = (rt * 16 + 4 * qq) / HP;
+        if (writer && t < a.T && s < s_end && s <= L - a.T + t) a.rows[(seq * a.T + t) * L + s] = part * sk;
+      }
+    }
+  };
+  // Two 64-key groups in flight per wave (fixed roles).
+  for (int64_t s0 = s_begin; s0 < s_end; s0 += 128) {
+    score(kb0, s0);
+    if (s0 + 128 < s_end) RowScorer<DT, 1>::load64(krows, s0 + 128, s_end, s_begin, kb0);
+    if (s0 + 64 < s_end) {
+      score(kb1, s0 + 64);
+      if (s0 + 192 < s_end) RowScorer<DT, 1>::load64(krows, s0 + 192, s_end, s_begin, kb1);
+    }
+  }
+}
+
+// Digit histogram record of each row (one 1024-thread workgroup per row,
+// the row's prefix n = L - T + 1 + r % T read in rounds of 16 scores per
+// thread, all of a round's loads in flight): fine bins, then coarse sums.
+constexpr int kRowHistThreads = 1024;
+
+__global__ __launch_bounds__(kRowHistThreads) void row_hist_kernel(const float* __restrict__ rows,
+                                                                   uint32_t* __restrict__ ghist, int32_t L,
+                                                                   int32_t T) {
+  __shared__ uint32_t hist[kDigits];
+  const int64_t r = blockIdx.x;
+  const int32_t n = L - T + 1 + static_cast<int32_t>(r % T);
+  const float* row = rows + r * L;
+  for (int b = threadIdx.x; b < kDigits; b += kRowHistThreads) hist[b] = 0;
+  __syncthreads();
+  constexpr int U = 16;
+  for (int c0 = 0; c0 < n; c0 += U * kRowHistThreads) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = c0 + u * kRowHistThreads + static_cast<int>(threadIdx.x);
+      v[u] = row[i < n ? i : n - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (c0 + u * kRowHistThreads + static_cast<int>(threadIdx.x) < n) atomicAdd(&hist[key_digit(v[u])], 1u);
+  }
+  __syncthreads();
+  uint32_t* gh = ghist + r * kHistWords;
+  for (int b = threadIdx.x; b < kDigits; b += kRowHistThreads) gh[b] = hist[b];
+  for (int cb = threadIdx.x; cb < kCoarse; cb += kRowHistThreads) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int u = 0; u < kFinePerCoarse; ++u) c += hist[cb * kFinePerCoarse + (u + cb) % kFinePerCoarse];
+    gh[kDigits + cb] = c;
+  }
+}
+
+int mq_band(int32_t nh) { return nh <= 4 ? 4 : (nh <= 8 ? 8 : 16); }
+
+// One row per (sequence, query): the layout of a T = 1 problem over
+// batch * T sequences.
+Shape mq_rows_shape(const Shape& s) {
+  Shape r = s;
+  r.batch = s.batch * s.T;
+  r.T = 1;
+  return r;
+}
+
+template <int DT, int HP>
+void launch_mq_dt(const Shape& s, const MQArgs& a, hipStream_t st) {
+  dim3 grid((s.L + kDecWaves * a.keys_per_wave - 1) / (kDecWaves * a.keys_per_wave), s.batch);
+  const int nrt = (s.T * HP + 15) / 16;
+  if (nrt <= 1) mq_score_kernel<DT, HP, 1><<<grid, kDecThreads, 0, st>>>(a);
+  else if (nrt == 2) mq_score_kernel<DT, HP, 2><<<grid, kDecThreads, 0, st>>>(a);
+  else if (nrt == 3) mq_score_kernel<DT, HP, 3><<<grid, kDecThreads, 0, st>>>(a);
+  else mq_score_kernel<DT, HP, 4><<<grid, kDecThreads, 0, st>>>(a);
 }
 
 }  // namespace
 
 size_t decode_ws_bytes(const Shape& s) { return decode_layout(s, nullptr).total; }
+
+bool decode_mq_supported(const Shape& s, int32_t nh) {
+  return s.T >= 2 && s.T <= kMaxMQ && s.dtype != kF32 && nh >= 1 && nh <= 16 && s.T * mq_band(nh) <= 64 &&
+         static_cast<int64_t>(s.batch) * s.T <= 65535;
+}
+
+size_t decode_mq_ws_bytes(const Shape& s) { return decode_layout(mq_rows_shape(s), nullptr).total; }
+
+hipError_t launch_decode_mq_score_topk(const Shape& s, int32_t nh, const int32_t* heads, int32_t k,
+                                       const void* q, const float* q_scale, const float* w,
+                                       const void* kk, const float* k_scale, int32_t* idx,
+                                       float* scores_out, void* ws, hipStream_t st) {
+  const Shape sr = mq_rows_shape(s);
+  const DecodeWs d = decode_layout(sr, ws);
+  const int64_t ncnt = 2 * static_cast<int64_t>(sr.batch);  // compaction counters and arrivals
+  clear_kernel<<<static_cast<unsigned>((ncnt + 1023) / 1024), 256, 0, st>>>(d.cnt, ncnt);
+  MQArgs a{q, q_scale, w, kk, k_scale, heads, nh, d.rows, s.L, s.T, s.H, MISA_DECODE_KEYS_PER_WAVE};
+  const int hp = mq_band(nh);
+#define MQ(DT) \
+  if (hp == 4) launch_mq_dt<DT, 4>(s, a, st); \
+  else if (hp == 8) launch_mq_dt<DT, 8>(s, a, st); \
+  else launch_mq_dt<DT, 16>(s, a, st);
+  if (s.dtype == kBF16) { MQ(kBF16) } else { MQ(kFP8) }
+#undef MQ
+  row_hist_kernel<<<static_cast<unsigned>(sr.batch), kRowHistThreads, 0, st>>>(d.rows, d.ghist, s.L, s.T);
+  dim3 g((s.L + kCompactChunk - 1) / kCompactChunk, sr.batch);
+  decode_select_kernel<<<g, kCompactThreads, 0, st>>>(d.rows, d.ghist, d.cnt, d.done, d.cand_s, d.cand_i,
+                                                      idx, scores_out, s.L, k, 1, nullptr, s.T);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_score_topk(const Shape& s, int32_t nh, const int32_t* heads, int32_t k,
                                     const void* q, const float* q_scale, const float* w,

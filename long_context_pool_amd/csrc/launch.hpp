@@ -54,6 +54,17 @@ hipError_t launch_decode_score_topk(const Shape& s, int32_t nh, const int32_t* h
                                     const void* kk, const float* k_scale, int32_t* idx,
                                     float* scores_out, void* ws, hipStream_t st);
 
+// Multi-query decode (2 <= T <= 8 queries at the end of each sequence,
+// bf16/fp8, nh <= 16): every key read once for all T queries, then a row
+// histogram and the decode select per (sequence, query).  ws must hold
+// decode_mq_ws_bytes(s).
+bool decode_mq_supported(const Shape& s, int32_t nh);
+size_t decode_mq_ws_bytes(const Shape& s);
+hipError_t launch_decode_mq_score_topk(const Shape& s, int32_t nh, const int32_t* heads, int32_t k,
+                                       const void* q, const float* q_scale, const float* w,
+                                       const void* kk, const float* k_scale, int32_t* idx,
+                                       float* scores_out, void* ws, hipStream_t st);
+
 // Fused decode step (T == 1, bf16/fp8): refresh the pooled key of the block
 // holding key L-1, route (E, top-h) and score + top-k; two kernels.  ws must
 // hold decode_ws_bytes(s).

@@ -80,6 +80,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(const float* __
 
 size_t score_ws_bytes(const Shape& s, int32_t nh, int32_t k) {
   if (s.T == 1 && s.dtype != kF32) return decode_ws_bytes(s);
+  if (decode_mq_supported(s, nh)) return decode_mq_ws_bytes(s);
   if (prefill_supported(s)) return prefill_ws_bytes(s, nh, k);
   return align_up(static_cast<size_t>(s.batch) * s.T * s.L * sizeof(float));
 }
@@ -91,6 +92,9 @@ hipError_t launch_score_topk(const Shape& s, int32_t nh, const int32_t* heads, i
   if (s.T == 1 && s.dtype != kF32)
     return launch_decode_score_topk(s, nh, heads, k, q, q_scale, w, kk, k_scale, idx, scores_out,
                                     ws, st);
+  if (decode_mq_supported(s, nh))
+    return launch_decode_mq_score_topk(s, nh, heads, k, q, q_scale, w, kk, k_scale, idx, scores_out,
+                                       ws, st);
   if (prefill_supported(s))
     return launch_prefill_score_topk(s, nh, heads, k, q, q_scale, w, kk, k_scale, idx, scores_out,
                                      ws, st);

@@ -51,6 +51,16 @@ SMALL = {
                                dtype=synth.BF16, needles=2, seed=30),
     "decode_two_blocks": synth.small("decode_two_blocks", batch=9, L=100, T=1, H=64, h=8, B=64, k=32,
                                      kprime=48, dtype=synth.FP8_E4M3, needles=2, seed=31),
+    # Multi-query decode (2 <= T <= 8 queries at the end of each sequence):
+    # head bands of 8, 8, 4 and 16 rows; 1, 4, 1 and 3 row tiles.
+    "mq_bf16_t2": synth.small("mq_bf16_t2", batch=3, L=3000, T=2, H=64, h=8, B=64, k=300, kprime=700,
+                              dtype=synth.BF16, needles=6, seed=32),
+    "mq_fp8_t8": synth.small("mq_fp8_t8", batch=2, L=2500, T=8, H=32, h=8, B=128, k=256, kprime=512,
+                             dtype=synth.FP8_E4M3, needles=6, seed=33),
+    "mq_h4_t4": synth.small("mq_h4_t4", batch=2, L=1500, T=4, H=64, h=4, B=64, k=100, kprime=200,
+                            dtype=synth.BF16, needles=4, seed=34),
+    "mq_h16_t3": synth.small("mq_h16_t3", batch=2, L=2000, T=3, H=64, h=16, B=64, k=128, kprime=256,
+                             dtype=synth.FP8_E4M3, needles=4, seed=35),
     "t_eq_l": synth.small("t_eq_l", batch=1, L=200, T=200, H=64, h=8, B=64, k=64, kprime=96,
                           dtype=synth.BF16, needles=0, seed=24),
     "b1_h16": synth.small("b1_h16", batch=1, L=700, T=9, H=64, h=16, B=1, k=100, kprime=200,
