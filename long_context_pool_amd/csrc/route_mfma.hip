@@ -28,7 +28,40 @@ namespace {
 
 constexpr int kRThreads = 256;
 constexpr int kRWaves = 4;
-constexpr int kLdsRow = kD * 2 + 16;  // bytes per pooled row in LDS (bf16 + pad)
+constexpr int kTileBytes = 32 * kD * 2;  // one bf16 plane of a 32-block pooled tile
+
+// Buffer resource over [base, base + bytes); direct buffer-to-LDS load of
+// lane l's 16 bytes at voff to lds + 16 l (lds wave-uniform); wait until at
+// most N of this wave's vector-memory operations are outstanding, then a
+// workgroup barrier.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rt_rsrc(const void* base, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void rt_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void rt_vmcnt_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate in the low field");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ void rt_vmcnt_zero() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// The wave-uniform value of a pointer, pinned to scalar registers.
+template <class T>
+__device__ __forceinline__ T* rt_uniform(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 
 // Load the A operand: head rows rt*32 + l%32 of query r, head-dim elements
 // [64*(l/32), 64*(l/32)+64) split over 8 k-steps.  Rows >= H are zero.
@@ -73,25 +106,30 @@ __device__ __forceinline__ void load_q_rows(const void* q, int64_t r, int H, bf1
 }
 
 // acc (rows x 32 blocks) = A . B_hi [+ A . B_lo]; rs += ReLU(acc) when
-// col_ok.  B comes from the LDS tile (rows of kLdsRow bytes: this lane's
-// block row, its 64-element half); the hi and lo products share one
-// accumulator per row tile, the RT row tiles giving independent chains.
+// col_ok.  B comes from an LDS tile of unpadded 256-byte rows (this lane's
+// block row, its 64-element half) whose 16-byte chunk c of row r sits at
+// chunk position c ^ (r % 16), so the 32 rows of a read hit distinct banks.
+// The hi and lo products share one accumulator per row tile, the RT row
+// tiles giving independent chains.
 template <int RT, bool SPLIT>
-__device__ __forceinline__ void accumulate_tile(const bf16x8 (&a)[RT][8], const uint8_t* bhi,
-                                                const uint8_t* blo, bool col_ok,
-                                                f32x16 (&rs)[RT]) {
-  const uint4* ph = reinterpret_cast<const uint4*>(bhi);
-  const uint4* pl = reinterpret_cast<const uint4*>(blo);
+__device__ __forceinline__ void accumulate_tile_sw(const bf16x8 (&a)[RT][8], const uint8_t* hb,
+                                                   const uint8_t* lb, bool col_ok, f32x16 (&rs)[RT]) {
+  const int lane = lane_id();
+  const int r = lane & 31;
+  const int hf = lane >> 5;
+  const uint8_t* rowh = hb + r * (kD * 2);
+  const uint8_t* rowl = lb + r * (kD * 2);
   f32x16 acc[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
-    const bf16x8 bh = as_bf16x8(ph[ks]);
+    const int pos = (8 * hf + ks) ^ (r & 15);
+    const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4*>(rowh + 16 * pos));
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_bf16(a[rt][ks], bh, acc[rt]);
     if constexpr (SPLIT) {
-      const bf16x8 bl = as_bf16x8(pl[ks]);
+      const bf16x8 bl = as_bf16x8(*reinterpret_cast<const uint4*>(rowl + 16 * pos));
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_bf16(a[rt][ks], bl, acc[rt]);
     }
@@ -146,7 +184,13 @@ __global__ __launch_bounds__(kRThreads) void route_prefill_kernel(
     const float* __restrict__ k_scale, int32_t* __restrict__ heads, float* __restrict__ E_out,
     int32_t L, int32_t T, int32_t H, int32_t B, int64_t M, int32_t h) {
   constexpr bool SPLIT = DT == kBF16;
-  __shared__ __attribute__((aligned(16))) uint8_t tile[2][SPLIT ? 2 : 1][32 * kLdsRow];
+  constexpr int LB = SPLIT ? kTileBytes : 16;
+  __shared__ __attribute__((aligned(16))) uint8_t h0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t h1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t h2[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t l0[LB];
+  __shared__ __attribute__((aligned(16))) uint8_t l1[LB];
+  __shared__ __attribute__((aligned(16))) uint8_t l2[LB];
   __shared__ float rowsum[kRWaves][64];
   __shared__ float partial[kRWaves][64];
   const int wave = threadIdx.x / kWave;
@@ -170,52 +214,58 @@ __global__ __launch_bounds__(kRThreads) void route_prefill_kernel(
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) rs[rt] = f32x16{};
 
-  // Pooled tiles of 32 blocks go through two LDS buffers: the global loads
-  // of tile bt+1 are in flight while tile bt is multiplied, and one barrier
-  // per tile separates the store of a buffer from its last readers.
+  // Pooled tiles of 32 blocks reach LDS by direct buffer-to-LDS loads into
+  // three buffers: while tile bt is multiplied, tiles bt+1 and bt+2 are in
+  // flight.  Each thread issues NL loads per tile (instruction i of wave w
+  // fills rows 8w + 4i .. +3 of a plane; lane l loads chunk
+  // (l % 16) ^ (row % 16) of its row into chunk position l % 16), so a fixed
+  // vmcnt wait before each barrier proves that a tile has landed.  Rows past
+  // the last complete block load block 0 and are masked in the product;
+  // tiles past the last repeat it, so every iteration issues the same loads.
+  constexpr int NL = SPLIT ? 4 : 2;
   const int64_t ntiles = (full_max + 31) / 32;
-  const int ld_row = threadIdx.x >> 3;  // 32 rows x 8 chunks of 32 bytes
-  const int ld_chunk = threadIdx.x & 7;
-  uint4 st[SPLIT ? 4 : 2];
-  auto fetch = [&](int64_t bt) {
-    const int64_t b = bt * 32 + ld_row;
-    const bool ok = b < full_max;
-    const int64_t off = (seq * M + (ok ? b : 0)) * kD + 16 * ld_chunk;
-    const uint4* sh = reinterpret_cast<const uint4*>(phi + off);
-    st[0] = ok ? sh[0] : make_uint4(0, 0, 0, 0);
-    st[1] = ok ? sh[1] : make_uint4(0, 0, 0, 0);
-    if constexpr (SPLIT) {
-      const uint4* sl = reinterpret_cast<const uint4*>(plo + off);
-      st[2] = ok ? sl[0] : make_uint4(0, 0, 0, 0);
-      st[3] = ok ? sl[1] : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto stash = [&](int buf) {
-    uint4* dst = reinterpret_cast<uint4*>(tile[buf][0] + ld_row * kLdsRow + 32 * ld_chunk);
-    dst[0] = st[0];
-    dst[1] = st[1];
-    if constexpr (SPLIT) {
-      uint4* dl = reinterpret_cast<uint4*>(tile[buf][SPLIT ? 1 : 0] + ld_row * kLdsRow + 32 * ld_chunk);
-      dl[0] = st[2];
-      dl[1] = st[3];
-    }
-  };
-  // Unconditional, so that every path into the loop has drained the A-operand
-  // loads (the stash waits for all of this thread's loads): the prefetch
-  // inside the loop then never waits on anything but itself.
-  fetch(0);
-  stash(0);
-  __syncthreads();
-  const int boff = (lane & 31) * kLdsRow + 128 * (lane >> 5);
-  for (int64_t bt = 0; bt < ntiles; ++bt) {
-    const int buf = static_cast<int>(bt & 1);
-    const bool more = bt + 1 < ntiles;
-    if (more) fetch(bt + 1);
-    const bool ok = bt * 32 + (lane & 31) < full;
-    accumulate_tile<RT, SPLIT>(a, tile[buf][0] + boff, tile[buf][SPLIT ? 1 : 0] + boff, ok, rs);
-    if (more) stash(buf ^ 1);
-    __syncthreads();
+  const int64_t last = ntiles > 0 ? ntiles - 1 : 0;
+  const __amdgpu_buffer_rsrc_t rh = rt_rsrc(rt_uniform(phi + seq * M * kD), static_cast<int32_t>(M * kD * 2));
+  const __amdgpu_buffer_rsrc_t rl = rt_rsrc(rt_uniform(plo + seq * M * kD), static_cast<int32_t>(M * kD * 2));
+  int rowi[2];
+  uint32_t chk[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    rowi[i] = 8 * wave + 4 * i + lane / 16;
+    chk[i] = 16u * static_cast<uint32_t>((lane % 16) ^ (rowi[i] & 15));
   }
+  auto issue = [&](int64_t bt, uint8_t* hb, uint8_t* lb) __attribute__((always_inline)) {
+    const int64_t tb = bt < last ? bt : last;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t blk = tb * 32 + rowi[i];
+      const uint32_t voff = static_cast<uint32_t>((blk < full_max ? blk : 0) * (kD * 2)) + chk[i];
+      rt_load16_lds(rh, hb + 1024 * (2 * wave + i), voff);
+      if constexpr (SPLIT) rt_load16_lds(rl, lb + 1024 * (2 * wave + i), voff);
+    }
+  };
+  // The A-operand loads complete here (the empty asm redefines the
+  // registers, so no later use waits on those loads): the counts below are
+  // the tiles' alone.
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(a[rt][ks]));
+  rt_vmcnt_zero();
+  issue(0, h0, l0);
+  issue(1, h1, l1);
+  auto step = [&](int64_t bt, const uint8_t* hb, const uint8_t* lb, uint8_t* nh, uint8_t* nl)
+      __attribute__((always_inline)) {
+    rt_vmcnt_barrier<NL>();  // tile bt has landed; every wave is done with tile bt-1
+    issue(bt + 2, nh, nl);   // into tile bt-1's buffer
+    accumulate_tile_sw<RT, SPLIT>(a, hb, lb, bt * 32 + (lane & 31) < full, rs);
+  };
+  for (int64_t bt = 0; bt < ntiles; bt += 3) {
+    step(bt, h0, l0, h2, l2);
+    if (bt + 1 < ntiles) step(bt + 1, h1, l1, h0, l0);
+    if (bt + 2 < ntiles) step(bt + 2, h2, l2, h1, l1);
+  }
+  rt_vmcnt_zero();  // the last two tiles' loads (repeats) before the buffers are left
   reduce_rows<RT>(rs, rowsum[wave]);
   const bool has_partial = Mt > full;
   if (has_partial) {
