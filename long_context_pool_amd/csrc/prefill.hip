@@ -675,11 +675,13 @@ __global__ void prefill_clear_kernel(int32_t* fail_count) {
 // Entries beyond the registers' NR * NT are read again from global memory,
 // 8 NT at a time.
 constexpr int kPCandCap = 1024;
-// Candidates held in registers per thread: kSelRegsSmall while the expected
-// count (about kSampleMargin k) fits comfortably, else kSelRegsLarge (more
-// registers, so one workgroup per CU).
+// Workgroup size and candidates held in registers per thread: 1024 threads
+// x kSelRegsSmall while the expected count (about kSampleMargin k) fits
+// comfortably, else 512 threads x kSelRegsLarge (two workgroups per CU, so
+// one's loads overlap the other's selection).
 constexpr int kSelRegsSmall = 8;
-constexpr int kSelRegsLarge = 24;
+constexpr int kSelThreadsLarge = 512;
+constexpr int kSelRegsLarge = 38;
 constexpr int kRelBins = 2048;
 
 struct PSelSmem {
@@ -693,18 +695,17 @@ struct PSelSmem {
   int pre[9];
   int scan_tmp[32];
   int digit, above, count, nge, bad;
-  int wtot[kTopkThreadsSel / kWave];  // per-wave packed counts above / at b*
+  int wtot[kTopkThreadsSel / kWave];  // per-wave packed counts above / at b* (up to 16 waves)
   uint32_t dmin, dmax;                 // candidate digit range (tau_min = -inf)
   float tau_max, tau_min;
 };
 
-template <int NR>
-__global__ __launch_bounds__(kTopkThreadsSel) void prefill_select_kernel(
+template <int NT, int NR>
+__global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
     const uint2* __restrict__ cand, const int32_t* __restrict__ cnt, const float* __restrict__ tau,
     int32_t S, int32_t cap, int32_t k, int32_t* __restrict__ idx, float* __restrict__ scores_out,
     int32_t* __restrict__ fail_count, int32_t* __restrict__ fail_list) {
-  constexpr int NT = kTopkThreadsSel;
-  static_assert(NR >= 1 && NR <= 32, "entry slots are bits of a 32-bit mask");
+  static_assert(NT <= kTopkThreadsSel && NR >= 1 && NR <= 64, "entry slots are bits of a 64-bit mask");
   constexpr int NO = 8;  // entries per thread per round beyond the registers
   __shared__ PSelSmem sm;
   const int64_t r = blockIdx.x;
@@ -893,7 +894,7 @@ __global__ __launch_bounds__(kTopkThreadsSel) void prefill_select_kernel(
   const uint32_t dlo = d0 + (bstar << shift), dhi = d0 + ((bstar + 1) << shift) - 1u;
   const uint32_t blo = digit_lo_key(dlo);
   const uint32_t bhi = (bstar == static_cast<uint32_t>(kRelBins - 1) || dhi >= kTopDigit) ? 0xFFFFFFFFu : digit_hi_key(dhi);
-  auto classify = [&](const uint2* ev, int n, int c0, uint32_t& mh, uint32_t& ma) __attribute__((always_inline)) {
+  auto classify = [&](const uint2* ev, int n, int c0, uint64_t& mh, uint64_t& ma) __attribute__((always_inline)) {
     mh = 0;
     ma = 0;
     const int nu = (total - c0 + NT - 1) / NT;  // slots holding entries (uniform)
@@ -902,15 +903,15 @@ __global__ __launch_bounds__(kTopkThreadsSel) void prefill_select_kernel(
       if (u < nu) {
         const int c = c0 + u * NT + static_cast<int>(threadIdx.x);
         const uint32_t key = float_key(__uint_as_float(ev[u].x));
-        mh |= (c < total && key > bhi) ? (1u << u) : 0u;
-        ma |= (c < total && key >= blo && key <= bhi) ? (1u << u) : 0u;
+        mh |= (c < total && key > bhi) ? (uint64_t{1} << u) : uint64_t{0};
+        ma |= (c < total && key >= blo && key <= bhi) ? (uint64_t{1} << u) : uint64_t{0};
       }
     }
   };
   const int wave = threadIdx.x / kWave;
   int run_h = 0, run_a = 0;  // entries placed by earlier rounds (block totals)
-  auto place = [&](const uint2* ev, int n, int c0, uint32_t mh, uint32_t ma) __attribute__((always_inline)) {
-    int wt = __popc(mh) | (__popc(ma) << 16);
+  auto place = [&](const uint2* ev, int n, int c0, uint64_t mh, uint64_t ma) __attribute__((always_inline)) {
+    int wt = __popcll(mh) | (__popcll(ma) << 16);
 #pragma unroll
     for (int o = kWave / 2; o >= 1; o >>= 1) wt += __shfl_xor(wt, o, kWave);
     if (lane == 0) sm.wtot[wave] = wt;
@@ -952,7 +953,7 @@ __global__ __launch_bounds__(kTopkThreadsSel) void prefill_select_kernel(
     __syncthreads();  // wtot is reused
   };
   {
-    uint32_t mh, ma;
+    uint64_t mh, ma;
     classify(e, NR, 0, mh, ma);
     place(e, NR, 0, mh, ma);
   }
@@ -963,7 +964,7 @@ __global__ __launch_bounds__(kTopkThreadsSel) void prefill_select_kernel(
       const int c = c0 + u * NT + static_cast<int>(threadIdx.x);
       f[u] = c < total ? entry(c) : make_uint2(0u, 0u);
     }
-    uint32_t mh, ma;
+    uint64_t mh, ma;
     classify(f, NO, c0, mh, ma);
     place(f, NO, c0, mh, ma);
   }
@@ -1120,10 +1121,10 @@ hipError_t launch_prefill_score_topk(const Shape& s, int32_t nh, const int32_t* 
   if (e != hipSuccess) return e;
   const int64_t rows = static_cast<int64_t>(s.batch) * s.T;
   if (kSampleMargin * 1.25f * k <= static_cast<float>(kSelRegsSmall * kTopkThreadsSel))
-    prefill_select_kernel<kSelRegsSmall><<<static_cast<unsigned>(rows), kTopkThreadsSel, 0, st>>>(
+    prefill_select_kernel<kTopkThreadsSel, kSelRegsSmall><<<static_cast<unsigned>(rows), kTopkThreadsSel, 0, st>>>(
         args.cand, args.cnt, args.tau, pl.S, pl.cap, k, idx, scores_out, fail_count, fail_list);
   else
-    prefill_select_kernel<kSelRegsLarge><<<static_cast<unsigned>(rows), kTopkThreadsSel, 0, st>>>(
+    prefill_select_kernel<kSelThreadsLarge, kSelRegsLarge><<<static_cast<unsigned>(rows), kSelThreadsLarge, 0, st>>>(
         args.cand, args.cnt, args.tau, pl.S, pl.cap, k, idx, scores_out, fail_count, fail_list);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
