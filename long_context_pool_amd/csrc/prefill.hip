@@ -675,11 +675,12 @@ __global__ void prefill_clear_kernel(int32_t* fail_count) {
 // Entries beyond the registers' NR * NT are read again from global memory,
 // 8 NT at a time.
 constexpr int kPCandCap = 1024;
-// Workgroup size and candidates held in registers per thread: 1024 threads
-// x kSelRegsSmall while the expected count (about kSampleMargin k) fits
-// comfortably, else 512 threads x kSelRegsLarge (two workgroups per CU, so
-// one's loads overlap the other's selection).
-constexpr int kSelRegsSmall = 8;
+// Workgroup size and candidates held in registers per thread: 512 threads x
+// kSelRegsSmall while the expected count (about kSampleMargin k) fits
+// comfortably, else 512 threads x kSelRegsLarge; either way at least two
+// workgroups share a CU, so one's loads overlap another's selection.
+constexpr int kSelThreadsSmall = 512;
+constexpr int kSelRegsSmall = 16;
 constexpr int kSelThreadsLarge = 512;
 constexpr int kSelRegsLarge = 38;
 constexpr int kRelBins = 2048;
@@ -1120,8 +1121,8 @@ hipError_t launch_prefill_score_topk(const Shape& s, int32_t nh, const int32_t* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = static_cast<int64_t>(s.batch) * s.T;
-  if (kSampleMargin * 1.25f * k <= static_cast<float>(kSelRegsSmall * kTopkThreadsSel))
-    prefill_select_kernel<kTopkThreadsSel, kSelRegsSmall><<<static_cast<unsigned>(rows), kTopkThreadsSel, 0, st>>>(
+  if (kSampleMargin * 1.25f * k <= static_cast<float>(kSelRegsSmall * kSelThreadsSmall))
+    prefill_select_kernel<kSelThreadsSmall, kSelRegsSmall><<<static_cast<unsigned>(rows), kSelThreadsSmall, 0, st>>>(
         args.cand, args.cnt, args.tau, pl.S, pl.cap, k, idx, scores_out, fail_count, fail_list);
   else
     prefill_select_kernel<kSelThreadsLarge, kSelRegsLarge><<<static_cast<unsigned>(rows), kSelThreadsLarge, 0, st>>>(
