@@ -326,32 +326,45 @@ __global__ __launch_bounds__(kRRThreads) void rerank_lds_kernel(
 // the stores coalesce) and those at b* go to an LDS list, which is resolved
 // exactly.  Invalid candidates carry score -inf and a distinct negative id
 // (so ties among them resolve), written out as -1.
-constexpr int kLSThreads = 1024;
-constexpr int kLSPer = kMaxKprime / kLSThreads;
+// 1024 threads per query when there are few queries (each workgroup's
+// latency is the time), 512 when there are many (two or more workgroups
+// per CU overlap).
 constexpr int kLSCap = 2048;
+constexpr int kLSBins = 2048;  // relative digit bins
 
+template <int kLSThreads>
 struct LSelSmem {
-  uint32_t hist[kDigits];
+  uint32_t hist[kLSBins];
   alignas(16) float cand_score[kLSCap];
   alignas(16) int32_t cand_idx[kLSCap];
-  ResolveSmem rs;
-  TopkSmem base;
+  union {
+    ResolveSmem rs;
+    TopkSmem base;
+  };
   int scan_tmp[32];
   int wtot[kLSThreads / kWave];
   int digit, above, count;
+  uint32_t dmin, dmax;
 };
 
+template <int kLSThreads>
 __global__ __launch_bounds__(kLSThreads) void list_select_kernel(
     const float* __restrict__ sc, const int32_t* __restrict__ cand, int32_t kprime, int32_t L,
     int32_t T, int32_t k, int32_t* __restrict__ idx, float* __restrict__ scores_out) {
-  __shared__ LSelSmem sm;
+  constexpr int kLSPer = kMaxKprime / kLSThreads;  // list entries per thread (bits of a 32-bit mask)
+  static_assert(kLSPer <= 32, "entry slots are bits of a 32-bit mask");
+  __shared__ LSelSmem<kLSThreads> sm;
   const int64_t r = static_cast<int64_t>(blockIdx.y) * T + blockIdx.x;
   const int64_t pos = static_cast<int64_t>(L) - T + blockIdx.x;
   const float* srow = sc + r * kprime;
   const int32_t* crow = cand + r * kprime;
   int32_t* out = idx + r * k;
   float* out_s = scores_out ? scores_out + r * k : nullptr;
-  for (int b = threadIdx.x; b < kDigits; b += kLSThreads) sm.hist[b] = 0;
+  for (int b = threadIdx.x; b < kLSBins; b += kLSThreads) sm.hist[b] = 0;
+  if (threadIdx.x == 0) {
+    sm.dmin = 0xFFFFFFFFu;
+    sm.dmax = 0u;
+  }
   float v[kLSPer];
   int32_t id[kLSPer];
 #pragma unroll
@@ -364,18 +377,44 @@ __global__ __launch_bounds__(kLSThreads) void list_select_kernel(
     v[j] = ok ? x : -__builtin_inff();
     id[j] = ok ? c : -1 - i;
   }
+  // Relative digit (d - dmin) >> shift over the list's digit range [dmin,
+  // dmax], the shift fitting the range in kLSBins bins.
+  {
+    uint32_t dmin = 0xFFFFFFFFu, dmax = 0u;
+#pragma unroll
+    for (int j = 0; j < kLSPer; ++j)
+      if (j * kLSThreads + static_cast<int>(threadIdx.x) < kprime) {
+        const uint32_t d = key_digit(v[j]);
+        dmin = min(dmin, d);
+        dmax = max(dmax, d);
+      }
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) {
+      dmin = min(dmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(dmin), o, kWave)));
+      dmax = max(dmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(dmax), o, kWave)));
+    }
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+      atomicMin(&sm.dmin, dmin);
+      atomicMax(&sm.dmax, dmax);
+    }
+  }
   __syncthreads();
+  const uint32_t d0 = sm.dmin;
+  const uint32_t span = sm.dmax - d0;
+  const uint32_t shift = span < static_cast<uint32_t>(kLSBins) ? 0u : static_cast<uint32_t>(32 - __clz(static_cast<int>(span)) - 11);
+  static_assert(kLSBins == 2048, "shift fits the span in 11 bits");
 #pragma unroll
   for (int j = 0; j < kLSPer; ++j)
-    if (j * kLSThreads + static_cast<int>(threadIdx.x) < kprime) atomicAdd(&sm.hist[key_digit(v[j])], 1u);
+    if (j * kLSThreads + static_cast<int>(threadIdx.x) < kprime)
+      atomicAdd(&sm.hist[min((key_digit(v[j]) - d0) >> shift, static_cast<uint32_t>(kLSBins - 1))], 1u);
   __syncthreads();
   {
-    constexpr int BPT = kDigits / kLSThreads;
+    constexpr int BPT = kLSBins / kLSThreads;
     int local[BPT];
     int lsum = 0;
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
-      local[u] = static_cast<int>(sm.hist[kDigits - 1 - (threadIdx.x * BPT + u)]);
+      local[u] = static_cast<int>(sm.hist[kLSBins - 1 - (threadIdx.x * BPT + u)]);
       lsum += local[u];
     }
     int tot;
@@ -383,7 +422,7 @@ __global__ __launch_bounds__(kLSThreads) void list_select_kernel(
 #pragma unroll
     for (int u = 0; u < BPT; ++u) {
       if (run < k && run + local[u] >= k) {
-        sm.digit = kDigits - 1 - (threadIdx.x * BPT + u);
+        sm.digit = kLSBins - 1 - (threadIdx.x * BPT + u);
         sm.above = run;
         sm.count = local[u];
       }
@@ -407,7 +446,10 @@ __global__ __launch_bounds__(kLSThreads) void list_select_kernel(
     for (int p = threadIdx.x; p < k; p += kLSThreads)
       if (out[p] < 0) out[p] = -1;
   } else {
-    const uint32_t lo = digit_lo_key(bstar), hi = digit_hi_key(bstar);
+    // Relative bin b* as a key interval [lo, hi].
+    const uint32_t dlo = d0 + (bstar << shift), dhi = d0 + ((bstar + 1) << shift) - 1u;
+    const uint32_t lo = digit_lo_key(dlo);
+    const uint32_t hi = (bstar == static_cast<uint32_t>(kLSBins - 1) || dhi >= kTopDigit) ? 0xFFFFFFFFu : digit_hi_key(dhi);
     uint32_t mh = 0, ma = 0;
 #pragma unroll
     for (int j = 0; j < kLSPer; ++j) {
@@ -522,7 +564,10 @@ hipError_t launch_rerank(const Shape& s, int32_t kprime, int32_t k, const void* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 g2(s.T, s.batch);
-  list_select_kernel<<<g2, kLSThreads, 0, st>>>(sc, cand, kprime, s.L, s.T, k, idx, scores_out);
+  if (rows >= 1024)
+    list_select_kernel<512><<<g2, 512, 0, st>>>(sc, cand, kprime, s.L, s.T, k, idx, scores_out);
+  else
+    list_select_kernel<1024><<<g2, 1024, 0, st>>>(sc, cand, kprime, s.L, s.T, k, idx, scores_out);
   return hipGetLastError();
 }
 
