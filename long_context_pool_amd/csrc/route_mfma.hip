@@ -182,7 +182,8 @@ __global__ __launch_bounds__(kRThreads) void route_prefill_kernel(
     const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint16_t* __restrict__ phi, const uint16_t* __restrict__ plo, const void* __restrict__ k,
     const float* __restrict__ k_scale, int32_t* __restrict__ heads, float* __restrict__ E_out,
-    int32_t L, int32_t T, int32_t H, int32_t B, int64_t M, int32_t h) {
+    int32_t L, int32_t T, int32_t H, int32_t B, int64_t M, int32_t h, int32_t nsplit,
+    float* __restrict__ part) {
   constexpr bool SPLIT = DT == kBF16;
   constexpr int LB = SPLIT ? kTileBytes : 16;
   __shared__ __attribute__((aligned(16))) uint8_t h0[kTileBytes];
@@ -223,8 +224,15 @@ __global__ __launch_bounds__(kRThreads) void route_prefill_kernel(
   // the last complete block load block 0 and are masked in the product;
   // tiles past the last repeat it, so every iteration issues the same loads.
   constexpr int NL = SPLIT ? 4 : 2;
-  const int64_t ntiles = (full_max + 31) / 32;
-  const int64_t last = ntiles > 0 ? ntiles - 1 : 0;
+  // Split z of nsplit takes tiles [tile0, tile1) (nsplit > 1: few query
+  // groups, so the blocks are spread over more workgroups; the partial sums
+  // then go to `part` and a finalize kernel adds them in split order).
+  const int z = blockIdx.z;
+  const int64_t ntiles_all = (full_max + 31) / 32;
+  const int64_t tps = (ntiles_all + nsplit - 1) / nsplit;
+  const int64_t tile0 = min<int64_t>(static_cast<int64_t>(z) * tps, ntiles_all);
+  const int64_t tile1 = min<int64_t>(tile0 + tps, ntiles_all);
+  const int64_t last = tile1 > tile0 ? tile1 - 1 : tile0;
   const __amdgpu_buffer_rsrc_t rh = rt_rsrc(rt_uniform(phi + seq * M * kD), static_cast<int32_t>(M * kD * 2));
   const __amdgpu_buffer_rsrc_t rl = rt_rsrc(rt_uniform(plo + seq * M * kD), static_cast<int32_t>(M * kD * 2));
   int rowi[2];
@@ -252,22 +260,25 @@ __global__ __launch_bounds__(kRThreads) void route_prefill_kernel(
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(a[rt][ks]));
   rt_vmcnt_zero();
-  issue(0, h0, l0);
-  issue(1, h1, l1);
+  const bool any = tile1 > tile0;
+  if (any) {
+    issue(tile0, h0, l0);
+    issue(tile0 + 1, h1, l1);
+  }
   auto step = [&](int64_t bt, const uint8_t* hb, const uint8_t* lb, uint8_t* nh, uint8_t* nl)
       __attribute__((always_inline)) {
     rt_vmcnt_barrier<NL>();  // tile bt has landed; every wave is done with tile bt-1
     issue(bt + 2, nh, nl);   // into tile bt-1's buffer
     accumulate_tile_sw<RT, SPLIT>(a, hb, lb, bt * 32 + (lane & 31) < full, rs);
   };
-  for (int64_t bt = 0; bt < ntiles; bt += 3) {
+  for (int64_t bt = tile0; bt < tile1; bt += 3) {
     step(bt, h0, l0, h2, l2);
-    if (bt + 1 < ntiles) step(bt + 1, h1, l1, h0, l0);
-    if (bt + 2 < ntiles) step(bt + 2, h2, l2, h1, l1);
+    if (bt + 1 < tile1) step(bt + 1, h1, l1, h0, l0);
+    if (bt + 2 < tile1) step(bt + 2, h2, l2, h1, l1);
   }
   rt_vmcnt_zero();  // the last two tiles' loads (repeats) before the buffers are left
   reduce_rows<RT>(rs, rowsum[wave]);
-  const bool has_partial = Mt > full;
+  const bool has_partial = Mt > full && z == nsplit - 1;
   if (has_partial) {
     // Partial block [full*B, pos]: ReLU(q . mean of its keys) = ReLU(mean of
     // q . k_s), so the per-key dots come from the same MFMA tiles (raw keys
@@ -326,19 +337,69 @@ __global__ __launch_bounds__(kRThreads) void route_prefill_kernel(
     }
   }
   __syncthreads();
-  if (active) {
+  if (!active) return;
+  if (nsplit == 1) {
     const float sq = (DT == kFP8) ? q_scale[r] : 1.f;
     finalize_query(&rowsum[wave], 1, has_partial ? partial[wave] : nullptr, H, h, w, sq, r, Mt,
                    heads, E_out);
+  } else {
+    // Slot z: this split's block sums; slot nsplit: the partial block's term.
+    float* pr = part + r * (nsplit + 1) * 64;
+    pr[z * 64 + lane] = rowsum[wave][lane];
+    if (z == nsplit - 1) pr[nsplit * 64 + lane] = has_partial ? partial[wave][lane] : 0.f;
   }
+}
+
+// Split router, second step: query row r's split sums added in split order,
+// plus its partial-block term, then E and the top-h heads.
+__global__ __launch_bounds__(kWave) void route_split_finalize_kernel(
+    const float* __restrict__ part, const float* __restrict__ q_scale, const float* __restrict__ w,
+    int32_t* __restrict__ heads, float* __restrict__ E_out, int32_t L, int32_t T, int32_t H, int32_t B,
+    int32_t h, int32_t nsplit, int32_t fp8) {
+  __shared__ float rowsum[1][64];
+  __shared__ float ptail[64];
+  const int lane = lane_id();
+  const int64_t r = blockIdx.x;
+  const int64_t n = static_cast<int64_t>(L) - T + 1 + r % T;
+  const int64_t full = n / B;
+  const int64_t Mt = (n + B - 1) / B;
+  const float* pr = part + r * (nsplit + 1) * 64;
+  // Every load in flight at once (nsplit <= 64), then the adds in order.
+  float v[65];
+#pragma unroll
+  for (int z = 0; z < 65; ++z) v[z] = z <= nsplit ? pr[z * 64 + lane] : 0.f;
+  float sum = 0.f;
+#pragma unroll
+  for (int z = 0; z < 64; ++z) sum += z < nsplit ? v[z] : 0.f;
+  float tail = 0.f;
+#pragma unroll
+  for (int z = 0; z < 65; ++z) tail = z == nsplit ? v[z] : tail;
+  rowsum[0][lane] = sum;
+  ptail[lane] = tail;
+  __builtin_amdgcn_wave_barrier();
+  const float sq = fp8 ? q_scale[r] : 1.f;
+  finalize_query(rowsum, 1, Mt > full ? ptail : nullptr, H, h, w, sq, r, Mt, heads, E_out);
 }
 
 }  // namespace
 
 bool route_mfma_supported(const Shape& s) { return s.dtype != kF32 && s.H <= 64 && s.T > 1; }
 
+// Block splits per query group: enough workgroups (about 512) to spread the
+// pooled keys over the chip when the queries alone do not.
+int32_t route_splits(const Shape& s) {
+  const int64_t wgs = static_cast<int64_t>((s.T + kRWaves - 1) / kRWaves) * s.batch;
+  if (wgs >= 512) return 1;
+  const int64_t tiles = (s.M() + 31) / 32;
+  int64_t n = (512 + wgs - 1) / wgs;
+  n = n < tiles ? n : tiles;
+  return static_cast<int32_t>(n < 1 ? 1 : (n > 64 ? 64 : n));
+}
+
 size_t route_mfma_ws_bytes(const Shape& s) {
-  return 2 * align_up(static_cast<size_t>(s.batch) * s.M() * kD * sizeof(uint16_t));
+  const int32_t ns = route_splits(s);
+  const size_t part = ns > 1 ? align_up(static_cast<size_t>(s.batch) * s.T * (ns + 1) * 64 * sizeof(float)) : 0;
+  return 2 * align_up(static_cast<size_t>(s.batch) * s.M() * kD * sizeof(uint16_t)) + part;
 }
 
 hipError_t launch_route_mfma(const Shape& s, int32_t h, const void* q, const float* q_scale,
@@ -352,11 +413,19 @@ hipError_t launch_route_mfma(const Shape& s, int32_t h, const void* q, const flo
   pooled_split_kernel<<<static_cast<unsigned>((n4 + 255) / 256), 256, 0, st>>>(
       pooled, reinterpret_cast<uint32_t*>(phi), reinterpret_cast<uint32_t*>(plo), n4);
   const bool two = s.H > 32;
-  dim3 grid((s.T + kRWaves - 1) / kRWaves, s.batch);
-#define RP(DT, RT) route_prefill_kernel<DT, RT><<<grid, kRThreads, 0, st>>>(q, q_scale, w, phi, plo, k, k_scale, heads, E_out, s.L, s.T, s.H, s.B, s.M(), h)
+  const int32_t ns = route_splits(s);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * plane);
+  dim3 grid((s.T + kRWaves - 1) / kRWaves, s.batch, ns);
+#define RP(DT, RT) route_prefill_kernel<DT, RT><<<grid, kRThreads, 0, st>>>(q, q_scale, w, phi, plo, k, k_scale, heads, E_out, s.L, s.T, s.H, s.B, s.M(), h, ns, part)
   if (s.dtype == kBF16) { if (two) RP(kBF16, 2); else RP(kBF16, 1); }
   else { if (two) RP(kFP8, 2); else RP(kFP8, 1); }
 #undef RP
+  if (ns > 1) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    route_split_finalize_kernel<<<static_cast<unsigned>(s.batch) * s.T, kWave, 0, st>>>(
+        part, q_scale, w, heads, E_out, s.L, s.T, s.H, s.B, h, ns, s.dtype == kFP8 ? 1 : 0);
+  }
   return hipGetLastError();
 }
 
