@@ -138,7 +138,7 @@ misa_status misa_rerank(const misa_shape* shape, int32_t kprime, int32_t k, cons
 /* One decode step of MISA (T = 1; bf16 or fp8 only): Eq. (4) for the block
  * holding the newest key, then Eq. (7)-(8) and Eq. (9)-(10) -- the results of
  *   misa_pool_keys_range(shape, M-1, 1, ...); misa_route(...); misa_score_topk(...)
- * in two kernel launches.
+ * in two kernel launches (three when batch < 8).
  *   pooled   [batch, M, d]  fp32, read and written: blocks 0 .. M-2 must hold
  *            their Eq. (4) means (the cache kept by misa_pool_keys); block
  *            M-1 (keys (M-1)*B .. L-1, possibly partial) is recomputed from k
