@@ -145,26 +145,33 @@ class Runner:
 
 
 def time_steps(fn, steps, warmup, stream):
-    """Run warmup then exactly `steps` steps; returns (wall ms per step,
-    mean ms of the bracketed call measured with events on `stream`, host ms
-    per step, {10, 50, 90: percentile of the bracketed call's ms})."""
+    """Run warmup, then exactly `steps` timed steps with nothing else on the
+    stream, then `steps` more with events around the dominant call.  Returns
+    (ms per step of the timed run, mean ms of the bracketed call, host ms per
+    step spent submitting the timed run, {10, 50, 90: percentile of the
+    bracketed call's ms})."""
     import torch
 
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(steps):
-        fn(i, evs[i])
+        fn(i)
     end.record(stream)
+    host_ms = (time.perf_counter() - t0) * 1e3 / steps  # submission only
     torch.cuda.synchronize()
-    host_ms = (time.perf_counter() - t0) * 1e3 / steps
     step_ms = start.elapsed_time(end) / steps
+    # Per-call durations, in a second run: events recorded between calls
+    # would add their own gaps to the timed run.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        fn(i, evs[i])
+    torch.cuda.synchronize()
     calls = sorted(a.elapsed_time(b) for a, b in evs)
     call_ms = sum(calls) / steps
     pct = {q: calls[min(len(calls) - 1, int(q / 100 * len(calls)))] for q in (10, 50, 90)}
@@ -355,7 +362,7 @@ def main():
         "dense_dsa": res_dense,
         "speedup_vs_dense": (res_dense["ms_per_step"] / m_step) if res_dense else None,
         "recall_vs_dense": recall,
-        "host_ms_per_step": m_host,
+        "host_submit_ms_per_step": m_host,
         "source_sha": sha,
         "roofline": roof,
         "cpu_baseline": cpu,

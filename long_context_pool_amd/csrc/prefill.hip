@@ -122,9 +122,10 @@ __device__ __forceinline__ uint2 buffer_load_u32x2(__amdgpu_buffer_rsrc_t r, uin
   const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
   return make_uint2(v.x, v.y);
 }
-__device__ __forceinline__ void buffer_store_u32x2(uint32_t lo, uint32_t hi, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+__device__ __forceinline__ void buffer_store_u32x2(uint32_t lo, uint32_t hi, __amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                   uint32_t soff = 0) {
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, r, off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, r, off, soff, 0);
 }
 // Wait until at most N vector-memory operations of this wave are
 // outstanding, then a workgroup barrier; the signal fences keep the
@@ -495,19 +496,25 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
   const __amdgpu_buffer_rsrc_t rcand =
       buffer_rsrc(uniform_ptr(a.cand + ((seq * a.T + tw0) * a.S + split) * static_cast<int64_t>(a.cap)),
                   __builtin_amdgcn_readfirstlane(QPW * a.S * a.cap * 8));
-  const uint32_t cap_last = static_cast<uint32_t>(a.cap - 1);
   // Candidate counts per (slot, half): scalar; (sl, h) is query
   // slot_query(sl, h).  They go to cnt at the end and may exceed the
   // capacity (the select kernel then queues the query for repair).
   int ctr2[NS][2];
 #pragma unroll
   for (int sl = 0; sl < NS; ++sl) ctr2[sl][0] = ctr2[sl][1] = 0;
+  // All ones in the upper half of the wave, zero in the lower; opaque to the
+  // compiler, so that (x & upper) stays one AND with a scalar operand instead
+  // of becoming a select that needs the scalar copied to a vector register.
+  uint32_t upper = 0u - static_cast<uint32_t>(hf);
+  asm volatile("" : "+v"(upper));
 
   // Epilogue, in parts: part 2*sl sums slot sl's heads (ReLU * w), part
   // 2*sl+1 tests and appends it.  live = false marks a placeholder column
-  // tile that stores nothing but issues the same instructions.
-  auto epi_part = [&](int p, const f32x16 (&acc)[kRT], int key0, bool live, float sk, float (&out)[NS])
-      __attribute__((always_inline)) {
+  // tile that stores nothing but issues the same instructions.  chk = false
+  // (a compile-time constant at every call) drops the per-key limit test, for
+  // column tiles that lie wholly at or below every query's limit.
+  auto epi_part = [&](int p, const f32x16 (&acc)[kRT], int key0, bool live, bool chk, float sk,
+                      float (&out)[NS]) __attribute__((always_inline)) {
     const int sl = p >> 1;
     if ((p & 1) == 0) {
       float sum = 0.f;
@@ -529,23 +536,32 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
     }
     const int key = key0 + colr;
     const float v = out[sl];
-    const uint64_t m = __builtin_amdgcn_ballot_w64(v >= tau_slot[sl]) &
-                       __builtin_amdgcn_ballot_w64(key <= lim_slot[sl]) & (live ? ~0ull : 0ull);
+    uint64_t m = __builtin_amdgcn_ballot_w64(v >= tau_slot[sl]) & (live ? ~0ull : 0ull);
+    if (chk) m &= __builtin_amdgcn_ballot_w64(key <= lim_slot[sl]);
     const uint32_t mlo = static_cast<uint32_t>(m), mhi = static_cast<uint32_t>(m >> 32);
-    // Position in this lane's half: lower half ctr_lo + passing lanes below
-    // it; upper half ctr_hi + passing upper lanes below it, which is the
-    // 64-lane count plus (ctr_hi - popcount(mlo)).
-    const uint32_t base = hf ? static_cast<uint32_t>(ctr2[sl][1]) - __builtin_popcount(mlo)
-                             : static_cast<uint32_t>(ctr2[sl][0]);
-    uint32_t pos = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, base));
-    pos = pos < cap_last ? pos : cap_last;
-    // Out of range (dropped) for lanes that do not pass; no select on the
-    // offset itself, so the step stays one basic block.
-    const uint32_t oob = __builtin_amdgcn_inverse_ballot_w64(m) ? 0u : 0x80000000u;
-    const uint32_t off = (seg_off[sl] + 8u * pos) | oob;
-    buffer_store_u32x2(__float_as_uint(v), static_cast<uint32_t>(key), rcand, off);
-    ctr2[sl][0] += __builtin_popcount(mlo);
-    ctr2[sl][1] += __builtin_popcount(mhi);
+    const int plo = __builtin_popcount(mlo), phi = __builtin_popcount(mhi);
+    // Write bases of the two halves, scalar: the half's count, lowered to
+    // cap - (its passing lanes) when this batch would take the half past the
+    // capacity (its count then ends above the capacity and the query goes to
+    // repair), so that every write stays inside the segment.
+    const int blo = min(ctr2[sl][0], a.cap - plo);
+    const int bhi = min(ctr2[sl][1], a.cap - phi);
+    // Entry position minus blo: lower half, the passing lanes below; upper
+    // half, (bhi - blo) + the passing upper lanes below, which is the 64-lane
+    // count plus (bhi - plo - blo).  blo itself goes in the store's scalar
+    // offset.  The upper half's segment starts at least cap entries after
+    // the lower half's, so the vector offset never goes below zero.
+    const uint32_t dhalf = static_cast<uint32_t>(bhi - plo - blo);
+    const uint32_t rel = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, dhalf & upper));
+    const uint32_t voff = seg_off[sl] + 8u * rel;
+    // Lanes that do not pass store at offset 0xC0800000 (the bits of -4.0,
+    // an inline operand), past the end of any candidate buffer: dropped.
+    uint32_t off;
+    asm("v_cndmask_b32_e64 %0, -4.0, %1, %2" : "=v"(off) : "v"(voff), "s"(m));
+    buffer_store_u32x2(__float_as_uint(v), static_cast<uint32_t>(key), rcand, off,
+                       8u * static_cast<uint32_t>(blo));
+    ctr2[sl][0] += plo;
+    ctr2[sl][1] += phi;
   };
 
   // One step: acc = this wave's rows x column tile c of buffer tb (skv = the
@@ -556,7 +572,8 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
   constexpr int NKS = DT == kBF16 ? 8 : 2;
   constexpr int NP = 2 * NS;
   auto step = [&](const uint8_t* tb, const float (*sk)[kTileKeys], int c, f32x16 (&acc)[kRT], float& skv,
-                  const f32x16 (&pacc)[kRT], int pkey0, bool plive, float pskv) __attribute__((always_inline)) {
+                  const f32x16 (&pacc)[kRT], int pkey0, bool plive, bool pchk, float pskv)
+      __attribute__((always_inline)) {
     const uint8_t* brow = tb + (32 * c + colr) * RB;
     float out[NS];
     if constexpr (DT == kBF16) {
@@ -570,7 +587,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
         for (int rt = 0; rt < kRT; ++rt)
           acc[rt] = mfma32_bf16(a16[rt][ks], as_bf16x8(bv[ks % 3]), ks == 0 ? f32x16{} : acc[rt]);
 #pragma unroll
-        for (int p = ks * NP / NKS; p < (ks + 1) * NP / NKS; ++p) epi_part(p, pacc, pkey0, plive, pskv, out);
+        for (int p = ks * NP / NKS; p < (ks + 1) * NP / NKS; ++p) epi_part(p, pacc, pkey0, plive, pchk, pskv, out);
         __builtin_amdgcn_sched_barrier(0);
       }
       skv = 1.f;
@@ -591,17 +608,18 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
           constexpr int PPM = NP / (NKS * kRT) > 0 ? NP / (NKS * kRT) : 1;  // parts per MFMA
           const int m = ks * kRT + rt;
 #pragma unroll
-          for (int p = m * PPM; p < (m + 1) * PPM && p < NP; ++p) epi_part(p, pacc, pkey0, plive, pskv, out);
+          for (int p = m * PPM; p < (m + 1) * PPM && p < NP; ++p)
+            epi_part(p, pacc, pkey0, plive, pchk, pskv, out);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
   };
   // Epilogue only (the last column tile).
-  auto epi_all = [&](const f32x16 (&pacc)[kRT], int pkey0, float pskv) __attribute__((always_inline)) {
+  auto epi_all = [&](const f32x16 (&pacc)[kRT], int pkey0, bool pchk, float pskv) __attribute__((always_inline)) {
     float out[NS];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) epi_part(p, pacc, pkey0, true, pskv, out);
+    for (int p = 0; p < NP; ++p) epi_part(p, pacc, pkey0, true, pchk, pskv, out);
   };
 
   const int64_t ntiles = len > 0 ? (len + kTileKeys - 1) / kTileKeys : 0;
@@ -617,26 +635,41 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
     for (int rt = 0; rt < kRT; ++rt) acc_b[rt] = f32x16{};
     float sk_a = 1.f, sk_b = 1.f;
     // Column tile 0 beside a placeholder epilogue.
-    step(tb0, sk0, 0, acc_a, sk_a, acc_b, 0, false, 1.f);
-    // Tile ti sits in buffer ti % 3: the loop is unrolled by three so that
-    // every buffer reference is static.
+    step(tb0, sk0, 0, acc_a, sk_a, acc_b, 0, false, false, 1.f);
+    // Tile ti sits in buffer ti % 3: the loops are unrolled by three so that
+    // every buffer reference is static.  chk: the epilogues of tile ti test
+    // each key against the query limits.
     auto tile_iter = [&](int64_t ti, uint8_t* tcur, float (*scur)[kTileKeys], uint8_t* tnext,
-                         float (*snext)[kTileKeys], uint8_t* tfill, float (*sfill)[kTileKeys])
+                         float (*snext)[kTileKeys], uint8_t* tfill, float (*sfill)[kTileKeys], bool chk)
         __attribute__((always_inline)) {
       const int key0 = static_cast<int>(s_begin + ti * kTileKeys);
       issue(ti + 2, tfill, sfill);
       compiler_fence();
-      step(tcur, scur, 1, acc_b, sk_b, acc_a, key0, true, sk_a);
+      step(tcur, scur, 1, acc_b, sk_b, acc_a, key0, true, chk, sk_a);
       vmcnt_barrier<kWaitCnt>();
-      if (ti + 1 < ntiles) step(tnext, snext, 0, acc_a, sk_a, acc_b, key0 + 32, true, sk_b);
-      else epi_all(acc_b, key0 + 32, sk_b);
+      if (ti + 1 < ntiles) step(tnext, snext, 0, acc_a, sk_a, acc_b, key0 + 32, true, chk, sk_b);
+      else epi_all(acc_b, key0 + 32, chk, sk_b);
     };
-    for (int64_t ti = 0; ti < ntiles; ti += 3) {
-      tile_iter(ti, tb0, sk0, tb1, sk1, tb2, sk2);
+    // The first nfull tiles lie wholly at or below the limit of every query
+    // of the workgroup (the split end and the causal bound of its first
+    // query), so their epilogues skip the limit test.  Workgroups with
+    // padding queries (never passing, limit -1) or with half-wave owners
+    // (32 or more heads per query) test every tile.
+    const int64_t lim_min = min<int64_t>(s_end - 1, static_cast<int64_t>(a.L) - a.T + t0);
+    const int64_t nlim = (HPQ < 32 && t0 + QWG <= a.T) ? (lim_min - s_begin + 1) / kTileKeys : 0;
+    const int64_t nfull = nlim < 0 ? 0 : (nlim < ntiles ? nlim : ntiles);
+    int64_t ti = 0;
+    for (; ti + 3 <= nfull; ti += 3) {
+      tile_iter(ti, tb0, sk0, tb1, sk1, tb2, sk2, false);
+      tile_iter(ti + 1, tb1, sk1, tb2, sk2, tb0, sk0, false);
+      tile_iter(ti + 2, tb2, sk2, tb0, sk0, tb1, sk1, false);
+    }
+    for (; ti < ntiles; ti += 3) {
+      tile_iter(ti, tb0, sk0, tb1, sk1, tb2, sk2, true);
       if (ti + 1 >= ntiles) break;
-      tile_iter(ti + 1, tb1, sk1, tb2, sk2, tb0, sk0);
+      tile_iter(ti + 1, tb1, sk1, tb2, sk2, tb0, sk0, true);
       if (ti + 2 >= ntiles) break;
-      tile_iter(ti + 2, tb2, sk2, tb0, sk0, tb1, sk1);
+      tile_iter(ti + 2, tb2, sk2, tb0, sk0, tb1, sk1, true);
     }
   }
   // No load may still be writing LDS when the wave ends.

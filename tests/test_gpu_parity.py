@@ -187,6 +187,37 @@ def test_exact_integer_inputs_bit_exact(dtype):
     parity.pmap(one, _all_queries(p))
 
 
+@pytest.mark.parametrize("dtype", [synth.BF16, synth.FP8_E4M3])
+def test_prefill_candidate_overflow_goes_to_repair(dtype):
+    """Every key of a sequence the same row: all scores of a query tie, every
+    key clears its split's threshold, and each (query, split) candidate
+    segment overflows (four splits of 2048 keys against 640 or 768 slots).
+    The writes past the capacity must stay inside their segment, and the
+    repaired selections must be the oracle's: the lowest token indices."""
+    import oracle
+
+    p = synth.small("overflow", batch=2, L=8192, T=40, H=64, h=8, B=64, k=32, kprime=64,
+                    dtype=dtype, needles=0, seed=50)
+    x = synth.generate(p)
+    x.k[:] = x.k[:, :1].clone()
+    if dtype == synth.FP8_E4M3:
+        x.k_scale[:] = x.k_scale[:, :1].clone()
+    _log(f"[gpu] candidate overflow {p}")
+    gpu = parity.run_gpu(x, stages=("pool", "route", "score", "dagger"))
+    op = parity.OracleProblem(x)
+
+    def one(bt):
+        b, t = bt
+        seq, pos = op.seq(b), op.pos(t)
+        I = seq.scores(pos, op.q[b, t], op.w[b, t], gpu["heads"][b, t])
+        for key, kk in (("idx", p.k), ("cand", p.kprime)):
+            ref = oracle.topk(I, kk)
+            assert set(gpu[key][b, t].tolist()) == set(ref.tolist()), f"{key}[{b},{t}]"
+            assert set(ref.tolist()) == set(range(kk)), "all scores tie"
+
+    parity.pmap(one, _all_queries(p))
+
+
 def test_h_equals_H_matches_dense_on_gpu():
     p = synth.small("hH", batch=1, L=1000, T=20, H=16, h=16, B=64, k=100, kprime=None,
                     dtype=synth.BF16, needles=4, seed=32)
