@@ -441,18 +441,20 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
   // Key tiles (64 keys) reach LDS by direct buffer-to-LDS loads (no VGPR
   // staging, no LDS store instructions) into three buffers: tile ti+2 is in
   // flight while tile ti is multiplied.  Every thread issues the same number
-  // of vector-memory operations per tile (NL loads, NSTEP candidate stores
-  // per column tile), so a fixed vmcnt wait before each barrier proves that
-  // the next tile has landed.  The column tiles are software-pipelined: the
-  // MFMAs of column tile j run while the epilogue (ReLU * w head sum,
-  // threshold test, candidate append) of column tile j-1 executes, with no
-  // branch in either, so the two interleave.
+  // of vector-memory operations per tile (NL loads, NS candidate stores per
+  // column tile), so a fixed vmcnt wait before each barrier proves that the
+  // next tile has landed.  The column tiles are software-pipelined: the
+  // MFMAs of column tile j are issued among the epilogue (ReLU * w head sum,
+  // threshold test, candidate append) of column tile j-1, with no branch in
+  // either.
   //
   // Candidate append: per slot, the wave ballot of passing lanes gives each
-  // lane its position in its half's (query's) segment; the entry is written
-  // by a buffer store whose offset is pushed out of range for lanes that do
-  // not pass, and positions past the capacity are clamped onto the last
-  // slot (the count still grows, which sends the query to repair).
+  // lane its position in its half's (query's) segment, so the entries of a
+  // slot land next to each other; the entry is written by a buffer store
+  // whose offset is pushed out of range for lanes that do not pass.  A batch
+  // that would take a segment past its capacity is written at its end
+  // instead (overwriting entries; the count still grows, which sends the
+  // query to repair).
   constexpr int ROWB = kD * (DT == kBF16 ? 2 : 1);  // key row bytes in HBM
   constexpr int NL = NDMA + (DT == kFP8 ? 1 : 0);
   // This thread's byte offset inside a tile's key rows for each of its DMA
