@@ -39,10 +39,14 @@ CSRC = os.path.join(ROOT, "long_context_pool_amd", "csrc")
 
 
 def source_sha() -> str:
+    """Hash of the kernel sources and of the build script (its flags shape
+    the kernels too)."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+    files = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC))]
+    files.append(os.path.join(os.path.dirname(CSRC), "build.py"))
+    for path in files:
+        with open(path, "rb") as fh:
+            h.update(os.path.basename(path).encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 

@@ -23,9 +23,14 @@ LIB = os.path.join(PKG, "libmisa.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops off: hipcc must not form packed fp32 ops from float code.
+# -amdgpu-mfma-vgpr-form: MFMA accumulators in ordinary vector registers.
+# Otherwise the compiler may place them in the accumulation registers, and
+# every epilogue read of an accumulator (ReLU, head sums) costs an extra
+# v_accvgpr_read.
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     "-I", INCLUDE, "-I", CSRC,
 ]
