@@ -274,18 +274,27 @@ __global__ __launch_bounds__(kRRThreads) void rerank_lds_kernel(
   float* orow = out + r * kprime;
   const int c_wg = blockIdx.x * per_wg;
   const int c_end = min(c_wg + per_wg, kprime);
-  for (int c_round = c_wg + wave * NTW * 32; c_round < c_end; c_round += kRRWaves * NTW * 32) {
-    int32_t sid[NTW];
-    float skv[NTW];
-    // This lane's candidate of each tile (lanes l and l+32 share one), then
-    // the tiles' rows into this wave's LDS slots.
+  constexpr int kRoundStep = kRRWaves * NTW * 32;
+  // This lane's candidate of each tile of a round (lanes l and l+32 share
+  // one).  The next round's are loaded while this round's rows are gathered.
+  int32_t svn[NTW];
+  auto load_ids = [&](int c_round) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NTW; ++u) {
       const int c = c_round + 32 * u + col;
-      const int32_t sv = c < c_end ? crow[c] : -1;
-      sid[u] = (sv >= 0 && sv <= pos) ? sv : -1;
-      skv[u] = (DT == kFP8 && sid[u] >= 0) ? k_scale[seq * L + sid[u]] : 1.f;
+      svn[u] = c < c_end ? crow[c] : -1;
     }
+  };
+  if (c_wg + wave * NTW * 32 < c_end) load_ids(c_wg + wave * NTW * 32);
+  for (int c_round = c_wg + wave * NTW * 32; c_round < c_end; c_round += kRoundStep) {
+    int32_t sid[NTW];
+    float skv[NTW];
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) sid[u] = (svn[u] >= 0 && svn[u] <= pos) ? svn[u] : -1;
+    if (c_round + kRoundStep < c_end) load_ids(c_round + kRoundStep);
+    // The tiles' key scales, and their rows into this wave's LDS slots.
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) skv[u] = (DT == kFP8 && sid[u] >= 0) ? k_scale[seq * L + sid[u]] : 1.f;
 #pragma unroll
     for (int u = 0; u < NTW; ++u) {
 #pragma unroll
