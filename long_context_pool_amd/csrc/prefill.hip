@@ -710,12 +710,14 @@ __global__ void prefill_clear_kernel(int32_t* fail_count) {
 // Entries beyond the registers' NR * NT are read again from global memory,
 // 8 NT at a time.
 constexpr int kPCandCap = 1024;
-// Workgroup size and candidates held in registers per thread: 512 threads x
+// Workgroup size and candidates held in registers per thread: 256 threads x
 // kSelRegsSmall while the expected count (about kSampleMargin k) fits
-// comfortably, else 512 threads x kSelRegsLarge; either way at least two
-// workgroups share a CU, so one's loads overlap another's selection.
-constexpr int kSelThreadsSmall = 512;
-constexpr int kSelRegsSmall = 16;
+// comfortably (120 registers: four workgroups per CU), else 512 threads x
+// kSelRegsLarge (two per CU).  Queries are independent, so more workgroups
+// per CU overlap more of each one's load and barrier latency: 256 x 32 took
+// the C3 select from 133 to 111 us against 512 x 16 (three per CU).
+constexpr int kSelThreadsSmall = 256;
+constexpr int kSelRegsSmall = 32;
 constexpr int kSelThreadsLarge = 512;
 constexpr int kSelRegsLarge = 38;
 constexpr int kRelBins = 2048;
