@@ -328,16 +328,18 @@ __global__ __launch_bounds__(kRRThreads) void rerank_lds_kernel(
   }
 }
 
-// Top-k of one query's k' (score, candidate) list, in one 1024-thread
-// workgroup: the list is read once into registers, a digit histogram (LDS)
-// gives the threshold digit b*; each wave's entries above b* take one run of
-// the output after those of the lower waves (slot by slot, wave ballots, so
+// Top-k of one query's k' (score, candidate) list, in one workgroup: the
+// list is read once into registers, a digit histogram (LDS) gives the
+// threshold digit b*; each wave's entries above b* take one run of the
+// output after those of the lower waves (slot by slot, wave ballots, so
 // the stores coalesce) and those at b* go to an LDS list, which is resolved
 // exactly.  Invalid candidates carry score -inf and a distinct negative id
 // (so ties among them resolve), written out as -1.
 // 1024 threads per query when there are few queries (each workgroup's
-// latency is the time), 512 when there are many (two or more workgroups
-// per CU overlap).
+// latency is the time), 256 when there are many: 32 entries per thread in at
+// most 128 registers, so four workgroups share a CU and overlap one
+// another's load and barrier latency (C5: 277 -> 242 us against 512
+// threads, three per CU).
 constexpr int kLSCap = 2048;
 constexpr int kLSBins = 2048;  // relative digit bins
 
@@ -357,7 +359,7 @@ struct LSelSmem {
 };
 
 template <int kLSThreads>
-__global__ __launch_bounds__(kLSThreads) void list_select_kernel(
+__global__ __launch_bounds__(kLSThreads, kLSThreads == 256 ? 4 : 1) void list_select_kernel(
     const float* __restrict__ sc, const int32_t* __restrict__ cand, int32_t kprime, int32_t L,
     int32_t T, int32_t k, int32_t* __restrict__ idx, float* __restrict__ scores_out) {
   constexpr int kLSPer = kMaxKprime / kLSThreads;  // list entries per thread (bits of a 32-bit mask)
@@ -574,7 +576,7 @@ hipError_t launch_rerank(const Shape& s, int32_t kprime, int32_t k, const void* 
   if (e != hipSuccess) return e;
   dim3 g2(s.T, s.batch);
   if (rows >= 1024)
-    list_select_kernel<512><<<g2, 512, 0, st>>>(sc, cand, kprime, s.L, s.T, k, idx, scores_out);
+    list_select_kernel<256><<<g2, 256, 0, st>>>(sc, cand, kprime, s.L, s.T, k, idx, scores_out);
   else
     list_select_kernel<1024><<<g2, 1024, 0, st>>>(sc, cand, kprime, s.L, s.T, k, idx, scores_out);
   return hipGetLastError();
