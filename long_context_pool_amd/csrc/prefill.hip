@@ -17,7 +17,8 @@
 //    and one of S key splits; blocks are numbered so that all workgroups of
 //    one split land on the same XCD and share its L2;
 //  * it first scores a strided 512-key sample of its split and sets, per
-//    query, a threshold tau at the sample's (2.5 k/n)-quantile;
+//    query, a threshold tau at the sample's (m k/n)-quantile, margin m =
+//    2.5, or 2 when that still puts the quantile at sample rank >= 64;
 //  * the full pass appends every score >= tau of a key inside the query's
 //    prefix to the (query, split) candidate segment (wave ballots give the
 //    positions, so each store writes consecutive entries; each segment has a
@@ -43,6 +44,13 @@ constexpr int kRT = 2;             // 32-row tiles per wave
 constexpr int kTileKeys = 64;      // keys per LDS tile (two 32-key column tiles)
 constexpr int kSamples = 512;      // sample keys per (workgroup, split)
 constexpr float kSampleMargin = 2.5f;
+// A lower margin where the threshold's sample rank j = margin k kSamples / n
+// is at least kMinSampleRank for every query (large k against L, as for a
+// re-rank candidate pass): the quantile's spread ~1/sqrt(j) is then small
+// enough that k certified candidates remain likely, and fewer candidates
+// mean fewer appends and a smaller select.
+constexpr float kLowMargin = 2.0f;
+constexpr double kMinSampleRank = 64.0;
 constexpr int kRepairSlots = 64;   // repair workgroups (one scratch row each)
 constexpr int kRepThreads = 512;
 constexpr int kTopkThreadsSel = 1024;
@@ -102,6 +110,7 @@ struct PrefillArgs {
   uint2* cand;           // [rows, S, cap] (score bits, token)
   int32_t* cnt;          // [rows, S]
   float* tau;            // [rows*S]
+  float margin;          // threshold sample rank = margin * k * samples / n_q
 };
 
 // Buffer resource over [base, base + bytes): loads past the end read zero,
@@ -400,7 +409,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
     const int t = tw0 + g;
     const int64_t nq = static_cast<int64_t>(a.L) - a.T + t + 1;
     // j = ceil(margin * k * nvs / n_q)
-    const double jd = static_cast<double>(kSampleMargin) * a.k_top * nvs / static_cast<double>(nq > 0 ? nq : 1);
+    const double jd = static_cast<double>(a.margin) * a.k_top * nvs / static_cast<double>(nq > 0 ? nq : 1);
     const int j = static_cast<int>(jd) + 1;
     // Padding queries (t >= T) never pass; a query whose split holds fewer
     // sampled keys than j keeps every key of the split (tau = -inf).
@@ -1068,6 +1077,7 @@ __global__ __launch_bounds__(kRepThreads) void prefill_repair_kernel(
 
 struct PrefillPlan {
   int32_t S, cap, nqt, qwg;
+  float margin;
   int64_t chunk;
   size_t off_cnt, off_tau, off_fail, off_list, off_scratch, total;
 };
@@ -1093,7 +1103,8 @@ PrefillPlan plan_prefill(const Shape& s, int32_t nh, int32_t k) {
   // queries: 2.5x + 16 sigma + 512 leaves overflow (then repair) very rare.
   const double nmin = static_cast<double>(s.L - s.T + 1);
   const double share = static_cast<double>(p.chunk) / nmin < 1.0 ? static_cast<double>(p.chunk) / nmin : 1.0;
-  const double mean = kSampleMargin * k * share;
+  p.margin = kLowMargin * static_cast<double>(k) * kSamples >= kMinSampleRank * s.L ? kLowMargin : kSampleMargin;
+  const double mean = p.margin * k * share;
   int64_t cap = static_cast<int64_t>(2.5 * mean + 16.0 * __builtin_sqrt(mean) + 512.0);
   cap = cap < p.chunk ? cap : p.chunk;
   cap = (cap + 63) / 64 * 64;
@@ -1142,7 +1153,7 @@ hipError_t launch_prefill_score_topk(const Shape& s, int32_t nh, const int32_t* 
   PrefillArgs args{q, q_scale, w, kk, k_scale, heads, nh, s.L, s.T, s.H, k, pl.S, pl.chunk,
                    pl.cap, pl.nqt, s.batch, reinterpret_cast<uint2*>(base),
                    reinterpret_cast<int32_t*>(base + pl.off_cnt),
-                   reinterpret_cast<float*>(base + pl.off_tau)};
+                   reinterpret_cast<float*>(base + pl.off_tau), pl.margin};
   int32_t* fail_count = reinterpret_cast<int32_t*>(base + pl.off_fail);
   int32_t* fail_list = reinterpret_cast<int32_t*>(base + pl.off_list);
   float* scratch = reinterpret_cast<float*>(base + pl.off_scratch);
@@ -1158,7 +1169,7 @@ hipError_t launch_prefill_score_topk(const Shape& s, int32_t nh, const int32_t* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = static_cast<int64_t>(s.batch) * s.T;
-  if (kSampleMargin * 1.25f * k <= static_cast<float>(kSelRegsSmall * kSelThreadsSmall))
+  if (pl.margin * 1.25f * k <= static_cast<float>(kSelRegsSmall * kSelThreadsSmall))
     prefill_select_kernel<kSelThreadsSmall, kSelRegsSmall><<<static_cast<unsigned>(rows), kSelThreadsSmall, 0, st>>>(
         args.cand, args.cnt, args.tau, pl.S, pl.cap, k, idx, scores_out, fail_count, fail_list);
   else
