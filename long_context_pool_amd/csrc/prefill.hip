@@ -720,7 +720,7 @@ __global__ void prefill_clear_kernel(int32_t* fail_count) {
 // 8 NT at a time.
 constexpr int kPCandCap = 1024;
 // Workgroup size and candidates held in registers per thread: 256 threads x
-// kSelRegsSmall while the expected count (about kSampleMargin k) fits
+// kSelRegsSmall while the expected count (about margin k) fits
 // comfortably (120 registers: four workgroups per CU), else 512 threads x
 // kSelRegsLarge (two per CU).  Queries are independent, so more workgroups
 // per CU overlap more of each one's load and barrier latency: 256 x 32 took
