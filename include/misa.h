@@ -29,6 +29,8 @@
  *    returns its status and launches nothing.  A launch failure returns
  *    MISA_ERR_HIP.  The library keeps no mutable global state: calls on
  *    different streams are independent when their workspaces are distinct.
+ *    The only state carried between calls lives in the caller's `ws` (see
+ *    misa_decode_step); no result ever depends on it.
  *  - Limits of this build: d = 128; 1 <= H <= 64; 1 <= h <= min(H, 16);
  *    1 <= k <= k' <= 8192; B >= 1; 1 <= T <= L < 2^31; batch*T*max(L,k')
  *    < 2^40.  Violations return MISA_ERR_UNSUPPORTED (a limit of this build)
@@ -147,7 +149,19 @@ misa_status misa_rerank(const misa_shape* shape, int32_t kprime, int32_t k, cons
  *   E_out    [batch, H]     fp32, written if non-NULL
  *   idx, scores_out [batch, k] as misa_score_topk.
  * Other arguments and layouts as misa_route and misa_score_topk.  T != 1 or
- * fp32 inputs return MISA_ERR_UNSUPPORTED. */
+ * fp32 inputs return MISA_ERR_UNSUPPORTED.
+ *
+ * State in `ws` (batch >= 8, the single-kernel form): the G workgroups of a
+ * sequence share their router partial sums through `ws`, using one 64-bit
+ * arrival word per sequence that this call's select kernel re-arms for the
+ * NEXT call on the same `ws`.  A call whose `ws` is fresh (first call), was
+ * used in between by another entry point, or was sized for another shape
+ * finds no armed word: every workgroup then computes all router partials
+ * itself (same additions in the same order, so the same result bits) and
+ * the call is slower (about the router cost times G).  An armed word whose
+ * peers are late makes a workgroup poll it up to 65536 times (with short
+ * sleeps) before it takes the same local path, so one call never waits on
+ * another.  Two calls that overlap on one `ws` race and are not allowed. */
 misa_status misa_decode_step(const misa_shape* shape, int32_t h, int32_t k, const void* q,
                              const float* q_scale, const float* w, float* pooled, const void* kk,
                              const float* k_scale, int32_t* heads, float* E_out, int32_t* idx,

@@ -79,8 +79,14 @@ size_t misa_workspace_bytes(const misa_shape* shape, int32_t h, int32_t k, int32
   if (check_shape(shape, s) != MISA_OK) return 0;
   const int32_t kp = std::max(k, kprime);
   size_t need = misa::route_ws_bytes(s);
-  need = std::max(need, misa::score_ws_bytes(s, std::max<int32_t>(h, 1), kp));
-  need = std::max(need, misa::score_ws_bytes(s, s.H, kp));
+  // Score workspace for both selection sizes: the prefill candidate
+  // capacity is not monotone in k (a larger k can take a lower sampling
+  // margin), so the smaller k may need more than the larger.
+  for (const int32_t kk : {k, kp}) {
+    if (kk < 1) continue;
+    need = std::max(need, misa::score_ws_bytes(s, std::max<int32_t>(h, 1), kk));
+    need = std::max(need, misa::score_ws_bytes(s, s.H, kk));
+  }
   need = std::max(need, misa::rerank_ws_bytes(s, kp));
   if (s.T == 1 && s.dtype != MISA_F32) need = std::max(need, misa::decode_ws_bytes(s));
   return need;

@@ -47,8 +47,9 @@ __device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(
 // ---------------------------------------------------------------- ordering keys
 
 // Order-preserving map fp32 -> u32 (larger float <=> larger key); -0 maps like +0.
-__device__ __forceinline__ uint32_t float_key(float f) {
-  uint32_t u = __float_as_uint(f);
+// Host-callable too (the top-k key intervals are checked exhaustively on the CPU).
+__host__ __device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
   if (u == 0x80000000u) u = 0;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }

@@ -803,12 +803,12 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
     }
     return buffer_load_u32x2(crs, static_cast<uint32_t>(sg * cap + (c - b)) * 8u);
   };
-  // Fewer than k candidates is fine only when nothing was filtered out.
-  if (sm.bad || (total < k && tm != -__builtin_inff())) {
+  const CandVerdict verdict = cand_verdict(sm.bad != 0, total, k, tm);
+  if (verdict == CandVerdict::kRepair) {
     if (threadIdx.x == 0) fail_list[atomicAdd(fail_count, 1)] = static_cast<int32_t>(r);
     return;
   }
-  if (total <= k) {
+  if (verdict == CandVerdict::kTakeAll) {
     // Every key of the prefix is a candidate: take them all, pad with -1.
     for (int c = threadIdx.x; c < total; c += NT) {
       const uint2 e = entry(c);

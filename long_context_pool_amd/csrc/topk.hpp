@@ -154,7 +154,7 @@ constexpr int kDigits = 8192;  // histogram bins of key_digit
 // bins 6% wide.
 constexpr int kExpLo = 127 - 31;  // window: values in [2^-31, 2^32)
 constexpr int kExpBins = 63;
-__device__ __forceinline__ uint32_t key_digit(float v) {
+__host__ __device__ __forceinline__ uint32_t key_digit(float v) {
   const uint32_t key = float_key(v);  // -0 has the key of +0
   if (key < 0x80000000u) return 0u;
   const uint32_t u = key & 0x7FFFFFFFu;
@@ -169,7 +169,7 @@ constexpr uint32_t kTopDigit = 2u + ((kExpBins - 1) << 7) + 127u;
 
 // The smallest order-preserving key (float_key) whose score has digit d, for
 // 0 <= d <= kTopDigit: key_digit(v) >= d  <=>  float_key(v) >= digit_lo_key(d).
-__device__ __forceinline__ uint32_t digit_lo_key(uint32_t d) {
+__host__ __device__ __forceinline__ uint32_t digit_lo_key(uint32_t d) {
   if (d == 0) return 0u;
   if (d == 1) return 0x80000000u;  // +0
   if (d == 2) return 0x80800000u;  // smallest positive normal
@@ -177,8 +177,33 @@ __device__ __forceinline__ uint32_t digit_lo_key(uint32_t d) {
   return 0x80000000u | ((kExpLo + (b >> 7)) << 23) | ((b & 127u) << 16);
 }
 // The largest key with digit d.
-__device__ __forceinline__ uint32_t digit_hi_key(uint32_t d) {
+__host__ __device__ __forceinline__ uint32_t digit_hi_key(uint32_t d) {
   return d >= kTopDigit ? 0xFFFFFFFFu : digit_lo_key(d + 1) - 1u;
+}
+
+// ---------------------------------------------------------------- candidate certificate
+//
+// A threshold-filtered candidate list (every key of split s scoring >= tau_s
+// was kept; no segment overflowed unless `overflow`) holds the true top-k
+// when at least k candidates score >= tau_max = max_s tau_s: any filtered key
+// scores below its own tau_s <= tau_max, so it cannot beat those k.  What a
+// select does with a list before it has counted the candidates >= tau_max:
+//   kRepair  - cannot be certified (an overflow, or fewer than k candidates
+//              while some key was filtered out);
+//   kTakeAll - nothing was filtered (tau_max = -inf) and at most k
+//              candidates: the list is the whole prefix, take every entry;
+//   kCount   - count the candidates >= tau_max; select if there are >= k,
+//              else repair.  This includes a list of exactly k candidates
+//              with a finite tau_max: a candidate of a low-tau split may lie
+//              below a filtered key of the tau_max split.
+enum class CandVerdict : int { kRepair = 0, kTakeAll = 1, kCount = 2 };
+
+__host__ __device__ __forceinline__ CandVerdict cand_verdict(bool overflow, int total, int k,
+                                                             float tau_max) {
+  const bool filtered = !(tau_max == -__builtin_inff());
+  if (overflow || (total < k && filtered)) return CandVerdict::kRepair;
+  if (total <= k && !filtered) return CandVerdict::kTakeAll;
+  return CandVerdict::kCount;
 }
 
 // ---------------------------------------------------------------- list resolve

@@ -129,3 +129,18 @@ def test_decode_step_argument_checks(case, expect):
     st = lib.misa_decode_step(ctypes.byref(shp), h, k, FAKE, qs, FAKE, pooled, FAKE, None, FAKE,
                               None, FAKE, None, FAKE, ws_bytes, None)
     assert st == expect
+
+
+@pytest.mark.parametrize("dtype", [1, 2])
+def test_workspace_covers_both_selection_sizes(dtype):
+    """misa_workspace_bytes(h, k, k') must cover misa_score_topk with k as
+    well as with k'.  The prefill candidate capacity is not monotone in k: a
+    k' large against L takes the lower sampling margin, so a k just below
+    that point can need more than k'.  Shape of a 128K prefill (T 8192)."""
+    import long_context_pool_amd as misa
+
+    shp = misa.shape(1, 131072, 8192, 64, 128, 128, dtype)
+    for k, kp in ((7000, 8192), (7900, 8192), (2048, 8192), (4000, 4096)):
+        both = misa.misa_workspace_bytes(shp, 8, k, kp)
+        assert both >= misa.misa_workspace_bytes(shp, 8, k, k), (k, kp)
+        assert both >= misa.misa_workspace_bytes(shp, 8, kp, kp), (k, kp)
