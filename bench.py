@@ -1,6 +1,10 @@
 """Benchmark of the MISA indexer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5]
+
+The default workload is the largest: a 128K-token prefill chunk in fp8 (T =
+8192 queries ending an L = 131072 causal prefix, H = 64, h = 8, B = 128,
+k = 2048) with MISA-dagger (k' = 8192 candidates re-ranked by all heads).
 
 A step is one pass of the hot path over one batch of synthetic input:
   decode (T = 1): misa_decode_step -- refresh the pooled key of the block
@@ -8,10 +12,12 @@ A step is one pass of the hot path over one batch of synthetic input:
                   route, routed score + top-k in two kernels
                   [-> rerank when the workload has k'];
   prefill:        pool all keys -> route -> routed score + top-k [-> rerank].
-The dense DSA indexer (all heads, same library) is timed the same way for the
-MISA-vs-DSA speedup.  Inputs are resident in HBM before timing starts; several
-input sets are rotated so that the decode workloads stream their keys from
-HBM instead of the 256 MB last-level cache.
+`value` is the whole step of the workload (MISA-dagger when it has k').  For
+such workloads the one-stage MISA step (routed top-k straight to k, no
+re-rank) is timed too.  The dense DSA indexer (all heads, same library) is
+timed the same way for the MISA-vs-DSA speedups.  Inputs are resident in HBM
+before timing starts; several input sets are rotated so that the decode
+workloads stream their keys from HBM instead of the 256 MB last-level cache.
 
 Prints one JSON line (metric/value = scored (query, token) pairs per second).
 """
@@ -55,7 +61,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2", help="c1..c5 (default c2, the decode workload)")
+    ap.add_argument("--workload", default="c5",
+                    help="c1..c5 (default c5, the 128K fp8 prefill with MISA-dagger)")
     ap.add_argument("--L", type=int, default=0,
                     help="override the workload's context length (a sweep point, not a headline "
                          "configuration: the line's workload name then carries _L<L>)")
@@ -103,7 +110,21 @@ class Runner:
             self.cand = torch.empty((p.batch, p.T, kp), dtype=torch.int32, device=dev)
             self.idx = torch.empty((p.batch, p.T, p.k), dtype=torch.int32, device=dev)
             self.didx = torch.empty((p.batch, p.T, p.k), dtype=torch.int32, device=dev)
+            self.idx1 = torch.empty((p.batch, p.T, p.k), dtype=torch.int32, device=dev)
         self.decode = p.T == 1
+
+    def _pool_route(self, s):
+        """Pooling (Eq. (4)) and routing (Eq. (7)-(8)) of a prefill step."""
+        m, p, st = self.misa, self.p, self.stream
+        if p.T <= 8:
+            # Multi-query decode: the pooled cache only changes in the
+            # blocks holding the T newest keys.
+            b0 = (p.L - p.T) // p.B
+            m.misa_pool_keys_range(self.shp, b0, p.M - b0, s["k"], s["ks"], s["pooled"], st)
+        else:
+            m.misa_pool_keys(self.shp, s["k"], s["ks"], s["pooled"], st)
+        m.misa_route(self.shp, p.h, s["q"], s["qs"], s["w"], s["pooled"], s["k"], s["ks"],
+                     self.heads, None, self.ws, st)
 
     def misa_step(self, i, ev=None):
         """One MISA pass on input set i; ev = (before, after) events around the
@@ -119,15 +140,7 @@ class Runner:
             if ev:
                 ev[1].record(st)
         else:
-            if p.T <= 8:
-                # Multi-query decode: the pooled cache only changes in the
-                # blocks holding the T newest keys.
-                b0 = (p.L - p.T) // p.B
-                m.misa_pool_keys_range(self.shp, b0, p.M - b0, s["k"], s["ks"], s["pooled"], st)
-            else:
-                m.misa_pool_keys(self.shp, s["k"], s["ks"], s["pooled"], st)
-            m.misa_route(self.shp, p.h, s["q"], s["qs"], s["w"], s["pooled"], s["k"], s["ks"],
-                         self.heads, None, self.ws, st)
+            self._pool_route(s)
             if ev:
                 ev[0].record(st)
             m.misa_score_topk(self.shp, p.h, p.kprime or p.k, s["q"], s["qs"], s["w"], s["k"],
@@ -137,6 +150,26 @@ class Runner:
         if p.kprime:
             m.misa_rerank(self.shp, p.kprime, p.k, s["q"], s["qs"], s["w"], s["k"], s["ks"],
                           self.cand, self.idx, None, self.ws, st)
+
+    def misa_1stage_step(self, i, ev=None):
+        """MISA without the re-rank (Eq. (7)-(10) with k), for workloads
+        whose headline step is MISA-dagger; ev brackets misa_score_topk."""
+        m, p, s, st = self.misa, self.p, self.sets[i % len(self.sets)], self.stream
+        if self.decode:
+            if ev:
+                ev[0].record(st)
+            m.misa_decode_step(self.shp, p.h, p.k, s["q"], s["qs"], s["w"], s["pooled"], s["k"],
+                               s["ks"], self.heads, None, self.idx1, None, self.ws, st)
+            if ev:
+                ev[1].record(st)
+            return
+        self._pool_route(s)
+        if ev:
+            ev[0].record(st)
+        m.misa_score_topk(self.shp, p.h, p.k, s["q"], s["qs"], s["w"], s["k"], s["ks"], self.heads,
+                          self.idx1, None, self.ws, st)
+        if ev:
+            ev[1].record(st)
 
     def dense_step(self, i, ev=None):
         m, p, s, st = self.misa, self.p, self.sets[i % len(self.sets)], self.stream
@@ -182,11 +215,28 @@ def time_steps(fn, steps, warmup, stream):
     return step_ms, call_ms, host_ms, pct
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(x, budget_s):
-    """The oracle as it stands, on a bounded sample of the same workload,
-    over a thread pool of host cores (ctypes releases the GIL).  The sample
-    (every sequence of a decode batch, or 32 evenly spaced queries of a
-    prefill) is run in whole passes until about budget_s seconds have gone."""
+    """The oracle as it stands, on a bounded sample of the same workload.
+
+    The sample is every sequence of a decode batch, or 32 evenly spaced
+    queries of a prefill.  Three legs, each in whole passes over (part of)
+    the sample until its share of budget_s has gone:
+      * the method of the workload (MISA: route + routed score + top-k,
+        plus the re-rank for MISA-dagger) on a thread pool of host cores
+        (ctypes releases the GIL; at most 16 threads) -- the reported value;
+      * the same on one core, over the first 4 queries of the sample;
+      * dense DSA (Eq. (1)-(2)) on the thread pool."""
     import concurrent.futures
 
     import numpy as np
@@ -215,7 +265,7 @@ def cpu_baseline(x, budget_s):
 
     inputs = {bt: query_inputs(bt) for bt in sample}
 
-    def one(bt):
+    def misa_one(bt):
         b, t = bt
         q, w = inputs[bt]
         pos = p.L - p.T + t
@@ -224,20 +274,35 @@ def cpu_baseline(x, budget_s):
             oracle.rerank(seqs[b].K, q, w, r["idx"], p.k)
         return pos + 1
 
-    pairs, passes = 0, 0
-    with concurrent.futures.ThreadPoolExecutor(cores) as ex:
-        t0 = time.perf_counter()
-        while True:
-            pairs += sum(ex.map(one, sample))
-            passes += 1
-            dt = time.perf_counter() - t0
-            if dt >= budget_s:
-                break
+    def dense_one(bt):
+        b, t = bt
+        q, w = inputs[bt]
+        pos = p.L - p.T + t
+        seqs[b].dense(pos, q, w, p.k)
+        return pos + 1
+
+    def timed(fn, items, threads, budget):
+        pairs, passes = 0, 0
+        with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+            t0 = time.perf_counter()
+            while True:
+                pairs += sum(ex.map(fn, items))
+                passes += 1
+                dt = time.perf_counter() - t0
+                if dt >= budget:
+                    return pairs / dt, passes, dt
+
+    v_n, passes, dt = timed(misa_one, sample, cores, budget_s * 0.6)
+    v_1, passes_1, _ = timed(misa_one, sample[:4], 1, budget_s * 0.2)
+    v_d, passes_d, _ = timed(dense_one, sample, cores, budget_s * 0.2)
+    what = "route + routed score + top-k" + (" + rerank" if p.kprime else "")
     desc = (f"{passes} pass(es) over {len(sample)} queries "
-            f"({'every sequence' if p.T == 1 else 'evenly spaced'}) of the workload: "
-            f"route + routed score + top-k{' + rerank' if p.kprime else ''}")
-    return {"value": pairs / dt, "unit": "pairs/s", "cores": cores, "kind": "oracle",
-            "sample": desc, "seconds": round(dt, 3)}
+            f"({'every sequence' if p.T == 1 else 'evenly spaced'}) of the workload: {what}; "
+            f"one core: {passes_1} pass(es) over the first 4; dense DSA: {passes_d} pass(es)")
+    return {"value": v_n, "unit": "pairs/s", "cores": cores, "kind": "oracle", "sample": desc,
+            "seconds": round(dt, 3), "one_core_value": v_1, "dense_value": v_d,
+            "dense_one_core_estimate": v_d / cores, "cpu_model": cpu_model(),
+            "host_cpus": os.cpu_count()}
 
 
 def traffic_from_profile(kernel, workload, sha):
@@ -282,24 +347,39 @@ def main():
 
     m_step, m_call, m_host, m_pct = time_steps(r.misa_step, args.steps, args.warmup, stream)
     pairs = p.pairs
+    res_1stage = None
+    if p.kprime:
+        s_step, s_call, _, _ = time_steps(r.misa_1stage_step, args.steps, args.warmup, stream)
+        res_1stage = {"value": pairs / (s_step / 1e3), "ms_per_step": s_step,
+                      "score_topk_call_ms": s_call, "k": p.k}
     res_dense = None
     if not args.no_dense:
         d_step, d_call, _, _ = time_steps(r.dense_step, args.steps, args.warmup, stream)
         res_dense = {"value": pairs / (d_step / 1e3), "ms_per_step": d_step}
     torch.cuda.synchronize()
 
-    # Recall of the dense top-k by MISA (sets; last step's outputs, same input set).
+    # Recall of the dense top-k (sets; last step's outputs, same input set).
+    def recall_of(sel):
+        a, b = sel.cpu().numpy(), r.didx.cpu().numpy()
+        tot = 0
+        for bi in range(p.batch):
+            for t in range(p.T):
+                tot += len(np.intersect1d(a[bi, t], b[bi, t]))
+        return tot / (p.batch * p.T * p.k)
+
+    import numpy as np
+
     recall = None
     if res_dense is not None:
         r.misa_step(0)
         r.dense_step(0)
+        if res_1stage is not None:
+            r.misa_1stage_step(0)
         torch.cuda.synchronize()
-        a, b = r.idx.cpu().numpy(), r.didx.cpu().numpy()
-        tot = 0
-        for bi in range(p.batch):
-            for t in range(p.T):
-                tot += len(set(a[bi, t].tolist()) & set(b[bi, t].tolist()))
-        recall = tot / (p.batch * p.T * p.k)
+        recall = recall_of(r.idx)
+        if res_1stage is not None:
+            res_1stage["recall_vs_dense"] = recall_of(r.idx1)
+            res_1stage["speedup_vs_dense"] = res_dense["ms_per_step"] / res_1stage["ms_per_step"]
 
     e = {synth.F32: 4, synth.BF16: 2, synth.FP8_E4M3: 1}[p.dtype]
     dtype = {synth.F32: "f32", synth.BF16: "bf16", synth.FP8_E4M3: "fp8"}[p.dtype]
@@ -363,9 +443,11 @@ def main():
         "config": {"workload": p.name, "batch": p.batch, "L": p.L, "T": p.T, "H": p.H, "h": p.h,
                    "d": p.d, "B": p.B, "k": p.k, "kprime": p.kprime, "pairs_per_step": pairs,
                    "input_sets": n_sets, "parallelism": "single-gpu"},
+        "method": "MISA-dagger (k' candidates re-ranked)" if p.kprime else "MISA",
         "dense_dsa": res_dense,
         "speedup_vs_dense": (res_dense["ms_per_step"] / m_step) if res_dense else None,
         "recall_vs_dense": recall,
+        "misa_1stage": res_1stage,
         "host_submit_ms_per_step": m_host,
         "source_sha": sha,
         "roofline": roof,

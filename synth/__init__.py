@@ -165,3 +165,24 @@ def small(name: str, **kw) -> Problem:
     base = dataclasses.asdict(C1)
     base.update(name=name, **kw)
     return Problem(**base)
+
+
+def sparse_rows(p: Problem, rows: np.ndarray, seed: int | None = None) -> Inputs:
+    """Exact-integer inputs (as ``generate(..., exact_ints=True)``) whose keys
+    are zero except at the given key positions ``rows`` (the same for every
+    sequence): a cheap stand-in for very long sequences where only a few
+    rows are ever read.  Scales are 1.  Draw order: q, w, then the rows."""
+    if p.dtype == F32:
+        raise ValueError("sparse_rows holds bf16 or fp8 keys")
+    rng = np.random.Generator(np.random.PCG64(p.seed if seed is None else seed))
+    b, L, T, H, d = p.batch, p.L, p.T, p.H, p.d
+    rows = np.asarray(rows, dtype=np.int64)
+    q = rng.integers(-4, 5, size=(b, T, H, d)).astype(np.float32)
+    w = np.ldexp(1.0, -rng.integers(0, 4, size=(b, T, H))).astype(np.float32)
+    kv = rng.integers(-4, 5, size=(b, len(rows), d)).astype(np.float32)
+    tdt = torch.bfloat16 if p.dtype == BF16 else torch.float8_e4m3fn
+    k = torch.zeros((b, L, d), dtype=tdt)
+    k[:, torch.from_numpy(rows)] = torch.from_numpy(kv).to(tdt)
+    return Inputs(p, torch.from_numpy(q).to(tdt).contiguous(), k, torch.from_numpy(w).contiguous(),
+                  torch.ones((b, T), dtype=torch.float32), torch.ones((b, L), dtype=torch.float32),
+                  [])
