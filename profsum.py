@@ -1,7 +1,7 @@
 """Summarise rocprofv3 CSV output into the short text files kept under profiles/.
 
-    python -m long_context_pool_amd.profsum stats  <rocprof_dir> <out.md> --cmd "<command>"
-    python -m long_context_pool_amd.profsum traffic <fetch_dir> <write_dir> <kernel_regex> \
+    python profsum.py stats  <rocprof_dir> <out.md> --cmd "<command>"
+    python profsum.py traffic <fetch_dir> <write_dir> <kernel_regex> \
         <copy_bytes> <workload> <out.json> --cmd "<command>"
 
 `stats` lists every kernel of a --kernel-trace --stats run (calls, average
@@ -26,7 +26,7 @@ import os
 import re
 import statistics
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "long_context_pool_amd", "csrc")
 
 
