@@ -167,6 +167,33 @@ misa_status misa_decode_step(const misa_shape* shape, int32_t h, int32_t k, cons
                              const float* k_scale, int32_t* heads, float* E_out, int32_t* idx,
                              float* scores_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* misa_decode_step for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments (minus ws), checks and results as
+ * misa_decode_step; the workspace is a fixed device array inside the library,
+ * MISA_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, which each GPU the library
+ * runs on holds until the process ends.  Nothing is allocated by the call
+ * (no hipMalloc, no allocating library routine).
+ *   - A shape whose decode workspace exceeds the array returns
+ *     MISA_ERR_UNSUPPORTED and launches nothing.  The need is batch * L * 4
+ *     bytes of scores, about 9 MB of digit histograms when batch >= 8 (34 KB
+ *     per sequence below that) and about 17 KB per sequence: batch 32 x
+ *     L 32768 takes 13.6 MB, batch 8 x L 131072 13.1 MB, batch 64 x
+ *     L 131072 43.9 MB, batch 1 x L 2^20 4.3 MB.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents (including the router arrival words documented at
+ *     misa_decode_step).  Calls that overlap in time on one GPU -- on
+ *     different streams, or from different threads -- race and give wrong
+ *     results: serialise them.
+ *   - The first call on each device looks up the array's device address
+ *     (hipGetSymbolAddress, no allocation); a failure returns MISA_ERR_HIP. */
+#define MISA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+misa_status misa_decode_step_noalloc(const misa_shape* shape, int32_t h, int32_t k, const void* q,
+                                     const float* q_scale, const float* w, float* pooled,
+                                     const void* kk, const float* k_scale, int32_t* heads,
+                                     float* E_out, int32_t* idx, float* scores_out,
+                                     hipStream_t stream);
+
 /* Eq. (1)-(2), the dense DSA indexer baseline: Eq. (9)-(10) with every head
  * j < H, no router.  Layouts as misa_score_topk. */
 misa_status dsa_index_dense(const misa_shape* shape, int32_t k, const void* q,

@@ -70,6 +70,26 @@ misa_status from_hip(hipError_t e) { return e == hipSuccess ? MISA_OK : MISA_ERR
     if (st_ != MISA_OK) return st_;      \
   } while (0)
 
+// Argument checks of the decode step (both forms); fills `s` on success.
+misa_status check_decode_step(const misa_shape* shape, int32_t h, int32_t k, const void* q,
+                              const float* q_scale, const float* w, const float* pooled,
+                              const void* kk, const float* k_scale, const int32_t* heads,
+                              const float* E_out, const int32_t* idx, const float* scores_out,
+                              Shape& s) {
+  MISA_TRY(check_shape(shape, s));
+  if (h < 1 || h > s.H) return MISA_ERR_INVALID_ARG;
+  if (h > kMaxRouted || s.T != 1 || s.dtype == MISA_F32) return MISA_ERR_UNSUPPORTED;
+  MISA_TRY(check_topk(k));
+  MISA_TRY(check_inputs(s, q, q_scale, w, kk, k_scale));
+  MISA_TRY(check_out(pooled, true));
+  MISA_TRY(check_out(heads, true));
+  MISA_TRY(check_out(E_out, false));
+  MISA_TRY(check_out(idx, true));
+  MISA_TRY(check_out(scores_out, false));
+  if (s.batch > 65535) return MISA_ERR_UNSUPPORTED;
+  return MISA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -156,21 +176,29 @@ misa_status misa_decode_step(const misa_shape* shape, int32_t h, int32_t k, cons
                              const float* k_scale, int32_t* heads, float* E_out, int32_t* idx,
                              float* scores_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   Shape s;
-  MISA_TRY(check_shape(shape, s));
-  if (h < 1 || h > s.H) return MISA_ERR_INVALID_ARG;
-  if (h > kMaxRouted || s.T != 1 || s.dtype == MISA_F32) return MISA_ERR_UNSUPPORTED;
-  MISA_TRY(check_topk(k));
-  MISA_TRY(check_inputs(s, q, q_scale, w, kk, k_scale));
-  MISA_TRY(check_out(pooled, true));
-  MISA_TRY(check_out(heads, true));
-  MISA_TRY(check_out(E_out, false));
-  MISA_TRY(check_out(idx, true));
-  MISA_TRY(check_out(scores_out, false));
+  MISA_TRY(check_decode_step(shape, h, k, q, q_scale, w, pooled, kk, k_scale, heads, E_out, idx,
+                             scores_out, s));
   MISA_TRY(check_ws(ws, ws_bytes, misa::decode_ws_bytes(s)));
-  if (s.batch > 65535) return MISA_ERR_UNSUPPORTED;
   return from_hip(misa::launch_decode_step(s, h, k, q, q_scale, w, pooled, kk, k_scale, heads,
                                            E_out, idx, scores_out, ws, stream));
 }
+
+misa_status misa_decode_step_noalloc(const misa_shape* shape, int32_t h, int32_t k,
+                                     const void* q, const float* q_scale, const float* w,
+                                     float* pooled, const void* kk, const float* k_scale,
+                                     int32_t* heads, float* E_out, int32_t* idx,
+                                     float* scores_out, hipStream_t stream) {
+  Shape s;
+  MISA_TRY(check_decode_step(shape, h, k, q, q_scale, w, pooled, kk, k_scale, heads, E_out, idx,
+                             scores_out, s));
+  static_assert(misa::kStaticScratchBytes == MISA_NOALLOC_SCRATCH_BYTES, "header limit");
+  if (misa::decode_ws_bytes(s) > misa::kStaticScratchBytes) return MISA_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  MISA_TRY(from_hip(misa::static_scratch(&ws)));
+  return from_hip(misa::launch_decode_step(s, h, k, q, q_scale, w, pooled, kk, k_scale, heads,
+                                           E_out, idx, scores_out, ws, stream));
+}
+
 
 misa_status dsa_index_dense(const misa_shape* shape, int32_t k, const void* q,
                             const float* q_scale, const float* w, const void* kk,

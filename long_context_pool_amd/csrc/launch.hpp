@@ -91,4 +91,9 @@ hipError_t launch_rerank(const Shape& s, int32_t kprime, int32_t k, const void* 
 
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 
+// The fixed device scratch of the no-allocation decode step: its size, and
+// this device's address of it (looked up on the first call on each device).
+constexpr size_t kStaticScratchBytes = size_t{64} << 20;
+hipError_t static_scratch(void** ptr);
+
 }  // namespace misa

@@ -144,3 +144,25 @@ def test_workspace_covers_both_selection_sizes(dtype):
         both = misa.misa_workspace_bytes(shp, 8, k, kp)
         assert both >= misa.misa_workspace_bytes(shp, 8, k, k), (k, kp)
         assert both >= misa.misa_workspace_bytes(shp, 8, kp, kp), (k, kp)
+
+
+def test_noalloc_decode_step_rejects_shapes_beyond_its_scratch():
+    """The no-allocation decode step refuses, before launching anything, a
+    shape whose workspace exceeds its fixed scratch (batch 256 x L 2^20 needs
+    about 1 GiB of scores), and applies misa_decode_step's argument checks."""
+    import long_context_pool_amd as misa
+
+    lib = misa.lib()
+    big = misa.shape(256, 1 << 20, 1, 64, 128, 128, misa.MISA_BF16)
+    st = lib.misa_decode_step_noalloc(ctypes.byref(big), 8, 64, FAKE, None, FAKE, FAKE, FAKE, None,
+                                      FAKE, None, FAKE, None, None)
+    assert st == misa.MISA_ERR_UNSUPPORTED
+    shp = misa.shape(4, 4096, 2, 64, 128, 64, misa.MISA_BF16)  # T = 2
+    st = lib.misa_decode_step_noalloc(ctypes.byref(shp), 8, 64, FAKE, None, FAKE, FAKE, FAKE, None,
+                                      FAKE, None, FAKE, None, None)
+    assert st == misa.MISA_ERR_UNSUPPORTED
+    shp = misa.shape(4, 4096, 1, 64, 128, 64, misa.MISA_BF16)
+    st = lib.misa_decode_step_noalloc(ctypes.byref(shp), 8, 64, FAKE, None, FAKE, None, FAKE, None,
+                                      FAKE, None, FAKE, None, None)  # null pooled
+    assert st == misa.MISA_ERR_INVALID_ARG
+    assert misa.MISA_NOALLOC_SCRATCH_BYTES == 64 << 20
