@@ -114,7 +114,7 @@ __device__ __forceinline__ void finalize_query(const float (*rowsum)[64], int np
     e = fabsf(w[r * H + lane]) * sq * sum / static_cast<float>(Mt);
     if (E_out) E_out[r * H + lane] = e;
   }
-  wave_top_heads(e, H, h, heads + r * h);
+  wave_top_heads_rank(e, H, h, heads + r * h);
 }
 
 }  // namespace misa

@@ -2,21 +2,27 @@
 // for bf16 and fp8 inputs.
 //
 // For query t the router needs S_{t,j} = sum over the floor(n_t/B) complete
-// blocks of ReLU(q_{t,j} . p_b): a dense contraction of the query's H head rows
-// (A operand, bf16; fp8 codes widen to bf16 exactly) with the pooled keys (B
-// operand: fp32 rounded to bf16, and for bf16 inputs also the bf16 rounding of
-// the remainder, so q.p = q.p_hi + q.p_lo holds to ~2^-16 -- a single bf16
-// rounding of p costs ~1e-3 relative in E on short prefixes), 32x32x16 MFMA
-// tiles, ReLU and a masked
-// running sum on the accumulators, then one cross-lane reduction per row.
+// blocks of ReLU(q_{t,j} . p_b): a dense contraction of the pooled keys (A
+// operand, 32 blocks per row tile: fp32 rounded to bf16, and for bf16 inputs
+// also the bf16 rounding of the remainder, so q.p = q.p_hi + q.p_lo holds to
+// ~2^-16 -- a single bf16 rounding of p costs ~1e-3 relative in E on short
+// prefixes) with the query head rows (B operand, 32 heads per column tile,
+// bf16; fp8 codes widen to bf16 exactly) on 32x32x16 MFMA tiles.  Each lane
+// then holds 16 blocks of one head, so ReLU and the block sum stay in the
+// lane; one cross-half add per head finishes the sum.
 // The partial last block (B not dividing n_t) uses ReLU(mean_s q . k_s): the
-// per-key dots come from the same MFMA tiles on the raw keys.  Then E_{t,j} = |w_{t,j}| * s_t * (S + partial) / M_t
-// (s_t = the fp8 query scale, else 1) and the h best heads are picked by h
-// rounds of a wave arg-max (ties to the lower head) and written ascending.
+// per-key dots come from the same MFMA tiles on the raw keys (the 32x32x16
+// fragments are laid out alike for A and B, so the query fragments serve as
+// A there).  Then E_{t,j} = |w_{t,j}| * s_t * (S + partial) / M_t (s_t = the
+// fp8 query scale, else 1) and the h best heads are picked by h rounds of a
+// wave arg-max (ties to the lower head) and written ascending.
 //
-// Prefill: one wave per query (4 per workgroup); the pooled tile is converted
-// to bf16 once into LDS and shared by the four waves.  (Decode has a single
-// query per sequence and is routed on the vector ALU, route_decode.hip.)
+// Prefill: each wave holds four column tiles of query head rows in registers
+// (two queries of 64 heads, or four of 32), so every A fragment read from LDS
+// feeds four MFMAs (eight with the lo plane); the 32-block pooled tiles are
+// staged in LDS once per workgroup and shared by its four waves.  (Decode
+// has a single query per sequence and is routed on the vector ALU,
+// route_decode.hip.)
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma.hpp"
@@ -42,9 +48,9 @@ __device__ __forceinline__ void rt_load16_lds(__amdgpu_buffer_rsrc_t r, void* ld
 }
 template <int N>
 __device__ __forceinline__ void rt_vmcnt_barrier() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate in the low field");
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits: [3:0] and [15:14]");
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -63,103 +69,90 @@ __device__ __forceinline__ T* rt_uniform(T* p) {
   return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// Load the A operand: head rows rt*32 + l%32 of query r, head-dim elements
-// [64*(l/32), 64*(l/32)+64) split over 8 k-steps.  Rows >= H are zero.
-template <int DT, int RT>
-__device__ __forceinline__ void load_q_rows(const void* q, int64_t r, int H, bf16x8 (&a)[RT][8]) {
-  const int lane = lane_id();
-  const int hf = lane >> 5;
+// Column tiles (32 query heads each) per wave.  Two (one query of 64 heads)
+// measured the same at 3% more time, and running one tile's block sums
+// among the next tile's MFMAs (two accumulator sets) gained nothing: the
+// kernel is not limited by the epilogue's issue slots.
+constexpr int kRCols = 4;
+
+// One 32x32x16 fragment set of a head row (either operand): this lane's head
+// row `row` (< 0: zeros), head-dim elements [64*(l/32), 64*(l/32)+64) over 8
+// k-steps; fp8 codes widen to bf16 exactly.
+template <int DT>
+__device__ __forceinline__ void load_head_frags(const void* q, int64_t row, bf16x8 (&a)[8]) {
+  const int hf = lane_id() >> 5;
+  if (row < 0) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int j = rt * 32 + (lane & 31);
-    if (j >= H) {
+    for (int ks = 0; ks < 8; ++ks) a[ks] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    return;
+  }
+  if constexpr (DT == kBF16) {
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + row * kD + 64 * hf);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) a[rt][ks] = as_bf16x8(make_uint4(0, 0, 0, 0));
-      continue;
-    }
-    if constexpr (DT == kBF16) {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) +
-                                                        (r * H + j) * kD + 64 * hf);
+    for (int ks = 0; ks < 8; ++ks) a[ks] = as_bf16x8(src[ks]);
+  } else {
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(q) + row * kD + 64 * hf);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) a[rt][ks] = as_bf16x8(src[ks]);
-    } else {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(q) +
-                                                        (r * H + j) * kD + 64 * hf);
+    for (int c = 0; c < 4; ++c) {
+      const uint4 v = src[c];  // 16 fp8 codes = k-steps 2c, 2c+1
+      const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[8];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint4 v = src[c];  // 16 fp8 codes = k-steps 2c, 2c+1
-        const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
-        uint32_t o[8];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          // e4m3 -> fp32 is exact and bf16 holds the 4-bit significand exactly.
-          const float f0 = fp8_to_f32(wds[u] & 0xFF), f1 = fp8_to_f32((wds[u] >> 8) & 0xFF);
-          const float f2 = fp8_to_f32((wds[u] >> 16) & 0xFF), f3 = fp8_to_f32(wds[u] >> 24);
-          o[2 * u] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
-          o[2 * u + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u);
-        }
-        a[rt][2 * c] = as_bf16x8(make_uint4(o[0], o[1], o[2], o[3]));
-        a[rt][2 * c + 1] = as_bf16x8(make_uint4(o[4], o[5], o[6], o[7]));
+      for (int u = 0; u < 4; ++u) {
+        // e4m3 -> fp32 is exact and bf16 holds the 4-bit significand exactly.
+        const float f0 = fp8_to_f32(wds[u] & 0xFF), f1 = fp8_to_f32((wds[u] >> 8) & 0xFF);
+        const float f2 = fp8_to_f32((wds[u] >> 16) & 0xFF), f3 = fp8_to_f32(wds[u] >> 24);
+        o[2 * u] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+        o[2 * u + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u);
       }
+      a[2 * c] = as_bf16x8(make_uint4(o[0], o[1], o[2], o[3]));
+      a[2 * c + 1] = as_bf16x8(make_uint4(o[4], o[5], o[6], o[7]));
     }
   }
 }
 
-// acc (rows x 32 blocks) = A . B_hi [+ A . B_lo]; rs += ReLU(acc) when
-// col_ok.  B comes from an LDS tile of unpadded 256-byte rows (this lane's
-// block row, its 64-element half) whose 16-byte chunk c of row r sits at
-// chunk position c ^ (r % 16), so the 32 rows of a read hit distinct banks.
-// The hi and lo products share one accumulator per row tile, the RT row
-// tiles giving independent chains.
-template <int RT, bool SPLIT>
-__device__ __forceinline__ void accumulate_tile_sw(const bf16x8 (&a)[RT][8], const uint8_t* hb,
-                                                   const uint8_t* lb, bool col_ok, f32x16 (&rs)[RT]) {
+// One 32-block pooled tile against the wave's kRCols column tiles:
+// acc[c] (blocks x heads) = P_hi . Q_c [+ P_lo . Q_c], then rs[c] += the
+// lane's 16 blocks of ReLU(acc[c]) -- all of them (MASK false), or those of
+// tile row < lim[c] (the column's complete-block count minus the tile's first
+// block).  P comes from an LDS tile of unpadded 256-byte rows whose 16-byte
+// chunk c of row r sits at chunk position c ^ (r % 16), so the 32 rows of a
+// read hit distinct banks; each fragment read feeds kRCols MFMAs.
+template <bool SPLIT, bool MASK>
+__device__ __forceinline__ void accumulate_tile(const bf16x8 (&bq)[kRCols][8], const uint8_t* hb,
+                                                const uint8_t* lb, const int (&lim)[kRCols],
+                                                float (&rs)[kRCols]) {
   const int lane = lane_id();
   const int r = lane & 31;
   const int hf = lane >> 5;
   const uint8_t* rowh = hb + r * (kD * 2);
   const uint8_t* rowl = lb + r * (kD * 2);
-  f32x16 acc[RT];
+  f32x16 acc[kRCols];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
+  for (int c = 0; c < kRCols; ++c) acc[c] = f32x16{};
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     const int pos = (8 * hf + ks) ^ (r & 15);
-    const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4*>(rowh + 16 * pos));
+    const bf16x8 ph = as_bf16x8(*reinterpret_cast<const uint4*>(rowh + 16 * pos));
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_bf16(a[rt][ks], bh, acc[rt]);
+    for (int c = 0; c < kRCols; ++c) acc[c] = mfma32_bf16(ph, bq[c][ks], acc[c]);
     if constexpr (SPLIT) {
-      const bf16x8 bl = as_bf16x8(*reinterpret_cast<const uint4*>(rowl + 16 * pos));
+      const bf16x8 pl = as_bf16x8(*reinterpret_cast<const uint4*>(rowl + 16 * pos));
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_bf16(a[rt][ks], bl, acc[rt]);
+      for (int c = 0; c < kRCols; ++c) acc[c] = mfma32_bf16(pl, bq[c][ks], acc[c]);
     }
   }
-  if (col_ok) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) rs[rt][i] += relu(acc[rt][i]);
-  }
-}
-
-// Sum rs over the 32 columns held by each half-wave; returns through LDS
-// rowsum[row] for rows of this wave (row = rt*32 + 8*(i/4) + 4*hf + i%4).
-template <int RT>
-__device__ __forceinline__ void reduce_rows(f32x16 (&rs)[RT], float* rowsum) {
-  const int lane = lane_id();
-  const int hf = lane >> 5;
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+  for (int c = 0; c < kRCols; ++c) {
+    float s = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float v = rs[rt][i];
-#pragma unroll
-      for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-      if ((lane & 31) == 0) {
-        const int row = rt * 32 + 8 * (i / 4) + 4 * hf + (i % 4);
-        rowsum[row] = v;
-      }
+      const float v = relu(acc[c][i]);
+      if constexpr (MASK) s += (8 * (i / 4) + 4 * hf + (i % 4) < lim[c]) ? v : 0.f;
+      else s += v;
     }
+    rs[c] += s;
+  }
 }
 
 // Pooled keys -> bf16 hi and lo (bf16 rounding of the remainder) planes,
@@ -177,8 +170,23 @@ __global__ void pooled_split_kernel(const float* __restrict__ pooled, uint32_t* 
   lo[2 * i + 1] = l1;
 }
 
-template <int DT, int RT>
-__global__ __launch_bounds__(kRThreads) void route_prefill_kernel(
+// HG: 32-head groups per query (1 for H <= 32, 2 for H <= 64); the wave's
+// kRCols column tiles are its kRCols / HG queries' head groups.
+#ifndef MISA_ROUTE_NBUF_FP8
+#define MISA_ROUTE_NBUF_FP8 4
+#endif
+#ifndef MISA_ROUTE_NBUF_BF16
+#define MISA_ROUTE_NBUF_BF16 3
+#endif
+// Pooled-tile buffers per workgroup (8 KiB per fp8 tile, 16 KiB per bf16
+// tile with its lo plane); NBUF - 1 tiles are in flight.  Deeper rings (up to
+// eight fp8 tiles) measured the same: the tiles come from L2.  The budget is
+// two workgroups per CU with the partial-block staging.
+template <int DT>
+constexpr int route_nbuf() { return DT == kBF16 ? MISA_ROUTE_NBUF_BF16 : MISA_ROUTE_NBUF_FP8; }
+
+template <int DT, int HG>
+__global__ __launch_bounds__(kRThreads, 2) void route_prefill_kernel(
     const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint16_t* __restrict__ phi, const uint16_t* __restrict__ plo, const void* __restrict__ k,
     const float* __restrict__ k_scale, int32_t* __restrict__ heads, float* __restrict__ E_out,
@@ -186,43 +194,52 @@ __global__ __launch_bounds__(kRThreads) void route_prefill_kernel(
     float* __restrict__ part) {
   constexpr bool SPLIT = DT == kBF16;
   constexpr int LB = SPLIT ? kTileBytes : 16;
-  __shared__ __attribute__((aligned(16))) uint8_t h0[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t h1[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t h2[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t l0[LB];
-  __shared__ __attribute__((aligned(16))) uint8_t l1[LB];
-  __shared__ __attribute__((aligned(16))) uint8_t l2[LB];
-  __shared__ float rowsum[kRWaves][64];
-  __shared__ float partial[kRWaves][64];
-  const int wave = threadIdx.x / kWave;
+  constexpr int QW = kRCols / HG;         // queries per wave
+  constexpr int QWG = QW * kRWaves;       // queries per workgroup
+  constexpr int NBUF = route_nbuf<DT>();  // tile buffers: NBUF - 1 tiles in flight
+  __shared__ __attribute__((aligned(16))) uint8_t hbuf[NBUF][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lbuf[NBUF][LB];
+  __shared__ float rowsum[kRWaves][QW][64];
+  __shared__ float partial[kRWaves][QW][64];
+  // Raw keys of the workgroup's partial blocks, [full_min B, last position]:
+  // at most B + QWG - 1 rows, staged once for all its queries when they fit
+  // (16-byte chunk c of row r at chunk position c ^ (r % chunks per row)).
+  constexpr int ROWB = DT == kBF16 ? kD * 2 : kD;
+  constexpr int CPR = ROWB / 16;
+  constexpr int kPartRows = DT == kBF16 ? 80 : 192;  // B = 64 (bf16) or 128 (fp8) + QWG - 1 rows
+  constexpr int kPartLoads = kPartRows * ROWB / 1024 / kRWaves;  // 1 KiB loads per wave
+  static_assert(kPartLoads * kRWaves * 1024 == kPartRows * ROWB, "whole loads per wave");
+  __shared__ __attribute__((aligned(16))) uint8_t pkeys[kPartRows * ROWB];
+  __shared__ float pscale[DT == kFP8 ? kRWaves * 64 : 1];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = lane_id();
+  const int hf = lane >> 5;
   const int64_t seq = blockIdx.y;
-  const int t0 = blockIdx.x * kRWaves;
-  const int t = t0 + wave;
-  const bool active = t < T;
-  const int64_t r = seq * T + (active ? t : t0);
-  const int64_t pos = static_cast<int64_t>(L) - T + (active ? t : t0);
-  const int64_t n = pos + 1;
-  const int64_t full = n / B;
-  const int64_t Mt = (n + B - 1) / B;
-  // Largest complete-block count among the workgroup's queries.
-  const int tl = min(t0 + kRWaves - 1, T - 1);
+  const int t0 = blockIdx.x * QWG;
+  const int tw = t0 + wave * QW;  // first query of this wave
+  // Complete-block counts: the workgroup's smallest and largest.
+  const int tl = min(t0 + QWG - 1, T - 1);
+  const int64_t full_min = (static_cast<int64_t>(L) - T + t0 + 1) / B;
   const int64_t full_max = (static_cast<int64_t>(L) - T + tl + 1) / B;
 
-  bf16x8 a[RT][8];
-  load_q_rows<DT, RT>(q, r, H, a);
-  f32x16 rs[RT];
+  int64_t full_c[kRCols];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) rs[rt] = f32x16{};
+  for (int c = 0; c < kRCols; ++c) {
+    const int t = tw + c / HG;
+    full_c[c] = t < T ? (static_cast<int64_t>(L) - T + t + 1) / B : 0;
+  }
+  float rs[kRCols];
+#pragma unroll
+  for (int c = 0; c < kRCols; ++c) rs[c] = 0.f;
 
   // Pooled tiles of 32 blocks reach LDS by direct buffer-to-LDS loads into
-  // three buffers: while tile bt is multiplied, tiles bt+1 and bt+2 are in
+  // NBUF buffers: while tile bt is multiplied, tiles bt+1 .. bt+NBUF-1 are in
   // flight.  Each thread issues NL loads per tile (instruction i of wave w
   // fills rows 8w + 4i .. +3 of a plane; lane l loads chunk
   // (l % 16) ^ (row % 16) of its row into chunk position l % 16), so a fixed
   // vmcnt wait before each barrier proves that a tile has landed.  Rows past
-  // the last complete block load block 0 and are masked in the product;
-  // tiles past the last repeat it, so every iteration issues the same loads.
+  // the last complete block load block 0 and are masked in the sums; tiles
+  // past the last repeat it, so every iteration issues the same loads.
   constexpr int NL = SPLIT ? 4 : 2;
   // Split z of nsplit takes tiles [tile0, tile1) (nsplit > 1: few query
   // groups, so the blocks are spread over more workgroups; the partial sums
@@ -252,101 +269,175 @@ __global__ __launch_bounds__(kRThreads) void route_prefill_kernel(
       if constexpr (SPLIT) rt_load16_lds(rl, lb + 1024 * (2 * wave + i), voff);
     }
   };
-  // The A-operand loads complete here (the empty asm redefines the
-  // registers, so no later use waits on those loads): the counts below are
-  // the tiles' alone.
+  // Issue order: the partial-block keys (last split), the first NBUF - 1
+  // tiles, then the query rows, so that the three latencies overlap; all of
+  // it has landed at the wait below, after which each step issues one tile.
+  const int64_t p_base = full_min * B;
+  const int64_t p_cnt = static_cast<int64_t>(L) - T + tl - p_base + 1;
+  const bool staged = z == nsplit - 1 && p_cnt <= kPartRows;  // workgroup-uniform
+  if (staged) {
+    const uint8_t* kb0 = static_cast<const uint8_t*>(k) + (seq * L + p_base) * static_cast<int64_t>(ROWB);
+    const __amdgpu_buffer_rsrc_t rk = rt_rsrc(rt_uniform(kb0), static_cast<int32_t>(p_cnt * ROWB));
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(a[rt][ks]));
-  rt_vmcnt_zero();
+    for (int i = 0; i < kPartLoads; ++i) {
+      const int o = 1024 * (wave * kPartLoads + i) + 16 * lane;  // LDS byte of this lane's chunk
+      const int row = o / ROWB, pc = (o % ROWB) / 16;
+      rt_load16_lds(rk, pkeys + 1024 * (wave * kPartLoads + i),
+                    static_cast<uint32_t>(row * ROWB + 16 * (pc ^ (row % CPR))));
+    }
+    if constexpr (DT == kFP8) {
+      const __amdgpu_buffer_rsrc_t rs_k =
+          rt_rsrc(rt_uniform(k_scale + seq * L + p_base), static_cast<int32_t>(p_cnt * 4));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_k, (__attribute__((address_space(3))) void*)(pscale + 64 * wave),
+                                               4, static_cast<uint32_t>(4 * (64 * wave + lane)), 0, 0, 0);
+    }
+  }
   const bool any = tile1 > tile0;
   if (any) {
-    issue(tile0, h0, l0);
-    issue(tile0 + 1, h1, l1);
-  }
-  auto step = [&](int64_t bt, const uint8_t* hb, const uint8_t* lb, uint8_t* nh, uint8_t* nl)
-      __attribute__((always_inline)) {
-    rt_vmcnt_barrier<NL>();  // tile bt has landed; every wave is done with tile bt-1
-    issue(bt + 2, nh, nl);   // into tile bt-1's buffer
-    accumulate_tile_sw<RT, SPLIT>(a, hb, lb, bt * 32 + (lane & 31) < full, rs);
-  };
-  for (int64_t bt = tile0; bt < tile1; bt += 3) {
-    step(bt, h0, l0, h2, l2);
-    if (bt + 1 < tile1) step(bt + 1, h1, l1, h0, l0);
-    if (bt + 2 < tile1) step(bt + 2, h2, l2, h1, l1);
-  }
-  rt_vmcnt_zero();  // the last two tiles' loads (repeats) before the buffers are left
-  reduce_rows<RT>(rs, rowsum[wave]);
-  const bool has_partial = Mt > full && z == nsplit - 1;
-  if (has_partial) {
-    // Partial block [full*B, pos]: ReLU(q . mean of its keys) = ReLU(mean of
-    // q . k_s), so the per-key dots come from the same MFMA tiles (raw keys
-    // as B, 32 per column tile, fp8 codes widened to bf16 exactly and the
-    // key scale applied per column), summed over the block and divided.
-    f32x16 ps[RT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) ps[rt] = f32x16{};
-    const int64_t s_lo = full * B;
-    const int hf = lane >> 5;
+    for (int u = 0; u + 1 < NBUF; ++u) issue(tile0 + u, hbuf[u], lbuf[u]);
+  }
+  // B operand: column tile c = query tw + c / HG, heads 32 (c % HG) + l % 32.
+  bf16x8 bq[kRCols][8];
+#pragma unroll
+  for (int c = 0; c < kRCols; ++c) {
+    const int t = tw + c / HG;
+    const int j = 32 * (c % HG) + (lane & 31);
+    load_head_frags<DT>(q, (t < T && j < H) ? (seq * T + t) * H + j : -1, bq[c]);
+  }
+  rt_vmcnt_zero();
+  auto tile_lim = [&](int64_t bt, int (&lim)[kRCols]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < kRCols; ++c) lim[c] = static_cast<int>(full_c[c] - bt * 32);
+  };
+  // Tile bt sits in buffer (bt - tile0) % NBUF; the loop is unrolled by
+  // NBUF so that every buffer reference is static.
+  for (int64_t base = tile0; base < tile1; base += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      const int64_t bt = base + u;
+      if (bt >= tile1) break;
+      // Tile bt has landed (the NBUF - 2 tiles after it may be in flight);
+      // every wave is done with tile bt-1, whose buffer takes tile
+      // bt + NBUF - 1.
+      rt_vmcnt_barrier<NL * (NBUF - 2)>();
+      issue(bt + NBUF - 1, hbuf[(u + NBUF - 1) % NBUF], lbuf[(u + NBUF - 1) % NBUF]);
+      int lim[kRCols];
+      tile_lim(bt, lim);
+      if ((bt + 1) * 32 <= full_min) accumulate_tile<SPLIT, false>(bq, hbuf[u], lbuf[u], lim, rs);
+      else accumulate_tile<SPLIT, true>(bq, hbuf[u], lbuf[u], lim, rs);
+    }
+  }
+  rt_vmcnt_zero();  // the last tiles' loads (repeats) before the buffers are left
+  // Head sums: the two half-waves held different blocks of the same head.
+#pragma unroll
+  for (int c = 0; c < kRCols; ++c) {
+    const float v = rs[c] + __shfl_xor(rs[c], 32, kWave);
+    if (lane < 32) rowsum[wave][c / HG][32 * (c % HG) + lane] = v;
+  }
+  // Partial block [full*B, pos] of each query (last split only): ReLU(q .
+  // mean of its keys) = ReLU(mean of q . k_s).  The per-key dots come from
+  // MFMA tiles with the query fragments as A (rows = heads) and 32 raw keys
+  // as B (fp8 codes widened to bf16 exactly, the key scale applied per
+  // column), summed over the block's keys and divided by their count.  The
+  // keys come from the staged LDS rows, or from global memory when the
+  // workgroup's partial blocks did not fit (B large against the staging).
+  __syncthreads();  // every wave's staged rows have landed (each waited above)
+  // B fragments of staged key row `row` (relative to p_base).
+  auto staged_frags = [&](int row, bf16x8 (&kb)[8]) __attribute__((always_inline)) {
+    const uint8_t* kr = pkeys + row * ROWB;
+    if constexpr (DT == kBF16) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        kb[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(kr + 16 * ((8 * hf + ks) ^ (row % CPR))));
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 v = *reinterpret_cast<const uint4*>(kr + 16 * ((4 * hf + c) ^ (row % CPR)));
+        const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float f0 = fp8_to_f32(wds[u] & 0xFF), f1 = fp8_to_f32((wds[u] >> 8) & 0xFF);
+          const float f2 = fp8_to_f32((wds[u] >> 16) & 0xFF), f3 = fp8_to_f32(wds[u] >> 24);
+          o[2 * u] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+          o[2 * u + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u);
+        }
+        kb[2 * c] = as_bf16x8(make_uint4(o[0], o[1], o[2], o[3]));
+        kb[2 * c + 1] = as_bf16x8(make_uint4(o[4], o[5], o[6], o[7]));
+      }
+    }
+  };
+  bool has_partial[QW];
+#pragma unroll
+  for (int qw = 0; qw < QW; ++qw) {
+    const int t = tw + qw;
+    const int64_t n = static_cast<int64_t>(L) - T + t + 1;
+    has_partial[qw] = t < T && n % B != 0 && z == nsplit - 1;
+    if (!has_partial[qw]) continue;
+    const int64_t pos = n - 1;
+    const int64_t s_lo = (n / B) * B;
+    f32x16 ps[HG];
+#pragma unroll
+    for (int g = 0; g < HG; ++g) ps[g] = f32x16{};
     for (int64_t s0 = s_lo; s0 <= pos; s0 += 32) {
       const int64_t sk_i = s0 + (lane & 31);
       const bool ok = sk_i <= pos;
       const int64_t row = seq * L + (ok ? sk_i : s_lo);
-      bf16x8 b[8];
-      if constexpr (DT == kBF16) {
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(k) + row * kD + 64 * hf);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) b[ks] = as_bf16x8(src[ks]);
+      bf16x8 kb[8];
+      float skv;
+      if (staged) {
+        const int sr = static_cast<int>((ok ? sk_i : s_lo) - p_base);
+        staged_frags(sr, kb);
+        skv = ok ? ((DT == kFP8) ? pscale[sr] : 1.f) : 0.f;
       } else {
-        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(k) + row * kD + 64 * hf);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint4 v = src[c];
-          const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
-          uint32_t o[8];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float f0 = fp8_to_f32(wds[u] & 0xFF), f1 = fp8_to_f32((wds[u] >> 8) & 0xFF);
-            const float f2 = fp8_to_f32((wds[u] >> 16) & 0xFF), f3 = fp8_to_f32(wds[u] >> 24);
-            o[2 * u] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
-            o[2 * u + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u);
-          }
-          b[2 * c] = as_bf16x8(make_uint4(o[0], o[1], o[2], o[3]));
-          b[2 * c + 1] = as_bf16x8(make_uint4(o[4], o[5], o[6], o[7]));
-        }
+        load_head_frags<DT>(k, row, kb);
+        skv = ok ? ((DT == kFP8) ? k_scale[row] : 1.f) : 0.f;
       }
-      const float skv = ok ? ((DT == kFP8) ? k_scale[row] : 1.f) : 0.f;
-      f32x16 acc[RT];
+      f32x16 acc[HG];
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
+      for (int g = 0; g < HG; ++g) acc[g] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_bf16(a[rt][ks], b[ks], acc[rt]);
+        for (int g = 0; g < HG; ++g) acc[g] = mfma32_bf16(bq[qw * HG + g][ks], kb[ks], acc[g]);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+      for (int g = 0; g < HG; ++g)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ps[rt][i] += acc[rt][i] * skv;
+        for (int i = 0; i < 16; ++i) ps[g][i] += acc[g][i] * skv;
     }
-    reduce_rows<RT>(ps, partial[wave]);
+    // Sum over the 32 key columns of each half-wave; rows are heads.
+#pragma unroll
+    for (int g = 0; g < HG; ++g)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float v = ps[g][i];
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+        if ((lane & 31) == 0) partial[wave][qw][32 * g + 8 * (i / 4) + 4 * hf + (i % 4)] = v;
+      }
     __builtin_amdgcn_wave_barrier();
-    if (lane < 64) {
-      const float cnt = static_cast<float>(pos - s_lo + 1);
-      partial[wave][lane] = fmaxf(partial[wave][lane] / cnt, 0.f);
-    }
+    const float cnt = static_cast<float>(pos - s_lo + 1);
+    partial[wave][qw][lane] = fmaxf(partial[wave][qw][lane] / cnt, 0.f);
   }
-  __syncthreads();
-  if (!active) return;
-  if (nsplit == 1) {
-    const float sq = (DT == kFP8) ? q_scale[r] : 1.f;
-    finalize_query(&rowsum[wave], 1, has_partial ? partial[wave] : nullptr, H, h, w, sq, r, Mt,
-                   heads, E_out);
-  } else {
-    // Slot z: this split's block sums; slot nsplit: the partial block's term.
-    float* pr = part + r * (nsplit + 1) * 64;
-    pr[z * 64 + lane] = rowsum[wave][lane];
-    if (z == nsplit - 1) pr[nsplit * 64 + lane] = has_partial ? partial[wave][lane] : 0.f;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int qw = 0; qw < QW; ++qw) {
+    const int t = tw + qw;
+    if (t >= T) break;
+    const int64_t r = seq * T + t;
+    const int64_t n = static_cast<int64_t>(L) - T + t + 1;
+    const int64_t Mt = (n + B - 1) / B;
+    if (nsplit == 1) {
+      const float sq = (DT == kFP8) ? q_scale[r] : 1.f;
+      finalize_query(&rowsum[wave][qw], 1, has_partial[qw] ? partial[wave][qw] : nullptr, H, h, w,
+                     sq, r, Mt, heads, E_out);
+    } else {
+      // Slot z: this split's block sums; slot nsplit: the partial-block term.
+      float* pr = part + r * (nsplit + 1) * 64;
+      pr[z * 64 + lane] = rowsum[wave][qw][lane];
+      if (z == nsplit - 1) pr[nsplit * 64 + lane] = has_partial[qw] ? partial[wave][qw][lane] : 0.f;
+    }
   }
 }
 
@@ -387,8 +478,10 @@ bool route_mfma_supported(const Shape& s) { return s.dtype != kF32 && s.H <= 64 
 
 // Block splits per query group: enough workgroups (about 512) to spread the
 // pooled keys over the chip when the queries alone do not.
+int32_t route_qwg(const Shape& s) { return kRCols / (s.H > 32 ? 2 : 1) * kRWaves; }
+
 int32_t route_splits(const Shape& s) {
-  const int64_t wgs = static_cast<int64_t>((s.T + kRWaves - 1) / kRWaves) * s.batch;
+  const int64_t wgs = static_cast<int64_t>((s.T + route_qwg(s) - 1) / route_qwg(s)) * s.batch;
   if (wgs >= 512) return 1;
   const int64_t tiles = (s.M() + 31) / 32;
   int64_t n = (512 + wgs - 1) / wgs;
@@ -415,8 +508,8 @@ hipError_t launch_route_mfma(const Shape& s, int32_t h, const void* q, const flo
   const bool two = s.H > 32;
   const int32_t ns = route_splits(s);
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * plane);
-  dim3 grid((s.T + kRWaves - 1) / kRWaves, s.batch, ns);
-#define RP(DT, RT) route_prefill_kernel<DT, RT><<<grid, kRThreads, 0, st>>>(q, q_scale, w, phi, plo, k, k_scale, heads, E_out, s.L, s.T, s.H, s.B, s.M(), h, ns, part)
+  dim3 grid((s.T + route_qwg(s) - 1) / route_qwg(s), s.batch, ns);
+#define RP(DT, HG) route_prefill_kernel<DT, HG><<<grid, kRThreads, 0, st>>>(q, q_scale, w, phi, plo, k, k_scale, heads, E_out, s.L, s.T, s.H, s.B, s.M(), h, ns, part)
   if (s.dtype == kBF16) { if (two) RP(kBF16, 2); else RP(kBF16, 1); }
   else { if (two) RP(kFP8, 2); else RP(kFP8, 1); }
 #undef RP
