@@ -42,15 +42,33 @@ constexpr int kPThreads = 256;
 constexpr int kPWaves = 4;
 constexpr int kRT = 2;             // 32-row tiles per wave
 constexpr int kTileKeys = 64;      // keys per LDS tile (two 32-key column tiles)
-constexpr int kSamples = 512;      // sample keys per (workgroup, split)
-constexpr float kSampleMargin = 2.5f;
-// A lower margin where the threshold's sample rank j = margin k kSamples / n
-// is at least kMinSampleRank for every query (large k against L, as for a
-// re-rank candidate pass): the quantile's spread ~1/sqrt(j) is then small
-// enough that k certified candidates remain likely, and fewer candidates
-// mean fewer appends and a smaller select.
-constexpr float kLowMargin = 2.0f;
-constexpr double kMinSampleRank = 64.0;
+constexpr int kSamplesLog2 = 9;
+constexpr int kSamples = 1 << kSamplesLog2;  // sample keys per (workgroup, split) and chunk
+constexpr int kMaxSampleChunks = 4;
+constexpr int kKeep = 128;         // sample values kept per query between chunks
+// Sampling plan.  The threshold of a (query, split) is the sample's j-th
+// largest, j = m k (samples) / n: about m k n_s / n keys of the split pass
+// it, and the query's candidates hold its true top-k when at least k of them
+// pass the largest split threshold.  The fraction of the split above the
+// sample's j-th largest is Beta-distributed; it falls below 1/m of its mean
+// -- too few candidates, so the query goes to the slow repair -- with
+// probability P(Poisson(j / m) >= j).  One repaired query costs a whole
+// prefix scored and selected by one workgroup, a latency tail of hundreds of
+// microseconds, so the plan keeps the expected repairs per call (T S P)
+// below kMaxRepairs.
+constexpr double kMaxRepairs = 0.01;
+constexpr float kMargins[] = {2.0f, 2.5f, 3.0f, 4.0f};
+
+// P(X >= j) for X ~ Poisson(lambda), j >= 1 (host).
+double poisson_tail(double lambda, int j) {
+  double logp = -lambda + j * __builtin_log(lambda) - __builtin_lgamma(j + 1.0);
+  double term = __builtin_exp(logp), sum = 0.0;
+  for (int x = j; x < j + 4096 && term > sum * 1e-12; ++x) {
+    sum += term;
+    term *= lambda / (x + 1);
+  }
+  return sum;
+}
 constexpr int kRepairSlots = 64;   // repair workgroups (one scratch row each)
 constexpr int kRepThreads = 512;
 constexpr int kTopkThreadsSel = 1024;
@@ -111,6 +129,7 @@ struct PrefillArgs {
   int32_t* cnt;          // [rows, S]
   float* tau;            // [rows*S]
   float margin;          // threshold sample rank = margin * k * samples / n_q
+  int32_t nch;           // sample chunks (1 .. kMaxSampleChunks)
 };
 
 // Buffer resource over [base, base + bytes): loads past the end read zero,
@@ -182,6 +201,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
   __shared__ __attribute__((aligned(16))) uint8_t tb1[BUF_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t tb2[BUF_BYTES];
   __shared__ float sk_tile[2][32];  // fp8 key scales of the two sample stage slots
+  __shared__ __attribute__((aligned(16))) uint16_t kept[kPWaves][QPW][kKeep];  // between sample chunks
   // fp8 key scales of the tile in buffer 0, 1, 2 (one copy per wave).
   __shared__ float sk0[DT == kFP8 ? kPWaves : 1][kTileKeys];
   __shared__ float sk1[DT == kFP8 ? kPWaves : 1][kTileKeys];
@@ -306,9 +326,21 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
   }
 
   // ---- 1. sample pass: thresholds per (query, split).
+  //
+  // The split's sample is a.nch (1, 2 or 4) chunks of kSamples strided keys
+  // (sample i of chunk c is key s_begin + ((i nch + c) len) / (kSamples nch),
+  // so every chunk spreads over the whole split).  Between chunks each query keeps
+  // the kKeep largest sample values seen so far (16-bit key prefixes) in
+  // LDS; the threshold is the j-th largest over all chunks, j <= kKeep
+  // (with one chunk, j <= kSamples).
   const int64_t len = s_end - s_begin;
+  const int nch = a.nch;
+  const int nch_log2 = nch == 4 ? 2 : (nch == 2 ? 1 : 0);   // nch is 1, 2 or 4
+  const int msamp_log2 = kSamplesLog2 + nch_log2;            // sample keys per split: 2^msamp_log2
   uint16_t* smp = reinterpret_cast<uint16_t*>(wave < 2 ? tb0 : tb1) + (wave & 1) * QPW * kSamples;  // [QPW][kSamples]
   float tau_slot[NS];
+  int nvs_acc = 0;  // valid samples of this lane's query group so far
+  for (int ch = 0; ch < nch; ++ch) {
   // Sample tiles (32 keys) are staged in buffer 2 (two stage slots); each
   // tile's scores go straight to the sample area (sample m of query qw at
   // smp[qw][m]).  The strided sample rows are loaded four tiles ahead into
@@ -321,10 +353,13 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
       uint4 v0, v1;
       float sk;
     };
+    auto sample_key = [&](int m) -> int64_t {
+      return len > 0 ? s_begin + (((static_cast<int64_t>(m) << nch_log2) + ch) * len >> msamp_log2) : -1;
+    };
     auto sload = [&](int st) -> SReg {
       SReg r;
       const int m_ld = st * 32 + kr;
-      const int64_t key_ld = (len > 0 && st < kSamples / 32) ? s_begin + (static_cast<int64_t>(m_ld) * len) / kSamples : -1;
+      const int64_t key_ld = st < kSamples / 32 ? sample_key(m_ld) : -1;
       const int64_t row = seq * a.L + (key_ld < 0 ? 0 : key_ld);
       if constexpr (DT == kBF16) {
         const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k) + row * kD + 16 * part);
@@ -354,7 +389,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
       float out[NS];
       score_tile(stage, 0, out);
       const int m = st * 32 + colr;
-      const int64_t key = len > 0 ? s_begin + (static_cast<int64_t>(m) * len) / kSamples : -1;
+      const int64_t key = sample_key(m);
       float skv = 1.f;
       if constexpr (DT == kFP8) skv = sk_tile[st & 1][colr];
 #pragma unroll
@@ -383,15 +418,15 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
     __syncthreads();
   }
   {
-    // Lanes [g*LPQ, (g+1)*LPQ) find the j-th largest sample of query g:
-    // bitwise search for the largest key v with #{samples >= v} >= j.
+    // Lanes [g*LPQ, (g+1)*LPQ) serve query g: VPL of this chunk's samples
+    // and KPL of the kept values per lane, as 16-bit keys two per register.
     constexpr int LPQ = kWave / QPW;
     constexpr int VPL = kSamples / LPQ;
+    constexpr int KPL = kKeep / LPQ;
     const int g = lane / LPQ;
     const int lg = lane % LPQ;
-    // This lane's VPL 16-bit sample keys, two per register.
-    static_assert(VPL % 8 == 0, "samples are read 8 at a time");
-    uint32_t kv[VPL / 2];
+    static_assert(VPL % 8 == 0 && KPL % 2 == 0, "samples are read 8, kept values 2 at a time");
+    uint32_t kv[VPL / 2], kk[KPL / 2];
     int nvs = 0;
 #pragma unroll
     for (int e = 0; e < VPL / 8; ++e) {
@@ -401,48 +436,96 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
       kv[4 * e + 2] = w4.z;
       kv[4 * e + 3] = w4.w;
     }
+    uint16_t* kq = &kept[wave][g][0];
+#pragma unroll
+    for (int e = 0; e < KPL / 2; ++e) kk[e] = ch > 0 ? reinterpret_cast<const uint32_t*>(kq + lg * KPL)[e] : 0u;
 #pragma unroll
     for (int e = 0; e < VPL / 2; ++e)
       nvs += ((kv[e] & 0xFFFFu) != 0 ? 1 : 0) + ((kv[e] >> 16) != 0 ? 1 : 0);
 #pragma unroll
     for (int o = LPQ / 2; o >= 1; o >>= 1) nvs += __shfl_xor(nvs, o, kWave);
+    nvs_acc += nvs;
     const int t = tw0 + g;
-    const int64_t nq = static_cast<int64_t>(a.L) - a.T + t + 1;
-    // j = ceil(margin * k * nvs / n_q)
-    const double jd = static_cast<double>(a.margin) * a.k_top * nvs / static_cast<double>(nq > 0 ? nq : 1);
-    const int j = static_cast<int>(jd) + 1;
-    // Padding queries (t >= T) never pass; a query whose split holds fewer
-    // sampled keys than j keeps every key of the split (tau = -inf).
-    float tq = t < a.T ? -__builtin_inff() : __builtin_inff();
-    if (t < a.T && nvs > 0 && j < nvs) {
-      uint32_t v = 0;
-      for (int bit = 15; bit >= 0; --bit) {
-        const uint32_t cand = v | (1u << bit);
-        int c = 0;
+    const bool last = ch + 1 == nch;
+    // Rank searched: kKeep between chunks; after the last, j = ceil(margin
+    // k nvs / n_q) (at most kKeep over several chunks).  Padding queries (t
+    // >= T) never pass; a query whose split holds fewer sampled keys than j
+    // keeps every key of the split (tau = -inf).
+    int rank = kKeep;
+    bool search = true;
+    if (last) {
+      const int64_t nq = static_cast<int64_t>(a.L) - a.T + t + 1;
+      const double jd = static_cast<double>(a.margin) * a.k_top * nvs_acc / static_cast<double>(nq > 0 ? nq : 1);
+      rank = static_cast<int>(jd) + 1;
+      if (nch > 1 && rank > kKeep) rank = kKeep;
+      search = t < a.T && nvs_acc > 0 && rank < nvs_acc;
+    }
+    // The largest 16-bit value v with #{values >= v} >= rank (0 when fewer
+    // than rank values are valid): a bitwise search from the top bit.
+    uint32_t v = 0;
+    for (int bit = 15; bit >= 0; --bit) {
+      const uint32_t c = v | (1u << bit);
+      int n = 0;
 #pragma unroll
-        for (int e = 0; e < VPL / 2; ++e)
-          c += ((kv[e] & 0xFFFFu) >= cand ? 1 : 0) + ((kv[e] >> 16) >= cand ? 1 : 0);
+      for (int e = 0; e < VPL / 2; ++e) n += ((kv[e] & 0xFFFFu) >= c ? 1 : 0) + ((kv[e] >> 16) >= c ? 1 : 0);
 #pragma unroll
-        for (int o = LPQ / 2; o >= 1; o >>= 1) c += __shfl_xor(c, o, kWave);
-        if (c >= j) v = cand;
+      for (int e = 0; e < KPL / 2; ++e) n += ((kk[e] & 0xFFFFu) >= c ? 1 : 0) + ((kk[e] >> 16) >= c ? 1 : 0);
+#pragma unroll
+      for (int o = LPQ / 2; o >= 1; o >>= 1) n += __shfl_xor(n, o, kWave);
+      if (n >= rank && search) v = c;
+    }
+    if (!last) {
+      // Keep the kKeep largest: every value above v, then copies of v.
+      int gt = 0;
+#pragma unroll
+      for (int e = 0; e < VPL / 2; ++e) gt += ((kv[e] & 0xFFFFu) > v ? 1 : 0) + ((kv[e] >> 16) > v ? 1 : 0);
+#pragma unroll
+      for (int e = 0; e < KPL / 2; ++e) gt += ((kk[e] & 0xFFFFu) > v ? 1 : 0) + ((kk[e] >> 16) > v ? 1 : 0);
+      int off = gt;  // inclusive scan over the group's lanes
+#pragma unroll
+      for (int o = 1; o < LPQ; o <<= 1) {
+        const int y = __shfl_up(off, o, kWave);
+        if (lg >= o) off += y;
       }
-      // The smallest float whose key has top bits v: every sample counted
-      // above scores at least this.
-      const uint32_t key = v << 16;
-      const uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
-      tq = __uint_as_float(u);
-    }
-    // Broadcast: every lane needs the tau of its slots' queries.
-    float tau_q[QPW];
+      const int total_gt = __shfl(off, g * LPQ + LPQ - 1, kWave);
+      off -= gt;
+      __builtin_amdgcn_wave_barrier();  // every lane has read the kept values
 #pragma unroll
-    for (int qq = 0; qq < QPW; ++qq) tau_q[qq] = __shfl(tq, qq * LPQ, kWave);
+      for (int e = 0; e < VPL / 2; ++e) {
+        const uint32_t x0 = kv[e] & 0xFFFFu, x1 = kv[e] >> 16;
+        if (x0 > v) kq[off++] = static_cast<uint16_t>(x0);
+        if (x1 > v) kq[off++] = static_cast<uint16_t>(x1);
+      }
 #pragma unroll
-    for (int sl = 0; sl < NS; ++sl) {
-      const int qw0 = slot_query<HPQ>(sl, 0), qw1 = slot_query<HPQ>(sl, 1);
-      tau_slot[sl] = hf ? tau_q[qw1] : tau_q[qw0];
+      for (int e = 0; e < KPL / 2; ++e) {
+        const uint32_t x0 = kk[e] & 0xFFFFu, x1 = kk[e] >> 16;
+        if (x0 > v) kq[off++] = static_cast<uint16_t>(x0);
+        if (x1 > v) kq[off++] = static_cast<uint16_t>(x1);
+      }
+      for (int i = total_gt + lg; i < kKeep; i += LPQ) kq[i] = static_cast<uint16_t>(v);
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      float tq = t < a.T ? -__builtin_inff() : __builtin_inff();
+      if (search) {
+        // The smallest float whose key has top bits v: every sample counted
+        // above scores at least this.
+        const uint32_t key = v << 16;
+        const uint32_t u = (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
+        tq = __uint_as_float(u);
+      }
+      // Broadcast: every lane needs the tau of its slots' queries.
+      float tau_q[QPW];
+#pragma unroll
+      for (int qq = 0; qq < QPW; ++qq) tau_q[qq] = __shfl(tq, qq * LPQ, kWave);
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) {
+        const int qw0 = slot_query<HPQ>(sl, 0), qw1 = slot_query<HPQ>(sl, 1);
+        tau_slot[sl] = hf ? tau_q[qw1] : tau_q[qw0];
+      }
+      if (lg == 0 && t < a.T) a.tau[(seq * a.T + t) * a.S + split] = tq;
     }
-    if (lg == 0 && t < a.T) a.tau[(seq * a.T + t) * a.S + split] = tq;
   }
+  }  // chunks
   __syncthreads();  // sample area is reused as tile buffers below
 
   // ---- 2. full pass over [s_begin, s_end): append scores >= tau.
@@ -1076,7 +1159,7 @@ __global__ __launch_bounds__(kRepThreads) void prefill_repair_kernel(
 }
 
 struct PrefillPlan {
-  int32_t S, cap, nqt, qwg;
+  int32_t S, cap, nqt, qwg, nch;
   float margin;
   int64_t chunk;
   size_t off_cnt, off_tau, off_fail, off_list, off_scratch, total;
@@ -1103,7 +1186,42 @@ PrefillPlan plan_prefill(const Shape& s, int32_t nh, int32_t k) {
   // queries: 2.5x + 16 sigma + 512 leaves overflow (then repair) very rare.
   const double nmin = static_cast<double>(s.L - s.T + 1);
   const double share = static_cast<double>(p.chunk) / nmin < 1.0 ? static_cast<double>(p.chunk) / nmin : 1.0;
-  p.margin = kLowMargin * static_cast<double>(k) * kSamples >= kMinSampleRank * s.L ? kLowMargin : kSampleMargin;
+  // Margin and sample chunks: the cheapest (candidates appended and
+  // selected, 2 m k / L per key, against sample keys scored, c kSamples per
+  // split key) whose expected repairs stay below kMaxRepairs; if none does,
+  // the one with the fewest.  The sample rank is taken for the worst split:
+  // the last one, of which the first query's prefix covers the least.
+  {
+    const double cover = static_cast<double>(s.L - s.T + 1 - (p.S - 1) * p.chunk) / static_cast<double>(p.chunk);
+    const double f = cover < 0.25 ? 0.25 : (cover > 1.0 ? 1.0 : cover);
+    const double nrows = static_cast<double>(s.batch) * s.T * p.S;
+    double best_cost = 1e300, best_rep = 1e300;
+    bool found = false;
+    p.margin = kMargins[0];
+    p.nch = 1;
+    for (int c = 1; c <= kMaxSampleChunks; c *= 2) {  // 1, 2 or 4: a power-of-two sample count
+      if (c > 1 && static_cast<int64_t>(c) * kSamples > p.chunk) break;
+      for (const float m : kMargins) {
+        const double j = static_cast<double>(m) * k * c * kSamples / static_cast<double>(s.L);
+        if (c > 1 && j > kKeep) continue;
+        const int jw = static_cast<int>(f * j) + 1;
+        const double rep = nrows * poisson_tail(jw / static_cast<double>(m), jw);
+        const double cost = 2.0 * m * k / s.L + static_cast<double>(c) * kSamples / static_cast<double>(p.chunk);
+        if (rep <= kMaxRepairs) {
+          if (!found || cost < best_cost) {
+            best_cost = cost;
+            p.margin = m;
+            p.nch = c;
+          }
+          found = true;
+        } else if (!found && rep < best_rep) {
+          best_rep = rep;
+          p.margin = m;
+          p.nch = c;
+        }
+      }
+    }
+  }
   const double mean = p.margin * k * share;
   int64_t cap = static_cast<int64_t>(2.5 * mean + 16.0 * __builtin_sqrt(mean) + 512.0);
   cap = cap < p.chunk ? cap : p.chunk;
@@ -1153,7 +1271,7 @@ hipError_t launch_prefill_score_topk(const Shape& s, int32_t nh, const int32_t* 
   PrefillArgs args{q, q_scale, w, kk, k_scale, heads, nh, s.L, s.T, s.H, k, pl.S, pl.chunk,
                    pl.cap, pl.nqt, s.batch, reinterpret_cast<uint2*>(base),
                    reinterpret_cast<int32_t*>(base + pl.off_cnt),
-                   reinterpret_cast<float*>(base + pl.off_tau), pl.margin};
+                   reinterpret_cast<float*>(base + pl.off_tau), pl.margin, pl.nch};
   int32_t* fail_count = reinterpret_cast<int32_t*>(base + pl.off_fail);
   int32_t* fail_list = reinterpret_cast<int32_t*>(base + pl.off_list);
   float* scratch = reinterpret_cast<float*>(base + pl.off_scratch);

@@ -63,6 +63,9 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_score_kernel(
   out[r * kprime + c] = acc;
 }
 
+#ifndef MISA_RERANK_NTW
+#define MISA_RERANK_NTW 2
+#endif
 constexpr int kRRThreads = 256;
 constexpr int kRRWaves = kRRThreads / kWave;
 constexpr int kMaxKprime = 8192;
@@ -197,137 +200,6 @@ __global__ __launch_bounds__(kRRThreads) void rerank_gather_kernel(
   }
 }
 
-// Gathers through LDS: a lane-per-candidate gather (lane l reads 16 bytes of
-// candidate l%32's row per instruction) touches 32 rows per instruction and
-// is limited by the address unit, not by memory.  Here each load instruction
-// instead covers whole rows -- 64 lanes = RPI rows of CPR 16-byte chunks --
-// and lands directly in LDS (buffer-to-LDS loads); the MFMA B operands are
-// then read from LDS.  Chunk c of tile row j sits at chunk position
-// c ^ (j % CPR), so the B reads (32 rows, one chunk each) hit distinct banks.
-// Workgroup (chunk, row): the query's head rows are staged once in LDS; wave
-// w scores NTW tiles of 32 candidates per round, all of a round's loads in
-// flight before its first MFMA, and its tiles are private (no barrier).
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rr_rsrc(const void* base, int32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-__device__ __forceinline__ void rr_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
-}
-__device__ __forceinline__ void rr_vmcnt0() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-template <int DT, int RT, int NTW>
-__global__ __launch_bounds__(kRRThreads) void rerank_lds_kernel(
-    const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
-    const void* __restrict__ k, const float* __restrict__ k_scale,
-    const int32_t* __restrict__ cand, int32_t kprime, int32_t L, int32_t T, int32_t H,
-    int32_t per_wg, float* __restrict__ out) {
-  constexpr int ROWB = kD * (DT == kBF16 ? 2 : 1);  // key row bytes
-  constexpr int CPR = ROWB / 16;                     // 16-byte chunks per row
-  constexpr int RPI = kWave / CPR;                   // rows per load instruction
-  constexpr int TILE = 32 * ROWB;                    // one 32-candidate tile
-  __shared__ __attribute__((aligned(16))) uint8_t keys[kRRWaves][NTW][TILE];
-  __shared__ __attribute__((aligned(16))) uint8_t qst[kMaxHeads * ROWB];
-  __shared__ float wst[kMaxHeads];
-  const int64_t seq = blockIdx.z;
-  const int64_t r = seq * T + blockIdx.y;
-  const int64_t pos = static_cast<int64_t>(L) - T + blockIdx.y;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int lane = lane_id();
-  const int hf = lane >> 5;
-  const int col = lane & 31;
-
-  // Query head rows and weights -> LDS.
-  const uint8_t* qrow = static_cast<const uint8_t*>(q) + r * H * ROWB;
-  for (int i = threadIdx.x; i < kMaxHeads * CPR; i += kRRThreads)
-    reinterpret_cast<uint4*>(qst)[i] = i < H * CPR ? reinterpret_cast<const uint4*>(qrow)[i] : make_uint4(0, 0, 0, 0);
-  const float sq = (DT == kFP8) ? q_scale[r] : 1.f;
-  if (threadIdx.x < kMaxHeads) wst[threadIdx.x] = threadIdx.x < H ? w[r * H + threadIdx.x] * sq : 0.f;
-  __syncthreads();
-  CandScorer<DT, RT> cs;
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int j = rt * 32 + col;
-    const uint8_t* src = qst + j * ROWB;
-    if constexpr (DT == kBF16) {
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) cs.a16[rt][ks] = as_bf16x8(reinterpret_cast<const uint4*>(src + 128 * hf)[ks]);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const uint4 lo = reinterpret_cast<const uint4*>(src + 64 * hf)[2 * ks];
-        const uint4 hi = reinterpret_cast<const uint4*>(src + 64 * hf)[2 * ks + 1];
-        cs.a8[rt][ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) cs.wl[rt][i] = wst[rt * 32 + 8 * (i / 4) + 4 * hf + (i % 4)];
-  }
-
-  const __amdgpu_buffer_rsrc_t rk =
-      rr_rsrc(static_cast<const uint8_t*>(k) + seq * static_cast<int64_t>(L) * ROWB, L * ROWB);
-  const int32_t* crow = cand + r * kprime;
-  float* orow = out + r * kprime;
-  const int c_wg = blockIdx.x * per_wg;
-  const int c_end = min(c_wg + per_wg, kprime);
-  constexpr int kRoundStep = kRRWaves * NTW * 32;
-  // This lane's candidate of each tile of a round (lanes l and l+32 share
-  // one).  The next round's are loaded while this round's rows are gathered.
-  int32_t svn[NTW];
-  auto load_ids = [&](int c_round) __attribute__((always_inline)) {
-#pragma unroll
-    for (int u = 0; u < NTW; ++u) {
-      const int c = c_round + 32 * u + col;
-      svn[u] = c < c_end ? crow[c] : -1;
-    }
-  };
-  if (c_wg + wave * NTW * 32 < c_end) load_ids(c_wg + wave * NTW * 32);
-  for (int c_round = c_wg + wave * NTW * 32; c_round < c_end; c_round += kRoundStep) {
-    int32_t sid[NTW];
-    float skv[NTW];
-#pragma unroll
-    for (int u = 0; u < NTW; ++u) sid[u] = (svn[u] >= 0 && svn[u] <= pos) ? svn[u] : -1;
-    if (c_round + kRoundStep < c_end) load_ids(c_round + kRoundStep);
-    // The tiles' key scales, and their rows into this wave's LDS slots.
-#pragma unroll
-    for (int u = 0; u < NTW; ++u) skv[u] = (DT == kFP8 && sid[u] >= 0) ? k_scale[seq * L + sid[u]] : 1.f;
-#pragma unroll
-    for (int u = 0; u < NTW; ++u) {
-#pragma unroll
-      for (int i = 0; i < 32 / RPI; ++i) {
-        const int j = i * RPI + lane / CPR;        // tile row of this lane's chunk
-        const int pc = lane % CPR;                 // its chunk position in LDS
-        const int lc = pc ^ (j % CPR);             // the row chunk stored there
-        const int32_t sj = __shfl(sid[u], j, kWave);
-        const uint32_t voff = static_cast<uint32_t>(sj < 0 ? 0 : sj) * ROWB + 16u * lc;
-        rr_load16_lds(rk, &keys[wave][u][i * 1024], voff);
-      }
-    }
-    rr_vmcnt0();  // this wave's rows have landed (its LDS slots are private)
-#pragma unroll
-    for (int u = 0; u < NTW; ++u) {
-      typename CandScorer<DT, RT>::KeyB kb;
-      const uint8_t* trow = &keys[wave][u][col * ROWB];
-      if constexpr (DT == kBF16) {
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) kb.b[ks] = reinterpret_cast<const uint4*>(trow)[(8 * hf + ks) ^ (col % CPR)];
-      } else {
-#pragma unroll
-        for (int uu = 0; uu < 4; ++uu) kb.b[uu] = reinterpret_cast<const uint4*>(trow)[(4 * hf + uu) ^ (col % CPR)];
-      }
-      const float v = cs.compute(kb) * skv[u];
-      const int c = c_round + 32 * u + col;
-      if (lane < 32 && c < c_end) orow[c] = sid[u] >= 0 ? v : -__builtin_inff();
-    }
-    // The next round's loads overwrite these slots: reads must be done.
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  }
-}
-
 // Top-k of one query's k' (score, candidate) list, in one workgroup: the
 // list is read once into registers, a digit histogram (LDS) gives the
 // threshold digit b*; each wave's entries above b* take one run of the
@@ -358,19 +230,16 @@ struct LSelSmem {
   uint32_t dmin, dmax;
 };
 
+// The k best of one query's list: srow/crow its k' scores and candidates,
+// pos the query's position (candidates outside [0, pos] are invalid), out /
+// out_s its k output slots.  All kLSThreads threads of the workgroup call.
 template <int kLSThreads>
-__global__ __launch_bounds__(kLSThreads, kLSThreads == 256 ? 4 : 1) void list_select_kernel(
-    const float* __restrict__ sc, const int32_t* __restrict__ cand, int32_t kprime, int32_t L,
-    int32_t T, int32_t k, int32_t* __restrict__ idx, float* __restrict__ scores_out) {
+__device__ __forceinline__ void list_select_row(const float* __restrict__ srow,
+                                                const int32_t* __restrict__ crow, int32_t kprime,
+                                                int64_t pos, int32_t k, int32_t* __restrict__ out,
+                                                float* __restrict__ out_s, LSelSmem<kLSThreads>& sm) {
   constexpr int kLSPer = kMaxKprime / kLSThreads;  // list entries per thread (bits of a 32-bit mask)
   static_assert(kLSPer <= 32, "entry slots are bits of a 32-bit mask");
-  __shared__ LSelSmem<kLSThreads> sm;
-  const int64_t r = static_cast<int64_t>(blockIdx.y) * T + blockIdx.x;
-  const int64_t pos = static_cast<int64_t>(L) - T + blockIdx.x;
-  const float* srow = sc + r * kprime;
-  const int32_t* crow = cand + r * kprime;
-  int32_t* out = idx + r * k;
-  float* out_s = scores_out ? scores_out + r * k : nullptr;
   for (int b = threadIdx.x; b < kLSBins; b += kLSThreads) sm.hist[b] = 0;
   if (threadIdx.x == 0) {
     sm.dmin = 0xFFFFFFFFu;
@@ -522,6 +391,169 @@ __global__ __launch_bounds__(kLSThreads, kLSThreads == 256 ? 4 : 1) void list_se
   }
 }
 
+template <int kLSThreads>
+__global__ __launch_bounds__(kLSThreads, kLSThreads == 256 ? 4 : 1) void list_select_kernel(
+    const float* __restrict__ sc, const int32_t* __restrict__ cand, int32_t kprime, int32_t L,
+    int32_t T, int32_t k, int32_t* __restrict__ idx, float* __restrict__ scores_out) {
+  __shared__ LSelSmem<kLSThreads> sm;
+  const int64_t r = static_cast<int64_t>(blockIdx.y) * T + blockIdx.x;
+  const int64_t pos = static_cast<int64_t>(L) - T + blockIdx.x;
+  list_select_row<kLSThreads>(sc + r * kprime, cand + r * kprime, kprime, pos, k, idx + r * k,
+                              scores_out ? scores_out + r * k : nullptr, sm);
+}
+
+// Gathers through LDS: a lane-per-candidate gather (lane l reads 16 bytes of
+// candidate l%32's row per instruction) touches 32 rows per instruction and
+// is limited by the address unit, not by memory.  Here each load instruction
+// instead covers whole rows -- 64 lanes = RPI rows of CPR 16-byte chunks --
+// and lands directly in LDS (buffer-to-LDS loads); the MFMA B operands are
+// then read from LDS.  Chunk c of tile row j sits at chunk position
+// c ^ (j % CPR), so the B reads (32 rows, one chunk each) hit distinct banks.
+// Workgroup (chunk, row): the query's head rows are staged once in LDS; wave
+// w scores NTW tiles of 32 candidates per round, all of a round's loads in
+// flight before its first MFMA, and its tiles are private (no barrier).
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rr_rsrc(const void* base, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void rr_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void rr_vmcnt0() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int DT, int NTW>
+struct RerankScoreSmem {
+  static constexpr int ROWB = kD * (DT == kBF16 ? 2 : 1);
+  alignas(16) uint8_t keys[kRRWaves][NTW][32 * ROWB];
+  alignas(16) uint8_t qst[kMaxHeads * ROWB];
+  float wst[kMaxHeads];
+};
+
+// FUSED (one workgroup per query, per_wg >= kprime): after scoring, the same
+// workgroup selects the query's k best from its scores (re-read from L2; the
+// score phase's LDS is reused) and writes idx / scores_out, so no list-select
+// launch follows and the scores never make the round trip to HBM.
+template <int DT, int RT, int NTW, bool FUSED>
+__global__ __launch_bounds__(kRRThreads) void rerank_lds_kernel(
+    const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const void* __restrict__ k, const float* __restrict__ k_scale,
+    const int32_t* __restrict__ cand, int32_t kprime, int32_t L, int32_t T, int32_t H,
+    int32_t per_wg, float* __restrict__ out, int32_t k_top, int32_t* __restrict__ idx,
+    float* __restrict__ scores_out) {
+  constexpr int ROWB = kD * (DT == kBF16 ? 2 : 1);  // key row bytes
+  constexpr int CPR = ROWB / 16;                     // 16-byte chunks per row
+  constexpr int RPI = kWave / CPR;                   // rows per load instruction
+  __shared__ union Smem {
+    RerankScoreSmem<DT, NTW> score;
+    LSelSmem<kRRThreads> sel;
+  } smem;
+  auto& keys = smem.score.keys;
+  uint8_t* qst = smem.score.qst;
+  float* wst = smem.score.wst;
+  const int64_t seq = blockIdx.z;
+  const int64_t r = seq * T + blockIdx.y;
+  const int64_t pos = static_cast<int64_t>(L) - T + blockIdx.y;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = lane_id();
+  const int hf = lane >> 5;
+  const int col = lane & 31;
+
+  // Query head rows and weights -> LDS.
+  const uint8_t* qrow = static_cast<const uint8_t*>(q) + r * H * ROWB;
+  for (int i = threadIdx.x; i < kMaxHeads * CPR; i += kRRThreads)
+    reinterpret_cast<uint4*>(qst)[i] = i < H * CPR ? reinterpret_cast<const uint4*>(qrow)[i] : make_uint4(0, 0, 0, 0);
+  const float sq = (DT == kFP8) ? q_scale[r] : 1.f;
+  if (threadIdx.x < kMaxHeads) wst[threadIdx.x] = threadIdx.x < H ? w[r * H + threadIdx.x] * sq : 0.f;
+  __syncthreads();
+  CandScorer<DT, RT> cs;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int j = rt * 32 + col;
+    const uint8_t* src = qst + j * ROWB;
+    if constexpr (DT == kBF16) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) cs.a16[rt][ks] = as_bf16x8(reinterpret_cast<const uint4*>(src + 128 * hf)[ks]);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint4 lo = reinterpret_cast<const uint4*>(src + 64 * hf)[2 * ks];
+        const uint4 hi = reinterpret_cast<const uint4*>(src + 64 * hf)[2 * ks + 1];
+        cs.a8[rt][ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cs.wl[rt][i] = wst[rt * 32 + 8 * (i / 4) + 4 * hf + (i % 4)];
+  }
+
+  const __amdgpu_buffer_rsrc_t rk =
+      rr_rsrc(static_cast<const uint8_t*>(k) + seq * static_cast<int64_t>(L) * ROWB, L * ROWB);
+  const int32_t* crow = cand + r * kprime;
+  float* orow = out + r * kprime;
+  const int c_wg = blockIdx.x * per_wg;
+  const int c_end = min(c_wg + per_wg, kprime);
+  constexpr int kRoundStep = kRRWaves * NTW * 32;
+  // This lane's candidate of each tile of a round (lanes l and l+32 share
+  // one).  The next round's are loaded while this round's rows are gathered.
+  int32_t svn[NTW];
+  auto load_ids = [&](int c_round) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) {
+      const int c = c_round + 32 * u + col;
+      svn[u] = c < c_end ? crow[c] : -1;
+    }
+  };
+  if (c_wg + wave * NTW * 32 < c_end) load_ids(c_wg + wave * NTW * 32);
+  for (int c_round = c_wg + wave * NTW * 32; c_round < c_end; c_round += kRoundStep) {
+    int32_t sid[NTW];
+    float skv[NTW];
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) sid[u] = (svn[u] >= 0 && svn[u] <= pos) ? svn[u] : -1;
+    if (c_round + kRoundStep < c_end) load_ids(c_round + kRoundStep);
+    // The tiles' key scales, and their rows into this wave's LDS slots.
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) skv[u] = (DT == kFP8 && sid[u] >= 0) ? k_scale[seq * L + sid[u]] : 1.f;
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) {
+#pragma unroll
+      for (int i = 0; i < 32 / RPI; ++i) {
+        const int j = i * RPI + lane / CPR;        // tile row of this lane's chunk
+        const int pc = lane % CPR;                 // its chunk position in LDS
+        const int lc = pc ^ (j % CPR);             // the row chunk stored there
+        const int32_t sj = __shfl(sid[u], j, kWave);
+        const uint32_t voff = static_cast<uint32_t>(sj < 0 ? 0 : sj) * ROWB + 16u * lc;
+        rr_load16_lds(rk, &keys[wave][u][i * 1024], voff);
+      }
+    }
+    rr_vmcnt0();  // this wave's rows have landed (its LDS slots are private)
+#pragma unroll
+    for (int u = 0; u < NTW; ++u) {
+      typename CandScorer<DT, RT>::KeyB kb;
+      const uint8_t* trow = &keys[wave][u][col * ROWB];
+      if constexpr (DT == kBF16) {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) kb.b[ks] = reinterpret_cast<const uint4*>(trow)[(8 * hf + ks) ^ (col % CPR)];
+      } else {
+#pragma unroll
+        for (int uu = 0; uu < 4; ++uu) kb.b[uu] = reinterpret_cast<const uint4*>(trow)[(4 * hf + uu) ^ (col % CPR)];
+      }
+      const float v = cs.compute(kb) * skv[u];
+      const int c = c_round + 32 * u + col;
+      if (lane < 32 && c < c_end) orow[c] = sid[u] >= 0 ? v : -__builtin_inff();
+    }
+    // The next round's loads overwrite these slots: reads must be done.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  }
+  if constexpr (FUSED) {
+    __syncthreads();  // every score is written; the score phase's LDS is free
+    list_select_row<kRRThreads>(orow, crow, kprime, pos, k_top, idx + r * k_top,
+                                scores_out ? scores_out + r * k_top : nullptr, smem.sel);
+  }
+}
+
 }  // namespace
 
 size_t rerank_ws_bytes(const Shape& s, int32_t kprime) {
@@ -534,6 +566,7 @@ hipError_t launch_rerank(const Shape& s, int32_t kprime, int32_t k, const void* 
                          hipStream_t st) {
   const int64_t rows = static_cast<int64_t>(s.batch) * s.T;
   float* sc = static_cast<float*>(ws);
+  bool fused = false;  // the score kernel also took each query's top-k
   if (s.dtype != kF32) {
     const bool two = s.H > 32;
     // Two tiles of 32 candidates in flight per wave (fp8: 64 B per lane
@@ -541,7 +574,7 @@ hipError_t launch_rerank(const Shape& s, int32_t kprime, int32_t k, const void* 
     // workgroups per CU, up to 32, so the query rows staged into LDS once
     // per workgroup are reused over many candidate tiles on long prefill
     // lists, while a short decode batch still spreads over the chip.
-    constexpr int kNtw = 2;
+    constexpr int kNtw = MISA_RERANK_NTW;
     int rounds = 32;
     while (rounds > 1) {
       const int64_t per = static_cast<int64_t>(kRRWaves) * 32 * kNtw * rounds;
@@ -552,9 +585,12 @@ hipError_t launch_rerank(const Shape& s, int32_t kprime, int32_t k, const void* 
     const int64_t seq_bytes = static_cast<int64_t>(s.L) * kD * (s.dtype == kBF16 ? 2 : 1);
     if (seq_bytes < (int64_t{1} << 31)) {
       dim3 g((kprime + per_wg - 1) / per_wg, s.T, s.batch);
-#define RG(DT, RT, NTW) rerank_lds_kernel<DT, RT, NTW><<<g, kRRThreads, 0, st>>>(q, q_scale, w, kk, k_scale, cand, kprime, s.L, s.T, s.H, per_wg, sc)
-      if (s.dtype == kBF16) { if (two) RG(kBF16, 2, kNtw); else RG(kBF16, 1, kNtw); }
-      else { if (two) RG(kFP8, 2, kNtw); else RG(kFP8, 1, kNtw); }
+      fused = per_wg >= kprime;
+#define RG(DT, RT, NTW, F) rerank_lds_kernel<DT, RT, NTW, F><<<g, kRRThreads, 0, st>>>(q, q_scale, w, kk, k_scale, cand, kprime, s.L, s.T, s.H, per_wg, sc, k, idx, scores_out)
+#define RGF(DT, RT) if (fused) RG(DT, RT, kNtw, true); else RG(DT, RT, kNtw, false);
+      if (s.dtype == kBF16) { if (two) { RGF(kBF16, 2) } else { RGF(kBF16, 1) } }
+      else { if (two) { RGF(kFP8, 2) } else { RGF(kFP8, 1) } }
+#undef RGF
 #undef RG
     } else {
       // A sequence's keys beyond the 32-bit reach of a buffer descriptor:
@@ -573,7 +609,7 @@ hipError_t launch_rerank(const Shape& s, int32_t kprime, int32_t k, const void* 
                                                              kprime, sc, s.L, s.T, s.H);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || fused) return e;
   dim3 g2(s.T, s.batch);
   if (rows >= 1024)
     list_select_kernel<256><<<g2, 256, 0, st>>>(sc, cand, kprime, s.L, s.T, k, idx, scores_out);

@@ -67,6 +67,22 @@ SMALL = {
                             dtype=synth.BF16, needles=4, seed=34),
     "mq_h16_t3": synth.small("mq_h16_t3", batch=2, L=2000, T=3, H=64, h=16, B=64, k=128, kprime=256,
                              dtype=synth.FP8_E4M3, needles=4, seed=35),
+    # Small k against L: the prefill threshold is sampled in several chunks
+    # (the kept top sample values carried between them).
+    "sample_chunks_bf16": synth.small("sample_chunks_bf16", batch=1, L=16384, T=100, H=64, h=8, B=64,
+                                      k=64, kprime=160, dtype=synth.BF16, needles=8, seed=38),
+    "sample_chunks_fp8": synth.small("sample_chunks_fp8", batch=2, L=12000, T=40, H=64, h=8, B=128,
+                                     k=48, kprime=96, dtype=synth.FP8_E4M3, needles=8, seed=39),
+    # k = 64 of a 64K prefix in eight splits: four sample chunks, and no plan
+    # meets the repair bound, so some queries also go to the repair path.
+    "sample_chunks4_fp8": synth.small("sample_chunks4_fp8", batch=1, L=65536, T=64, H=64, h=8, B=128,
+                                      k=64, kprime=128, dtype=synth.FP8_E4M3, needles=8, seed=40),
+    # 2048 queries: the re-rank gives each query one workgroup and takes its
+    # top-k in the same workgroup (64 or 32 heads, fp8 or bf16).
+    "fused_rerank_fp8": synth.small("fused_rerank_fp8", batch=1, L=4096, T=2048, H=64, h=8, B=128,
+                                    k=128, kprime=512, dtype=synth.FP8_E4M3, needles=16, seed=36),
+    "fused_rerank_bf16_h32": synth.small("fused_rerank_bf16_h32", batch=2, L=3000, T=1024, H=32, h=8,
+                                         B=64, k=100, kprime=300, dtype=synth.BF16, needles=8, seed=37),
     "t_eq_l": synth.small("t_eq_l", batch=1, L=200, T=200, H=64, h=8, B=64, k=64, kprime=96,
                           dtype=synth.BF16, needles=0, seed=24),
     "b1_h16": synth.small("b1_h16", batch=1, L=700, T=9, H=64, h=16, B=1, k=100, kprime=200,
