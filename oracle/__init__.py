@@ -9,7 +9,10 @@ precision, full sorts); this module builds it with g++, loads it with ctypes
 and strings the per-equation functions together per query.  It follows the
 MISA summary page ("MISA: Mixture of Indexer Sparse Attention for Long-Context
 LLM Inference"): Eq. (1)-(2) in "Introduction and Theoretical Foundation",
-Eq. (4), (7)-(10) in "Methodology" 1 and Eq. (11)-(12) in "Methodology" 2.
+Eq. (4), (7)-(10) in "Methodology" 1 and Eq. (11)-(12) in "Methodology" 2,
+and the MISA x HISA combination that "Methodology" 1 ("Key distinction from
+HISA") and "Theoretical and Practical Implications" ("Scalability") describe:
+the Eq. (7) affinities reduced across heads to pick the top-m blocks.
 
 Every function is pinned by tests in ``tests/test_oracle_*.py`` against
 closed forms, brute force, exact-arithmetic cases and the method's own
@@ -61,8 +64,9 @@ def _load():
         lib.orc_token_scores.argtypes = [P, I64, I32, P, P, P, I32, P]
         lib.orc_topk.argtypes = [P, I64, I32, P]
         lib.orc_rerank.argtypes = [P, I32, P, P, I32, P, I32, I32, P, P]
+        lib.orc_block_scores.argtypes = [P, P, I64, I32, I32, I32, P, P, P]
         for f in (lib.orc_decode, lib.orc_pool, lib.orc_expert_scores, lib.orc_top_heads,
-                  lib.orc_token_scores, lib.orc_topk, lib.orc_rerank):
+                  lib.orc_token_scores, lib.orc_topk, lib.orc_rerank, lib.orc_block_scores):
             f.restype = None
         _lib = lib
     return _lib
@@ -111,6 +115,19 @@ def expert_scores(K, pooled, pos: int, B: int, q_t, w_t) -> np.ndarray:
     E = np.empty(H, dtype=np.float64)
     _load().orc_expert_scores(_p(K), _p(pooled), pos, d, B, H, _p(q_t), _p(w_t), _p(E))
     return E
+
+
+def block_scores(K, pooled, pos: int, B: int, q_t, w_t) -> np.ndarray:
+    """MISA x HISA block scores for the query at ``pos``: G [M_t], the Eq. (7)
+    affinities summed over the heads."""
+    K = _c(K, np.float64)
+    pooled = _c(pooled, np.float64)
+    q_t = _c(q_t, np.float64)
+    w_t = _c(w_t, np.float64)
+    H, d = q_t.shape
+    G = np.empty((pos + 1 + B - 1) // B, dtype=np.float64)
+    _load().orc_block_scores(_p(K), _p(pooled), pos, d, B, H, _p(q_t), _p(w_t), _p(G))
+    return G
 
 
 def top_heads(E, h: int) -> np.ndarray:
@@ -188,6 +205,28 @@ class Sequence:
         H = np.asarray(q_t).shape[0]
         I = self.scores(pos, q_t, w_t, np.arange(H, dtype=np.int32))
         return {"scores": I, "idx": topk(I, k)}
+
+    def block_scores(self, pos: int, q_t, w_t) -> np.ndarray:
+        return block_scores(self.K, self.pooled, pos, self.B, q_t, w_t)
+
+    def hisa_tokens(self, pos: int, q_t, w_t, heads, m: int, k: int):
+        """MISA x HISA for one query: the top-m blocks by G (ties: lower
+        block), then Eq. (9) with the given heads over the tokens of those
+        blocks (causal: s <= pos) and the top-k of them (ties: lower token;
+        -1 padding).  Returns dict with G, blocks (ascending), tokens (the
+        candidate tokens, ascending), scores (Eq. (9) of each candidate) and
+        idx (rank order)."""
+        G = self.block_scores(pos, q_t, w_t)
+        blocks = np.sort(topk(G, m))
+        blocks = blocks[blocks >= 0]
+        tokens = np.concatenate([np.arange(b * self.B, min((b + 1) * self.B, pos + 1))
+                                 for b in blocks]).astype(np.int64)
+        I = self.scores(pos, q_t, w_t, heads)
+        cs = I[tokens]
+        sel = topk(cs, k)
+        idx = np.where(sel >= 0, tokens[np.maximum(sel, 0)], -1).astype(np.int32)
+        return {"G": G, "blocks": blocks.astype(np.int32), "tokens": tokens, "scores": cs,
+                "idx": idx}
 
     def misa_dagger(self, pos: int, q_t, w_t, h: int, kprime: int, k: int):
         """Eq. (11)-(12) for one query: dict with E, heads, cand, idx, scores."""

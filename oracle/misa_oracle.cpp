@@ -153,6 +153,39 @@ void orc_expert_scores(const double* K, const double* pooled, int64_t pos, int32
   }
 }
 
+// Block scores of the MISA x HISA combination ("Methodology" 1, "Key
+// distinction from HISA"; "Theoretical and Practical Implications",
+// "Scalability"): the same affinities A_{j,b} = w_j * ReLU(q_j . k~_b) as in
+// Eq. (7), reduced across the heads instead of across the blocks:
+//   G_b = sum_{j < H, ascending} A_{j,b},   b < M_t,
+// over the same causal blocks as orc_expert_scores (complete blocks pooled by
+// Eq. (4), the partial last block pooled over [floor(n/B)*B, pos]).
+// Reading: the head reduction is the plain sum of the signed A (the page's
+// HISA aggregates the heads' block affinities; |A| belongs to the head
+// ranking of Eq. (7)).  G has M_t = ceil((pos+1)/B) entries.
+void orc_block_scores(const double* K, const double* pooled, int64_t pos, int32_t d, int32_t B,
+                      int32_t H, const double* q, const double* w, double* G) {
+  const int64_t n = pos + 1;
+  const int64_t full = n / B;
+  const int64_t Mt = (n + B - 1) / B;
+  std::vector<double> partial;
+  if (Mt > full) {
+    partial.assign(d, 0.0);
+    const int64_t s0 = full * B;
+    for (int32_t i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (int64_t s = s0; s <= pos; ++s) acc += K[s * d + i];
+      partial[i] = acc / static_cast<double>(n - s0);
+    }
+  }
+  for (int64_t b = 0; b < Mt; ++b) {
+    const double* kb = (b < full) ? pooled + b * d : partial.data();
+    double sum = 0.0;
+    for (int32_t j = 0; j < H; ++j) sum += w[j] * relu(dot(q + static_cast<int64_t>(j) * d, kb, d));
+    G[b] = sum;
+  }
+}
+
 // Eq. (8): the h heads with the largest E (ties: the lower head index first),
 // written out in ascending head order.
 void orc_top_heads(const double* E, int32_t H, int32_t h, int32_t* heads) {

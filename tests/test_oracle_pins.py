@@ -336,3 +336,94 @@ def test_short_prefix_pads_with_minus_one():
     r = seq.misa(4, q[4], w[4], 4, 10)        # n = 5 < k = 10
     assert sorted(r["idx"][:5].tolist()) == [0, 1, 2, 3, 4]
     assert r["idx"][5:].tolist() == [-1] * 5
+
+
+# ------------------------------------------------------------ MISA x HISA
+
+
+def test_hisa_hand_example():
+    g = json.load(open(GOLDEN))
+    seq = oracle.Sequence(np.array(g["K"], dtype=np.float64), g["B"])
+    for qd in g["queries"]:
+        q = np.array(qd["q"], dtype=np.float64)
+        w = np.array(qd["w"], dtype=np.float64)
+        G = seq.block_scores(qd["pos"], q, w)
+        assert G.tolist() == qd["hisa_G"]
+        for case in qd["hisa_cases"]:
+            r = seq.hisa_tokens(qd["pos"], q, w, np.array(qd["heads"], np.int32), case["m"], case["k"])
+            assert r["blocks"].tolist() == case["blocks"], case
+            assert r["idx"].tolist() == case["idx"], case
+
+
+def test_hisa_block_scores_with_B1_are_the_dense_token_scores():
+    """B = 1: every pooled key is its token's key and no block is partial, so
+    G_b is Eq. (1) of token b (summed by a different oracle routine)."""
+    p = synth.small("hisa_b1", L=300, T=3, B=1, dtype=synth.F32, needles=2, seed=61)
+    x = synth.generate(p)
+    K = x.k[0].double().numpy()
+    seq = oracle.Sequence(K, 1)
+    for t in range(p.T):
+        pos = p.L - p.T + t
+        q, w = x.q[0, t].double().numpy(), x.w[0, t].double().numpy()
+        G = seq.block_scores(pos, q, w)
+        I = seq.scores(pos, q, w, np.arange(p.H, dtype=np.int32))
+        np.testing.assert_array_equal(G, I)
+
+
+@pytest.mark.parametrize("pos", [511, 517, 700])
+def test_hisa_single_head_block_scores_give_the_expert_score(pos):
+    """H = 1: G_b is that head's A_b, so Eq. (7)'s E = mean_b |G_b| (complete
+    and partial blocks alike)."""
+    p = synth.small("hisa_h1", L=701, T=1, H=1, h=1, B=64, dtype=synth.F32, needles=0, seed=62)
+    x = synth.generate(p)
+    seq = oracle.Sequence(x.k[0].double().numpy(), p.B)
+    q, w = x.q[0, 0].double().numpy(), x.w[0, 0].double().numpy()
+    w = -w  # the sign survives in G, not in E
+    G = seq.block_scores(pos, q, w)
+    assert len(G) == (pos + 1 + p.B - 1) // p.B
+    E, _ = seq.route(pos, q, w, 1)
+    np.testing.assert_allclose(E[0], np.abs(G).mean(), rtol=1e-14)
+    assert (G <= 0).all()
+
+
+def test_hisa_with_every_block_is_misa():
+    """m >= M_t keeps every token of the prefix, so the restricted top-k is
+    the plain Eq. (10) top-k, and with every head it is Eq. (2)."""
+    p = synth.small("hisa_all", L=900, T=4, B=64, k=50, dtype=synth.BF16, needles=4, seed=63)
+    x = synth.generate(p)
+    K = oracle.decode(x.raw_numpy("k")[0], oracle.BF16)
+    seq = oracle.Sequence(K, p.B)
+    qd = oracle.decode(x.raw_numpy("q")[0].reshape(p.T, -1), oracle.BF16).reshape(p.T, p.H, p.d)
+    for t in range(p.T):
+        pos = p.L - p.T + t
+        w = x.w[0, t].double().numpy()
+        E, heads = seq.route(pos, qd[t], w, p.h)
+        r = seq.hisa_tokens(pos, qd[t], w, heads, 64, p.k)
+        assert r["tokens"].tolist() == list(range(pos + 1))
+        assert r["idx"].tolist() == seq.misa(pos, qd[t], w, p.h, p.k)["idx"].tolist()
+        rd = seq.hisa_tokens(pos, qd[t], w, np.arange(p.H, dtype=np.int32), 64, p.k)
+        assert rd["idx"].tolist() == seq.dense(pos, qd[t], w, p.k)["idx"].tolist()
+
+
+def test_hisa_causality_and_planted_block():
+    """Keys after the query change nothing; a block whose keys all lie along
+    the scored heads' query directions (every dot product large and
+    positive, all w > 0) is selected, and its tokens lead the top-k."""
+    p = synth.small("hisa_plant", L=1024, T=1, B=64, dtype=synth.F32, needles=0, seed=64)
+    x = synth.generate(p)
+    K = x.k[0].double().numpy().copy()
+    q, w = x.q[0, 0].double().numpy(), x.w[0, 0].double().numpy()
+    pos = 700
+    heads = np.arange(8, dtype=np.int32)
+    base = oracle.Sequence(K, p.B).hisa_tokens(pos, q, w, heads, 3, 20)
+    K2 = K.copy()
+    K2[pos + 1:] = 100.0
+    fut = oracle.Sequence(K2, p.B).hisa_tokens(pos, q, w, heads, 3, 20)
+    assert fut["blocks"].tolist() == base["blocks"].tolist() and fut["idx"].tolist() == base["idx"].tolist()
+    np.testing.assert_array_equal(fut["G"], base["G"])
+    K3 = K.copy()
+    K3[5 * 64:6 * 64] = 100.0 * sum(q[j] / np.linalg.norm(q[j]) for j in heads)
+    r = oracle.Sequence(K3, p.B).hisa_tokens(pos, q, w, heads, 3, 20)
+    assert 5 in r["blocks"].tolist()
+    assert np.argmax(r["G"]) == 5
+    assert set(r["idx"].tolist()) <= set(range(5 * 64, 6 * 64))
