@@ -201,6 +201,33 @@ misa_status dsa_index_dense(const misa_shape* shape, int32_t k, const void* q,
                             const float* k_scale, int32_t* idx, float* scores_out, void* ws,
                             size_t ws_bytes, hipStream_t stream);
 
+/* MISA x HISA ("Methodology" 1, "Key distinction from HISA"; "Theoretical
+ * and Practical Implications", "Scalability"): the Eq. (7) affinities
+ * A = w * ReLU(q . p) reduced across the heads instead of the blocks pick the
+ * query's top-m blocks, and the routed scoring of Eq. (9) runs only over their
+ * tokens.  For query t (n_t = L-T+t+1, the same causal blocks as misa_route):
+ *   G[b,t,blk] = sum_{j < H} w[b,t,j] * ReLU(q[b,t,j,:] . p_blk),  blk < M_t
+ *   the m blocks of largest G (ties: lower block; all M_t when M_t <= m)
+ *   I[b,t,s] = sum_{j in heads[b,t,:]} w[b,t,j] * ReLU(q[b,t,j,:] . k[b,s,:])
+ *              for the tokens s <= L-T+t of those blocks
+ *   idx[b,t,:] = the k of those tokens with the largest I (ties: lower token;
+ *                -1 / -INFINITY padding when they are fewer than k).
+ *   pooled            [batch, M, d]  fp32 (misa_pool_keys)
+ *   heads             [batch, T, h]  int32 (misa_route)
+ *   blocks_out        [batch, T, m]  int32, written if non-NULL: the blocks,
+ *                     ascending, -1 padding
+ *   block_scores_out  [batch, T, m]  fp32, written if non-NULL: G of each slot
+ *   idx, scores_out   [batch, T, k]  as misa_score_topk
+ * Limits: bf16 or fp8 inputs, m * B <= 8192, one sequence's keys below 2 GiB;
+ * otherwise MISA_ERR_UNSUPPORTED.  ws must hold misa_hisa_workspace_bytes(). */
+size_t misa_hisa_workspace_bytes(const misa_shape* shape, int32_t h, int32_t m, int32_t k);
+misa_status misa_hisa_score_topk(const misa_shape* shape, int32_t h, int32_t m, int32_t k,
+                                 const void* q, const float* q_scale, const float* w,
+                                 const float* pooled, const void* kk, const float* k_scale,
+                                 const int32_t* heads, int32_t* blocks_out,
+                                 float* block_scores_out, int32_t* idx, float* scores_out,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* A static, human-readable name of a status code. */
 const char* misa_status_string(misa_status status);
 

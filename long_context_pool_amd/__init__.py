@@ -30,7 +30,7 @@ MISA_F32, MISA_BF16, MISA_FP8_E4M3 = 0, 1, 2
 EXPORTED = (
     "misa_workspace_bytes", "misa_pool_keys", "misa_pool_keys_range", "misa_route",
     "misa_score_topk", "misa_decode_step", "misa_decode_step_noalloc", "misa_rerank",
-    "dsa_index_dense", "misa_status_string",
+    "dsa_index_dense", "misa_hisa_workspace_bytes", "misa_hisa_score_topk", "misa_status_string",
 )
 MISA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -65,10 +65,14 @@ _lib.misa_route.argtypes = [_SHP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
 _lib.misa_score_topk.argtypes = [_SHP, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.misa_decode_step.argtypes = [_SHP, _I32, _I32] + [_P] * 11 + [_SZ, _P]
 _lib.misa_decode_step_noalloc.argtypes = [_SHP, _I32, _I32] + [_P] * 11
+_lib.misa_hisa_workspace_bytes.argtypes = [_SHP, _I32, _I32, _I32]
+_lib.misa_hisa_workspace_bytes.restype = _SZ
+_lib.misa_hisa_score_topk.argtypes = [_SHP, _I32, _I32, _I32] + [_P] * 12 + [_SZ, _P]
 _lib.misa_rerank.argtypes = [_SHP, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.dsa_index_dense.argtypes = [_SHP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
 for _f in ("misa_pool_keys", "misa_pool_keys_range", "misa_route", "misa_score_topk",
-           "misa_decode_step", "misa_decode_step_noalloc", "misa_rerank", "dsa_index_dense"):
+           "misa_decode_step", "misa_decode_step_noalloc", "misa_rerank", "dsa_index_dense",
+           "misa_hisa_score_topk"):
     getattr(_lib, _f).restype = ctypes.c_int
 _lib.misa_status_string.argtypes = [ctypes.c_int]
 _lib.misa_status_string.restype = ctypes.c_char_p
@@ -171,3 +175,16 @@ def dsa_index_dense(shp, k, q, q_scale, w, kk, k_scale, idx, scores_out, ws, str
     _check(_lib.dsa_index_dense(ctypes.byref(shp), k, _ptr(q), _ptr(q_scale), _ptr(w), _ptr(kk),
                                 _ptr(k_scale), _ptr(idx), _ptr(scores_out), _ptr(ws),
                                 _nbytes(ws), _stream(stream)), "dsa_index_dense")
+
+
+def misa_hisa_workspace_bytes(shp: misa_shape, h: int, m: int, k: int) -> int:
+    return int(_lib.misa_hisa_workspace_bytes(ctypes.byref(shp), h, m, k))
+
+
+def misa_hisa_score_topk(shp, h, m, k, q, q_scale, w, pooled, kk, k_scale, heads, blocks_out,
+                         block_scores_out, idx, scores_out, ws, stream=None):
+    _check(_lib.misa_hisa_score_topk(ctypes.byref(shp), h, m, k, _ptr(q), _ptr(q_scale), _ptr(w),
+                                     _ptr(pooled), _ptr(kk), _ptr(k_scale), _ptr(heads),
+                                     _ptr(blocks_out), _ptr(block_scores_out), _ptr(idx),
+                                     _ptr(scores_out), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "misa_hisa_score_topk")

@@ -235,6 +235,37 @@ misa_status misa_rerank(const misa_shape* shape, int32_t kprime, int32_t k, cons
                                       scores_out, ws, stream));
 }
 
+size_t misa_hisa_workspace_bytes(const misa_shape* shape, int32_t h, int32_t m, int32_t k) {
+  Shape s;
+  if (check_shape(shape, s) != MISA_OK || h < 1 || m < 1 || k < 1) return 0;
+  if (check_topk(k) != MISA_OK) return 0;
+  return misa::hisa_ws_bytes(s, m, k);
+}
+
+misa_status misa_hisa_score_topk(const misa_shape* shape, int32_t h, int32_t m, int32_t k,
+                                 const void* q, const float* q_scale, const float* w,
+                                 const float* pooled, const void* kk, const float* k_scale,
+                                 const int32_t* heads, int32_t* blocks_out,
+                                 float* block_scores_out, int32_t* idx, float* scores_out,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  MISA_TRY(check_shape(shape, s));
+  if (h < 1 || h > s.H || m < 1) return MISA_ERR_INVALID_ARG;
+  if (h > kMaxRouted) return MISA_ERR_UNSUPPORTED;
+  MISA_TRY(check_topk(k));
+  MISA_TRY(check_inputs(s, q, q_scale, w, kk, k_scale));
+  if (!pooled || !aligned16(pooled) || !heads || !aligned16(heads)) return MISA_ERR_INVALID_ARG;
+  MISA_TRY(check_out(blocks_out, false));
+  MISA_TRY(check_out(block_scores_out, false));
+  MISA_TRY(check_out(idx, true));
+  MISA_TRY(check_out(scores_out, false));
+  if (!misa::hisa_supported(s, m) || s.batch > 65535 || s.T > 65535) return MISA_ERR_UNSUPPORTED;
+  MISA_TRY(check_ws(ws, ws_bytes, misa::hisa_ws_bytes(s, m, k)));
+  return from_hip(misa::launch_hisa_score_topk(s, h, heads, m, k, q, q_scale, w, pooled, kk,
+                                               k_scale, blocks_out, block_scores_out, idx,
+                                               scores_out, ws, stream));
+}
+
 const char* misa_status_string(misa_status status) {
   switch (status) {
     case MISA_OK: return "MISA_OK";

@@ -1,0 +1,436 @@
+// MISA x HISA: the combination the MISA summary page describes in
+// "Methodology" 1 ("Key distinction from HISA") and "Theoretical and Practical
+// Implications" ("Scalability").  MISA reduces the router affinities
+// A_{t,j,b} = w_{t,j} * ReLU(q_{t,j} . p_b) of Eq. (7) across the blocks to
+// pick heads; HISA reduces the same affinities across the heads to pick
+// blocks.  Here both run: the query's top-m blocks by
+//   G_{t,b} = sum_{j < H} A_{t,j,b}
+// (the same causal blocks as the router: complete blocks from the pooled
+// cache of Eq. (4), the partial last block pooled over the query's own keys)
+// bound the Eq. (9) routed-head scoring, and the top-k of those tokens is
+// the selection.
+//
+// Kernels:
+//  1. hisa_block_kernel: one query per wave, its H head rows as the A operand
+//     of 32x32x16 MFMA tiles (held in registers; fp8 codes widen to bf16
+//     exactly), 32-block pooled tiles as B (bf16 hi plane, plus the lo plane
+//     for bf16 inputs, staged in LDS by buffer-to-LDS loads and shared by the
+//     workgroup's four waves).  A lane then holds 16 heads of one block, so
+//     w * ReLU and the head sum stay in the lane (one cross-half add).  The
+//     partial block's G comes from per-key MFMA dots on the raw keys.  G goes
+//     to the workspace; the wave then finds the m-th largest G by a bitwise
+//     search on the order-preserving keys (ballot counts) and writes its m
+//     blocks in ascending order (ties: lower block).
+//  2. hisa_expand_kernel: the blocks' tokens, in order, as a candidate list
+//     of m B entries (tokens past the query's position, and padding, -1).
+//  3. the re-rank kernels with the routed heads (launch_rerank_heads): Eq. (9)
+//     over the candidates and their top-k.
+#include "common.hpp"
+#include "launch.hpp"
+#include "mfma.hpp"
+#include "topk.hpp"
+
+namespace misa {
+
+namespace {
+
+constexpr int kHThreads = 256;
+constexpr int kHWaves = 4;
+constexpr int kHTileBytes = 32 * kD * 2;  // one bf16 plane of a 32-block pooled tile
+constexpr int kHMaxCache = 32;            // G values per lane kept in registers for the top-m
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t hs_rsrc(const void* base, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void hs_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void hs_vmcnt_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate in the low field");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ void hs_vmcnt_zero() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+template <class T>
+__device__ __forceinline__ T* hs_uniform(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// 32x32x16 fragments (8 k-steps) of one head or key row `row` (< 0: zeros):
+// this lane's elements [64*(l/32), 64*(l/32)+64); fp8 codes widen to bf16.
+template <int DT>
+__device__ __forceinline__ void row_frags(const void* base, int64_t row, bf16x8 (&a)[8]) {
+  const int hf = lane_id() >> 5;
+  if (row < 0) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) a[ks] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    return;
+  }
+  if constexpr (DT == kBF16) {
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + row * kD + 64 * hf);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) a[ks] = as_bf16x8(src[ks]);
+  } else {
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(base) + row * kD + 64 * hf);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 v = src[c];
+      const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float f0 = fp8_to_f32(wds[u] & 0xFF), f1 = fp8_to_f32((wds[u] >> 8) & 0xFF);
+        const float f2 = fp8_to_f32((wds[u] >> 16) & 0xFF), f3 = fp8_to_f32(wds[u] >> 24);
+        o[2 * u] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+        o[2 * u + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u);
+      }
+      a[2 * c] = as_bf16x8(make_uint4(o[0], o[1], o[2], o[3]));
+      a[2 * c + 1] = as_bf16x8(make_uint4(o[4], o[5], o[6], o[7]));
+    }
+  }
+}
+
+// Block scores and the top-m blocks.  Workgroup = four queries (one per
+// wave) of one sequence; RT = 32-head row tiles (H <= 32 RT ... ).
+template <int DT, int RT>
+__global__ __launch_bounds__(kHThreads, 2) void hisa_block_kernel(
+    const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const uint16_t* __restrict__ phi, const uint16_t* __restrict__ plo, const void* __restrict__ k,
+    const float* __restrict__ k_scale, int32_t L, int32_t T, int32_t H, int32_t B, int64_t M,
+    int32_t m, float* __restrict__ G, int32_t* __restrict__ blocks, float* __restrict__ bscores) {
+  constexpr bool SPLIT = DT == kBF16;
+  constexpr int LB = SPLIT ? kHTileBytes : 16;
+  __shared__ __attribute__((aligned(16))) uint8_t h0[kHTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t h1[kHTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t h2[kHTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t l0[LB];
+  __shared__ __attribute__((aligned(16))) uint8_t l1[LB];
+  __shared__ __attribute__((aligned(16))) uint8_t l2[LB];
+  __shared__ float pdot[kHWaves][64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = lane_id();
+  const int hf = lane >> 5;
+  const int64_t seq = blockIdx.y;
+  const int t0 = blockIdx.x * kHWaves;
+  const int t = t0 + wave;
+  const bool active = t < T;
+  const int64_t r = seq * T + (active ? t : t0);
+  const int64_t pos = static_cast<int64_t>(L) - T + (active ? t : t0);
+  const int64_t n = pos + 1;
+  const int64_t full = n / B;
+  const int64_t Mt = (n + B - 1) / B;
+  const int tl = min(t0 + kHWaves - 1, T - 1);
+  const int64_t full_max = (static_cast<int64_t>(L) - T + tl + 1) / B;
+  float* Gq = G + r * M;
+
+  // A operand: head rows rt*32 + l%32; row weights w * s_q (fp8 q scale, > 0,
+  // so it commutes with ReLU) of the lane's accumulator rows.
+  bf16x8 a[RT][8];
+  float wl[RT][16];
+  const float sq = (DT == kFP8) ? q_scale[r] : 1.f;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int j = rt * 32 + (lane & 31);
+    row_frags<DT>(q, j < H ? r * H + j : -1, a[rt]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = rt * 32 + 8 * (i / 4) + 4 * hf + (i % 4);
+      wl[rt][i] = row < H ? w[r * H + row] * sq : 0.f;
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(a[rt][ks]));
+  hs_vmcnt_zero();
+
+  // Pooled tiles: three LDS buffers, two tiles in flight (the router's
+  // pattern); 16-byte chunk c of tile row rr at chunk position c ^ (rr % 16).
+  constexpr int NL = SPLIT ? 4 : 2;
+  const int64_t ntiles = (full_max + 31) / 32;
+  const int64_t last = ntiles > 0 ? ntiles - 1 : 0;
+  const __amdgpu_buffer_rsrc_t rh = hs_rsrc(hs_uniform(phi + seq * M * kD), static_cast<int32_t>(M * kD * 2));
+  const __amdgpu_buffer_rsrc_t rl = hs_rsrc(hs_uniform(plo + seq * M * kD), static_cast<int32_t>(M * kD * 2));
+  int rowi[2];
+  uint32_t chk[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    rowi[i] = 8 * wave + 4 * i + lane / 16;
+    chk[i] = 16u * static_cast<uint32_t>((lane % 16) ^ (rowi[i] & 15));
+  }
+  auto issue = [&](int64_t bt, uint8_t* hb, uint8_t* lb) __attribute__((always_inline)) {
+    const int64_t tb = bt < last ? bt : last;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t blk = tb * 32 + rowi[i];
+      const uint32_t voff = static_cast<uint32_t>((blk < full_max ? blk : 0) * (kD * 2)) + chk[i];
+      hs_load16_lds(rh, hb + 1024 * (2 * wave + i), voff);
+      if constexpr (SPLIT) hs_load16_lds(rl, lb + 1024 * (2 * wave + i), voff);
+    }
+  };
+  // G of the tile's 32 blocks: lane (l % 32) holds its block's 16 heads per
+  // half-wave; the two halves add.
+  auto tile = [&](int64_t bt, const uint8_t* hb, const uint8_t* lb) __attribute__((always_inline)) {
+    const int rr = lane & 31;
+    const uint8_t* rowh = hb + rr * (kD * 2);
+    const uint8_t* rowl = lb + rr * (kD * 2);
+    f32x16 acc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int pc = (8 * hf + ks) ^ (rr & 15);
+      const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4*>(rowh + 16 * pc));
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_bf16(a[rt][ks], bh, acc[rt]);
+      if constexpr (SPLIT) {
+        const bf16x8 bl = as_bf16x8(*reinterpret_cast<const uint4*>(rowl + 16 * pc));
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_bf16(a[rt][ks], bl, acc[rt]);
+      }
+    }
+    float g = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) g += wl[rt][i] * relu(acc[rt][i]);
+    g += __shfl_xor(g, 32, kWave);
+    const int64_t blk = bt * 32 + rr;
+    if (active && lane < 32 && blk < full) Gq[blk] = g;
+  };
+  if (ntiles > 0) {
+    issue(0, h0, l0);
+    issue(1, h1, l1);
+  }
+  auto step = [&](int64_t bt, const uint8_t* hb, const uint8_t* lb, uint8_t* nh, uint8_t* nl)
+      __attribute__((always_inline)) {
+    hs_vmcnt_barrier<NL>();  // tile bt has landed; every wave is done with tile bt-1
+    issue(bt + 2, nh, nl);
+    tile(bt, hb, lb);
+  };
+  for (int64_t bt = 0; bt < ntiles; bt += 3) {
+    step(bt, h0, l0, h2, l2);
+    if (bt + 1 < ntiles) step(bt + 1, h1, l1, h0, l0);
+    if (bt + 2 < ntiles) step(bt + 2, h2, l2, h1, l1);
+  }
+  hs_vmcnt_zero();
+
+  // The partial last block [full B, pos]: G = sum_j w_j ReLU(mean_s q_j . k_s)
+  // with the per-key dots from MFMA tiles (32 raw keys as B, the fp8 key
+  // scale per column), summed over the keys.
+  if (active && Mt > full) {
+    f32x16 ps[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) ps[rt] = f32x16{};
+    const int64_t s_lo = full * B;
+    for (int64_t s0 = s_lo; s0 <= pos; s0 += 32) {
+      const int64_t sk_i = s0 + (lane & 31);
+      const bool ok = sk_i <= pos;
+      const int64_t row = seq * L + (ok ? sk_i : s_lo);
+      bf16x8 kb[8];
+      row_frags<DT>(k, row, kb);
+      const float skv = ok ? ((DT == kFP8) ? k_scale[row] : 1.f) : 0.f;
+      f32x16 acc[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_bf16(a[rt][ks], kb[ks], acc[rt]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ps[rt][i] += acc[rt][i] * skv;
+    }
+    // Sum over the key columns: head row rt*32 + 8(i/4) + 4hf + i%4.
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float v = ps[rt][i];
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+        if ((lane & 31) == 0) pdot[wave][rt * 32 + 8 * (i / 4) + 4 * hf + (i % 4)] = v;
+      }
+    __builtin_amdgcn_wave_barrier();
+    const float cnt = static_cast<float>(pos - s_lo + 1);
+    float g = lane < H ? w[r * H + lane] * sq * relu(pdot[wave][lane] / cnt) : 0.f;
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) g += __shfl_xor(g, o, kWave);
+    if (lane == 0) Gq[full] = g;
+  }
+  if (!active) return;
+  // The lanes read back G values other lanes of this wave stored: once the
+  // stores have completed they are visible to loads from the same compute
+  // unit (its vector L1 is write-through and shared by the unit's waves).
+  hs_vmcnt_zero();
+  __builtin_amdgcn_wave_barrier();
+
+  // Top-m blocks of G[0 .. Mt), ascending (ties: lower block).
+  int32_t* bq = blocks + r * m;
+  float* bs = bscores ? bscores + r * m : nullptr;
+  const int nch = static_cast<int>((Mt + kWave - 1) / kWave);
+  if (Mt <= m) {
+    for (int i = lane; i < m; i += kWave) {
+      bq[i] = i < Mt ? i : -1;
+      if (bs) bs[i] = i < Mt ? Gq[i] : -__builtin_inff();
+    }
+    return;
+  }
+  uint32_t kc[kHMaxCache];
+  const bool cached = nch <= kHMaxCache;
+  if (cached) {
+#pragma unroll
+    for (int j = 0; j < kHMaxCache; ++j) {
+      const int64_t b = static_cast<int64_t>(j) * kWave + lane;
+      kc[j] = (j < nch && b < Mt) ? float_key(Gq[b]) : 0u;
+    }
+  }
+  auto key_of = [&](int j) -> uint32_t {
+    const int64_t b = static_cast<int64_t>(j) * kWave + lane;
+    return b < Mt ? float_key(Gq[b]) : 0u;
+  };
+  // Count of keys >= c (every valid key is >= 0x00800000: float_key of any
+  // finite float is at least that, so the padding key 0 never counts).
+  auto count_ge = [&](uint32_t c) -> int {
+    int cnt = 0;
+    if (cached) {
+#pragma unroll
+      for (int j = 0; j < kHMaxCache; ++j)
+        if (j < nch) cnt += __popcll(__ballot(kc[j] >= c));
+    } else {
+      for (int j = 0; j < nch; ++j) cnt += __popcll(__ballot(key_of(j) >= c));
+    }
+    return cnt;
+  };
+  uint32_t v = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = v | (1u << bit);
+    if (count_ge(c) >= m) v = c;
+  }
+  // Keys above v all go; of those equal to v, the lowest blocks fill m.
+  const int need_eq = m - count_ge(v + 1u);
+  int base = 0, eq_seen = 0;
+  auto emit = [&](int j, uint32_t key) __attribute__((always_inline)) {
+    const int64_t b = static_cast<int64_t>(j) * kWave + lane;
+    const bool valid = b < Mt;
+    const uint64_t eqm = __ballot(valid && key == v);
+    const bool sel = valid && (key > v || (key == v && eq_seen + lanes_below(eqm) < need_eq));
+    const uint64_t sm = __ballot(sel);
+    if (sel) {
+      const int p = base + lanes_below(sm);
+      bq[p] = static_cast<int32_t>(b);
+      if (bs) bs[p] = Gq[b];
+    }
+    base += __popcll(sm);
+    eq_seen += __popcll(eqm);
+  };
+  if (cached) {
+#pragma unroll
+    for (int j = 0; j < kHMaxCache; ++j)
+      if (j < nch) emit(j, kc[j]);
+  } else {
+    for (int j = 0; j < nch; ++j) emit(j, key_of(j));
+  }
+}
+
+// Candidate tokens of the selected blocks, block by block: entry i < m B is
+// token blocks[i / B] * B + i % B, or -1 (padding block, or past the query);
+// entries m B <= i < nc (a list long enough for the top-k) are -1.  One
+// workgroup per query row.
+__global__ void hisa_expand_kernel(const int32_t* __restrict__ blocks, int32_t m, int32_t B,
+                                   int32_t nc, int32_t L, int32_t T, int32_t* __restrict__ cand) {
+  const int64_t r = blockIdx.x;
+  const int64_t pos = static_cast<int64_t>(L) - T + r % T;
+  const int32_t nb = m * B;
+  for (int32_t i = threadIdx.x; i < nc; i += blockDim.x) {
+    int32_t tok = -1;
+    if (i < nb) {
+      const int32_t b = blocks[r * m + i / B];
+      const int64_t t = static_cast<int64_t>(b) * B + i % B;
+      if (b >= 0 && t <= pos) tok = static_cast<int32_t>(t);
+    }
+    cand[r * nc + i] = tok;
+  }
+}
+
+struct HisaLayout {
+  size_t planes, G, blocks, cand, rerank, total;
+};
+
+// Candidate list length: the m blocks' tokens, at least k entries.
+int32_t hisa_cands(const Shape& s, int32_t m, int32_t k) { return max(m * s.B, k); }
+
+HisaLayout hisa_layout(const Shape& s, int32_t m, int32_t k) {
+  HisaLayout lo{};
+  const size_t rows = static_cast<size_t>(s.batch) * s.T;
+  const size_t plane = align_up(static_cast<size_t>(s.batch) * s.M() * kD * sizeof(uint16_t));
+  size_t off = 0;
+  lo.planes = off;
+  off += 2 * plane;
+  lo.G = off;
+  off += align_up(rows * s.M() * sizeof(float));
+  lo.blocks = off;
+  off += align_up(rows * m * sizeof(int32_t));
+  lo.cand = off;
+  off += align_up(rows * static_cast<size_t>(hisa_cands(s, m, k)) * sizeof(int32_t));
+  lo.rerank = off;
+  off += rerank_ws_bytes(s, hisa_cands(s, m, k));
+  lo.total = off;
+  return lo;
+}
+
+}  // namespace
+
+bool hisa_supported(const Shape& s, int32_t m) {
+  return s.dtype != kF32 && static_cast<int64_t>(m) * s.B <= 8192 &&
+         static_cast<int64_t>(s.L) * kD * (s.dtype == kBF16 ? 2 : 1) < (int64_t{1} << 31) &&
+         s.M() * kD * 2 < (int64_t{1} << 31);
+}
+
+size_t hisa_ws_bytes(const Shape& s, int32_t m, int32_t k) { return hisa_layout(s, m, k).total; }
+
+hipError_t launch_hisa_score_topk(const Shape& s, int32_t nh, const int32_t* heads, int32_t m,
+                                  int32_t k, const void* q, const float* q_scale, const float* w,
+                                  const float* pooled, const void* kk, const float* k_scale,
+                                  int32_t* blocks_out, float* block_scores_out, int32_t* idx,
+                                  float* scores_out, void* ws, hipStream_t st) {
+  const HisaLayout lo = hisa_layout(s, m, k);
+  char* base = static_cast<char*>(ws);
+  const size_t plane = align_up(static_cast<size_t>(s.batch) * s.M() * kD * sizeof(uint16_t));
+  uint16_t* phi = reinterpret_cast<uint16_t*>(base + lo.planes);
+  uint16_t* plo = reinterpret_cast<uint16_t*>(base + lo.planes + plane);
+  hipError_t e = launch_pooled_split(s, pooled, phi, plo, st);
+  if (e != hipSuccess) return e;
+  float* G = reinterpret_cast<float*>(base + lo.G);
+  int32_t* blocks = blocks_out ? blocks_out : reinterpret_cast<int32_t*>(base + lo.blocks);
+  dim3 g1((s.T + kHWaves - 1) / kHWaves, s.batch);
+  const bool two = s.H > 32;
+#define HB(DT, RT) hisa_block_kernel<DT, RT><<<g1, kHThreads, 0, st>>>(q, q_scale, w, phi, plo, kk, k_scale, s.L, s.T, s.H, s.B, s.M(), m, G, blocks, block_scores_out)
+  if (s.dtype == kBF16) { if (two) HB(kBF16, 2); else HB(kBF16, 1); }
+  else { if (two) HB(kFP8, 2); else HB(kFP8, 1); }
+#undef HB
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int32_t kp = hisa_cands(s, m, k);
+  int32_t* cand = reinterpret_cast<int32_t*>(base + lo.cand);
+  hisa_expand_kernel<<<static_cast<unsigned>(static_cast<int64_t>(s.batch) * s.T), 256, 0, st>>>(
+      blocks, m, s.B, kp, s.L, s.T, cand);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_rerank_heads(s, kp, k, q, q_scale, w, kk, k_scale, cand, heads, nh, idx, scores_out,
+                             base + lo.rerank, st);
+}
+
+}  // namespace misa

@@ -89,6 +89,30 @@ hipError_t launch_rerank(const Shape& s, int32_t kprime, int32_t k, const void* 
                          const int32_t* cand, int32_t* idx, float* scores_out, void* ws,
                          hipStream_t st);
 
+// The re-rank with a list of heads per query (heads [batch*T, nh]; nullptr:
+// every head) -- the routed scoring over a candidate list.  bf16/fp8 keys
+// within a buffer descriptor's reach only when heads != nullptr.
+hipError_t launch_rerank_heads(const Shape& s, int32_t kprime, int32_t k, const void* q,
+                               const float* q_scale, const float* w, const void* kk,
+                               const float* k_scale, const int32_t* cand, const int32_t* heads,
+                               int32_t nh, int32_t* idx, float* scores_out, void* ws,
+                               hipStream_t st);
+
+// Pooled keys -> bf16 hi and lo planes [batch*M, 128] (the router's B
+// operand).
+hipError_t launch_pooled_split(const Shape& s, const float* pooled, uint16_t* hi, uint16_t* lo,
+                               hipStream_t st);
+
+// MISA x HISA: block scores G (Eq. (7) affinities summed over heads), the
+// top-m blocks, and the routed top-k over their tokens.
+bool hisa_supported(const Shape& s, int32_t m);
+size_t hisa_ws_bytes(const Shape& s, int32_t m, int32_t k);
+hipError_t launch_hisa_score_topk(const Shape& s, int32_t nh, const int32_t* heads, int32_t m,
+                                  int32_t k, const void* q, const float* q_scale, const float* w,
+                                  const float* pooled, const void* kk, const float* k_scale,
+                                  int32_t* blocks_out, float* block_scores_out, int32_t* idx,
+                                  float* scores_out, void* ws, hipStream_t st);
+
 inline size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
 
 // The fixed device scratch of the no-allocation decode step: its size, and

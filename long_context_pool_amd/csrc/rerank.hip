@@ -443,7 +443,7 @@ __global__ __launch_bounds__(kRRThreads) void rerank_lds_kernel(
     const void* __restrict__ k, const float* __restrict__ k_scale,
     const int32_t* __restrict__ cand, int32_t kprime, int32_t L, int32_t T, int32_t H,
     int32_t per_wg, float* __restrict__ out, int32_t k_top, int32_t* __restrict__ idx,
-    float* __restrict__ scores_out) {
+    float* __restrict__ scores_out, const int32_t* __restrict__ heads, int32_t nh) {
   constexpr int ROWB = kD * (DT == kBF16 ? 2 : 1);  // key row bytes
   constexpr int CPR = ROWB / 16;                     // 16-byte chunks per row
   constexpr int RPI = kWave / CPR;                   // rows per load instruction
@@ -462,12 +462,24 @@ __global__ __launch_bounds__(kRRThreads) void rerank_lds_kernel(
   const int hf = lane >> 5;
   const int col = lane & 31;
 
-  // Query head rows and weights -> LDS.
+  // Query head rows and weights -> LDS: row a is head a (every head), or
+  // the a-th listed head (heads != nullptr: nh of them; ids outside [0, H)
+  // contribute nothing).
   const uint8_t* qrow = static_cast<const uint8_t*>(q) + r * H * ROWB;
-  for (int i = threadIdx.x; i < kMaxHeads * CPR; i += kRRThreads)
-    reinterpret_cast<uint4*>(qst)[i] = i < H * CPR ? reinterpret_cast<const uint4*>(qrow)[i] : make_uint4(0, 0, 0, 0);
+  auto head_of = [&](int a) -> int {
+    const int j = heads ? (a < nh ? heads[r * nh + a] : -1) : (a < H ? a : -1);
+    return (j >= 0 && j < H) ? j : -1;
+  };
+  for (int i = threadIdx.x; i < kMaxHeads * CPR; i += kRRThreads) {
+    const int j = head_of(i / CPR);
+    reinterpret_cast<uint4*>(qst)[i] =
+        j >= 0 ? reinterpret_cast<const uint4*>(qrow + j * ROWB)[i % CPR] : make_uint4(0, 0, 0, 0);
+  }
   const float sq = (DT == kFP8) ? q_scale[r] : 1.f;
-  if (threadIdx.x < kMaxHeads) wst[threadIdx.x] = threadIdx.x < H ? w[r * H + threadIdx.x] * sq : 0.f;
+  if (threadIdx.x < kMaxHeads) {
+    const int j = head_of(threadIdx.x);
+    wst[threadIdx.x] = j >= 0 ? w[r * H + j] * sq : 0.f;
+  }
   __syncthreads();
   CandScorer<DT, RT> cs;
 #pragma unroll
@@ -564,11 +576,23 @@ hipError_t launch_rerank(const Shape& s, int32_t kprime, int32_t k, const void* 
                          const float* q_scale, const float* w, const void* kk, const float* k_scale,
                          const int32_t* cand, int32_t* idx, float* scores_out, void* ws,
                          hipStream_t st) {
+  return launch_rerank_heads(s, kprime, k, q, q_scale, w, kk, k_scale, cand, nullptr, s.H, idx,
+                             scores_out, ws, st);
+}
+
+hipError_t launch_rerank_heads(const Shape& s, int32_t kprime, int32_t k, const void* q,
+                               const float* q_scale, const float* w, const void* kk,
+                               const float* k_scale, const int32_t* cand, const int32_t* heads,
+                               int32_t nh, int32_t* idx, float* scores_out, void* ws,
+                               hipStream_t st) {
   const int64_t rows = static_cast<int64_t>(s.batch) * s.T;
   float* sc = static_cast<float*>(ws);
   bool fused = false;  // the score kernel also took each query's top-k
+  const int64_t seq_bytes_all = static_cast<int64_t>(s.L) * kD * (s.dtype == kBF16 ? 2 : 1);
+  if (heads && (s.dtype == kF32 || seq_bytes_all >= (int64_t{1} << 31)))
+    return hipErrorInvalidValue;  // a head list is served by the LDS-gather kernel only
   if (s.dtype != kF32) {
-    const bool two = s.H > 32;
+    const bool two = (heads ? nh : s.H) > 32;
     // Two tiles of 32 candidates in flight per wave (fp8: 64 B per lane
     // each, bf16: 128 B).  Rounds per wave: as many as keep at least eight
     // workgroups per CU, up to 32, so the query rows staged into LDS once
@@ -586,7 +610,7 @@ hipError_t launch_rerank(const Shape& s, int32_t kprime, int32_t k, const void* 
     if (seq_bytes < (int64_t{1} << 31)) {
       dim3 g((kprime + per_wg - 1) / per_wg, s.T, s.batch);
       fused = per_wg >= kprime;
-#define RG(DT, RT, NTW, F) rerank_lds_kernel<DT, RT, NTW, F><<<g, kRRThreads, 0, st>>>(q, q_scale, w, kk, k_scale, cand, kprime, s.L, s.T, s.H, per_wg, sc, k, idx, scores_out)
+#define RG(DT, RT, NTW, F) rerank_lds_kernel<DT, RT, NTW, F><<<g, kRRThreads, 0, st>>>(q, q_scale, w, kk, k_scale, cand, kprime, s.L, s.T, s.H, per_wg, sc, k, idx, scores_out, heads, nh)
 #define RGF(DT, RT) if (fused) RG(DT, RT, kNtw, true); else RG(DT, RT, kNtw, false);
       if (s.dtype == kBF16) { if (two) { RGF(kBF16, 2) } else { RGF(kBF16, 1) } }
       else { if (two) { RGF(kFP8, 2) } else { RGF(kFP8, 1) } }

@@ -495,6 +495,14 @@ size_t route_mfma_ws_bytes(const Shape& s) {
   return 2 * align_up(static_cast<size_t>(s.batch) * s.M() * kD * sizeof(uint16_t)) + part;
 }
 
+hipError_t launch_pooled_split(const Shape& s, const float* pooled, uint16_t* hi, uint16_t* lo,
+                               hipStream_t st) {
+  const int64_t n4 = static_cast<int64_t>(s.batch) * s.M() * kD / 4;
+  pooled_split_kernel<<<static_cast<unsigned>((n4 + 255) / 256), 256, 0, st>>>(
+      pooled, reinterpret_cast<uint32_t*>(hi), reinterpret_cast<uint32_t*>(lo), n4);
+  return hipGetLastError();
+}
+
 hipError_t launch_route_mfma(const Shape& s, int32_t h, const void* q, const float* q_scale,
                              const float* w, const float* pooled, const void* k,
                              const float* k_scale, int32_t* heads, float* E_out, void* ws,

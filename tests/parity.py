@@ -70,12 +70,14 @@ class OracleProblem:
 
 
 def run_gpu(x: synth.Inputs, stages=("pool", "route", "score", "dense", "dagger", "step"), h=None,
-            k=None, kprime=None, device="cuda:0"):
+            k=None, kprime=None, m=None, device="cuda:0"):
     """Run the requested stages through the C ABI; returns numpy outputs.
 
     "step" (decode problems with bf16/fp8 inputs only) runs misa_decode_step
     on a copy of the pooled cache whose last block was overwritten, so the
-    step must rebuild it; its outputs carry the prefix "s_"."""
+    step must rebuild it; its outputs carry the prefix "s_".  "hisa" runs
+    misa_hisa_score_topk with m blocks on the routed heads; its outputs carry
+    the prefix "h"."""
     import torch
 
     import long_context_pool_amd as misa
@@ -96,7 +98,7 @@ def run_gpu(x: synth.Inputs, stages=("pool", "route", "score", "dense", "dagger"
     pooled = torch.empty((p.batch, p.M, p.d), dtype=torch.float32, device=dev)
     misa.misa_pool_keys(shp, kk, ks, pooled)
     out["pooled"] = pooled
-    if "route" in stages or "score" in stages or "dagger" in stages:
+    if "route" in stages or "score" in stages or "dagger" in stages or "hisa" in stages:
         heads = torch.empty((p.batch, p.T, h), dtype=torch.int32, device=dev)
         E = torch.empty((p.batch, p.T, p.H), dtype=torch.float32, device=dev)
         misa.misa_route(shp, h, q, qs, w, pooled, kk, ks, heads, E, ws)
@@ -119,6 +121,16 @@ def run_gpu(x: synth.Inputs, stages=("pool", "route", "score", "dense", "dagger"
         sc = torch.empty((p.batch, p.T, k), dtype=torch.float32, device=dev)
         misa.misa_rerank(shp, kprime, k, q, qs, w, kk, ks, cand, idx, sc, ws)
         out["cand"], out["cand_scores"], out["r_idx"], out["r_scores"] = cand, csc, idx, sc
+    if "hisa" in stages:
+        hws = torch.empty(max(1, misa.misa_hisa_workspace_bytes(shp, h, m, k)), dtype=torch.uint8,
+                          device=dev)
+        hb = torch.empty((p.batch, p.T, m), dtype=torch.int32, device=dev)
+        hbs = torch.empty((p.batch, p.T, m), dtype=torch.float32, device=dev)
+        idx = torch.empty((p.batch, p.T, k), dtype=torch.int32, device=dev)
+        sc = torch.empty((p.batch, p.T, k), dtype=torch.float32, device=dev)
+        misa.misa_hisa_score_topk(shp, h, m, k, q, qs, w, pooled, kk, ks, out["heads"], hb, hbs,
+                                  idx, sc, hws)
+        out["hb"], out["hbs"], out["h_idx"], out["h_scores"] = hb, hbs, idx, sc
     if "step" in stages and p.T == 1 and p.dtype != synth.F32:
         sp = pooled.clone()
         sp[:, p.M - 1].fill_(7.0)
@@ -244,3 +256,56 @@ def check_query_dagger(op: OracleProblem, gpu: dict, b: int, t: int, tol: float)
     check_values(gpu["r_scores"][b, t][v], [dense_of[int(s)] for s in sel[v]], tol, tau2,
                  f"rerank scores[{b},{t}]")
     return {"cand_swaps": sw1, "rerank_swaps": sw2}
+
+
+def check_query_hisa(op: OracleProblem, gpu: dict, b: int, t: int, tol: float):
+    """MISA x HISA for query (b, t): the blocks against the oracle's block
+    scores G (all heads), then the top-k given the GPU's heads and blocks.
+
+    G sums w * ReLU over heads and may cancel when weights are negative, so
+    its tolerance scale also takes the same sum with |w| (the size of the
+    terms that were added)."""
+    p = op.p
+    seq = op.seq(b)
+    pos = op.pos(t)
+    q, w = op.q[b, t], op.w[b, t]
+    m = gpu["hb"].shape[2]
+    G = seq.block_scores(pos, q, w)
+    Gabs = seq.block_scores(pos, q, np.abs(w))
+    Mt = len(G)
+    gb = gpu["hb"][b, t]
+    nb = min(m, Mt)
+    assert np.all(gb[nb:] == -1), f"hb[{b},{t}]: padding {gb[nb:]}"
+    sel = gb[:nb]
+    assert np.all(sel >= 0) and np.all(sel < Mt), f"hb[{b},{t}]: blocks out of range {sel}"
+    assert np.all(np.diff(sel) > 0), f"hb[{b},{t}] not ascending: {sel}"
+    tau = kth_value(G, m)
+    scale = np.maximum(np.abs(G), np.abs(tau))
+    scale = np.maximum(scale, Gabs)
+    G_sel = set(int(i) for i in sel)
+    ref_sel = set(int(i) for i in oracle.topk(G, m) if i >= 0)
+    assert len(G_sel) == len(ref_sel), f"hb[{b},{t}]: {len(G_sel)} blocks, oracle {len(ref_sel)}"
+    for j in G_sel ^ ref_sel:
+        assert abs(G[j] - tau) <= tol * scale[j], (
+            f"hb[{b},{t}]: block {j} (G {G[j]!r}, |w| sum {Gabs[j]!r}) differs outside the tie "
+            f"band around {tau!r}")
+    hbs = gpu["hbs"][b, t][:nb].astype(np.float64)
+    bad = np.abs(hbs - G[sel]) > tol * scale[sel]
+    assert not bad.any(), f"hbs[{b},{t}]: {bad.sum()} block scores out of tolerance"
+    assert np.all(gpu["hbs"][b, t][nb:] == -np.inf)
+    # Tokens: the oracle's Eq. (9) over the GPU's blocks with the GPU's heads.
+    heads = gpu["heads"][b, t]
+    I = seq.scores(pos, q, w, heads)
+    toks = np.concatenate([np.arange(j * p.B, min((j + 1) * p.B, pos + 1)) for j in sel])
+    k = gpu["h_idx"].shape[2]
+    cs = I[toks]
+    ref = toks[oracle.topk(cs, k)[: min(k, len(toks))]]
+    tau2 = kth_value(cs, k)
+    gi = gpu["h_idx"][b, t]
+    tokset = set(int(s) for s in toks)
+    assert all(int(s) in tokset for s in gi if s >= 0), f"h_idx[{b},{t}]: token outside the blocks"
+    sw = check_selection(gi, ref, lambda s: I[s], tau2, tol, f"h_idx[{b},{t}]")
+    v = gi >= 0
+    check_values(gpu["h_scores"][b, t][v], I[gi[v]], tol, tau2, f"h_scores[{b},{t}]")
+    assert np.all(gi[~v] == -1) and np.all(gpu["h_scores"][b, t][~v] == -np.inf)
+    return {"block_swaps": len(G_sel ^ ref_sel), "tok_swaps": sw}

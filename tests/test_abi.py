@@ -18,6 +18,28 @@ def _declared():
     return sorted(set(re.findall(r"\b((?:misa|dsa)_[a-z_]+)\s*\(", text)))
 
 
+def _param_counts():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = {}
+    for name, params in re.findall(r"\b((?:misa|dsa)_[a-z_]+)\s*\(([^;{]*?)\)\s*;", text, flags=re.S):
+        params = params.strip()
+        out[name] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_argument_lists_match_the_header():
+    """Each ctypes signature has as many parameters as its C declaration (a
+    missing one shifts the stream argument and crashes the launch)."""
+    import long_context_pool_amd as misa
+
+    lib = misa.lib()
+    counts = _param_counts()
+    assert set(counts) == set(_declared())
+    for name, n in counts.items():
+        assert len(getattr(lib, name).argtypes) == n, name
+
+
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("misa_pool_keys", "misa_route", "misa_score_topk", "misa_rerank", "dsa_index_dense",
@@ -166,3 +188,50 @@ def test_noalloc_decode_step_rejects_shapes_beyond_its_scratch():
                                       FAKE, None, FAKE, None, None)  # null pooled
     assert st == misa.MISA_ERR_INVALID_ARG
     assert misa.MISA_NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("ok-shape, ws too small", -3), ("fp32", -2), ("m=0", -1), ("m*B>8192", -2), ("h>16", -2),
+    ("null heads", -1), ("null pooled", -1), ("k>8192", -2), ("misaligned blocks_out", -1),
+])
+def test_hisa_argument_checks(case, expect):
+    import long_context_pool_amd as misa
+
+    lib = misa.lib()
+    shp = misa.shape(1, 4096, 64, 64, 128, 64, misa.MISA_BF16)
+    h, m, k, pooled, heads, bo, ws_bytes = 8, 16, 256, FAKE, FAKE, None, 1 << 40
+    if case == "ok-shape, ws too small":
+        ws_bytes = misa.misa_hisa_workspace_bytes(shp, h, m, k) - 1
+        assert ws_bytes > 0
+    elif case == "fp32":
+        shp = misa.shape(1, 4096, 64, 64, 128, 64, misa.MISA_F32)
+    elif case == "m=0":
+        m = 0
+    elif case == "m*B>8192":
+        m = 129
+    elif case == "h>16":
+        h = 17
+    elif case == "null heads":
+        heads = None
+    elif case == "null pooled":
+        pooled = None
+    elif case == "k>8192":
+        k = 8193
+    elif case == "misaligned blocks_out":
+        bo = FAKE + 4
+    st = lib.misa_hisa_score_topk(ctypes.byref(shp), h, m, k, FAKE, None, FAKE, pooled, FAKE, None,
+                                  heads, bo, None, FAKE, None, FAKE, ws_bytes, None)
+    assert st == expect
+
+
+def test_hisa_workspace_grows_with_the_candidate_list():
+    """The HISA workspace holds m B candidates per query, or k when k is
+    larger (the list is padded up to k)."""
+    import long_context_pool_amd as misa
+
+    shp = misa.shape(1, 65536, 4096, 64, 128, 64, misa.MISA_BF16)
+    a = misa.misa_hisa_workspace_bytes(shp, 8, 32, 2048)   # 2048 candidates
+    b = misa.misa_hisa_workspace_bytes(shp, 8, 128, 2048)  # 8192 candidates
+    c = misa.misa_hisa_workspace_bytes(shp, 8, 8, 2048)    # 512 blocks' tokens, padded to 2048
+    assert 0 < a < b and c >= a - 4096 * 24 * 4
+    assert misa.misa_hisa_workspace_bytes(shp, 8, 0, 2048) == 0

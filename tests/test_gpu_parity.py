@@ -175,6 +175,46 @@ def test_small_dagger(small_case):
          f"cand swaps {sum(r['cand_swaps'] for r in res)}, rerank swaps {sum(r['rerank_swaps'] for r in res)}")
 
 
+# MISA x HISA: (case, m).  m B below k (the list padded up to k), every
+# block of the early queries (M_t <= m), the fused re-rank select (2048
+# queries), 32 heads, a context shorter than one block.
+HISA = {
+    "bf16_ragged": 8, "fp8_ragged": 4, "h32_decode": 8, "t_eq_l": 2, "mq_fp8_t8": 4,
+    "fused_rerank_fp8": 4, "decode_lt_k": 1, "sample_chunks4_fp8": 2, "fp8_decode_b12": 3,
+}
+HISA_PAD = {"bf16_ragged": 4}  # 4 * 64 < k = 300
+
+
+@pytest.mark.parametrize("name,m", list(HISA.items()) + [(n + "/pad", m) for n, m in HISA_PAD.items()])
+def test_small_hisa(name, m):
+    p = SMALL[name.split("/")[0]]
+    _log(f"[gpu] hisa {name} m={m}: {p}")
+    x = synth.generate(p)
+    gpu = parity.run_gpu(x, stages=("pool", "route", "hisa"), m=m)
+    op = parity.OracleProblem(x)
+    res = parity.pmap(lambda bt: parity.check_query_hisa(op, gpu, *bt, parity.TOL[p.dtype]),
+                      _all_queries(p))
+    _log(f"[gpu] hisa {name}: {len(res)} queries; block swaps in band "
+         f"{sum(r['block_swaps'] for r in res)}, token swaps {sum(r['tok_swaps'] for r in res)}")
+
+
+def test_hisa_with_every_block_is_the_routed_top_k():
+    """m >= M: the block stage keeps every block, so the selection is the
+    routed top-k of misa_score_topk (both exact on integer inputs)."""
+    p = synth.small("hisa_all", batch=2, L=1000, T=20, H=64, h=8, B=64, k=100, kprime=None,
+                    dtype=synth.BF16, needles=0, seed=41)
+    x = synth.generate(p, exact_ints=True)
+    gpu = parity.run_gpu(x, stages=("pool", "route", "score", "hisa"), m=p.M)
+    for name, idx, sc in (("h", gpu["h_idx"], gpu["h_scores"]), ("misa", gpu["idx"], gpu["scores"])):
+        o = np.argsort(idx, axis=-1, kind="stable")
+        gpu[name + "_sorted"] = (np.take_along_axis(idx, o, -1), np.take_along_axis(sc, o, -1))
+    np.testing.assert_array_equal(gpu["h_sorted"][0], gpu["misa_sorted"][0])
+    np.testing.assert_array_equal(gpu["h_sorted"][1], gpu["misa_sorted"][1])
+    for t in range(p.T):
+        Mt = (p.L - p.T + t + p.B) // p.B
+        assert np.all(gpu["hb"][:, t, :Mt] == np.arange(Mt)) and np.all(gpu["hb"][:, t, Mt:] == -1)
+
+
 # ---------------------------------------------------------------- exact arithmetic
 
 
@@ -486,7 +526,7 @@ FULL = ["c2", "c3", "c4", "c5"]
 # Recall floors of the dense-DSA top-k on these synthetic workloads (measured
 # 0.70 / 0.81 for MISA at C2 / C3 and 0.99 / 0.96 for MISA-dagger at C4 / C5):
 # a gross error in any stage drops recall far below them.
-RECALL_FLOOR = {"misa": 0.6, "dagger": 0.9}
+RECALL_FLOOR = {"misa": 0.6, "dagger": 0.9, "hisa": 0.0}
 
 
 @pytest.fixture(scope="module", params=FULL)
@@ -535,6 +575,37 @@ def test_full_size_decode_step(full_case):
         pytest.skip("misa_decode_step covers decode (T = 1)")
     _check_step(op, gpu, _tile_queries(p), parity.TOL[p.dtype], name)
     assert (gpu["s_idx"].min(axis=2) >= 0).all()
+
+
+# MISA x HISA at the full workloads: m B = 8192 candidate tokens (4k).
+HISA_FULL_M = {"c2": 128, "c3": 128, "c4": 64, "c5": 64}
+
+
+def test_full_size_hisa(full_case):
+    """The block scores, top-m blocks and the routed top-k inside them on the
+    sampled queries, plus properties of every query's selection, and recall
+    of the dense top-k against the MISA floor."""
+    name, x, gpu, op = full_case
+    p = x.problem
+    m = HISA_FULL_M[name]
+    hg = parity.run_gpu(x, stages=("pool", "route", "hisa"), m=m)
+    qs = _tile_queries(p)
+    res = parity.pmap(lambda bt: parity.check_query_hisa(op, hg, *bt, parity.TOL[p.dtype]), qs)
+    pos = (p.L - p.T + np.arange(p.T))[None, :, None]
+    a = hg["h_idx"]
+    assert (a >= 0).all() and (a <= pos).all()
+    assert (np.diff(np.sort(a, axis=2), axis=2) > 0).all(), "duplicate indices"
+    for b in range(p.batch):
+        for t0 in range(0, p.T, 256):
+            blk = (a[b, t0:t0 + 256] // p.B)[..., None] == hg["hb"][b, t0:t0 + 256, None, :]
+            assert blk.any(axis=2).all(), f"seq {b}: a token outside its query's blocks"
+    rec = float(np.mean([len(np.intersect1d(a[i, t], gpu["d_idx"][i, t], assume_unique=True)) / p.k
+                         for i in range(p.batch) for t in range(p.T)]))
+    msg = (f"[gpu] {name}: MISA x HISA (m {m}) ok on {len(qs)} queries; block swaps "
+           f"{sum(r['block_swaps'] for r in res)}, token swaps {sum(r['tok_swaps'] for r in res)}; "
+           f"recall of dense top-k = {rec:.4f}")
+    _log(msg)
+    assert rec >= RECALL_FLOOR["hisa"], msg
 
 
 def test_full_size_output_properties_and_recall(full_case):
