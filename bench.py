@@ -70,6 +70,9 @@ def parse():
                     help="override the workload's queries per sequence (likewise; _T<T>)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--hisa-m", type=int, default=-1,
+                    help="blocks per query of the MISA x HISA leg (-1: 8192 / B, 4k candidates "
+                         "at k = 2048; 0: skip the leg)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate wall time of the oracle baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -111,7 +114,17 @@ class Runner:
             self.idx = torch.empty((p.batch, p.T, p.k), dtype=torch.int32, device=dev)
             self.didx = torch.empty((p.batch, p.T, p.k), dtype=torch.int32, device=dev)
             self.idx1 = torch.empty((p.batch, p.T, p.k), dtype=torch.int32, device=dev)
+            self.idxh = torch.empty((p.batch, p.T, p.k), dtype=torch.int32, device=dev)
         self.decode = p.T == 1
+        self.hisa_m = 0
+        self.hws = None
+
+    def set_hisa(self, m):
+        import torch
+
+        self.hisa_m = m
+        self.hws = torch.empty(self.misa.misa_hisa_workspace_bytes(self.shp, self.p.h, m, self.p.k),
+                               dtype=torch.uint8, device="cuda:0")
 
     def _pool_route(self, s):
         """Pooling (Eq. (4)) and routing (Eq. (7)-(8)) of a prefill step."""
@@ -168,6 +181,20 @@ class Runner:
             ev[0].record(st)
         m.misa_score_topk(self.shp, p.h, p.k, s["q"], s["qs"], s["w"], s["k"], s["ks"], self.heads,
                           self.idx1, None, self.ws, st)
+        if ev:
+            ev[1].record(st)
+
+    def hisa_step(self, i, ev=None):
+        """MISA x HISA: pooling and routing, then the top-m blocks by the
+        head-summed affinities and the routed top-k inside them; ev brackets
+        misa_hisa_score_topk."""
+        m, p, s, st = self.misa, self.p, self.sets[i % len(self.sets)], self.stream
+        self._pool_route(s)
+        if ev:
+            ev[0].record(st)
+        m.misa_hisa_score_topk(self.shp, p.h, self.hisa_m, p.k, s["q"], s["qs"], s["w"],
+                               s["pooled"], s["k"], s["ks"], self.heads, None, None, self.idxh,
+                               None, self.hws, st)
         if ev:
             ev[1].record(st)
 
@@ -352,6 +379,13 @@ def main():
         s_step, s_call, _, _ = time_steps(r.misa_1stage_step, args.steps, args.warmup, stream)
         res_1stage = {"value": pairs / (s_step / 1e3), "ms_per_step": s_step,
                       "score_topk_call_ms": s_call, "k": p.k}
+    res_hisa = None
+    hisa_m = (8192 // p.B) if args.hisa_m < 0 else args.hisa_m
+    if hisa_m > 0 and p.dtype != synth.F32:
+        r.set_hisa(hisa_m)
+        h_step, h_call, _, _ = time_steps(r.hisa_step, args.steps, args.warmup, stream)
+        res_hisa = {"m": hisa_m, "value": pairs / (h_step / 1e3), "ms_per_step": h_step,
+                    "hisa_call_ms": h_call, "k": p.k}
     res_dense = None
     if not args.no_dense:
         d_step, d_call, _, _ = time_steps(r.dense_step, args.steps, args.warmup, stream)
@@ -375,11 +409,16 @@ def main():
         r.dense_step(0)
         if res_1stage is not None:
             r.misa_1stage_step(0)
+        if res_hisa is not None:
+            r.hisa_step(0)
         torch.cuda.synchronize()
         recall = recall_of(r.idx)
         if res_1stage is not None:
             res_1stage["recall_vs_dense"] = recall_of(r.idx1)
             res_1stage["speedup_vs_dense"] = res_dense["ms_per_step"] / res_1stage["ms_per_step"]
+        if res_hisa is not None:
+            res_hisa["recall_vs_dense"] = recall_of(r.idxh)
+            res_hisa["speedup_vs_dense"] = res_dense["ms_per_step"] / res_hisa["ms_per_step"]
 
     e = {synth.F32: 4, synth.BF16: 2, synth.FP8_E4M3: 1}[p.dtype]
     dtype = {synth.F32: "f32", synth.BF16: "bf16", synth.FP8_E4M3: "fp8"}[p.dtype]
@@ -448,6 +487,7 @@ def main():
         "speedup_vs_dense": (res_dense["ms_per_step"] / m_step) if res_dense else None,
         "recall_vs_dense": recall,
         "misa_1stage": res_1stage,
+        "misa_x_hisa": res_hisa,
         "host_submit_ms_per_step": m_host,
         "source_sha": sha,
         "roofline": roof,

@@ -21,10 +21,11 @@
 //     to the workspace; the wave then finds the m-th largest G by a bitwise
 //     search on the order-preserving keys (ballot counts) and writes its m
 //     blocks in ascending order (ties: lower block).
-//  2. hisa_expand_kernel: the blocks' tokens, in order, as a candidate list
-//     of m B entries (tokens past the query's position, and padding, -1).
-//  3. the re-rank kernels with the routed heads (launch_rerank_heads): Eq. (9)
-//     over the candidates and their top-k.
+//  2. the re-rank kernels with the routed heads and the blocks as candidates
+//     (launch_rerank_heads with m > 0): entry i of a query's list is token
+//     blocks[i / B] * B + i % B, so no list is written; Eq. (9) over them and
+//     their top-k (tokens past the query's position, padding blocks and the
+//     entries past m B that pad the list to k are invalid).
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma.hpp"
@@ -345,28 +346,8 @@ __global__ __launch_bounds__(kHThreads, 2) void hisa_block_kernel(
   }
 }
 
-// Candidate tokens of the selected blocks, block by block: entry i < m B is
-// token blocks[i / B] * B + i % B, or -1 (padding block, or past the query);
-// entries m B <= i < nc (a list long enough for the top-k) are -1.  One
-// workgroup per query row.
-__global__ void hisa_expand_kernel(const int32_t* __restrict__ blocks, int32_t m, int32_t B,
-                                   int32_t nc, int32_t L, int32_t T, int32_t* __restrict__ cand) {
-  const int64_t r = blockIdx.x;
-  const int64_t pos = static_cast<int64_t>(L) - T + r % T;
-  const int32_t nb = m * B;
-  for (int32_t i = threadIdx.x; i < nc; i += blockDim.x) {
-    int32_t tok = -1;
-    if (i < nb) {
-      const int32_t b = blocks[r * m + i / B];
-      const int64_t t = static_cast<int64_t>(b) * B + i % B;
-      if (b >= 0 && t <= pos) tok = static_cast<int32_t>(t);
-    }
-    cand[r * nc + i] = tok;
-  }
-}
-
 struct HisaLayout {
-  size_t planes, G, blocks, cand, rerank, total;
+  size_t planes, G, blocks, rerank, total;
 };
 
 // Candidate list length: the m blocks' tokens, at least k entries.
@@ -383,8 +364,6 @@ HisaLayout hisa_layout(const Shape& s, int32_t m, int32_t k) {
   off += align_up(rows * s.M() * sizeof(float));
   lo.blocks = off;
   off += align_up(rows * m * sizeof(int32_t));
-  lo.cand = off;
-  off += align_up(rows * static_cast<size_t>(hisa_cands(s, m, k)) * sizeof(int32_t));
   lo.rerank = off;
   off += rerank_ws_bytes(s, hisa_cands(s, m, k));
   lo.total = off;
@@ -423,14 +402,8 @@ hipError_t launch_hisa_score_topk(const Shape& s, int32_t nh, const int32_t* hea
 #undef HB
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int32_t kp = hisa_cands(s, m, k);
-  int32_t* cand = reinterpret_cast<int32_t*>(base + lo.cand);
-  hisa_expand_kernel<<<static_cast<unsigned>(static_cast<int64_t>(s.batch) * s.T), 256, 0, st>>>(
-      blocks, m, s.B, kp, s.L, s.T, cand);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_rerank_heads(s, kp, k, q, q_scale, w, kk, k_scale, cand, heads, nh, idx, scores_out,
-                             base + lo.rerank, st);
+  return launch_rerank_heads(s, hisa_cands(s, m, k), k, q, q_scale, w, kk, k_scale, blocks, m, heads,
+                             nh, idx, scores_out, base + lo.rerank, st);
 }
 
 }  // namespace misa

@@ -90,13 +90,16 @@ hipError_t launch_rerank(const Shape& s, int32_t kprime, int32_t k, const void* 
                          hipStream_t st);
 
 // The re-rank with a list of heads per query (heads [batch*T, nh]; nullptr:
-// every head) -- the routed scoring over a candidate list.  bf16/fp8 keys
-// within a buffer descriptor's reach only when heads != nullptr.
+// every head) -- the routed scoring over a candidate list.  m > 0: `cand`
+// holds m blocks per query ([batch*T, m]) whose B tokens each are the first
+// m B of the kprime candidates (the rest padding); needs a head list of at
+// most 16.  Head lists and blocks: bf16/fp8 keys within a buffer
+// descriptor's reach only.
 hipError_t launch_rerank_heads(const Shape& s, int32_t kprime, int32_t k, const void* q,
                                const float* q_scale, const float* w, const void* kk,
-                               const float* k_scale, const int32_t* cand, const int32_t* heads,
-                               int32_t nh, int32_t* idx, float* scores_out, void* ws,
-                               hipStream_t st);
+                               const float* k_scale, const int32_t* cand, int32_t m,
+                               const int32_t* heads, int32_t nh, int32_t* idx, float* scores_out,
+                               void* ws, hipStream_t st);
 
 // Pooled keys -> bf16 hi and lo planes [batch*M, 128] (the router's B
 // operand).

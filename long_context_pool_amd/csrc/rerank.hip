@@ -13,6 +13,8 @@
 // Then one workgroup per query selects the k best of its k' scores in
 // registers: a digit histogram in LDS, the threshold digit from a block scan,
 // a block-scan compaction, and an exact resolve of the threshold digit.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma.hpp"
@@ -70,8 +72,40 @@ constexpr int kRRThreads = 256;
 constexpr int kRRWaves = kRRThreads / kWave;
 constexpr int kMaxKprime = 8192;
 
-// Per-wave state: the query's head rows (A) and per-lane row weights.
-template <int DT, int RT>
+// Candidate ids of a query's list: entry i of an explicit list, or of the
+// list that m blocks of B tokens spell out (entry i < m B is token
+// blocks[i / B] * B + i % B, -1 for a padding block; entries past m B are
+// -1).  Out-of-prefix ids are masked by the callers.
+struct ListIds {
+  const int32_t* p;
+  __device__ __forceinline__ int32_t operator()(int64_t i) const { return p[i]; }
+};
+struct BlockIds {
+  const int32_t* blk;  // the query's m blocks
+  int32_t B, nb;       // block size, m B
+  float invB;          // 1 / B (the quotient is corrected below)
+  __device__ __forceinline__ int32_t operator()(int64_t i) const {
+    if (i >= nb) return -1;
+    const int32_t ii = static_cast<int32_t>(i);
+    int32_t qb = static_cast<int32_t>(static_cast<float>(ii) * invB);
+    int32_t rem = ii - qb * B;
+    if (rem < 0) {
+      --qb;
+      rem += B;
+    } else if (rem >= B) {
+      ++qb;
+      rem -= B;
+    }
+    const int32_t b = blk[qb];
+    return b < 0 ? -1 : b * B + rem;
+  }
+};
+
+// Per-wave state: the query's head rows (A) and per-lane row weights.  NI:
+// accumulator values per lane and row tile that can hold a listed head (16;
+// 8 or 4 when at most 16 or 8 heads are scored: the lane's rows
+// 8 (i / 4) + 4 hf + i % 4 past them are zero).
+template <int DT, int RT, int NI = 16>
 struct CandScorer {
   bf16x8 a16[RT][8];
   i32x8 a8[RT][2];
@@ -147,11 +181,12 @@ struct CandScorer {
         for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_fp8(a8[rt][ks], bb, ks == 0 ? f32x16{} : acc[rt]);
       }
     }
+    static_assert(NI == 16 || (RT == 1 && (NI == 8 || NI == 4)), "narrow head sums: one row tile");
     float part = 0.f;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) part += wl[rt][i] * relu(acc[rt][i]);
+      for (int i = 0; i < NI; ++i) part += wl[rt][i] * relu(acc[rt][i]);
     return part + __shfl_xor(part, 32, kWave);  // rows 4hf..: the other half-wave
   }
 
@@ -233,11 +268,11 @@ struct LSelSmem {
 // The k best of one query's list: srow/crow its k' scores and candidates,
 // pos the query's position (candidates outside [0, pos] are invalid), out /
 // out_s its k output slots.  All kLSThreads threads of the workgroup call.
-template <int kLSThreads>
-__device__ __forceinline__ void list_select_row(const float* __restrict__ srow,
-                                                const int32_t* __restrict__ crow, int32_t kprime,
-                                                int64_t pos, int32_t k, int32_t* __restrict__ out,
-                                                float* __restrict__ out_s, LSelSmem<kLSThreads>& sm) {
+template <int kLSThreads, class Ids>
+__device__ __forceinline__ void list_select_row(const float* __restrict__ srow, Ids crow,
+                                                int32_t kprime, int64_t pos, int32_t k,
+                                                int32_t* __restrict__ out, float* __restrict__ out_s,
+                                                LSelSmem<kLSThreads>& sm) {
   constexpr int kLSPer = kMaxKprime / kLSThreads;  // list entries per thread (bits of a 32-bit mask)
   static_assert(kLSPer <= 32, "entry slots are bits of a 32-bit mask");
   for (int b = threadIdx.x; b < kLSBins; b += kLSThreads) sm.hist[b] = 0;
@@ -252,7 +287,7 @@ __device__ __forceinline__ void list_select_row(const float* __restrict__ srow,
     const int i = j * kLSThreads + threadIdx.x;
     const int ic = min(i, kprime - 1);
     const float x = srow[ic];
-    const int32_t c = crow[ic];
+    const int32_t c = crow(ic);
     const bool ok = c >= 0 && c <= pos;
     v[j] = ok ? x : -__builtin_inff();
     id[j] = ok ? c : -1 - i;
@@ -318,9 +353,9 @@ __device__ __forceinline__ void list_select_row(const float* __restrict__ srow,
     // with thousands of -inf ties).
     block_topk<kLSThreads>(
         kprime, k, [](int64_t) { return true; },
-        [=](int64_t i) { const int32_t c = crow[i]; return float_key(c >= 0 && c <= pos ? srow[i] : -__builtin_inff()); },
-        [=](int64_t i) { const int32_t c = crow[i]; return c >= 0 && c <= pos ? c : static_cast<int32_t>(-1 - i); },
-        [=](int64_t i) { const int32_t c = crow[i]; return c >= 0 && c <= pos ? srow[i] : -__builtin_inff(); },
+        [=](int64_t i) { const int32_t c = crow(i); return float_key(c >= 0 && c <= pos ? srow[i] : -__builtin_inff()); },
+        [=](int64_t i) { const int32_t c = crow(i); return c >= 0 && c <= pos ? c : static_cast<int32_t>(-1 - i); },
+        [=](int64_t i) { const int32_t c = crow(i); return c >= 0 && c <= pos ? srow[i] : -__builtin_inff(); },
         out, out_s, sm.base);
     __syncthreads();
     for (int p = threadIdx.x; p < k; p += kLSThreads)
@@ -391,15 +426,23 @@ __device__ __forceinline__ void list_select_row(const float* __restrict__ srow,
   }
 }
 
-template <int kLSThreads>
+// BLK: `cand` holds each query's m blocks of B tokens (BlockIds), else its
+// explicit list.
+template <int kLSThreads, bool BLK>
 __global__ __launch_bounds__(kLSThreads, kLSThreads == 256 ? 4 : 1) void list_select_kernel(
     const float* __restrict__ sc, const int32_t* __restrict__ cand, int32_t kprime, int32_t L,
-    int32_t T, int32_t k, int32_t* __restrict__ idx, float* __restrict__ scores_out) {
+    int32_t T, int32_t k, int32_t* __restrict__ idx, float* __restrict__ scores_out, int32_t m,
+    int32_t B) {
   __shared__ LSelSmem<kLSThreads> sm;
   const int64_t r = static_cast<int64_t>(blockIdx.y) * T + blockIdx.x;
   const int64_t pos = static_cast<int64_t>(L) - T + blockIdx.x;
-  list_select_row<kLSThreads>(sc + r * kprime, cand + r * kprime, kprime, pos, k, idx + r * k,
-                              scores_out ? scores_out + r * k : nullptr, sm);
+  float* so = scores_out ? scores_out + r * k : nullptr;
+  if constexpr (BLK)
+    list_select_row<kLSThreads>(sc + r * kprime, BlockIds{cand + r * m, B, m * B, 1.f / static_cast<float>(B)},
+                                kprime, pos, k, idx + r * k, so, sm);
+  else
+    list_select_row<kLSThreads>(sc + r * kprime, ListIds{cand + r * kprime}, kprime, pos, k, idx + r * k,
+                                so, sm);
 }
 
 // Gathers through LDS: a lane-per-candidate gather (lane l reads 16 bytes of
@@ -437,13 +480,17 @@ struct RerankScoreSmem {
 // workgroup selects the query's k best from its scores (re-read from L2; the
 // score phase's LDS is reused) and writes idx / scores_out, so no list-select
 // launch follows and the scores never make the round trip to HBM.
-template <int DT, int RT, int NTW, bool FUSED>
+// BLK: the candidates are the tokens of m blocks per query (`cand` holds the
+// blocks, [rows, m], of B tokens; entries past m B are padding), else an
+// explicit list.  NI as for CandScorer.
+template <int DT, int RT, int NTW, bool FUSED, bool BLK, int NI>
 __global__ __launch_bounds__(kRRThreads) void rerank_lds_kernel(
     const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const void* __restrict__ k, const float* __restrict__ k_scale,
     const int32_t* __restrict__ cand, int32_t kprime, int32_t L, int32_t T, int32_t H,
     int32_t per_wg, float* __restrict__ out, int32_t k_top, int32_t* __restrict__ idx,
-    float* __restrict__ scores_out, const int32_t* __restrict__ heads, int32_t nh) {
+    float* __restrict__ scores_out, const int32_t* __restrict__ heads, int32_t nh, int32_t m,
+    int32_t B) {
   constexpr int ROWB = kD * (DT == kBF16 ? 2 : 1);  // key row bytes
   constexpr int CPR = ROWB / 16;                     // 16-byte chunks per row
   constexpr int RPI = kWave / CPR;                   // rows per load instruction
@@ -481,7 +528,7 @@ __global__ __launch_bounds__(kRRThreads) void rerank_lds_kernel(
     wst[threadIdx.x] = j >= 0 ? w[r * H + j] * sq : 0.f;
   }
   __syncthreads();
-  CandScorer<DT, RT> cs;
+  CandScorer<DT, RT, NI> cs;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int j = rt * 32 + col;
@@ -503,7 +550,10 @@ __global__ __launch_bounds__(kRRThreads) void rerank_lds_kernel(
 
   const __amdgpu_buffer_rsrc_t rk =
       rr_rsrc(static_cast<const uint8_t*>(k) + seq * static_cast<int64_t>(L) * ROWB, L * ROWB);
-  const int32_t* crow = cand + r * kprime;
+  using Ids = typename std::conditional<BLK, BlockIds, ListIds>::type;
+  Ids crow;
+  if constexpr (BLK) crow = BlockIds{cand + r * m, B, m * B, 1.f / static_cast<float>(B)};
+  else crow = ListIds{cand + r * kprime};
   float* orow = out + r * kprime;
   const int c_wg = blockIdx.x * per_wg;
   const int c_end = min(c_wg + per_wg, kprime);
@@ -515,7 +565,7 @@ __global__ __launch_bounds__(kRRThreads) void rerank_lds_kernel(
 #pragma unroll
     for (int u = 0; u < NTW; ++u) {
       const int c = c_round + 32 * u + col;
-      svn[u] = c < c_end ? crow[c] : -1;
+      svn[u] = c < c_end ? crow(c) : -1;
     }
   };
   if (c_wg + wave * NTW * 32 < c_end) load_ids(c_wg + wave * NTW * 32);
@@ -543,7 +593,7 @@ __global__ __launch_bounds__(kRRThreads) void rerank_lds_kernel(
     rr_vmcnt0();  // this wave's rows have landed (its LDS slots are private)
 #pragma unroll
     for (int u = 0; u < NTW; ++u) {
-      typename CandScorer<DT, RT>::KeyB kb;
+      typename CandScorer<DT, RT, NI>::KeyB kb;
       const uint8_t* trow = &keys[wave][u][col * ROWB];
       if constexpr (DT == kBF16) {
 #pragma unroll
@@ -576,21 +626,22 @@ hipError_t launch_rerank(const Shape& s, int32_t kprime, int32_t k, const void* 
                          const float* q_scale, const float* w, const void* kk, const float* k_scale,
                          const int32_t* cand, int32_t* idx, float* scores_out, void* ws,
                          hipStream_t st) {
-  return launch_rerank_heads(s, kprime, k, q, q_scale, w, kk, k_scale, cand, nullptr, s.H, idx,
+  return launch_rerank_heads(s, kprime, k, q, q_scale, w, kk, k_scale, cand, 0, nullptr, s.H, idx,
                              scores_out, ws, st);
 }
 
 hipError_t launch_rerank_heads(const Shape& s, int32_t kprime, int32_t k, const void* q,
                                const float* q_scale, const float* w, const void* kk,
-                               const float* k_scale, const int32_t* cand, const int32_t* heads,
-                               int32_t nh, int32_t* idx, float* scores_out, void* ws,
-                               hipStream_t st) {
+                               const float* k_scale, const int32_t* cand, int32_t m,
+                               const int32_t* heads, int32_t nh, int32_t* idx, float* scores_out,
+                               void* ws, hipStream_t st) {
   const int64_t rows = static_cast<int64_t>(s.batch) * s.T;
   float* sc = static_cast<float*>(ws);
   bool fused = false;  // the score kernel also took each query's top-k
   const int64_t seq_bytes_all = static_cast<int64_t>(s.L) * kD * (s.dtype == kBF16 ? 2 : 1);
-  if (heads && (s.dtype == kF32 || seq_bytes_all >= (int64_t{1} << 31)))
-    return hipErrorInvalidValue;  // a head list is served by the LDS-gather kernel only
+  if ((heads || m > 0) && (s.dtype == kF32 || seq_bytes_all >= (int64_t{1} << 31)))
+    return hipErrorInvalidValue;  // head lists and block candidates: the LDS-gather kernel only
+  if (m > 0 && (!heads || nh > 16)) return hipErrorInvalidValue;
   if (s.dtype != kF32) {
     const bool two = (heads ? nh : s.H) > 32;
     // Two tiles of 32 candidates in flight per wave (fp8: 64 B per lane
@@ -610,10 +661,16 @@ hipError_t launch_rerank_heads(const Shape& s, int32_t kprime, int32_t k, const 
     if (seq_bytes < (int64_t{1} << 31)) {
       dim3 g((kprime + per_wg - 1) / per_wg, s.T, s.batch);
       fused = per_wg >= kprime;
-#define RG(DT, RT, NTW, F) rerank_lds_kernel<DT, RT, NTW, F><<<g, kRRThreads, 0, st>>>(q, q_scale, w, kk, k_scale, cand, kprime, s.L, s.T, s.H, per_wg, sc, k, idx, scores_out, heads, nh)
-#define RGF(DT, RT) if (fused) RG(DT, RT, kNtw, true); else RG(DT, RT, kNtw, false);
-      if (s.dtype == kBF16) { if (two) { RGF(kBF16, 2) } else { RGF(kBF16, 1) } }
+#define RG(DT, RT, NTW, F, BLK, NI) rerank_lds_kernel<DT, RT, NTW, F, BLK, NI><<<g, kRRThreads, 0, st>>>(q, q_scale, w, kk, k_scale, cand, kprime, s.L, s.T, s.H, per_wg, sc, k, idx, scores_out, heads, nh, m, s.B)
+#define RGF(DT, RT) if (fused) RG(DT, RT, kNtw, true, false, 16); else RG(DT, RT, kNtw, false, false, 16);
+#define RGB(DT, NI) if (fused) RG(DT, 1, kNtw, true, true, NI); else RG(DT, 1, kNtw, false, true, NI);
+      if (m > 0) {
+        // Block candidates with at most 16 routed heads: one row tile.
+        if (s.dtype == kBF16) { if (nh <= 8) { RGB(kBF16, 4) } else { RGB(kBF16, 8) } }
+        else { if (nh <= 8) { RGB(kFP8, 4) } else { RGB(kFP8, 8) } }
+      } else if (s.dtype == kBF16) { if (two) { RGF(kBF16, 2) } else { RGF(kBF16, 1) } }
       else { if (two) { RGF(kFP8, 2) } else { RGF(kFP8, 1) } }
+#undef RGB
 #undef RGF
 #undef RG
     } else {
@@ -635,10 +692,10 @@ hipError_t launch_rerank_heads(const Shape& s, int32_t kprime, int32_t k, const 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || fused) return e;
   dim3 g2(s.T, s.batch);
-  if (rows >= 1024)
-    list_select_kernel<256><<<g2, 256, 0, st>>>(sc, cand, kprime, s.L, s.T, k, idx, scores_out);
-  else
-    list_select_kernel<1024><<<g2, 1024, 0, st>>>(sc, cand, kprime, s.L, s.T, k, idx, scores_out);
+#define LS(NT, BLK) list_select_kernel<NT, BLK><<<g2, NT, 0, st>>>(sc, cand, kprime, s.L, s.T, k, idx, scores_out, m, s.B)
+  if (rows >= 1024) { if (m > 0) LS(256, true); else LS(256, false); }
+  else { if (m > 0) LS(1024, true); else LS(1024, false); }
+#undef LS
   return hipGetLastError();
 }
 

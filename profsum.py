@@ -3,6 +3,7 @@
     python profsum.py stats  <rocprof_dir> <out.md> --cmd "<command>"
     python profsum.py traffic <fetch_dir> <write_dir> <kernel_regex> \
         <copy_bytes> <workload> <out.json> --cmd "<command>"
+    python profsum.py pmc <kernel_regex> <workload> <out.md> <pmc_dir>... --cmd "<command>"
 
 `stats` lists every kernel of a --kernel-trace --stats run (calls, average
 and median duration).  `traffic` turns two --pmc runs (FETCH_SIZE, then
@@ -109,6 +110,51 @@ def traffic(fetch_dir: str, write_dir: str, regex: str, copy_bytes: int, workloa
         fh.write("\n")
 
 
+# Chip constants for the derived ratios (MI355X: 256 compute units of 4 SIMDs).
+CU_NUM, SIMD_NUM = 256, 1024
+
+
+def pmc(dirs: list, regex: str, workload: str, out: str, cmd: str) -> None:
+    """Median per dispatch of every counter collected for the kernels that
+    match ``regex`` (one or more --pmc runs of the same command), plus
+    ratios: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs),
+    VALU busy = SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE x CUs), and
+    instructions per MFMA instruction."""
+    vals = {}
+    for d in dirs:
+        for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+            if not re.search(regex, r["Kernel_Name"]):
+                continue
+            k = short_name(r["Kernel_Name"])
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    if not vals:
+        raise RuntimeError(f"no dispatch of {regex!r} in {dirs}")
+    lines = ["# rocprofv3 counters", "", f"Workload: {workload}", "", f"Command: `{cmd}`", "",
+             f"Kernels measured on the source tree with hash `{source_sha()}`. Values are medians "
+             "per dispatch; one --pmc pass per group of counters.", ""]
+    for k, cs in sorted(vals.items()):
+        med = {c: statistics.median(v) for c, v in cs.items()}
+        lines += [f"## `{k}`", "", "| counter | median per dispatch |", "|---|---|"]
+        lines += [f"| {c} | {v:.6g} |" for c, v in sorted(med.items())]
+        gui = med.get("GRBM_GUI_ACTIVE")
+        der = []
+        if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+            der.append(("MFMA busy (% of SIMD cycles)",
+                        100 * med["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMD_NUM)))
+        if gui and "SQ_ACTIVE_INST_VALU" in med:
+            der.append(("VALU issue (% of CU cycles)", 100 * med["SQ_ACTIVE_INST_VALU"] / (gui * CU_NUM)))
+        if "SQ_INSTS_MFMA" in med and med["SQ_INSTS_MFMA"] > 0:
+            for c in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM"):
+                if c in med:
+                    der.append((f"{c} per SQ_INSTS_MFMA", med[c] / med["SQ_INSTS_MFMA"]))
+        if der:
+            lines += ["", "| derived | value |", "|---|---|"]
+            lines += [f"| {n} | {v:.3g} |" for n, v in der]
+        lines.append("")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -124,8 +170,16 @@ def main():
     b.add_argument("workload")
     b.add_argument("out")
     b.add_argument("--cmd", required=True)
+    c = sub.add_parser("pmc")
+    c.add_argument("regex")
+    c.add_argument("workload")
+    c.add_argument("out")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--cmd", required=True)
     args = ap.parse_args()
-    if args.cmd_name == "stats":
+    if args.cmd_name == "pmc":
+        pmc(args.dirs, args.regex, args.workload, args.out, args.cmd)
+    elif args.cmd_name == "stats":
         stats(args.dir, args.out, args.cmd)
     else:
         traffic(args.fetch_dir, args.write_dir, args.regex, args.copy_bytes, args.workload, args.out,

@@ -526,7 +526,7 @@ FULL = ["c2", "c3", "c4", "c5"]
 # Recall floors of the dense-DSA top-k on these synthetic workloads (measured
 # 0.70 / 0.81 for MISA at C2 / C3 and 0.99 / 0.96 for MISA-dagger at C4 / C5):
 # a gross error in any stage drops recall far below them.
-RECALL_FLOOR = {"misa": 0.6, "dagger": 0.9, "hisa": 0.0}
+RECALL_FLOOR = {"misa": 0.6, "dagger": 0.9}
 
 
 @pytest.fixture(scope="module", params=FULL)
@@ -605,7 +605,11 @@ def test_full_size_hisa(full_case):
            f"{sum(r['block_swaps'] for r in res)}, token swaps {sum(r['tok_swaps'] for r in res)}; "
            f"recall of dense top-k = {rec:.4f}")
     _log(msg)
-    assert rec >= RECALL_FLOOR["hisa"], msg
+    # On these inputs (i.i.d. keys, no block locality) block means say little,
+    # so the floor is chance: m B of the L keys chosen at random (measured
+    # 0.31 / 0.19 / 0.094 / 0.092 against 0.25 / 0.125 / 0.0625 / 0.0625 at
+    # C2 / C3 / C4 / C5); a wrong block choice or scoring falls below it.
+    assert rec >= m * p.B / p.L, msg
 
 
 def test_full_size_output_properties_and_recall(full_case):
