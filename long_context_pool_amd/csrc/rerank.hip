@@ -13,8 +13,6 @@
 // Then one workgroup per query selects the k best of its k' scores in
 // registers: a digit histogram in LDS, the threshold digit from a block scan,
 // a block-scan compaction, and an exact resolve of the threshold digit.
-#include <type_traits>
-
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma.hpp"
@@ -77,27 +75,46 @@ constexpr int kMaxKprime = 8192;
 // blocks[i / B] * B + i % B, -1 for a padding block; entries past m B are
 // -1).  Out-of-prefix ids are masked by the callers.
 struct ListIds {
+  static constexpr bool kBlocks = false;
   const int32_t* p;
   __device__ __forceinline__ int32_t operator()(int64_t i) const { return p[i]; }
 };
 struct BlockIds {
+  static constexpr bool kBlocks = true;
   const int32_t* blk;  // the query's m blocks
   int32_t B, nb;       // block size, m B
   float invB;          // 1 / B (the quotient is corrected below)
-  __device__ __forceinline__ int32_t operator()(int64_t i) const {
-    if (i >= nb) return -1;
-    const int32_t ii = static_cast<int32_t>(i);
-    int32_t qb = static_cast<int32_t>(static_cast<float>(ii) * invB);
-    int32_t rem = ii - qb * B;
-    if (rem < 0) {
-      --qb;
-      rem += B;
-    } else if (rem >= B) {
-      ++qb;
-      rem -= B;
+  int32_t lgB;         // log2 B when B is a power of two, else -1
+  __device__ __forceinline__ BlockIds(const int32_t* blk_, int32_t B_, int32_t m)
+      : blk(blk_), B(B_), nb(m * B_), invB(1.f / static_cast<float>(B_)),
+        lgB((B_ & (B_ - 1)) == 0 ? 31 - __clz(B_) : -1) {}
+  // Entry i as (block slot, offset in the block); slot -1 past m B.
+  __device__ __forceinline__ void split(int32_t i, int32_t& qb, int32_t& rem) const {
+    if (i >= nb) {
+      qb = -1;
+      rem = 0;
+    } else if (lgB >= 0) {
+      qb = i >> lgB;
+      rem = i & (B - 1);
+    } else {
+      qb = static_cast<int32_t>(static_cast<float>(i) * invB);
+      rem = i - qb * B;
+      if (rem < 0) {
+        --qb;
+        rem += B;
+      } else if (rem >= B) {
+        ++qb;
+        rem -= B;
+      }
     }
-    const int32_t b = blk[qb];
-    return b < 0 ? -1 : b * B + rem;
+  }
+  // The loaded block of a slot (-1 for slot -1) and an offset -> token id.
+  __device__ __forceinline__ int32_t block_of(int32_t qb) const { return qb < 0 ? -1 : blk[qb]; }
+  __device__ __forceinline__ int32_t token(int32_t b, int32_t rem) const { return b < 0 ? -1 : b * B + rem; }
+  __device__ __forceinline__ int32_t operator()(int64_t i) const {
+    int32_t qb, rem;
+    split(static_cast<int32_t>(i), qb, rem);
+    return token(block_of(qb), rem);
   }
 };
 
@@ -249,6 +266,7 @@ __global__ __launch_bounds__(kRRThreads) void rerank_gather_kernel(
 // threads, three per CU).
 constexpr int kLSCap = 2048;
 constexpr int kLSBins = 2048;  // relative digit bins
+constexpr int kLSBlk = 512;    // block candidates: blocks staged in LDS (m B <= 8192, B >= 16)
 
 template <int kLSThreads>
 struct LSelSmem {
@@ -260,6 +278,7 @@ struct LSelSmem {
     TopkSmem base;
   };
   int scan_tmp[32];
+  int32_t blk[kLSBlk];
   int wtot[kLSThreads / kWave];
   int digit, above, count;
   uint32_t dmin, dmax;
@@ -269,7 +288,7 @@ struct LSelSmem {
 // pos the query's position (candidates outside [0, pos] are invalid), out /
 // out_s its k output slots.  All kLSThreads threads of the workgroup call.
 template <int kLSThreads, class Ids>
-__device__ __forceinline__ void list_select_row(const float* __restrict__ srow, Ids crow,
+__device__ __forceinline__ void list_select_row(const float* __restrict__ srow, const Ids crow,
                                                 int32_t kprime, int64_t pos, int32_t k,
                                                 int32_t* __restrict__ out, float* __restrict__ out_s,
                                                 LSelSmem<kLSThreads>& sm) {
@@ -280,18 +299,47 @@ __device__ __forceinline__ void list_select_row(const float* __restrict__ srow, 
     sm.dmin = 0xFFFFFFFFu;
     sm.dmax = 0u;
   }
+  // Block candidates: the ids are formed only for the entries written out,
+  // from the query's blocks staged in LDS (held ids would cost 32 registers
+  // per thread).  Their invalid entries (padding, outside the prefix) carry
+  // score -inf from the scoring pass, and a valid one never does (a finite
+  // sum), so the score tells them apart.
+  constexpr bool kBlk = Ids::kBlocks;
   float v[kLSPer];
-  int32_t id[kLSPer];
+  int32_t id[kBlk ? 1 : kLSPer];
+  bool blk_lds = false;
+  if constexpr (kBlk) {
+    const int32_t m = crow.nb / crow.B;
+    blk_lds = m <= kLSBlk;
+    if (blk_lds)
+      for (int i = threadIdx.x; i < m; i += kLSThreads) sm.blk[i] = crow.blk[i];
+    // (published by the barrier after the digit range below)
+  }
 #pragma unroll
   for (int j = 0; j < kLSPer; ++j) {
     const int i = j * kLSThreads + threadIdx.x;
     const int ic = min(i, kprime - 1);
     const float x = srow[ic];
-    const int32_t c = crow(ic);
-    const bool ok = c >= 0 && c <= pos;
-    v[j] = ok ? x : -__builtin_inff();
-    id[j] = ok ? c : -1 - i;
+    if constexpr (kBlk) {
+      v[j] = x;
+    } else {
+      const int32_t c = crow(ic);
+      const bool ok = c >= 0 && c <= pos;
+      v[j] = ok ? x : -__builtin_inff();
+      id[j] = ok ? c : -1 - i;
+    }
   }
+  auto id_of = [&](int j) -> int32_t {
+    if constexpr (kBlk) {
+      const int i = j * kLSThreads + threadIdx.x;
+      if (v[j] == -__builtin_inff()) return -1 - i;
+      int32_t qb, rem;
+      crow.split(i, qb, rem);
+      return crow.token(blk_lds ? sm.blk[qb] : crow.blk[qb], rem);
+    } else {
+      return id[j];
+    }
+  };
   // Relative digit (d - dmin) >> shift over the list's digit range [dmin,
   // dmax], the shift fitting the range in kLSBins bins.
   {
@@ -396,14 +444,14 @@ __device__ __forceinline__ void list_select_row(const float* __restrict__ srow, 
       if (h) {
         const int pos = ph + lanes_below(bh);
         if (pos < k) {
-          out[pos] = id[j];  // above b*: a valid candidate
+          out[pos] = id_of(j);  // above b*: a valid candidate
           if (out_s) out_s[pos] = v[j];
         }
       } else if (at) {
         const int pos = pa + lanes_below(ba);
         if (pos < kLSCap) {
           sm.cand_score[pos] = v[j];
-          sm.cand_idx[pos] = id[j];
+          sm.cand_idx[pos] = id_of(j);
         }
       }
       ph += __popcll(bh);
@@ -438,8 +486,8 @@ __global__ __launch_bounds__(kLSThreads, kLSThreads == 256 ? 4 : 1) void list_se
   const int64_t pos = static_cast<int64_t>(L) - T + blockIdx.x;
   float* so = scores_out ? scores_out + r * k : nullptr;
   if constexpr (BLK)
-    list_select_row<kLSThreads>(sc + r * kprime, BlockIds{cand + r * m, B, m * B, 1.f / static_cast<float>(B)},
-                                kprime, pos, k, idx + r * k, so, sm);
+    list_select_row<kLSThreads>(sc + r * kprime, BlockIds(cand + r * m, B, m), kprime, pos, k,
+                                idx + r * k, so, sm);
   else
     list_select_row<kLSThreads>(sc + r * kprime, ListIds{cand + r * kprime}, kprime, pos, k, idx + r * k,
                                 so, sm);
@@ -550,22 +598,30 @@ __global__ __launch_bounds__(kRRThreads) void rerank_lds_kernel(
 
   const __amdgpu_buffer_rsrc_t rk =
       rr_rsrc(static_cast<const uint8_t*>(k) + seq * static_cast<int64_t>(L) * ROWB, L * ROWB);
-  using Ids = typename std::conditional<BLK, BlockIds, ListIds>::type;
-  Ids crow;
-  if constexpr (BLK) crow = BlockIds{cand + r * m, B, m * B, 1.f / static_cast<float>(B)};
-  else crow = ListIds{cand + r * kprime};
+  const auto crow = [&]() {
+    if constexpr (BLK) return BlockIds(cand + r * m, B, m);
+    else return ListIds{cand + r * kprime};
+  }();
   float* orow = out + r * kprime;
   const int c_wg = blockIdx.x * per_wg;
   const int c_end = min(c_wg + per_wg, kprime);
   constexpr int kRoundStep = kRRWaves * NTW * 32;
   // This lane's candidate of each tile of a round (lanes l and l+32 share
-  // one).  The next round's are loaded while this round's rows are gathered.
-  int32_t svn[NTW];
+  // one).  The next round's are loaded while this round's rows are gathered
+  // (block candidates: the block is loaded then, and the token id formed
+  // when the round starts, so nothing waits for the load before that).
+  int32_t svn[NTW], svr[NTW];
   auto load_ids = [&](int c_round) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < NTW; ++u) {
       const int c = c_round + 32 * u + col;
-      svn[u] = c < c_end ? crow(c) : -1;
+      if constexpr (BLK) {
+        int32_t qb;
+        crow.split(c < c_end ? c : crow.nb, qb, svr[u]);
+        svn[u] = crow.block_of(qb);
+      } else {
+        svn[u] = c < c_end ? crow(c) : -1;
+      }
     }
   };
   if (c_wg + wave * NTW * 32 < c_end) load_ids(c_wg + wave * NTW * 32);
@@ -573,7 +629,11 @@ __global__ __launch_bounds__(kRRThreads) void rerank_lds_kernel(
     int32_t sid[NTW];
     float skv[NTW];
 #pragma unroll
-    for (int u = 0; u < NTW; ++u) sid[u] = (svn[u] >= 0 && svn[u] <= pos) ? svn[u] : -1;
+    for (int u = 0; u < NTW; ++u) {
+      int32_t id = svn[u];
+      if constexpr (BLK) id = crow.token(id, svr[u]);
+      sid[u] = (id >= 0 && id <= pos) ? id : -1;
+    }
     if (c_round + kRoundStep < c_end) load_ids(c_round + kRoundStep);
     // The tiles' key scales, and their rows into this wave's LDS slots.
 #pragma unroll
@@ -650,13 +710,16 @@ hipError_t launch_rerank_heads(const Shape& s, int32_t kprime, int32_t k, const 
     // per workgroup are reused over many candidate tiles on long prefill
     // lists, while a short decode batch still spreads over the chip.
     constexpr int kNtw = MISA_RERANK_NTW;
-    int rounds = 32;
+    // bf16 block candidates (MISA x HISA): one tile per round, so two
+    // workgroups fit a CU's LDS (their few heads leave the gathers exposed).
+    const int ntw = (m > 0 && s.dtype == kBF16) ? 1 : kNtw;
+    int rounds = 32 * kNtw / ntw;
     while (rounds > 1) {
-      const int64_t per = static_cast<int64_t>(kRRWaves) * 32 * kNtw * rounds;
+      const int64_t per = static_cast<int64_t>(kRRWaves) * 32 * ntw * rounds;
       if (rows * ((kprime + per - 1) / per) >= 2048) break;
       rounds >>= 1;
     }
-    const int per_wg = kRRWaves * 32 * kNtw * rounds;
+    const int per_wg = kRRWaves * 32 * ntw * rounds;
     const int64_t seq_bytes = static_cast<int64_t>(s.L) * kD * (s.dtype == kBF16 ? 2 : 1);
     if (seq_bytes < (int64_t{1} << 31)) {
       dim3 g((kprime + per_wg - 1) / per_wg, s.T, s.batch);
@@ -664,12 +727,14 @@ hipError_t launch_rerank_heads(const Shape& s, int32_t kprime, int32_t k, const 
 #define RG(DT, RT, NTW, F, BLK, NI) rerank_lds_kernel<DT, RT, NTW, F, BLK, NI><<<g, kRRThreads, 0, st>>>(q, q_scale, w, kk, k_scale, cand, kprime, s.L, s.T, s.H, per_wg, sc, k, idx, scores_out, heads, nh, m, s.B)
 #define RGF(DT, RT) if (fused) RG(DT, RT, kNtw, true, false, 16); else RG(DT, RT, kNtw, false, false, 16);
 #define RGB(DT, NI) if (fused) RG(DT, 1, kNtw, true, true, NI); else RG(DT, 1, kNtw, false, true, NI);
+#define RGB1(DT, NI) if (fused) RG(DT, 1, 1, true, true, NI); else RG(DT, 1, 1, false, true, NI);
       if (m > 0) {
         // Block candidates with at most 16 routed heads: one row tile.
-        if (s.dtype == kBF16) { if (nh <= 8) { RGB(kBF16, 4) } else { RGB(kBF16, 8) } }
+        if (s.dtype == kBF16) { if (nh <= 8) { RGB1(kBF16, 4) } else { RGB1(kBF16, 8) } }
         else { if (nh <= 8) { RGB(kFP8, 4) } else { RGB(kFP8, 8) } }
       } else if (s.dtype == kBF16) { if (two) { RGF(kBF16, 2) } else { RGF(kBF16, 1) } }
       else { if (two) { RGF(kFP8, 2) } else { RGF(kFP8, 1) } }
+#undef RGB1
 #undef RGB
 #undef RGF
 #undef RG
