@@ -813,6 +813,10 @@ constexpr int kSelRegsSmall = 32;
 constexpr int kSelThreadsLarge = 512;
 constexpr int kSelRegsLarge = 38;
 constexpr int kRelBins = 2048;
+// 64-entry chunks of the register-held entries (at most 512 x 38 of them);
+// a chunk that straddles a segment boundary is marked mixed.
+constexpr int kSelChunks = (kSelThreadsLarge * kSelRegsLarge + 63) / 64;
+constexpr int kChunkMixed = -0x7FFFFFFF;
 
 struct PSelSmem {
   uint32_t hist[kRelBins];
@@ -823,6 +827,7 @@ struct PSelSmem {
     TopkSmem ts;
   };
   int pre[9];
+  int ctab[kSelChunks];  // per 64-entry chunk: the slot offset of its one segment, or kChunkMixed
   int scan_tmp[32];
   int digit, above, count, nge, bad;
   int wtot[kTopkThreadsSel / kWave];  // per-wave packed counts above / at b* (up to 16 waves)
@@ -904,12 +909,38 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
     }
     return;
   }
-  // 1. entries t + NT u (u < NR) into registers.
+  // 1. entries t + NT u (u < NR) into registers.  Entry c of segment s sits
+  // at slot c + s cap - pre[s]; the 64 entries a wave loads per step form one
+  // chunk, and for a chunk within one segment that offset is taken from a
+  // table built here (one entry per thread), so only the few chunks that
+  // straddle a boundary search the segments lane by lane.
+  static_assert(NT % kWave == 0 && NT * NR <= kSelChunks * 64, "chunk table covers the registers");
+  const int nchunk = (min(total, NR * NT) + 63) / 64;
+  for (int j = threadIdx.x; j < nchunk; j += NT) {
+    auto seg_of = [&](int c) {
+      int sg = 0;
+#pragma unroll
+      for (int u = 1; u < 8; ++u) sg = (c >= pre[u] && u < S) ? u : sg;
+      return sg;
+    };
+    const int s_lo = seg_of(64 * j), s_hi = seg_of(min(64 * j + 63, total - 1));
+    sm.ctab[j] = s_lo == s_hi ? s_lo * cap - pre[s_lo] : kChunkMixed;
+  }
+  __syncthreads();
+  const int wave_e = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   uint2 e[NR];
 #pragma unroll
   for (int u = 0; u < NR; ++u) {
     const int c = u * NT + static_cast<int>(threadIdx.x);
-    e[u] = (u * NT < total && c < total) ? entry(c) : make_uint2(0u, 0u);
+    if (u * NT < total) {
+      const int j = (u * NT) / 64 + wave_e;  // this wave's chunk (uniform)
+      const int o = j < nchunk ? __builtin_amdgcn_readfirstlane(sm.ctab[j]) : kChunkMixed;
+      if (c >= total) e[u] = make_uint2(0u, 0u);
+      else if (o != kChunkMixed) e[u] = buffer_load_u32x2(crs, static_cast<uint32_t>(c + o) * 8u);
+      else e[u] = entry(c);
+    } else {
+      e[u] = make_uint2(0u, 0u);
+    }
   }
   // Relative digit (d - d0) >> shift.  Every candidate is >= tau_min, so
   // with a finite tau_min, d0 = its digit (and digits more than kRelBins

@@ -110,16 +110,20 @@ def traffic(fetch_dir: str, write_dir: str, regex: str, copy_bytes: int, workloa
         fh.write("\n")
 
 
-# Chip constants for the derived ratios (MI355X: 256 compute units of 4 SIMDs).
-CU_NUM, SIMD_NUM = 256, 1024
+# Chip constants for the derived ratios (MI355X: 256 compute units of 4 SIMDs
+# in 8 XCDs; GRBM_GUI_ACTIVE comes summed over the XCDs, so one XCD's busy
+# cycles are a eighth of it).
+CU_NUM, SIMD_NUM, XCD_NUM = 256, 1024, 8
 
 
 def pmc(dirs: list, regex: str, workload: str, out: str, cmd: str) -> None:
     """Median per dispatch of every counter collected for the kernels that
     match ``regex`` (one or more --pmc runs of the same command), plus
-    ratios: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs),
-    VALU busy = SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE x CUs), and
-    instructions per MFMA instruction."""
+    ratios over the kernel's cycles G = GRBM_GUI_ACTIVE / XCDs: MFMA busy =
+    SQ_VALU_MFMA_BUSY_CYCLES / (G x SIMDs), VALU issue = 4 SQ_INSTS_VALU /
+    (G x SIMDs) (a wave64 vector instruction holds a 16-lane SIMD four
+    cycles), waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES, and instructions per
+    MFMA instruction."""
     vals = {}
     for d in dirs:
         for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
@@ -137,12 +141,20 @@ def pmc(dirs: list, regex: str, workload: str, out: str, cmd: str) -> None:
         lines += [f"## `{k}`", "", "| counter | median per dispatch |", "|---|---|"]
         lines += [f"| {c} | {v:.6g} |" for c, v in sorted(med.items())]
         gui = med.get("GRBM_GUI_ACTIVE")
+        gui = gui / XCD_NUM if gui else None
         der = []
+        if gui:
+            der.append(("kernel cycles per XCD (GRBM_GUI_ACTIVE / 8)", gui))
         if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in med:
             der.append(("MFMA busy (% of SIMD cycles)",
                         100 * med["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMD_NUM)))
-        if gui and "SQ_ACTIVE_INST_VALU" in med:
-            der.append(("VALU issue (% of CU cycles)", 100 * med["SQ_ACTIVE_INST_VALU"] / (gui * CU_NUM)))
+        if gui and "SQ_INSTS_VALU" in med:
+            der.append(("VALU issue (% of SIMD cycles)", 100 * 4 * med["SQ_INSTS_VALU"] / (gui * SIMD_NUM)))
+        if gui and "SQ_VALU_MFMA_COEXEC_CYCLES" in med:
+            der.append(("VALU and MFMA together (% of SIMD cycles)",
+                        100 * med["SQ_VALU_MFMA_COEXEC_CYCLES"] / (gui * SIMD_NUM)))
+        if "SQ_WAIT_ANY" in med and med.get("SQ_WAVE_CYCLES"):
+            der.append(("waves waiting (% of wave cycles)", 100 * med["SQ_WAIT_ANY"] / med["SQ_WAVE_CYCLES"]))
         if "SQ_INSTS_MFMA" in med and med["SQ_INSTS_MFMA"] > 0:
             for c in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM"):
                 if c in med:
