@@ -38,7 +38,7 @@ namespace {
 constexpr int kHThreads = 256;
 constexpr int kHWaves = 4;
 constexpr int kHTileBytes = 32 * kD * 2;  // one bf16 plane of a 32-block pooled tile
-constexpr int kHMaxCache = 32;            // G values per lane kept in registers for the top-m
+constexpr int kHMaxCache = 64;            // G values per lane kept in registers for the top-m
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t hs_rsrc(const void* base, int32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
@@ -315,8 +315,33 @@ __global__ __launch_bounds__(kHThreads, 2) void hisa_block_kernel(
     }
     return cnt;
   };
-  uint32_t v = 0;
-  for (int bit = 31; bit >= 0; --bit) {
+  // The bits above the highest one on which the keys differ are common to
+  // all of them, so the search starts below those.
+  uint32_t kand = 0xFFFFFFFFu, kor = 0u;
+  if (cached) {
+#pragma unroll
+    for (int j = 0; j < kHMaxCache; ++j)
+      if (j < nch && static_cast<int64_t>(j) * kWave + lane < Mt) {
+        kand &= kc[j];
+        kor |= kc[j];
+      }
+  } else {
+    for (int j = 0; j < nch; ++j)
+      if (static_cast<int64_t>(j) * kWave + lane < Mt) {
+        const uint32_t key = key_of(j);
+        kand &= key;
+        kor |= key;
+      }
+  }
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) {
+    kand &= static_cast<uint32_t>(__shfl_xor(static_cast<int>(kand), o, kWave));
+    kor |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(kor), o, kWave));
+  }
+  const uint32_t diff = kand ^ kor;  // zero: every key is the same
+  const int top = diff ? 31 - __clz(static_cast<int>(diff)) : -1;
+  uint32_t v = top < 0 ? kand : (top == 31 ? 0u : kand & ~((2u << top) - 1u));
+  for (int bit = top; bit >= 0; --bit) {
     const uint32_t c = v | (1u << bit);
     if (count_ge(c) >= m) v = c;
   }

@@ -183,13 +183,27 @@ HISA = {
     "fused_rerank_fp8": 4, "decode_lt_k": 1, "sample_chunks4_fp8": 2, "fp8_decode_b12": 3,
 }
 HISA_PAD = {"bf16_ragged": 4}  # 4 * 64 < k = 300
+# Many blocks per query: the top-m search over G held in registers (up to
+# 64 per lane: 2048 < M_t <= 4096) and re-read from memory (M_t > 4096); and
+# every key equal (all block scores tie: the search has no differing bit).
+HISA_EXTRA = {
+    "hisa_b2_mid": (synth.small("hisa_b2_mid", batch=1, L=6000, T=5, H=64, h=8, B=2, k=100,
+                                kprime=None, dtype=synth.BF16, needles=4, seed=42), 256),
+    "hisa_b1_long": (synth.small("hisa_b1_long", batch=1, L=5000, T=3, H=32, h=4, B=1, k=64,
+                                 kprime=None, dtype=synth.FP8_E4M3, needles=4, seed=43), 512),
+    "hisa_equal_keys": (synth.small("hisa_equal_keys", batch=2, L=1000, T=6, H=64, h=8, B=64, k=50,
+                                    kprime=None, dtype=synth.BF16, needles=0, seed=44), 3),
+}
 
 
-@pytest.mark.parametrize("name,m", list(HISA.items()) + [(n + "/pad", m) for n, m in HISA_PAD.items()])
+@pytest.mark.parametrize("name,m", list(HISA.items()) + [(n + "/pad", m) for n, m in HISA_PAD.items()]
+                         + [(n, m) for n, (_, m) in HISA_EXTRA.items()])
 def test_small_hisa(name, m):
-    p = SMALL[name.split("/")[0]]
+    p = HISA_EXTRA[name][0] if name in HISA_EXTRA else SMALL[name.split("/")[0]]
     _log(f"[gpu] hisa {name} m={m}: {p}")
     x = synth.generate(p)
+    if name == "hisa_equal_keys":
+        x.k[:] = x.k[:, :1].clone()
     gpu = parity.run_gpu(x, stages=("pool", "route", "hisa"), m=m)
     op = parity.OracleProblem(x)
     res = parity.pmap(lambda bt: parity.check_query_hisa(op, gpu, *bt, parity.TOL[p.dtype]),
