@@ -14,8 +14,10 @@ A step is one pass of the hot path over one batch of synthetic input:
   prefill:        pool all keys -> route -> routed score + top-k [-> rerank].
 `value` is the whole step of the workload (MISA-dagger when it has k').  For
 such workloads the one-stage MISA step (routed top-k straight to k, no
-re-rank) is timed too.  The dense DSA indexer (all heads, same library) is
-timed the same way for the MISA-vs-DSA speedups.  Inputs are resident in HBM
+re-rank) is timed too, and for bf16/fp8 workloads the MISA x HISA step
+(pool -> route -> the top m = 8192 / B blocks by the head-summed router
+affinities -> routed top-k inside them).  The dense DSA indexer (all heads,
+same library) is timed the same way for the MISA-vs-DSA speedups.  Inputs are resident in HBM
 before timing starts; several input sets are rotated so that the decode
 workloads stream their keys from HBM instead of the 256 MB last-level cache.
 
