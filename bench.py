@@ -72,6 +72,8 @@ def parse():
                     help="override the workload's queries per sequence (likewise; _T<T>)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-1stage", action="store_true",
+                    help="skip the one-stage MISA leg of workloads with k' (profiling the main call alone)")
     ap.add_argument("--hisa-m", type=int, default=-1,
                     help="blocks per query of the MISA x HISA leg (-1: 8192 / B, 4k candidates "
                          "at k = 2048; 0: skip the leg)")
@@ -377,7 +379,7 @@ def main():
     m_step, m_call, m_host, m_pct = time_steps(r.misa_step, args.steps, args.warmup, stream)
     pairs = p.pairs
     res_1stage = None
-    if p.kprime:
+    if p.kprime and not args.no_1stage:
         s_step, s_call, _, _ = time_steps(r.misa_1stage_step, args.steps, args.warmup, stream)
         res_1stage = {"value": pairs / (s_step / 1e3), "ms_per_step": s_step,
                       "score_topk_call_ms": s_call, "k": p.k}

@@ -68,6 +68,11 @@ __device__ __forceinline__ T* hs_uniform(T* p) {
   return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+// The inverse of float_key.
+__device__ __forceinline__ float key_float(uint32_t key) {
+  return __builtin_bit_cast(float, (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
 // 32x32x16 fragments (8 k-steps) of one head or key row `row` (< 0: zeros):
 // this lane's elements [64*(l/32), 64*(l/32)+64); fp8 codes widen to bf16.
 template <int DT>
@@ -102,14 +107,128 @@ __device__ __forceinline__ void row_frags(const void* base, int64_t row, bf16x8 
   }
 }
 
+// Top-m blocks of one query's block scores Gq[0 .. Mt), written ascending
+// to bq (and their scores to bs when non-null); one wave; ties go to the
+// lower block.  The m-th largest order-preserving key v is found bit by bit
+// (ballot counts of keys >= a candidate value), starting below the leading
+// bits that every key shares; keys above v are taken, then the lowest blocks
+// of those equal to v.  CN > 0: the query's ceil(Mt / 64) <= CN keys per
+// lane are held in registers (CN a compile-time size, so the loops carry no
+// per-entry branch); CN = 0: they are re-read from memory.
+template <int CN>
+__device__ __forceinline__ void hisa_topm_n(const float* __restrict__ Gq, int64_t Mt, int32_t m,
+                                            int32_t* __restrict__ bq, float* __restrict__ bs) {
+  const int lane = lane_id();
+  const int nch = static_cast<int>((Mt + kWave - 1) / kWave);
+  constexpr int NC = CN > 0 ? CN : 1;
+  uint32_t kc[NC];
+  if constexpr (CN > 0) {
+    // Every load first (lanes past Mt re-read the last score, so no lane
+    // branches around a load), then the keys; padding keys are 0.
+    float gv[NC];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const int64_t b = static_cast<int64_t>(j) * kWave + lane;
+      gv[j] = Gq[b < Mt ? b : Mt - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < NC; ++j) kc[j] = static_cast<int64_t>(j) * kWave + lane < Mt ? float_key(gv[j]) : 0u;
+  }
+  auto key_of = [&](int j) -> uint32_t {
+    const int64_t b = static_cast<int64_t>(j) * kWave + lane;
+    return b < Mt ? float_key(Gq[b]) : 0u;
+  };
+  // Count of keys >= c (every valid key is >= 0x00800000: float_key of any
+  // finite float is at least that, so the padding key 0 never counts).
+  auto count_ge = [&](uint32_t c) -> int {
+    int cnt = 0;
+    if constexpr (CN > 0) {
+#pragma unroll
+      for (int j = 0; j < NC; ++j) cnt += __popcll(__ballot(kc[j] >= c));
+    } else {
+      for (int j = 0; j < nch; ++j) cnt += __popcll(__ballot(key_of(j) >= c));
+    }
+    return cnt;
+  };
+  uint32_t kand = 0xFFFFFFFFu, kor = 0u;
+  if constexpr (CN > 0) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j)
+      if (static_cast<int64_t>(j) * kWave + lane < Mt) {
+        kand &= kc[j];
+        kor |= kc[j];
+      }
+  } else {
+    for (int j = 0; j < nch; ++j)
+      if (static_cast<int64_t>(j) * kWave + lane < Mt) {
+        const uint32_t key = key_of(j);
+        kand &= key;
+        kor |= key;
+      }
+  }
+#pragma unroll
+  for (int o = kWave / 2; o >= 1; o >>= 1) {
+    kand &= static_cast<uint32_t>(__shfl_xor(static_cast<int>(kand), o, kWave));
+    kor |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(kor), o, kWave));
+  }
+  const uint32_t diff = kand ^ kor;  // zero: every key is the same
+  const int top = diff ? 31 - __clz(static_cast<int>(diff)) : -1;
+  uint32_t v = top < 0 ? kand : (top == 31 ? 0u : kand & ~((2u << top) - 1u));
+  for (int bit = top; bit >= 0; --bit) {
+    const uint32_t c = v | (1u << bit);
+    if (count_ge(c) >= m) v = c;
+  }
+  const int need_eq = m - count_ge(v + 1u);
+  int base = 0, eq_seen = 0;
+  auto emit = [&](int j, uint32_t key) __attribute__((always_inline)) {
+    const int64_t b = static_cast<int64_t>(j) * kWave + lane;
+    const bool valid = b < Mt;
+    const uint64_t eqm = __ballot(valid && key == v);
+    const bool sel = valid && (key > v || (key == v && eq_seen + lanes_below(eqm) < need_eq));
+    const uint64_t sm = __ballot(sel);
+    if (sel) {
+      const int p = base + lanes_below(sm);
+      bq[p] = static_cast<int32_t>(b);
+      if (bs) bs[p] = key_float(key);  // the score itself (-0 comes back as +0)
+    }
+    base += __popcll(sm);
+    eq_seen += __popcll(eqm);
+  };
+  if constexpr (CN > 0) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) emit(j, kc[j]);
+  } else {
+    for (int j = 0; j < nch; ++j) emit(j, key_of(j));
+  }
+}
+
+__device__ __forceinline__ void hisa_topm(const float* __restrict__ Gq, int64_t Mt, int32_t m,
+                                          int32_t* __restrict__ bq, float* __restrict__ bs) {
+  if (Mt <= m) {  // every block, then padding
+    for (int i = lane_id(); i < m; i += kWave) {
+      bq[i] = i < Mt ? i : -1;
+      if (bs) bs[i] = i < Mt ? Gq[i] : -__builtin_inff();
+    }
+    return;
+  }
+  const int64_t nch = (Mt + kWave - 1) / kWave;
+  if (nch <= 4) hisa_topm_n<4>(Gq, Mt, m, bq, bs);
+  else if (nch <= 8) hisa_topm_n<8>(Gq, Mt, m, bq, bs);
+  else if (nch <= 16) hisa_topm_n<16>(Gq, Mt, m, bq, bs);
+  else if (nch <= 32) hisa_topm_n<32>(Gq, Mt, m, bq, bs);
+  else if (nch <= kHMaxCache) hisa_topm_n<kHMaxCache>(Gq, Mt, m, bq, bs);
+  else hisa_topm_n<0>(Gq, Mt, m, bq, bs);
+}
+
 // Block scores and the top-m blocks.  Workgroup = four queries (one per
-// wave) of one sequence; RT = 32-head row tiles (H <= 32 RT ... ).
+// wave) of one sequence; RT = 32-head row tiles (1 for H <= 32, else 2).
 template <int DT, int RT>
 __global__ __launch_bounds__(kHThreads, 2) void hisa_block_kernel(
     const void* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint16_t* __restrict__ phi, const uint16_t* __restrict__ plo, const void* __restrict__ k,
     const float* __restrict__ k_scale, int32_t L, int32_t T, int32_t H, int32_t B, int64_t M,
-    int32_t m, float* __restrict__ G, int32_t* __restrict__ blocks, float* __restrict__ bscores) {
+    int32_t m, int32_t nsplit, float* __restrict__ G, int32_t* __restrict__ blocks,
+    float* __restrict__ bscores) {
   constexpr bool SPLIT = DT == kBF16;
   constexpr int LB = SPLIT ? kHTileBytes : 16;
   __shared__ __attribute__((aligned(16))) uint8_t h0[kHTileBytes];
@@ -159,8 +278,16 @@ __global__ __launch_bounds__(kHThreads, 2) void hisa_block_kernel(
   // Pooled tiles: three LDS buffers, two tiles in flight (the router's
   // pattern); 16-byte chunk c of tile row rr at chunk position c ^ (rr % 16).
   constexpr int NL = SPLIT ? 4 : 2;
-  const int64_t ntiles = (full_max + 31) / 32;
-  const int64_t last = ntiles > 0 ? ntiles - 1 : 0;
+  // Split z of nsplit takes tiles [tile0, tile1) (nsplit > 1: few queries,
+  // so each query's blocks are spread over more workgroups; the last split
+  // also takes the partial block, and hisa_topm_kernel picks the blocks).
+  const int z = blockIdx.z;
+  const int64_t ntiles_all = (full_max + 31) / 32;
+  const int64_t tps = (ntiles_all + nsplit - 1) / nsplit;
+  const int64_t tile0 = min<int64_t>(static_cast<int64_t>(z) * tps, ntiles_all);
+  const int64_t tile1 = min<int64_t>(tile0 + tps, ntiles_all);
+  const int64_t ntiles = tile1 - tile0;
+  const int64_t last = ntiles > 0 ? tile1 - 1 : 0;
   const __amdgpu_buffer_rsrc_t rh = hs_rsrc(hs_uniform(phi + seq * M * kD), static_cast<int32_t>(M * kD * 2));
   const __amdgpu_buffer_rsrc_t rl = hs_rsrc(hs_uniform(plo + seq * M * kD), static_cast<int32_t>(M * kD * 2));
   int rowi[2];
@@ -211,8 +338,8 @@ __global__ __launch_bounds__(kHThreads, 2) void hisa_block_kernel(
     if (active && lane < 32 && blk < full) Gq[blk] = g;
   };
   if (ntiles > 0) {
-    issue(0, h0, l0);
-    issue(1, h1, l1);
+    issue(tile0, h0, l0);
+    issue(tile0 + 1, h1, l1);
   }
   auto step = [&](int64_t bt, const uint8_t* hb, const uint8_t* lb, uint8_t* nh, uint8_t* nl)
       __attribute__((always_inline)) {
@@ -220,17 +347,17 @@ __global__ __launch_bounds__(kHThreads, 2) void hisa_block_kernel(
     issue(bt + 2, nh, nl);
     tile(bt, hb, lb);
   };
-  for (int64_t bt = 0; bt < ntiles; bt += 3) {
+  for (int64_t bt = tile0; bt < tile1; bt += 3) {
     step(bt, h0, l0, h2, l2);
-    if (bt + 1 < ntiles) step(bt + 1, h1, l1, h0, l0);
-    if (bt + 2 < ntiles) step(bt + 2, h2, l2, h1, l1);
+    if (bt + 1 < tile1) step(bt + 1, h1, l1, h0, l0);
+    if (bt + 2 < tile1) step(bt + 2, h2, l2, h1, l1);
   }
   hs_vmcnt_zero();
 
   // The partial last block [full B, pos]: G = sum_j w_j ReLU(mean_s q_j . k_s)
   // with the per-key dots from MFMA tiles (32 raw keys as B, the fp8 key
   // scale per column), summed over the keys.
-  if (active && Mt > full) {
+  if (active && Mt > full && z == nsplit - 1) {
     f32x16 ps[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) ps[rt] = f32x16{};
@@ -271,104 +398,26 @@ __global__ __launch_bounds__(kHThreads, 2) void hisa_block_kernel(
     for (int o = kWave / 2; o >= 1; o >>= 1) g += __shfl_xor(g, o, kWave);
     if (lane == 0) Gq[full] = g;
   }
-  if (!active) return;
+  if (!active || nsplit > 1) return;
   // The lanes read back G values other lanes of this wave stored: once the
   // stores have completed they are visible to loads from the same compute
   // unit (its vector L1 is write-through and shared by the unit's waves).
   hs_vmcnt_zero();
   __builtin_amdgcn_wave_barrier();
+  hisa_topm(Gq, Mt, m, blocks + r * m, bscores ? bscores + r * m : nullptr);
+}
 
-  // Top-m blocks of G[0 .. Mt), ascending (ties: lower block).
-  int32_t* bq = blocks + r * m;
-  float* bs = bscores ? bscores + r * m : nullptr;
-  const int nch = static_cast<int>((Mt + kWave - 1) / kWave);
-  if (Mt <= m) {
-    for (int i = lane; i < m; i += kWave) {
-      bq[i] = i < Mt ? i : -1;
-      if (bs) bs[i] = i < Mt ? Gq[i] : -__builtin_inff();
-    }
-    return;
-  }
-  uint32_t kc[kHMaxCache];
-  const bool cached = nch <= kHMaxCache;
-  if (cached) {
-#pragma unroll
-    for (int j = 0; j < kHMaxCache; ++j) {
-      const int64_t b = static_cast<int64_t>(j) * kWave + lane;
-      kc[j] = (j < nch && b < Mt) ? float_key(Gq[b]) : 0u;
-    }
-  }
-  auto key_of = [&](int j) -> uint32_t {
-    const int64_t b = static_cast<int64_t>(j) * kWave + lane;
-    return b < Mt ? float_key(Gq[b]) : 0u;
-  };
-  // Count of keys >= c (every valid key is >= 0x00800000: float_key of any
-  // finite float is at least that, so the padding key 0 never counts).
-  auto count_ge = [&](uint32_t c) -> int {
-    int cnt = 0;
-    if (cached) {
-#pragma unroll
-      for (int j = 0; j < kHMaxCache; ++j)
-        if (j < nch) cnt += __popcll(__ballot(kc[j] >= c));
-    } else {
-      for (int j = 0; j < nch; ++j) cnt += __popcll(__ballot(key_of(j) >= c));
-    }
-    return cnt;
-  };
-  // The bits above the highest one on which the keys differ are common to
-  // all of them, so the search starts below those.
-  uint32_t kand = 0xFFFFFFFFu, kor = 0u;
-  if (cached) {
-#pragma unroll
-    for (int j = 0; j < kHMaxCache; ++j)
-      if (j < nch && static_cast<int64_t>(j) * kWave + lane < Mt) {
-        kand &= kc[j];
-        kor |= kc[j];
-      }
-  } else {
-    for (int j = 0; j < nch; ++j)
-      if (static_cast<int64_t>(j) * kWave + lane < Mt) {
-        const uint32_t key = key_of(j);
-        kand &= key;
-        kor |= key;
-      }
-  }
-#pragma unroll
-  for (int o = kWave / 2; o >= 1; o >>= 1) {
-    kand &= static_cast<uint32_t>(__shfl_xor(static_cast<int>(kand), o, kWave));
-    kor |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(kor), o, kWave));
-  }
-  const uint32_t diff = kand ^ kor;  // zero: every key is the same
-  const int top = diff ? 31 - __clz(static_cast<int>(diff)) : -1;
-  uint32_t v = top < 0 ? kand : (top == 31 ? 0u : kand & ~((2u << top) - 1u));
-  for (int bit = top; bit >= 0; --bit) {
-    const uint32_t c = v | (1u << bit);
-    if (count_ge(c) >= m) v = c;
-  }
-  // Keys above v all go; of those equal to v, the lowest blocks fill m.
-  const int need_eq = m - count_ge(v + 1u);
-  int base = 0, eq_seen = 0;
-  auto emit = [&](int j, uint32_t key) __attribute__((always_inline)) {
-    const int64_t b = static_cast<int64_t>(j) * kWave + lane;
-    const bool valid = b < Mt;
-    const uint64_t eqm = __ballot(valid && key == v);
-    const bool sel = valid && (key > v || (key == v && eq_seen + lanes_below(eqm) < need_eq));
-    const uint64_t sm = __ballot(sel);
-    if (sel) {
-      const int p = base + lanes_below(sm);
-      bq[p] = static_cast<int32_t>(b);
-      if (bs) bs[p] = Gq[b];
-    }
-    base += __popcll(sm);
-    eq_seen += __popcll(eqm);
-  };
-  if (cached) {
-#pragma unroll
-    for (int j = 0; j < kHMaxCache; ++j)
-      if (j < nch) emit(j, kc[j]);
-  } else {
-    for (int j = 0; j < nch; ++j) emit(j, key_of(j));
-  }
+// The top-m blocks of each query from the block scores of the split kernel
+// (one wave per query row).
+__global__ __launch_bounds__(kHThreads) void hisa_topm_kernel(const float* __restrict__ G, int32_t L,
+                                                               int32_t T, int32_t B, int64_t M,
+                                                               int64_t rows, int32_t m,
+                                                               int32_t* __restrict__ blocks,
+                                                               float* __restrict__ bscores) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * kHWaves + threadIdx.x / kWave;
+  if (r >= rows) return;
+  const int64_t n = static_cast<int64_t>(L) - T + r % T + 1;
+  hisa_topm(G + r * M, (n + B - 1) / B, m, blocks + r * m, bscores ? bscores + r * m : nullptr);
 }
 
 struct HisaLayout {
@@ -405,6 +454,17 @@ bool hisa_supported(const Shape& s, int32_t m) {
 
 size_t hisa_ws_bytes(const Shape& s, int32_t m, int32_t k) { return hisa_layout(s, m, k).total; }
 
+// Block splits per query group: enough workgroups (about 512) to spread
+// the block scoring over the chip when the queries alone do not (decode).
+int32_t hisa_splits(const Shape& s) {
+  const int64_t wgs = static_cast<int64_t>((s.T + kHWaves - 1) / kHWaves) * s.batch;
+  if (wgs >= 512) return 1;
+  const int64_t tiles = (s.M() + 31) / 32;
+  int64_t n = (512 + wgs - 1) / wgs;
+  n = n < tiles ? n : tiles;
+  return static_cast<int32_t>(n < 1 ? 1 : (n > 64 ? 64 : n));
+}
+
 hipError_t launch_hisa_score_topk(const Shape& s, int32_t nh, const int32_t* heads, int32_t m,
                                   int32_t k, const void* q, const float* q_scale, const float* w,
                                   const float* pooled, const void* kk, const float* k_scale,
@@ -419,14 +479,22 @@ hipError_t launch_hisa_score_topk(const Shape& s, int32_t nh, const int32_t* hea
   if (e != hipSuccess) return e;
   float* G = reinterpret_cast<float*>(base + lo.G);
   int32_t* blocks = blocks_out ? blocks_out : reinterpret_cast<int32_t*>(base + lo.blocks);
-  dim3 g1((s.T + kHWaves - 1) / kHWaves, s.batch);
+  const int32_t nsplit = hisa_splits(s);
+  dim3 g1((s.T + kHWaves - 1) / kHWaves, s.batch, nsplit);
   const bool two = s.H > 32;
-#define HB(DT, RT) hisa_block_kernel<DT, RT><<<g1, kHThreads, 0, st>>>(q, q_scale, w, phi, plo, kk, k_scale, s.L, s.T, s.H, s.B, s.M(), m, G, blocks, block_scores_out)
+#define HB(DT, RT) hisa_block_kernel<DT, RT><<<g1, kHThreads, 0, st>>>(q, q_scale, w, phi, plo, kk, k_scale, s.L, s.T, s.H, s.B, s.M(), m, nsplit, G, blocks, block_scores_out)
   if (s.dtype == kBF16) { if (two) HB(kBF16, 2); else HB(kBF16, 1); }
   else { if (two) HB(kFP8, 2); else HB(kFP8, 1); }
 #undef HB
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (nsplit > 1) {
+    const int64_t rows = static_cast<int64_t>(s.batch) * s.T;
+    hisa_topm_kernel<<<static_cast<unsigned>((rows + kHWaves - 1) / kHWaves), kHThreads, 0, st>>>(
+        G, s.L, s.T, s.B, s.M(), rows, m, blocks, block_scores_out);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   return launch_rerank_heads(s, hisa_cands(s, m, k), k, q, q_scale, w, kk, k_scale, blocks, m, heads,
                              nh, idx, scores_out, base + lo.rerank, st);
 }
