@@ -287,7 +287,7 @@ struct LSelSmem {
 // The k best of one query's list: srow/crow its k' scores and candidates,
 // pos the query's position (candidates outside [0, pos] are invalid), out /
 // out_s its k output slots.  All kLSThreads threads of the workgroup call.
-template <int kLSThreads, class Ids>
+template <int kLSThreads, bool CACHE, class Ids>
 __device__ __forceinline__ void list_select_row(const float* __restrict__ srow, const Ids crow,
                                                 int32_t kprime, int64_t pos, int32_t k,
                                                 int32_t* __restrict__ out, float* __restrict__ out_s,
@@ -342,12 +342,29 @@ __device__ __forceinline__ void list_select_row(const float* __restrict__ srow, 
   };
   // Relative digit (d - dmin) >> shift over the list's digit range [dmin,
   // dmax], the shift fitting the range in kLSBins bins.
+  // CACHE: each entry's digit is computed once and kept, two 13-bit digits
+  // per register (where the registers allow); the histogram and the
+  // classification below then work on it (an entry lies above / in the
+  // threshold bin exactly when its digit does).
+  uint32_t dgp[CACHE ? (kLSPer + 1) / 2 : 1];
+  if constexpr (CACHE) {
+#pragma unroll
+    for (int j = 0; j < kLSPer; j += 2) {
+      const uint32_t d0j = key_digit(v[j]);
+      const uint32_t d1j = j + 1 < kLSPer ? key_digit(v[j + 1]) : 0u;
+      dgp[j / 2] = d0j | (d1j << 16);
+    }
+  }
+  auto digit_of = [&](int j) -> uint32_t {
+    if constexpr (CACHE) return (dgp[j / 2] >> (16 * (j & 1))) & 0xFFFFu;
+    else return key_digit(v[j]);
+  };
   {
     uint32_t dmin = 0xFFFFFFFFu, dmax = 0u;
 #pragma unroll
     for (int j = 0; j < kLSPer; ++j)
       if (j * kLSThreads + static_cast<int>(threadIdx.x) < kprime) {
-        const uint32_t d = key_digit(v[j]);
+        const uint32_t d = CACHE ? digit_of(j) : key_digit(v[j]);
         dmin = min(dmin, d);
         dmax = max(dmax, d);
       }
@@ -366,10 +383,19 @@ __device__ __forceinline__ void list_select_row(const float* __restrict__ srow, 
   const uint32_t span = sm.dmax - d0;
   const uint32_t shift = span < static_cast<uint32_t>(kLSBins) ? 0u : static_cast<uint32_t>(32 - __clz(static_cast<int>(span)) - 11);
   static_assert(kLSBins == 2048, "shift fits the span in 11 bits");
+  auto rel_of = [&](int j) -> uint32_t {
+    return min((digit_of(j) - d0) >> shift, static_cast<uint32_t>(kLSBins - 1));
+  };
+  if constexpr (CACHE) {
 #pragma unroll
-  for (int j = 0; j < kLSPer; ++j)
-    if (j * kLSThreads + static_cast<int>(threadIdx.x) < kprime)
-      atomicAdd(&sm.hist[min((key_digit(v[j]) - d0) >> shift, static_cast<uint32_t>(kLSBins - 1))], 1u);
+    for (int j = 0; j < kLSPer; ++j)
+      if (j * kLSThreads + static_cast<int>(threadIdx.x) < kprime) atomicAdd(&sm.hist[rel_of(j)], 1u);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kLSPer; ++j)
+      if (j * kLSThreads + static_cast<int>(threadIdx.x) < kprime)
+        atomicAdd(&sm.hist[min((key_digit(v[j]) - d0) >> shift, static_cast<uint32_t>(kLSBins - 1))], 1u);
+  }
   __syncthreads();
   {
     constexpr int BPT = kLSBins / kLSThreads;
@@ -409,17 +435,28 @@ __device__ __forceinline__ void list_select_row(const float* __restrict__ srow, 
     for (int p = threadIdx.x; p < k; p += kLSThreads)
       if (out[p] < 0) out[p] = -1;
   } else {
-    // Relative bin b* as a key interval [lo, hi].
-    const uint32_t dlo = d0 + (bstar << shift), dhi = d0 + ((bstar + 1) << shift) - 1u;
-    const uint32_t lo = digit_lo_key(dlo);
-    const uint32_t hi = (bstar == static_cast<uint32_t>(kLSBins - 1) || dhi >= kTopDigit) ? 0xFFFFFFFFu : digit_hi_key(dhi);
+    // Above / in the relative bin b*: by the cached digits, or by the key
+    // interval of b*'s digits (the last bin also holds every higher digit).
     uint32_t mh = 0, ma = 0;
+    if constexpr (CACHE) {
 #pragma unroll
-    for (int j = 0; j < kLSPer; ++j) {
-      const bool in = j * kLSThreads + static_cast<int>(threadIdx.x) < kprime;
-      const uint32_t key = float_key(v[j]);
-      mh |= (in && key > hi) ? (1u << j) : 0u;
-      ma |= (in && key >= lo && key <= hi) ? (1u << j) : 0u;
+      for (int j = 0; j < kLSPer; ++j) {
+        const bool in = j * kLSThreads + static_cast<int>(threadIdx.x) < kprime;
+        const uint32_t rb = rel_of(j);
+        mh |= (in && rb > bstar) ? (1u << j) : 0u;
+        ma |= (in && rb == bstar) ? (1u << j) : 0u;
+      }
+    } else {
+      const uint32_t dlo = d0 + (bstar << shift), dhi = d0 + ((bstar + 1) << shift) - 1u;
+      const uint32_t lo = digit_lo_key(dlo);
+      const uint32_t hi = (bstar == static_cast<uint32_t>(kLSBins - 1) || dhi >= kTopDigit) ? 0xFFFFFFFFu : digit_hi_key(dhi);
+#pragma unroll
+      for (int j = 0; j < kLSPer; ++j) {
+        const bool in = j * kLSThreads + static_cast<int>(threadIdx.x) < kprime;
+        const uint32_t key = float_key(v[j]);
+        mh |= (in && key > hi) ? (1u << j) : 0u;
+        ma |= (in && key >= lo && key <= hi) ? (1u << j) : 0u;
+      }
     }
     // Per-wave packed counts (above-b* low 16 bits: < k <= 8192; at-b*
     // high), then each wave's runs.
@@ -485,12 +522,15 @@ __global__ __launch_bounds__(kLSThreads, kLSThreads == 256 ? 4 : 1) void list_se
   const int64_t r = static_cast<int64_t>(blockIdx.y) * T + blockIdx.x;
   const int64_t pos = static_cast<int64_t>(L) - T + blockIdx.x;
   float* so = scores_out ? scores_out + r * k : nullptr;
+  // 256 threads (32 entries each, four workgroups per CU): no room to keep
+  // the digits.
+  constexpr bool kCache = kLSThreads != 256;
   if constexpr (BLK)
-    list_select_row<kLSThreads>(sc + r * kprime, BlockIds(cand + r * m, B, m), kprime, pos, k,
-                                idx + r * k, so, sm);
+    list_select_row<kLSThreads, kCache>(sc + r * kprime, BlockIds(cand + r * m, B, m), kprime, pos,
+                                        k, idx + r * k, so, sm);
   else
-    list_select_row<kLSThreads>(sc + r * kprime, ListIds{cand + r * kprime}, kprime, pos, k, idx + r * k,
-                                so, sm);
+    list_select_row<kLSThreads, kCache>(sc + r * kprime, ListIds{cand + r * kprime}, kprime, pos, k,
+                                        idx + r * k, so, sm);
 }
 
 // Gathers through LDS: a lane-per-candidate gather (lane l reads 16 bytes of
@@ -671,7 +711,7 @@ __global__ __launch_bounds__(kRRThreads) void rerank_lds_kernel(
   }
   if constexpr (FUSED) {
     __syncthreads();  // every score is written; the score phase's LDS is free
-    list_select_row<kRRThreads>(orow, crow, kprime, pos, k_top, idx + r * k_top,
+    list_select_row<kRRThreads, true>(orow, crow, kprime, pos, k_top, idx + r * k_top,
                                 scores_out ? scores_out + r * k_top : nullptr, smem.sel);
   }
 }
