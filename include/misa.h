@@ -218,8 +218,11 @@ misa_status dsa_index_dense(const misa_shape* shape, int32_t k, const void* q,
  *                     ascending, -1 padding
  *   block_scores_out  [batch, T, m]  fp32, written if non-NULL: G of each slot
  *   idx, scores_out   [batch, T, k]  as misa_score_topk
- * Limits: bf16 or fp8 inputs, m * B <= 8192, one sequence's keys below 2 GiB;
- * otherwise MISA_ERR_UNSUPPORTED.  ws must hold misa_hisa_workspace_bytes(). */
+ * Limits: bf16 or fp8 inputs, h <= 16, k <= 8192, m * B <= 8192, one
+ * sequence's keys below 2 GiB; otherwise MISA_ERR_UNSUPPORTED (h > H, m < 1,
+ * k < 1 or a NULL/misaligned input: MISA_ERR_INVALID_ARG).  ws must hold
+ * misa_hisa_workspace_bytes(shape, h, m, k) bytes (0 for invalid arguments);
+ * it carries nothing from one call to the next. */
 size_t misa_hisa_workspace_bytes(const misa_shape* shape, int32_t h, int32_t m, int32_t k);
 misa_status misa_hisa_score_topk(const misa_shape* shape, int32_t h, int32_t m, int32_t k,
                                  const void* q, const float* q_scale, const float* w,

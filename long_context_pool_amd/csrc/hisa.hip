@@ -20,7 +20,9 @@
 //     partial block's G comes from per-key MFMA dots on the raw keys.  G goes
 //     to the workspace; the wave then finds the m-th largest G by a bitwise
 //     search on the order-preserving keys (ballot counts) and writes its m
-//     blocks in ascending order (ties: lower block).
+//     blocks in ascending order (ties: lower block).  With few queries
+//     (decode) each query's blocks are split over up to 64 workgroups and
+//     hisa_topm_kernel picks the blocks afterwards.
 //  2. the re-rank kernels with the routed heads and the blocks as candidates
 //     (launch_rerank_heads with m > 0): entry i of a query's list is token
 //     blocks[i / B] * B + i % B, so no list is written; Eq. (9) over them and
