@@ -154,15 +154,18 @@ constexpr int kDigits = 8192;  // histogram bins of key_digit
 // bins 6% wide.
 constexpr int kExpLo = 127 - 31;  // window: values in [2^-31, 2^32)
 constexpr int kExpBins = 63;
+// Straight-line selects (no branches: it runs per entry in the top-k
+// kernels).  Inside the window the digit is 2 + (e - kExpLo) * 128 + the top
+// 7 mantissa bits, i.e. (u >> 16) - kExpLo * 128 + 2.
 __host__ __device__ __forceinline__ uint32_t key_digit(float v) {
   const uint32_t key = float_key(v);  // -0 has the key of +0
-  if (key < 0x80000000u) return 0u;
   const uint32_t u = key & 0x7FFFFFFFu;
-  const int e = static_cast<int>(u >> 23);
-  if (e == 0) return 1u;
-  if (e < kExpLo) return 2u;
-  if (e >= kExpLo + kExpBins) return 2u + ((kExpBins - 1) << 7) + 127u;
-  return 2u + (static_cast<uint32_t>(e - kExpLo) << 7) + ((u >> 16) & 0x7Fu);
+  const uint32_t e = u >> 23;
+  uint32_t d = (u >> 16) - (static_cast<uint32_t>(kExpLo) << 7) + 2u;
+  d = e >= static_cast<uint32_t>(kExpLo + kExpBins) ? 2u + ((kExpBins - 1) << 7) + 127u : d;
+  d = e < static_cast<uint32_t>(kExpLo) ? 2u : d;
+  d = e == 0u ? 1u : d;
+  return key < 0x80000000u ? 0u : d;
 }
 static_assert(2 + (kExpBins << 7) <= kDigits, "digit range");
 constexpr uint32_t kTopDigit = 2u + ((kExpBins - 1) << 7) + 127u;
