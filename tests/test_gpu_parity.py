@@ -182,7 +182,7 @@ HISA = {
     "bf16_ragged": 8, "fp8_ragged": 4, "h32_decode": 8, "t_eq_l": 2, "mq_fp8_t8": 4,
     "fused_rerank_fp8": 4, "decode_lt_k": 1, "sample_chunks4_fp8": 2, "fp8_decode_b12": 3,
 }
-HISA_PAD = {"bf16_ragged": 4}  # 4 * 64 < k = 300
+HISA_PAD = {"bf16_ragged": 4, "fp8_decode_b12": 1}  # m B = 256 < k = 300; 128 < 200 (decode)
 # Many blocks per query: the top-m search over G held in registers (up to
 # 64 per lane: 2048 < M_t <= 4096) and re-read from memory (M_t > 4096); and
 # every key equal (all block scores tie: the search has no differing bit).
@@ -193,6 +193,10 @@ HISA_EXTRA = {
                                  kprime=None, dtype=synth.FP8_E4M3, needles=4, seed=43), 512),
     "hisa_equal_keys": (synth.small("hisa_equal_keys", batch=2, L=1000, T=6, H=64, h=8, B=64, k=50,
                                     kprime=None, dtype=synth.BF16, needles=0, seed=44), 3),
+    # 2048 queries (the re-rank takes each query's top-k in its own
+    # workgroup) with m B = 128 < k = 200: the list is padded up to k.
+    "hisa_fused_pad": (synth.small("hisa_fused_pad", batch=1, L=3000, T=2048, H=32, h=8, B=64, k=200,
+                                   kprime=None, dtype=synth.FP8_E4M3, needles=4, seed=45), 2),
 }
 
 
