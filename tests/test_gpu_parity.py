@@ -85,6 +85,13 @@ SMALL = {
                                          B=64, k=100, kprime=300, dtype=synth.BF16, needles=8, seed=37),
     "t_eq_l": synth.small("t_eq_l", batch=1, L=200, T=200, H=64, h=8, B=64, k=64, kprime=96,
                           dtype=synth.BF16, needles=0, seed=24),
+    # The pages' own block size, B = 1024: five blocks, the last partial
+    # (router partial blocks larger than the staged rows), prefill and a
+    # batch-8 fp8 decode step (newest-block mean over up to 1024 keys).
+    "b1024_prefill": synth.small("b1024_prefill", batch=1, L=4500, T=40, H=64, h=8, B=1024, k=256,
+                                 kprime=600, dtype=synth.BF16, needles=6, seed=46),
+    "b1024_decode_fp8": synth.small("b1024_decode_fp8", batch=8, L=3900, T=1, H=32, h=8, B=1024, k=200,
+                                    kprime=400, dtype=synth.FP8_E4M3, needles=4, seed=47),
     "b1_h16": synth.small("b1_h16", batch=1, L=700, T=9, H=64, h=16, B=1, k=100, kprime=200,
                           dtype=synth.F32, needles=4, seed=25),
 }
