@@ -233,5 +233,8 @@ def test_hisa_workspace_grows_with_the_candidate_list():
     a = misa.misa_hisa_workspace_bytes(shp, 8, 32, 2048)   # 2048 candidates
     b = misa.misa_hisa_workspace_bytes(shp, 8, 128, 2048)  # 8192 candidates
     c = misa.misa_hisa_workspace_bytes(shp, 8, 8, 2048)    # 512 blocks' tokens, padded to 2048
-    assert 0 < a < b and c >= a - 4096 * 24 * 4
+    # c holds the same 2048 candidate scores per query as a, and 24 fewer
+    # block slots per query.
+    assert 0 < c < a < b
+    assert a - c <= 4096 * 24 * 4 + 2 * 256
     assert misa.misa_hisa_workspace_bytes(shp, 8, 0, 2048) == 0
