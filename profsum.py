@@ -155,6 +155,18 @@ def pmc(dirs: list, regex: str, workload: str, out: str, cmd: str) -> None:
                         100 * med["SQ_VALU_MFMA_COEXEC_CYCLES"] / (gui * SIMD_NUM)))
         if "SQ_WAIT_ANY" in med and med.get("SQ_WAVE_CYCLES"):
             der.append(("waves waiting (% of wave cycles)", 100 * med["SQ_WAIT_ANY"] / med["SQ_WAVE_CYCLES"]))
+        # Memory pipeline, per compute unit (one TA, TD and TCP each):
+        # busy or stalled cycles over the kernel's cycles.
+        for c, name in (("TA_TA_BUSY", "TA (address unit) busy"),
+                        ("TD_TD_BUSY", "TD (data unit) busy"),
+                        ("TA_ADDR_STALLED_BY_TC_CYCLES", "TA stalled by the L1 cache"),
+                        ("TCP_PENDING_STALL_CYCLES", "L1 cache stalled on data pending from L2")):
+            if gui and c in med:
+                der.append((f"{name} (% of CU cycles)", 100 * med[c] / (gui * CU_NUM)))
+        if med.get("TCP_TCC_READ_REQ"):
+            if "TCP_TCC_READ_REQ_LATENCY" in med:
+                der.append(("L1-to-L2 read latency (cycles per request)",
+                            med["TCP_TCC_READ_REQ_LATENCY"] / med["TCP_TCC_READ_REQ"]))
         if "SQ_INSTS_MFMA" in med and med["SQ_INSTS_MFMA"] > 0:
             for c in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM"):
                 if c in med:
