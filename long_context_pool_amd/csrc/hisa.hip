@@ -13,8 +13,8 @@
 // Kernels:
 //  1. hisa_block_kernel: one query per wave, its H head rows as the A operand
 //     of 32x32x16 MFMA tiles (held in registers; fp8 codes widen to bf16
-//     exactly), 32-block pooled tiles as B (bf16 hi plane, plus the lo plane
-//     for bf16 inputs, staged in LDS by buffer-to-LDS loads and shared by the
+//     exactly), 32-block pooled tiles as B (bf16 hi and lo planes of the
+//     pooled keys, staged in LDS by buffer-to-LDS loads and shared by the
 //     workgroup's four waves).  A lane then holds 16 heads of one block, so
 //     w * ReLU and the head sum stay in the lane (one cross-half add).  The
 //     partial block's G comes from per-key MFMA dots on the raw keys.  G goes
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kHThreads, 2) void hisa_block_kernel(
     const float* __restrict__ k_scale, int32_t L, int32_t T, int32_t H, int32_t B, int64_t M,
     int32_t m, int32_t nsplit, float* __restrict__ G, int32_t* __restrict__ blocks,
     float* __restrict__ bscores) {
-  constexpr bool SPLIT = DT == kBF16;
+  constexpr bool SPLIT = true;  // hi and lo bf16 planes of the pooled keys, for every input type
   constexpr int LB = SPLIT ? kHTileBytes : 16;
   __shared__ __attribute__((aligned(16))) uint8_t h0[kHTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t h1[kHTileBytes];

@@ -3,10 +3,10 @@
 //
 // For query t the router needs S_{t,j} = sum over the floor(n_t/B) complete
 // blocks of ReLU(q_{t,j} . p_b): a dense contraction of the pooled keys (A
-// operand, 32 blocks per row tile: fp32 rounded to bf16, and for bf16 inputs
-// also the bf16 rounding of the remainder, so q.p = q.p_hi + q.p_lo holds to
-// ~2^-16 -- a single bf16 rounding of p costs ~1e-3 relative in E on short
-// prefixes) with the query head rows (B operand, 32 heads per column tile,
+// operand, 32 blocks per row tile: fp32 rounded to bf16, plus the bf16
+// rounding of the remainder, so q.p = q.p_hi + q.p_lo holds to ~2^-16; a
+// single bf16 rounding of p alone put E 2.2% off on a two-block prefix, past
+// even the fp8 tolerance) with the query head rows (B operand, 32 heads per column tile,
 // bf16; fp8 codes widen to bf16 exactly) on 32x32x16 MFMA tiles.  Each lane
 // then holds 16 blocks of one head, so ReLU and the block sum stay in the
 // lane; one cross-half add per head finishes the sum.
@@ -173,15 +173,15 @@ __global__ void pooled_split_kernel(const float* __restrict__ pooled, uint32_t* 
 // HG: 32-head groups per query (1 for H <= 32, 2 for H <= 64); the wave's
 // kRCols column tiles are its kRCols / HG queries' head groups.
 #ifndef MISA_ROUTE_NBUF_FP8
-#define MISA_ROUTE_NBUF_FP8 4
+#define MISA_ROUTE_NBUF_FP8 3
 #endif
 #ifndef MISA_ROUTE_NBUF_BF16
 #define MISA_ROUTE_NBUF_BF16 3
 #endif
-// Pooled-tile buffers per workgroup (8 KiB per fp8 tile, 16 KiB per bf16
-// tile with its lo plane); NBUF - 1 tiles are in flight.  Deeper rings (up to
-// eight fp8 tiles) measured the same: the tiles come from L2.  The budget is
-// two workgroups per CU with the partial-block staging.
+// Pooled-tile buffers per workgroup (16 KiB per tile: the hi and lo bf16
+// planes); NBUF - 1 tiles are in flight.  Deeper rings (up to eight tiles of
+// one plane) measured the same: the tiles come from L2.  The budget is two
+// workgroups per CU with the partial-block staging.
 template <int DT>
 constexpr int route_nbuf() { return DT == kBF16 ? MISA_ROUTE_NBUF_BF16 : MISA_ROUTE_NBUF_FP8; }
 
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kRThreads, 2) void route_prefill_kernel(
     const float* __restrict__ k_scale, int32_t* __restrict__ heads, float* __restrict__ E_out,
     int32_t L, int32_t T, int32_t H, int32_t B, int64_t M, int32_t h, int32_t nsplit,
     float* __restrict__ part) {
-  constexpr bool SPLIT = DT == kBF16;
+  constexpr bool SPLIT = true;  // both planes, for every input type
   constexpr int LB = SPLIT ? kTileBytes : 16;
   constexpr int QW = kRCols / HG;         // queries per wave
   constexpr int QWG = QW * kRWaves;       // queries per workgroup
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kRThreads, 2) void route_prefill_kernel(
   // (16-byte chunk c of row r at chunk position c ^ (r % chunks per row)).
   constexpr int ROWB = DT == kBF16 ? kD * 2 : kD;
   constexpr int CPR = ROWB / 16;
-  constexpr int kPartRows = DT == kBF16 ? 80 : 192;  // B = 64 (bf16) or 128 (fp8) + QWG - 1 rows
+  constexpr int kPartRows = DT == kBF16 ? 80 : 160;  // B = 64 (bf16) or 128 (fp8) + QWG - 1 rows
   constexpr int kPartLoads = kPartRows * ROWB / 1024 / kRWaves;  // 1 KiB loads per wave
   static_assert(kPartLoads * kRWaves * 1024 == kPartRows * ROWB, "whole loads per wave");
   __shared__ __attribute__((aligned(16))) uint8_t pkeys[kPartRows * ROWB];

@@ -5,8 +5,10 @@ Comparison rule (values): |gpu - ref| <= tol * max(|ref|, |tau|), where tau is
 that query's oracle h-th (for E) or k-th (for scores) value; the floor avoids
 meaningless relative error on near-zero values that can never be selected.
 
-When a query has fewer candidates than k (all are returned), tau for the
-values is the largest of its candidate scores instead.
+When a query's list (its prefix, its MISA-dagger candidates or its MISA x
+HISA candidates) holds no more than k entries, all are returned and no k-th
+value separates them; likewise when the k-th value is a ReLU zero, every
+positive value is returned.  tau is then the largest of them instead.
 
 Comparison rule (selections): let band = {i : |ref_i - tau| <= tol*|tau|}.
 The GPU set and the oracle set must have the same size, agree exactly outside
@@ -158,9 +160,20 @@ def step_view(gpu: dict) -> dict:
 
 
 def kth_value(vals: np.ndarray, k: int) -> float:
-    """The k-th largest value (the last one when fewer than k)."""
+    """The k-th largest value (the last one when fewer than k): the centre of
+    the selection tie band."""
     k = min(k, len(vals))
     return float(np.partition(vals, len(vals) - k)[len(vals) - k])
+
+
+def value_tau(vals: np.ndarray, k: int) -> float:
+    """tau of the value comparison: the k-th largest value.  A list of at most
+    k values is selected whole, and when the k-th value is a ReLU zero every
+    positive value is selected: either way no value separates selected from
+    rejected entries, and tau is then the largest value (the scale of the
+    list)."""
+    v = kth_value(vals, k)
+    return float(np.max(vals)) if len(vals) <= k or v == 0.0 else v
 
 
 def check_values(gpu, ref, tol, tau, what=""):
@@ -199,7 +212,7 @@ def check_query_misa(op: OracleProblem, gpu: dict, b: int, t: int, tol: float):
         E_ref, heads_ref = seq.route(pos, q, w, gpu["heads"].shape[2])
         h = gpu["heads"].shape[2]
         tau = kth_value(E_ref, h)
-        check_values(gpu["E"][b, t], E_ref, tol, tau, f"E[{b},{t}]")
+        check_values(gpu["E"][b, t], E_ref, tol, value_tau(E_ref, h), f"E[{b},{t}]")
         gh = gpu["heads"][b, t]
         assert np.all(np.diff(gh) > 0), f"heads[{b},{t}] not ascending: {gh}"
         out["head_swaps"] = check_selection(gh, heads_ref, lambda j: E_ref[j], tau, tol,
@@ -214,7 +227,7 @@ def check_query_misa(op: OracleProblem, gpu: dict, b: int, t: int, tol: float):
                                            f"idx[{b},{t}]")
         sel = gpu["idx"][b, t]
         valid = sel >= 0
-        check_values(gpu["scores"][b, t][valid], I[sel[valid]], tol, tau, f"scores[{b},{t}]")
+        check_values(gpu["scores"][b, t][valid], I[sel[valid]], tol, value_tau(I, k), f"scores[{b},{t}]")
     return out
 
 
@@ -228,7 +241,8 @@ def check_query_dense(op: OracleProblem, gpu: dict, b: int, t: int, tol: float):
     sw = check_selection(gpu["d_idx"][b, t], r["idx"], lambda s: I[s], tau, tol, f"dense[{b},{t}]")
     sel = gpu["d_idx"][b, t]
     valid = sel >= 0
-    check_values(gpu["d_scores"][b, t][valid], I[sel[valid]], tol, tau, f"dense scores[{b},{t}]")
+    check_values(gpu["d_scores"][b, t][valid], I[sel[valid]], tol, value_tau(I, k),
+                 f"dense scores[{b},{t}]")
     return {"dense_swaps": sw, "dense_idx": r["idx"]}
 
 
@@ -254,9 +268,10 @@ def check_query_dagger(op: OracleProblem, gpu: dict, b: int, t: int, tol: float)
     sel = gpu["r_idx"][b, t]
     assert all(int(s) in dense_of for s in sel if s >= 0), f"rerank[{b},{t}]: index not a candidate"
     tau2 = float(sc_ref[min(k, len(valid_c)) - 1])
+    tau2_v = value_tau(np.asarray([dense_of[int(i)] for i in valid_c if int(i) in dense_of]), k)
     sw2 = check_selection(sel, idx_ref, lambda s: dense_of[s], tau2, tol, f"rerank[{b},{t}]")
     v = sel >= 0
-    check_values(gpu["r_scores"][b, t][v], [dense_of[int(s)] for s in sel[v]], tol, tau2,
+    check_values(gpu["r_scores"][b, t][v], [dense_of[int(s)] for s in sel[v]], tol, tau2_v,
                  f"rerank scores[{b},{t}]")
     return {"cand_swaps": sw1, "rerank_swaps": sw2}
 
@@ -304,10 +319,11 @@ def check_query_hisa(op: OracleProblem, gpu: dict, b: int, t: int, tol: float):
     cs = I[toks]
     ref = toks[oracle.topk(cs, k)[: min(k, len(toks))]]
     tau2 = kth_value(cs, k)
-    # Fewer candidates than k: every one is taken (no selection boundary), so
-    # the values' error scale is the size of the query's scores, not the
-    # smallest of them (fp8 codes are accumulated in fp32 at their own scale).
-    tau_v = tau2 if len(cs) > k else max(abs(tau2), float(np.abs(cs).max()))
+    # At most k candidates (every one is taken) or a ReLU-zero k-th value: no
+    # selection boundary among the values, so their error scale is the size
+    # of the query's scores (fp8 codes are accumulated in fp32 at their own
+    # scale).
+    tau_v = value_tau(cs, k)
     gi = gpu["h_idx"][b, t]
     tokset = set(int(s) for s in toks)
     assert all(int(s) in tokset for s in gi if s >= 0), f"h_idx[{b},{t}]: token outside the blocks"

@@ -240,6 +240,66 @@ def test_hisa_with_every_block_is_the_routed_top_k():
         assert np.all(gpu["hb"][:, t, :Mt] == np.arange(Mt)) and np.all(gpu["hb"][:, t, Mt:] == -1)
 
 
+# ---------------------------------------------------------------- random shapes
+#
+# Seeded random problems over the shape space the entry points accept:
+# decode and prefill, bf16 / fp8 (fp32 now and then), 16-64 heads and 1-16
+# routed, block sizes that are and are not powers of two (1 to 256), lists
+# shorter than k, k' above k, and MISA x HISA with m B up to the limit.
+# Every stage of every query is checked against the oracle.
+
+
+def _random_problem(seed: int):
+    rng = np.random.default_rng(9000 + seed)
+    dtype = (synth.F32 if seed % 7 == 6 else (synth.BF16, synth.FP8_E4M3)[seed % 2])
+    H = int(rng.choice([16, 32, 64]))
+    h = int(rng.integers(1, min(H, 16) + 1))
+    u = rng.random()
+    T = 1 if u < 0.4 else (int(rng.integers(2, 9)) if u < 0.6 else int(rng.integers(9, 301)))
+    batch = int(rng.integers(1, 9)) if T <= 8 else int(rng.integers(1, 3))
+    B = int(rng.choice([1, 2, 7, 16, 64, 100, 128, 256, 1024]))
+    u = rng.random()
+    if u < 0.15 and T <= 16:
+        L = int(rng.integers(6000, 40001))  # several key splits, long decode rows
+    elif u < 0.3:
+        L = int(rng.integers(T, T + 200))  # context about as long as the query chunk
+    else:
+        L = int(rng.integers(max(T, 2), 6001))
+    k = int(rng.integers(1, min(L, 1024) + 1)) if rng.random() < 0.8 else int(rng.integers(L, L + 300))
+    k = max(1, min(k, 8192))
+    kprime = int(rng.integers(k + 1, min(4 * k, 8192) + 2)) if rng.random() < 0.7 and k < 8192 else None
+    needles = int(rng.integers(0, 9))
+    p = synth.small(f"rand{seed}", batch=batch, L=L, T=T, H=H, h=h, B=B, k=k, kprime=kprime,
+                    dtype=dtype, needles=needles, seed=700 + seed)
+    mmax = max(1, 8192 // B)
+    m = int(rng.integers(1, min(mmax, 2 * p.M + 2) + 1))
+    return p, m
+
+
+@pytest.mark.parametrize("seed", range(64))
+def test_random_shapes(seed):
+    p, m = _random_problem(seed)
+    hisa = p.dtype != synth.F32
+    _log(f"[gpu] random shape {seed}: {p}" + (f", hisa m={m}" if hisa else ""))
+    x = synth.generate(p)
+    stages = ("pool", "route", "score", "dense", "dagger", "step") + (("hisa",) if hisa else ())
+    gpu = parity.run_gpu(x, stages=stages, m=m)
+    op = parity.OracleProblem(x)
+    tol = parity.TOL[p.dtype]
+    qs = _all_queries(p)
+    for b in range(p.batch):
+        ref = op.seq(b).pooled
+        np.testing.assert_allclose(gpu["pooled"][b], ref, rtol=1e-5, atol=1e-6 * np.abs(op.seq(b).K).max())
+    parity.pmap(lambda bt: parity.check_query_misa(op, gpu, *bt, tol), qs)
+    parity.pmap(lambda bt: parity.check_query_dense(op, gpu, *bt, tol), qs)
+    if p.kprime:
+        parity.pmap(lambda bt: parity.check_query_dagger(op, gpu, *bt, tol), qs)
+    if "s_idx" in gpu:
+        _check_step(op, gpu, qs, tol, f"rand{seed}")
+    if hisa:
+        parity.pmap(lambda bt: parity.check_query_hisa(op, gpu, *bt, tol), qs)
+
+
 # ---------------------------------------------------------------- exact arithmetic
 
 
