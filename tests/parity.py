@@ -11,6 +11,14 @@ value separates them; likewise when the k-th value is a ReLU zero, every
 positive value is returned.  tau is then the largest of them instead.
 
 Comparison rule (selections): let band = {i : |ref_i - tau| <= tol*|tau|}.
+
+Rounding allowance: where q_j . k cancels to near zero (or signed weights
+cancel across heads), no accumulation order holds a relative bound; each
+entry's bound and band are then at least EPS * M with M = sum_j |w_j|
+(|q_j| . |k|), the size of the products the score adds up, and EPS = 2^-16
+(fp32 accumulation of 128 products stays within about 2^-17 M).  M exceeds
+the plain bound only for such cancelling entries, and is computed just for
+the entries the plain rule rejects.
 The GPU set and the oracle set must have the same size, agree exactly outside
 the band, and differ only inside it.  Later stages are compared with the
 oracle fed the GPU's own (already checked) upstream output, so a legitimate
@@ -170,25 +178,50 @@ def value_tau(vals: np.ndarray, k: int) -> float:
     """tau of the value comparison: the k-th largest value.  A list of at most
     k values is selected whole, and when the k-th value is a ReLU zero every
     positive value is selected: either way no value separates selected from
-    rejected entries, and tau is then the largest value (the scale of the
-    list)."""
+    rejected entries, and tau is then the largest magnitude (the scale of
+    the list)."""
     v = kth_value(vals, k)
-    return float(np.max(vals)) if len(vals) <= k or v == 0.0 else v
+    return float(np.max(np.abs(vals))) if len(vals) <= k or v == 0.0 else v
 
 
-def check_values(gpu, ref, tol, tau, what=""):
+EPS = 2.0 ** -16
+
+
+def gross(seq, q, w, heads):
+    """keys -> M = sum over the (valid) heads of |w_j| (|q_j| . |k|): the size
+    of the products a score adds up (the rounding allowance's scale)."""
+    hs = np.asarray([j for j in np.asarray(heads).tolist() if 0 <= j < len(w)], dtype=np.int64)
+    qa = np.abs(np.asarray(q)[hs]) * np.abs(np.asarray(w)[hs])[:, None]  # [h, d]
+    qsum = qa.sum(axis=0)  # sum_j |w_j| |q_j|  (d,)
+    K = seq.K
+
+    def m(keys):
+        keys = np.asarray(keys, dtype=np.int64)
+        return np.abs(K[keys]) @ qsum
+    return m
+
+
+def check_values(gpu, ref, tol, tau, what="", mag=None):
+    """mag: callable (positions in these arrays) -> M of those entries (the
+    rounding allowance EPS * M), or None."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     lim = tol * np.maximum(np.abs(ref), abs(tau))
+    over = np.abs(gpu - ref) > lim
+    if mag is not None and over.any():
+        pos = np.nonzero(over)[0]
+        lim = lim.copy()
+        lim[pos] = np.maximum(lim[pos], EPS * mag(pos))
     bad = np.abs(gpu - ref) > lim
     assert not bad.any(), (
         f"{what}: {bad.sum()} values out of tolerance; first at {np.argmax(bad)}: "
         f"gpu={gpu[bad][0]!r} ref={ref[bad][0]!r} tau={tau!r}")
 
 
-def check_selection(gpu_sel, ref_sel, ref_score_of, tau, tol, what=""):
+def check_selection(gpu_sel, ref_sel, ref_score_of, tau, tol, what="", mag_of=None):
     """gpu_sel/ref_sel: 1-D index arrays (-1 = padding); ref_score_of: callable
-    index -> oracle score (double)."""
+    index -> oracle score (double); mag_of: callable index -> M of that index
+    (the rounding allowance), or None."""
     g = [int(i) for i in gpu_sel if i >= 0]
     r = [int(i) for i in ref_sel if i >= 0]
     assert len(g) == len(set(g)), f"{what}: duplicate indices in the GPU selection"
@@ -196,7 +229,10 @@ def check_selection(gpu_sel, ref_sel, ref_score_of, tau, tol, what=""):
     assert len(G) == len(R), f"{what}: |gpu| = {len(G)} != |ref| = {len(R)}"
     for i in G ^ R:
         s = ref_score_of(i)
-        assert abs(s - tau) <= tol * abs(tau), (
+        band = tol * abs(tau)
+        if abs(s - tau) > band and mag_of is not None:
+            band = max(band, EPS * float(mag_of(i)))
+        assert abs(s - tau) <= band, (
             f"{what}: index {i} (ref score {s!r}) differs outside the tie band around {tau!r}")
     return len(G ^ R)
 
@@ -220,14 +256,16 @@ def check_query_misa(op: OracleProblem, gpu: dict, b: int, t: int, tol: float):
     if "idx" in gpu:
         heads = gpu["heads"][b, t]
         I = seq.scores(pos, q, w, heads)
+        M = gross(seq, q, w, heads)
         k = gpu["idx"].shape[2]
         ref = oracle.topk(I, k)
         tau = kth_value(I, k)
         out["tok_swaps"] = check_selection(gpu["idx"][b, t], ref, lambda s: I[s], tau, tol,
-                                           f"idx[{b},{t}]")
+                                           f"idx[{b},{t}]", M)
         sel = gpu["idx"][b, t]
         valid = sel >= 0
-        check_values(gpu["scores"][b, t][valid], I[sel[valid]], tol, value_tau(I, k), f"scores[{b},{t}]")
+        check_values(gpu["scores"][b, t][valid], I[sel[valid]], tol, value_tau(I, k), f"scores[{b},{t}]",
+                     lambda ps: M(sel[valid][ps]))
     return out
 
 
@@ -237,12 +275,13 @@ def check_query_dense(op: OracleProblem, gpu: dict, b: int, t: int, tol: float):
     k = gpu["d_idx"].shape[2]
     r = seq.dense(pos, op.q[b, t], op.w[b, t], k)
     I = r["scores"]
+    M = gross(seq, op.q[b, t], op.w[b, t], np.arange(op.p.H))
     tau = kth_value(I, k)
-    sw = check_selection(gpu["d_idx"][b, t], r["idx"], lambda s: I[s], tau, tol, f"dense[{b},{t}]")
+    sw = check_selection(gpu["d_idx"][b, t], r["idx"], lambda s: I[s], tau, tol, f"dense[{b},{t}]", M)
     sel = gpu["d_idx"][b, t]
     valid = sel >= 0
     check_values(gpu["d_scores"][b, t][valid], I[sel[valid]], tol, value_tau(I, k),
-                 f"dense scores[{b},{t}]")
+                 f"dense scores[{b},{t}]", lambda ps: M(sel[valid][ps]))
     return {"dense_swaps": sw, "dense_idx": r["idx"]}
 
 
@@ -256,23 +295,25 @@ def check_query_dagger(op: OracleProblem, gpu: dict, b: int, t: int, tol: float)
     kp = gpu["cand"].shape[2]
     k = gpu["r_idx"].shape[2]
     I = seq.scores(pos, q, w, heads)
+    M = gross(seq, q, w, heads)
     tau = kth_value(I, kp)
     sw1 = check_selection(gpu["cand"][b, t], oracle.topk(I, kp), lambda s: I[s], tau, tol,
-                          f"cand[{b},{t}]")
+                          f"cand[{b},{t}]", M)
     cand = gpu["cand"][b, t]
     idx_ref, sc_ref = oracle.rerank(seq.K, q, w, cand, k)
     valid_c = cand[cand >= 0]
     # Eq. (1) score of every candidate, from the oracle (rerank keeping all).
     all_idx, all_sc = oracle.rerank(seq.K, q, w, cand, kp)
     dense_of = {int(i): float(v) for i, v in zip(all_idx, all_sc) if i >= 0}
+    Mall = gross(seq, q, w, np.arange(op.p.H))
     sel = gpu["r_idx"][b, t]
     assert all(int(s) in dense_of for s in sel if s >= 0), f"rerank[{b},{t}]: index not a candidate"
     tau2 = float(sc_ref[min(k, len(valid_c)) - 1])
     tau2_v = value_tau(np.asarray([dense_of[int(i)] for i in valid_c if int(i) in dense_of]), k)
-    sw2 = check_selection(sel, idx_ref, lambda s: dense_of[s], tau2, tol, f"rerank[{b},{t}]")
+    sw2 = check_selection(sel, idx_ref, lambda s: dense_of[s], tau2, tol, f"rerank[{b},{t}]", Mall)
     v = sel >= 0
     check_values(gpu["r_scores"][b, t][v], [dense_of[int(s)] for s in sel[v]], tol, tau2_v,
-                 f"rerank scores[{b},{t}]")
+                 f"rerank scores[{b},{t}]", lambda ps: Mall(sel[v][ps]))
     return {"cand_swaps": sw1, "rerank_swaps": sw2}
 
 
@@ -314,6 +355,7 @@ def check_query_hisa(op: OracleProblem, gpu: dict, b: int, t: int, tol: float):
     # Tokens: the oracle's Eq. (9) over the GPU's blocks with the GPU's heads.
     heads = gpu["heads"][b, t]
     I = seq.scores(pos, q, w, heads)
+    M = gross(seq, q, w, heads)
     toks = np.concatenate([np.arange(j * p.B, min((j + 1) * p.B, pos + 1)) for j in sel])
     k = gpu["h_idx"].shape[2]
     cs = I[toks]
@@ -327,8 +369,9 @@ def check_query_hisa(op: OracleProblem, gpu: dict, b: int, t: int, tol: float):
     gi = gpu["h_idx"][b, t]
     tokset = set(int(s) for s in toks)
     assert all(int(s) in tokset for s in gi if s >= 0), f"h_idx[{b},{t}]: token outside the blocks"
-    sw = check_selection(gi, ref, lambda s: I[s], tau2, tol, f"h_idx[{b},{t}]")
+    sw = check_selection(gi, ref, lambda s: I[s], tau2, tol, f"h_idx[{b},{t}]", M)
     v = gi >= 0
-    check_values(gpu["h_scores"][b, t][v], I[gi[v]], tol, tau_v, f"h_scores[{b},{t}]")
+    check_values(gpu["h_scores"][b, t][v], I[gi[v]], tol, tau_v, f"h_scores[{b},{t}]",
+                 lambda ps: M(gi[v][ps]))
     assert np.all(gi[~v] == -1) and np.all(gpu["h_scores"][b, t][~v] == -np.inf)
     return {"block_swaps": len(G_sel ^ ref_sel), "tok_swaps": sw}

@@ -15,10 +15,13 @@ Tolerances and the tie-band rule are in tests/parity.py.
 
 from __future__ import annotations
 
+import dataclasses
+import os
 import sys
 
 import numpy as np
 import pytest
+import torch
 
 import synth
 from tests import parity
@@ -276,12 +279,22 @@ def _random_problem(seed: int):
     return p, m
 
 
-@pytest.mark.parametrize("seed", range(64))
+# Number of seeded shapes (MISA_RANDOM_SHAPES / MISA_RANDOM_EXACT raise them
+# for a longer sweep).
+N_RANDOM = int(os.environ.get("MISA_RANDOM_SHAPES", "64"))
+N_RANDOM_EXACT = int(os.environ.get("MISA_RANDOM_EXACT", "32"))
+
+
+@pytest.mark.parametrize("seed", range(N_RANDOM))
 def test_random_shapes(seed):
     p, m = _random_problem(seed)
     hisa = p.dtype != synth.F32
-    _log(f"[gpu] random shape {seed}: {p}" + (f", hisa m={m}" if hisa else ""))
     x = synth.generate(p)
+    neg = seed % 4 == 3  # signed weights: Eq. (9) keeps the sign (Eq. (7) takes |w|)
+    if neg:
+        sign = np.random.default_rng(3000 + seed).choice([-1.0, 1.0], size=tuple(x.w.shape))
+        x.w.mul_(torch.from_numpy(sign).to(x.w.dtype))
+    _log(f"[gpu] random shape {seed}: {p}" + (f", hisa m={m}" if hisa else "") + (", signed w" if neg else ""))
     stages = ("pool", "route", "score", "dense", "dagger", "step") + (("hisa",) if hisa else ())
     gpu = parity.run_gpu(x, stages=stages, m=m)
     op = parity.OracleProblem(x)
@@ -298,6 +311,26 @@ def test_random_shapes(seed):
         _check_step(op, gpu, qs, tol, f"rand{seed}")
     if hisa:
         parity.pmap(lambda bt: parity.check_query_hisa(op, gpu, *bt, tol), qs)
+
+
+@pytest.mark.parametrize("seed", range(N_RANDOM_EXACT))
+def test_random_shapes_exact(seed):
+    """Random shapes on exact-integer inputs (every fp32 sum exact, heavy
+    ties; now and then all keys from some position on the same row): every
+    stage bit for bit, the oracle's tie rule included."""
+    p, _ = _random_problem(1000 + seed)
+    rng = np.random.default_rng(5000 + seed)
+    p = dataclasses.replace(p, needles=0, kprime=p.kprime or min(p.k + 1 + int(rng.integers(0, p.k + 1)), 8192))
+    x = synth.generate(p, exact_ints=True)
+    if rng.random() < 0.3:
+        dup = int(rng.integers(0, p.L))
+        x.k[:, dup:] = x.k[:, dup:dup + 1].clone()
+    neg = seed % 4 == 1
+    if neg:  # signed weights (exact: +-2^-m)
+        x.w.mul_(torch.from_numpy(rng.choice([-1.0, 1.0], size=tuple(x.w.shape))).to(x.w.dtype))
+    _log(f"[gpu] random exact shape {seed}: {p}" + (", signed w" if neg else ""))
+    gpu = parity.run_gpu(x)
+    _check_exact(x, gpu)
 
 
 # ---------------------------------------------------------------- exact arithmetic
@@ -317,24 +350,28 @@ def _check_exact(x, gpu):
         assert set(got.tolist()) == set(ref.tolist()), (
             f"{what}: {len(set(got.tolist()) ^ set(ref.tolist()))} indices differ")
 
+    def vals(what, got_idx, got_sc, ref_scores):
+        # Entries past a list shorter than k are padding: index -1, score -inf.
+        v = got_idx >= 0
+        assert np.all(got_sc[~v] == -np.inf), f"{what}: padding scores not -inf"
+        np.testing.assert_array_equal(got_sc[v], ref_scores[got_idx[v]].astype(np.float32), err_msg=what)
+
     def one(bt):
         b, t = bt
         seq, pos, q, w = op.seq(b), op.pos(t), op.q[b, t], op.w[b, t]
         I = seq.scores(pos, q, w, gpu["heads"][b, t])
         sel(f"idx[{b},{t}]", gpu["idx"][b, t], oracle.topk(I, p.k))
-        np.testing.assert_array_equal(gpu["scores"][b, t], I[gpu["idx"][b, t]].astype(np.float32))
+        vals(f"scores[{b},{t}]", gpu["idx"][b, t], gpu["scores"][b, t], I)
         d = seq.dense(pos, q, w, p.k)
         sel(f"dense[{b},{t}]", gpu["d_idx"][b, t], d["idx"])
-        np.testing.assert_array_equal(gpu["d_scores"][b, t],
-                                      d["scores"][gpu["d_idx"][b, t]].astype(np.float32))
+        vals(f"dense scores[{b},{t}]", gpu["d_idx"][b, t], gpu["d_scores"][b, t], d["scores"])
         sel(f"cand[{b},{t}]", gpu["cand"][b, t], oracle.topk(I, p.kprime))
         ridx, _ = oracle.rerank(seq.K, q, w, gpu["cand"][b, t], p.k)
         sel(f"rerank[{b},{t}]", gpu["r_idx"][b, t], ridx)
         if "s_idx" in gpu:
             Is = seq.scores(pos, q, w, gpu["s_heads"][b, t])
             sel(f"step idx[{b},{t}]", gpu["s_idx"][b, t], oracle.topk(Is, p.k))
-            np.testing.assert_array_equal(gpu["s_scores"][b, t],
-                                          Is[gpu["s_idx"][b, t]].astype(np.float32))
+            vals(f"step scores[{b},{t}]", gpu["s_idx"][b, t], gpu["s_scores"][b, t], Is)
 
     parity.pmap(one, _all_queries(p))
 
