@@ -299,22 +299,36 @@ def check_query_dagger(op: OracleProblem, gpu: dict, b: int, t: int, tol: float)
     tau = kth_value(I, kp)
     sw1 = check_selection(gpu["cand"][b, t], oracle.topk(I, kp), lambda s: I[s], tau, tol,
                           f"cand[{b},{t}]", M)
-    cand = gpu["cand"][b, t]
-    idx_ref, sc_ref = oracle.rerank(seq.K, q, w, cand, k)
+    sw2 = check_rerank(op, gpu["cand"][b, t], gpu["r_idx"][b, t], gpu["r_scores"][b, t], b, t, tol)
+    return {"cand_swaps": sw1, "rerank_swaps": sw2}
+
+
+def check_rerank(op: OracleProblem, cand, r_idx, r_scores, b: int, t: int, tol: float):
+    """Eq. (12) for query (b, t) given its candidate list (entries < 0 are
+    padding): the selection within the tie band and the returned scores."""
+    seq = op.seq(b)
+    q, w = op.q[b, t], op.w[b, t]
+    kp = len(cand)
+    k = len(r_idx)
     valid_c = cand[cand >= 0]
+    if len(valid_c) == 0:
+        assert np.all(r_idx == -1) and np.all(r_scores == -np.inf), f"rerank[{b},{t}]: no candidate"
+        return 0
+    idx_ref, sc_ref = oracle.rerank(seq.K, q, w, cand, k)
     # Eq. (1) score of every candidate, from the oracle (rerank keeping all).
     all_idx, all_sc = oracle.rerank(seq.K, q, w, cand, kp)
     dense_of = {int(i): float(v) for i, v in zip(all_idx, all_sc) if i >= 0}
     Mall = gross(seq, q, w, np.arange(op.p.H))
-    sel = gpu["r_idx"][b, t]
+    sel = r_idx
     assert all(int(s) in dense_of for s in sel if s >= 0), f"rerank[{b},{t}]: index not a candidate"
     tau2 = float(sc_ref[min(k, len(valid_c)) - 1])
     tau2_v = value_tau(np.asarray([dense_of[int(i)] for i in valid_c if int(i) in dense_of]), k)
     sw2 = check_selection(sel, idx_ref, lambda s: dense_of[s], tau2, tol, f"rerank[{b},{t}]", Mall)
     v = sel >= 0
-    check_values(gpu["r_scores"][b, t][v], [dense_of[int(s)] for s in sel[v]], tol, tau2_v,
+    check_values(r_scores[v], [dense_of[int(s)] for s in sel[v]], tol, tau2_v,
                  f"rerank scores[{b},{t}]", lambda ps: Mall(sel[v][ps]))
-    return {"cand_swaps": sw1, "rerank_swaps": sw2}
+    assert np.all(r_scores[~v] == -np.inf), f"rerank[{b},{t}]: padding scores not -inf"
+    return sw2
 
 
 def check_query_hisa(op: OracleProblem, gpu: dict, b: int, t: int, tol: float):

@@ -313,6 +313,58 @@ def test_random_shapes(seed):
         parity.pmap(lambda bt: parity.check_query_hisa(op, gpu, *bt, tol), qs)
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_random_rerank_lists(seed):
+    """misa_rerank on caller-made candidate lists: distinct prefix positions
+    in random slots among -1 padding, some queries with fewer valid entries
+    than k (or none), k' up to 8192, and row counts on both sides of the
+    fused (one workgroup per query) and the separate list-select paths."""
+    import long_context_pool_amd as misa
+
+    rng = np.random.default_rng(8000 + seed)
+    dtype = (synth.BF16, synth.FP8_E4M3)[seed % 2]
+    H = int(rng.choice([16, 32, 64]))
+    u = rng.random()
+    T = 1 if u < 0.3 else (int(rng.integers(2, 9)) if u < 0.5 else int(rng.integers(100, 1301)))
+    batch = int(rng.integers(1, 9)) if T <= 8 else 1
+    L = int(rng.integers(T + 50, 9000))
+    kprime = int(rng.integers(2, min(8192, L) + 1))
+    k = int(rng.integers(1, kprime + 1))
+    p = synth.small(f"rr{seed}", batch=batch, L=L, T=T, H=H, h=8, B=64, k=k, kprime=kprime,
+                    dtype=dtype, needles=4, seed=600 + seed)
+    x = synth.generate(p)
+    cand = np.full((batch, T, kprime), -1, dtype=np.int32)
+    for b in range(batch):
+        for t in range(T):
+            n = p.L - p.T + t + 1
+            r = rng.random()
+            nv = 0 if r < 0.03 else (int(rng.integers(1, min(n, k) + 1)) if r < 0.2 else int(rng.integers(1, min(n, kprime) + 1)))
+            slots = rng.choice(kprime, size=nv, replace=False)
+            cand[b, t, slots] = rng.choice(n, size=nv, replace=False)
+    _log(f"[gpu] random rerank lists {seed}: {p}")
+    dev = torch.device("cuda:0")
+    fp8 = dtype == synth.FP8_E4M3
+    q, kk, w = x.q.to(dev), x.k.to(dev), x.w.to(dev)
+    qs = x.q_scale.to(dev) if fp8 else None
+    ks = x.k_scale.to(dev) if fp8 else None
+    shp = misa.shape(p.batch, p.L, p.T, p.H, p.d, p.B, p.dtype)
+    ws = torch.empty(max(1, misa.misa_workspace_bytes(shp, p.h, k, kprime)), dtype=torch.uint8, device=dev)
+    c = torch.from_numpy(cand).to(dev)
+    idx = torch.empty((batch, T, k), dtype=torch.int32, device=dev)
+    sc = torch.empty((batch, T, k), dtype=torch.float32, device=dev)
+    misa.misa_rerank(shp, kprime, k, q, qs, w, kk, ks, c, idx, sc, ws)
+    torch.cuda.synchronize()
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    op = parity.OracleProblem(x)
+    tol = parity.TOL[dtype]
+    qs_all = _all_queries(p)
+    if len(qs_all) > 48:  # the oracle re-scores k' candidates with every head: a spread sample
+        pick = np.unique(np.linspace(0, len(qs_all) - 1, 48).astype(int))
+        qs_all = [qs_all[i] for i in pick]
+    parity.pmap(lambda bt: parity.check_rerank(op, cand[bt[0], bt[1]], idx[bt[0], bt[1]], sc[bt[0], bt[1]],
+                                               bt[0], bt[1], tol), qs_all)
+
+
 @pytest.mark.parametrize("seed", range(N_RANDOM_EXACT))
 def test_random_shapes_exact(seed):
     """Random shapes on exact-integer inputs (every fp32 sum exact, heavy
