@@ -201,6 +201,31 @@ def gross(seq, q, w, heads):
     return m
 
 
+def gross_E(seq, q, w, pos: int, B: int):
+    """Per head j, M of E_j (Eq. 7): |w_j| / M_t times the sum over the
+    complete blocks of |q_j| . |p_b| plus, for a partial last block, the mean
+    over its keys of |q_j| . |k_s| (the size of the products E adds up)."""
+    n = pos + 1
+    full, Mt = n // B, (n + B - 1) // B
+    qa = np.abs(np.asarray(q))  # [H, d]
+    acc = qa @ np.abs(np.asarray(seq.pooled)[:full]).sum(axis=0) if full else np.zeros(qa.shape[0])
+    if n % B:
+        acc = acc + qa @ np.abs(seq.K[full * B:n]).mean(axis=0)
+    return np.abs(np.asarray(w)) * acc / Mt
+
+
+def gross_G(seq, q, w, pos: int, B: int):
+    """Per block b, M of the block score G_b: sum_j |w_j| |q_j| . |p_b|, the
+    partial last block taking the mean over its keys of the same with |k_s|."""
+    n = pos + 1
+    full = n // B
+    qa = (np.abs(np.asarray(q)) * np.abs(np.asarray(w))[:, None]).sum(axis=0)  # (d,)
+    out = np.abs(np.asarray(seq.pooled)[:full]) @ qa
+    if n % B:
+        out = np.append(out, np.abs(seq.K[full * B:n]).mean(axis=0) @ qa)
+    return out
+
+
 def check_values(gpu, ref, tol, tau, what="", mag=None):
     """mag: callable (positions in these arrays) -> M of those entries (the
     rounding allowance EPS * M), or None."""
@@ -248,11 +273,12 @@ def check_query_misa(op: OracleProblem, gpu: dict, b: int, t: int, tol: float):
         E_ref, heads_ref = seq.route(pos, q, w, gpu["heads"].shape[2])
         h = gpu["heads"].shape[2]
         tau = kth_value(E_ref, h)
-        check_values(gpu["E"][b, t], E_ref, tol, value_tau(E_ref, h), f"E[{b},{t}]")
+        ME = gross_E(seq, q, w, pos, p.B)
+        check_values(gpu["E"][b, t], E_ref, tol, value_tau(E_ref, h), f"E[{b},{t}]", lambda ps: ME[ps])
         gh = gpu["heads"][b, t]
         assert np.all(np.diff(gh) > 0), f"heads[{b},{t}] not ascending: {gh}"
         out["head_swaps"] = check_selection(gh, heads_ref, lambda j: E_ref[j], tau, tol,
-                                            f"heads[{b},{t}]")
+                                            f"heads[{b},{t}]", lambda j: ME[j])
     if "idx" in gpu:
         heads = gpu["heads"][b, t]
         I = seq.scores(pos, q, w, heads)
@@ -355,15 +381,16 @@ def check_query_hisa(op: OracleProblem, gpu: dict, b: int, t: int, tol: float):
     tau = kth_value(G, m)
     scale = np.maximum(np.abs(G), np.abs(tau))
     scale = np.maximum(scale, Gabs)
+    allow = np.maximum(tol * scale, EPS * gross_G(seq, q, w, pos, p.B))  # (rounding allowance)
     G_sel = set(int(i) for i in sel)
     ref_sel = set(int(i) for i in oracle.topk(G, m) if i >= 0)
     assert len(G_sel) == len(ref_sel), f"hb[{b},{t}]: {len(G_sel)} blocks, oracle {len(ref_sel)}"
     for j in G_sel ^ ref_sel:
-        assert abs(G[j] - tau) <= tol * scale[j], (
+        assert abs(G[j] - tau) <= allow[j], (
             f"hb[{b},{t}]: block {j} (G {G[j]!r}, |w| sum {Gabs[j]!r}) differs outside the tie "
             f"band around {tau!r}")
     hbs = gpu["hbs"][b, t][:nb].astype(np.float64)
-    bad = np.abs(hbs - G[sel]) > tol * scale[sel]
+    bad = np.abs(hbs - G[sel]) > allow[sel]
     assert not bad.any(), f"hbs[{b},{t}]: {bad.sum()} block scores out of tolerance"
     assert np.all(gpu["hbs"][b, t][nb:] == -np.inf)
     # Tokens: the oracle's Eq. (9) over the GPU's blocks with the GPU's heads.

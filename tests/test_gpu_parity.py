@@ -262,13 +262,16 @@ def _random_problem(seed: int):
     batch = int(rng.integers(1, 9)) if T <= 8 else int(rng.integers(1, 3))
     B = int(rng.choice([1, 2, 7, 16, 64, 100, 128, 256, 1024]))
     u = rng.random()
-    if u < 0.15 and T <= 16:
+    if seed >= 300 and T <= 4 and u < 0.3:
+        L = int(rng.integers(40000, 120001))  # (long sweeps only) long decode rows
+    elif u < 0.15 and T <= 16:
         L = int(rng.integers(6000, 40001))  # several key splits, long decode rows
     elif u < 0.3:
         L = int(rng.integers(T, T + 200))  # context about as long as the query chunk
     else:
         L = int(rng.integers(max(T, 2), 6001))
-    k = int(rng.integers(1, min(L, 1024) + 1)) if rng.random() < 0.8 else int(rng.integers(L, L + 300))
+    kmax = 8192 if seed >= 300 else 1024
+    k = int(rng.integers(1, min(L, kmax) + 1)) if rng.random() < 0.8 else int(rng.integers(L, L + 300))
     k = max(1, min(k, 8192))
     kprime = int(rng.integers(k + 1, min(4 * k, 8192) + 2)) if rng.random() < 0.7 and k < 8192 else None
     needles = int(rng.integers(0, 9))
