@@ -231,14 +231,13 @@ __global__ __launch_bounds__(kHThreads, 2) void hisa_block_kernel(
     const float* __restrict__ k_scale, int32_t L, int32_t T, int32_t H, int32_t B, int64_t M,
     int32_t m, int32_t nsplit, float* __restrict__ G, int32_t* __restrict__ blocks,
     float* __restrict__ bscores) {
-  constexpr bool SPLIT = true;  // hi and lo bf16 planes of the pooled keys, for every input type
-  constexpr int LB = SPLIT ? kHTileBytes : 16;
+  // Hi and lo bf16 planes of the pooled-key tiles.
   __shared__ __attribute__((aligned(16))) uint8_t h0[kHTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t h1[kHTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t h2[kHTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t l0[LB];
-  __shared__ __attribute__((aligned(16))) uint8_t l1[LB];
-  __shared__ __attribute__((aligned(16))) uint8_t l2[LB];
+  __shared__ __attribute__((aligned(16))) uint8_t l0[kHTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t l1[kHTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t l2[kHTileBytes];
   __shared__ float pdot[kHWaves][64];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = lane_id();
@@ -279,7 +278,7 @@ __global__ __launch_bounds__(kHThreads, 2) void hisa_block_kernel(
 
   // Pooled tiles: three LDS buffers, two tiles in flight (the router's
   // pattern); 16-byte chunk c of tile row rr at chunk position c ^ (rr % 16).
-  constexpr int NL = SPLIT ? 4 : 2;
+  constexpr int NL = 4;
   // Split z of nsplit takes tiles [tile0, tile1) (nsplit > 1: few queries,
   // so each query's blocks are spread over more workgroups; the last split
   // also takes the partial block, and hisa_topm_kernel picks the blocks).
@@ -306,7 +305,7 @@ __global__ __launch_bounds__(kHThreads, 2) void hisa_block_kernel(
       const int64_t blk = tb * 32 + rowi[i];
       const uint32_t voff = static_cast<uint32_t>((blk < full_max ? blk : 0) * (kD * 2)) + chk[i];
       hs_load16_lds(rh, hb + 1024 * (2 * wave + i), voff);
-      if constexpr (SPLIT) hs_load16_lds(rl, lb + 1024 * (2 * wave + i), voff);
+      hs_load16_lds(rl, lb + 1024 * (2 * wave + i), voff);
     }
   };
   // G of the tile's 32 blocks: lane (l % 32) holds its block's 16 heads per
@@ -324,11 +323,9 @@ __global__ __launch_bounds__(kHThreads, 2) void hisa_block_kernel(
       const bf16x8 bh = as_bf16x8(*reinterpret_cast<const uint4*>(rowh + 16 * pc));
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_bf16(a[rt][ks], bh, acc[rt]);
-      if constexpr (SPLIT) {
-        const bf16x8 bl = as_bf16x8(*reinterpret_cast<const uint4*>(rowl + 16 * pc));
+      const bf16x8 bl = as_bf16x8(*reinterpret_cast<const uint4*>(rowl + 16 * pc));
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_bf16(a[rt][ks], bl, acc[rt]);
-      }
+      for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32_bf16(a[rt][ks], bl, acc[rt]);
     }
     float g = 0.f;
 #pragma unroll

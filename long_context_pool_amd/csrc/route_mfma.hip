@@ -112,13 +112,13 @@ __device__ __forceinline__ void load_head_frags(const void* q, int64_t row, bf16
 }
 
 // One 32-block pooled tile against the wave's kRCols column tiles:
-// acc[c] (blocks x heads) = P_hi . Q_c [+ P_lo . Q_c], then rs[c] += the
+// acc[c] (blocks x heads) = P_hi . Q_c + P_lo . Q_c, then rs[c] += the
 // lane's 16 blocks of ReLU(acc[c]) -- all of them (MASK false), or those of
 // tile row < lim[c] (the column's complete-block count minus the tile's first
 // block).  P comes from an LDS tile of unpadded 256-byte rows whose 16-byte
 // chunk c of row r sits at chunk position c ^ (r % 16), so the 32 rows of a
 // read hit distinct banks; each fragment read feeds kRCols MFMAs.
-template <bool SPLIT, bool MASK>
+template <bool MASK>
 __device__ __forceinline__ void accumulate_tile(const bf16x8 (&bq)[kRCols][8], const uint8_t* hb,
                                                 const uint8_t* lb, const int (&lim)[kRCols],
                                                 float (&rs)[kRCols]) {
@@ -136,11 +136,9 @@ __device__ __forceinline__ void accumulate_tile(const bf16x8 (&bq)[kRCols][8], c
     const bf16x8 ph = as_bf16x8(*reinterpret_cast<const uint4*>(rowh + 16 * pos));
 #pragma unroll
     for (int c = 0; c < kRCols; ++c) acc[c] = mfma32_bf16(ph, bq[c][ks], acc[c]);
-    if constexpr (SPLIT) {
-      const bf16x8 pl = as_bf16x8(*reinterpret_cast<const uint4*>(rowl + 16 * pos));
+    const bf16x8 pl = as_bf16x8(*reinterpret_cast<const uint4*>(rowl + 16 * pos));
 #pragma unroll
-      for (int c = 0; c < kRCols; ++c) acc[c] = mfma32_bf16(pl, bq[c][ks], acc[c]);
-    }
+    for (int c = 0; c < kRCols; ++c) acc[c] = mfma32_bf16(pl, bq[c][ks], acc[c]);
   }
 #pragma unroll
   for (int c = 0; c < kRCols; ++c) {
@@ -172,18 +170,11 @@ __global__ void pooled_split_kernel(const float* __restrict__ pooled, uint32_t* 
 
 // HG: 32-head groups per query (1 for H <= 32, 2 for H <= 64); the wave's
 // kRCols column tiles are its kRCols / HG queries' head groups.
-#ifndef MISA_ROUTE_NBUF_FP8
-#define MISA_ROUTE_NBUF_FP8 3
-#endif
-#ifndef MISA_ROUTE_NBUF_BF16
-#define MISA_ROUTE_NBUF_BF16 3
-#endif
 // Pooled-tile buffers per workgroup (16 KiB per tile: the hi and lo bf16
 // planes); NBUF - 1 tiles are in flight.  Deeper rings (up to eight tiles of
 // one plane) measured the same: the tiles come from L2.  The budget is two
 // workgroups per CU with the partial-block staging.
-template <int DT>
-constexpr int route_nbuf() { return DT == kBF16 ? MISA_ROUTE_NBUF_BF16 : MISA_ROUTE_NBUF_FP8; }
+constexpr int kRNBuf = 3;
 
 template <int DT, int HG>
 __global__ __launch_bounds__(kRThreads, 2) void route_prefill_kernel(
@@ -192,13 +183,11 @@ __global__ __launch_bounds__(kRThreads, 2) void route_prefill_kernel(
     const float* __restrict__ k_scale, int32_t* __restrict__ heads, float* __restrict__ E_out,
     int32_t L, int32_t T, int32_t H, int32_t B, int64_t M, int32_t h, int32_t nsplit,
     float* __restrict__ part) {
-  constexpr bool SPLIT = true;  // both planes, for every input type
-  constexpr int LB = SPLIT ? kTileBytes : 16;
   constexpr int QW = kRCols / HG;         // queries per wave
   constexpr int QWG = QW * kRWaves;       // queries per workgroup
-  constexpr int NBUF = route_nbuf<DT>();  // tile buffers: NBUF - 1 tiles in flight
+  constexpr int NBUF = kRNBuf;            // tile buffers: NBUF - 1 tiles in flight
   __shared__ __attribute__((aligned(16))) uint8_t hbuf[NBUF][kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lbuf[NBUF][LB];
+  __shared__ __attribute__((aligned(16))) uint8_t lbuf[NBUF][kTileBytes];
   __shared__ float rowsum[kRWaves][QW][64];
   __shared__ float partial[kRWaves][QW][64];
   // Raw keys of the workgroup's partial blocks, [full_min B, last position]:
@@ -240,7 +229,7 @@ __global__ __launch_bounds__(kRThreads, 2) void route_prefill_kernel(
   // vmcnt wait before each barrier proves that a tile has landed.  Rows past
   // the last complete block load block 0 and are masked in the sums; tiles
   // past the last repeat it, so every iteration issues the same loads.
-  constexpr int NL = SPLIT ? 4 : 2;
+  constexpr int NL = 4;
   // Split z of nsplit takes tiles [tile0, tile1) (nsplit > 1: few query
   // groups, so the blocks are spread over more workgroups; the partial sums
   // then go to `part` and a finalize kernel adds them in split order).
@@ -266,7 +255,7 @@ __global__ __launch_bounds__(kRThreads, 2) void route_prefill_kernel(
       const int64_t blk = tb * 32 + rowi[i];
       const uint32_t voff = static_cast<uint32_t>((blk < full_max ? blk : 0) * (kD * 2)) + chk[i];
       rt_load16_lds(rh, hb + 1024 * (2 * wave + i), voff);
-      if constexpr (SPLIT) rt_load16_lds(rl, lb + 1024 * (2 * wave + i), voff);
+      rt_load16_lds(rl, lb + 1024 * (2 * wave + i), voff);
     }
   };
   // Issue order: the partial-block keys (last split), the first NBUF - 1
@@ -324,8 +313,8 @@ __global__ __launch_bounds__(kRThreads, 2) void route_prefill_kernel(
       issue(bt + NBUF - 1, hbuf[(u + NBUF - 1) % NBUF], lbuf[(u + NBUF - 1) % NBUF]);
       int lim[kRCols];
       tile_lim(bt, lim);
-      if ((bt + 1) * 32 <= full_min) accumulate_tile<SPLIT, false>(bq, hbuf[u], lbuf[u], lim, rs);
-      else accumulate_tile<SPLIT, true>(bq, hbuf[u], lbuf[u], lim, rs);
+      if ((bt + 1) * 32 <= full_min) accumulate_tile<false>(bq, hbuf[u], lbuf[u], lim, rs);
+      else accumulate_tile<true>(bq, hbuf[u], lbuf[u], lim, rs);
     }
   }
   rt_vmcnt_zero();  // the last tiles' loads (repeats) before the buffers are left
