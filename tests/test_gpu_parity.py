@@ -283,12 +283,15 @@ def _random_problem(seed: int):
 
 
 # Number of seeded shapes (MISA_RANDOM_SHAPES / MISA_RANDOM_EXACT raise them
-# for a longer sweep).
+# for a longer sweep; MISA_RANDOM_FIRST / MISA_RANDOM_EXACT_FIRST start it
+# at a later seed, so that a sweep can cover shapes not run before).
 N_RANDOM = int(os.environ.get("MISA_RANDOM_SHAPES", "64"))
 N_RANDOM_EXACT = int(os.environ.get("MISA_RANDOM_EXACT", "32"))
+RANDOM_FIRST = int(os.environ.get("MISA_RANDOM_FIRST", "0"))
+RANDOM_EXACT_FIRST = int(os.environ.get("MISA_RANDOM_EXACT_FIRST", "0"))
 
 
-@pytest.mark.parametrize("seed", range(N_RANDOM))
+@pytest.mark.parametrize("seed", range(RANDOM_FIRST, RANDOM_FIRST + N_RANDOM))
 def test_random_shapes(seed):
     p, m = _random_problem(seed)
     hisa = p.dtype != synth.F32
@@ -368,7 +371,7 @@ def test_random_rerank_lists(seed):
                                                bt[0], bt[1], tol), qs_all)
 
 
-@pytest.mark.parametrize("seed", range(N_RANDOM_EXACT))
+@pytest.mark.parametrize("seed", range(RANDOM_EXACT_FIRST, RANDOM_EXACT_FIRST + N_RANDOM_EXACT))
 def test_random_shapes_exact(seed):
     """Random shapes on exact-integer inputs (every fp32 sum exact, heavy
     ties; now and then all keys from some position on the same row): every
