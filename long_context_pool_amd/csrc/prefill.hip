@@ -111,6 +111,11 @@ __device__ __forceinline__ int slot_query(int slot, int hf) {
   else return 0;
 }
 
+// Slots past a segment's capacity.  One append adds at most 32 entries to a
+// segment (one half-wave's passing lanes) at a position clamped to the
+// capacity, so it always lands inside the segment.
+constexpr int kSegPad = 32;
+
 struct PrefillArgs {
   const void* q;
   const float* q_scale;
@@ -122,10 +127,11 @@ struct PrefillArgs {
   int32_t L, T, H, k_top;
   int32_t S;             // key splits
   int64_t chunk;         // keys per split
-  int32_t cap;           // candidate slots per (query, split)
+  int32_t cap;           // candidate capacity per (query, split)
+  int32_t seg;           // segment stride: cap + kSegPad slots
   int32_t nqt;           // query tiles per sequence
   int32_t batch;
-  uint2* cand;           // [rows, S, cap] (score bits, token)
+  uint2* cand;           // [rows, S, seg] (score bits, token)
   int32_t* cnt;          // [rows, S]
   float* tau;            // [rows*S]
   float margin;          // threshold sample rank = margin * k * samples / n_q
@@ -544,9 +550,9 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
   // lane its position in its half's (query's) segment, so the entries of a
   // slot land next to each other; the entry is written by a buffer store
   // whose offset is pushed out of range for lanes that do not pass.  A batch
-  // that would take a segment past its capacity is written at its end
-  // instead (overwriting entries; the count still grows, which sends the
-  // query to repair).
+  // that starts past a segment's capacity is written at the capacity, into
+  // the segment's padding (overwriting entries there; the count still grows
+  // past the capacity, which sends the query to repair).
   constexpr int ROWB = kD * (DT == kBF16 ? 2 : 1);  // key row bytes in HBM
   constexpr int NL = NDMA + (DT == kFP8 ? 1 : 0);
   // This thread's byte offset inside a tile's key rows for each of its DMA
@@ -585,11 +591,11 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
     const int64_t lim = min<int64_t>(s_end - 1, pos_slot[sl]);
     lim_slot[sl] = owner ? static_cast<int>(lim) : -1;
     seg_off[sl] = static_cast<uint32_t>(slot_query<HPQ>(sl, hf)) * static_cast<uint32_t>(a.S) *
-                  static_cast<uint32_t>(a.cap) * 8u;
+                  static_cast<uint32_t>(a.seg) * 8u;
   }
   const __amdgpu_buffer_rsrc_t rcand =
-      buffer_rsrc(uniform_ptr(a.cand + ((seq * a.T + tw0) * a.S + split) * static_cast<int64_t>(a.cap)),
-                  __builtin_amdgcn_readfirstlane(QPW * a.S * a.cap * 8));
+      buffer_rsrc(uniform_ptr(a.cand + ((seq * a.T + tw0) * a.S + split) * static_cast<int64_t>(a.seg)),
+                  __builtin_amdgcn_readfirstlane(QPW * a.S * a.seg * 8));
   // Candidate counts per (slot, half): scalar; (sl, h) is query
   // slot_query(sl, h).  They go to cnt at the end and may exceed the
   // capacity (the select kernel then queues the query for repair).
@@ -634,17 +640,16 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_score_kernel(PrefillArgs
     if (chk) m &= __builtin_amdgcn_ballot_w64(key <= lim_slot[sl]);
     const uint32_t mlo = static_cast<uint32_t>(m), mhi = static_cast<uint32_t>(m >> 32);
     const int plo = __builtin_popcount(mlo), phi = __builtin_popcount(mhi);
-    // Write bases of the two halves, scalar: the half's count, lowered to
-    // cap - (its passing lanes) when this batch would take the half past the
-    // capacity (its count then ends above the capacity and the query goes to
-    // repair), so that every write stays inside the segment.
-    const int blo = min(ctr2[sl][0], a.cap - plo);
-    const int bhi = min(ctr2[sl][1], a.cap - phi);
+    // Write bases of the two halves, scalar: the half's count, at most the
+    // capacity, so that the batch (at most 32 entries) stays inside the
+    // padded segment; a count past the capacity sends the query to repair.
+    const int blo = min(ctr2[sl][0], a.cap);
+    const int bhi = min(ctr2[sl][1], a.cap);
     // Entry position minus blo: lower half, the passing lanes below; upper
     // half, (bhi - blo) + the passing upper lanes below, which is the 64-lane
     // count plus (bhi - plo - blo).  blo itself goes in the store's scalar
-    // offset.  The upper half's segment starts at least cap entries after
-    // the lower half's, so the vector offset never goes below zero.
+    // offset.  The upper half's segment starts at least seg > cap entries
+    // after the lower half's, so the vector offset never goes below zero.
     const uint32_t dhalf = static_cast<uint32_t>(bhi - plo - blo);
     const uint32_t rel = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, dhalf & upper));
     const uint32_t voff = seg_off[sl] + 8u * rel;
@@ -838,8 +843,8 @@ struct PSelSmem {
 template <int NT, int NR>
 __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
     const uint2* __restrict__ cand, const int32_t* __restrict__ cnt, const float* __restrict__ tau,
-    int32_t S, int32_t cap, int32_t k, int32_t* __restrict__ idx, float* __restrict__ scores_out,
-    int32_t* __restrict__ fail_count, int32_t* __restrict__ fail_list) {
+    int32_t S, int32_t cap, int32_t seg, int32_t k, int32_t* __restrict__ idx,
+    float* __restrict__ scores_out, int32_t* __restrict__ fail_count, int32_t* __restrict__ fail_list) {
   static_assert(NT <= kTopkThreadsSel && NR >= 1 && NR <= 64, "entry slots are bits of a 64-bit mask");
   constexpr int NO = 8;  // entries per thread per round beyond the registers
   __shared__ PSelSmem sm;
@@ -847,7 +852,7 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
   const int lane = lane_id();
   int32_t* out = idx + r * k;
   float* out_s = scores_out ? scores_out + r * k : nullptr;
-  const uint2* base = cand + r * S * static_cast<int64_t>(cap);
+  const uint2* base = cand + r * S * static_cast<int64_t>(seg);
   for (int b = threadIdx.x; b < kRelBins; b += NT) sm.hist[b] = 0;
   if (threadIdx.x == 0) {
     int total = 0, bad = 0;
@@ -878,9 +883,9 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
   const int total = pre[8];
   const float tm = sm.tau_max;
   // The query's S segments through one buffer resource (32-bit offsets:
-  // S * cap * 8 bytes < 2^31 for L <= 2^24); entry c at byte offset
-  // 8 (s cap + c - pre[s]).
-  const __amdgpu_buffer_rsrc_t crs = buffer_rsrc(uniform_ptr(base), S * cap * 8);
+  // S * seg * 8 bytes < 2^31 for L <= 2^24); entry c at byte offset
+  // 8 (s seg + c - pre[s]).
+  const __amdgpu_buffer_rsrc_t crs = buffer_rsrc(uniform_ptr(base), S * seg * 8);
   auto entry = [=](int c) -> uint2 {
     int sg = 0, b = 0;
 #pragma unroll
@@ -889,7 +894,7 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
       sg = ge ? u : sg;
       b = ge ? pre[u] : b;
     }
-    return buffer_load_u32x2(crs, static_cast<uint32_t>(sg * cap + (c - b)) * 8u);
+    return buffer_load_u32x2(crs, static_cast<uint32_t>(sg * seg + (c - b)) * 8u);
   };
   const CandVerdict verdict = cand_verdict(sm.bad != 0, total, k, tm);
   if (verdict == CandVerdict::kRepair) {
@@ -910,7 +915,7 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
     return;
   }
   // 1. entries t + NT u (u < NR) into registers.  Entry c of segment s sits
-  // at slot c + s cap - pre[s]; the 64 entries a wave loads per step form one
+  // at slot c + s seg - pre[s]; the 64 entries a wave loads per step form one
   // chunk, and for a chunk within one segment that offset is taken from a
   // table built here (one entry per thread), so only the few chunks that
   // straddle a boundary search the segments lane by lane.
@@ -924,7 +929,7 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
       return sg;
     };
     const int s_lo = seg_of(64 * j), s_hi = seg_of(min(64 * j + 63, total - 1));
-    sm.ctab[j] = s_lo == s_hi ? s_lo * cap - pre[s_lo] : kChunkMixed;
+    sm.ctab[j] = s_lo == s_hi ? s_lo * seg - pre[s_lo] : kChunkMixed;
   }
   __syncthreads();
   const int wave_e = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
@@ -1190,7 +1195,7 @@ __global__ __launch_bounds__(kRepThreads) void prefill_repair_kernel(
 }
 
 struct PrefillPlan {
-  int32_t S, cap, nqt, qwg, nch;
+  int32_t S, cap, seg, nqt, qwg, nch;
   float margin;
   int64_t chunk;
   size_t off_cnt, off_tau, off_fail, off_list, off_scratch, total;
@@ -1258,9 +1263,10 @@ PrefillPlan plan_prefill(const Shape& s, int32_t nh, int32_t k) {
   cap = cap < p.chunk ? cap : p.chunk;
   cap = (cap + 63) / 64 * 64;
   p.cap = static_cast<int32_t>(cap);
+  p.seg = p.cap + kSegPad;
   const int64_t rows = static_cast<int64_t>(s.batch) * s.T;
   const size_t segs = static_cast<size_t>(rows) * S;
-  size_t off = align_up(segs * cap * sizeof(uint2));
+  size_t off = align_up(segs * p.seg * sizeof(uint2));
   p.off_cnt = off;
   off += align_up(segs * sizeof(int32_t));
   p.off_tau = off;
@@ -1300,7 +1306,7 @@ hipError_t launch_prefill_score_topk(const Shape& s, int32_t nh, const int32_t* 
   const PrefillPlan pl = plan_prefill(s, nh, k);
   char* base = static_cast<char*>(ws);
   PrefillArgs args{q, q_scale, w, kk, k_scale, heads, nh, s.L, s.T, s.H, k, pl.S, pl.chunk,
-                   pl.cap, pl.nqt, s.batch, reinterpret_cast<uint2*>(base),
+                   pl.cap, pl.seg, pl.nqt, s.batch, reinterpret_cast<uint2*>(base),
                    reinterpret_cast<int32_t*>(base + pl.off_cnt),
                    reinterpret_cast<float*>(base + pl.off_tau), pl.margin, pl.nch};
   int32_t* fail_count = reinterpret_cast<int32_t*>(base + pl.off_fail);
@@ -1320,10 +1326,10 @@ hipError_t launch_prefill_score_topk(const Shape& s, int32_t nh, const int32_t* 
   const int64_t rows = static_cast<int64_t>(s.batch) * s.T;
   if (pl.margin * 1.25f * k <= static_cast<float>(kSelRegsSmall * kSelThreadsSmall))
     prefill_select_kernel<kSelThreadsSmall, kSelRegsSmall><<<static_cast<unsigned>(rows), kSelThreadsSmall, 0, st>>>(
-        args.cand, args.cnt, args.tau, pl.S, pl.cap, k, idx, scores_out, fail_count, fail_list);
+        args.cand, args.cnt, args.tau, pl.S, pl.cap, pl.seg, k, idx, scores_out, fail_count, fail_list);
   else
     prefill_select_kernel<kSelThreadsLarge, kSelRegsLarge><<<static_cast<unsigned>(rows), kSelThreadsLarge, 0, st>>>(
-        args.cand, args.cnt, args.tau, pl.S, pl.cap, k, idx, scores_out, fail_count, fail_list);
+        args.cand, args.cnt, args.tau, pl.S, pl.cap, pl.seg, k, idx, scores_out, fail_count, fail_list);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nrt = nh <= 16 ? 1 : (nh <= 32 ? 2 : 4);
