@@ -57,7 +57,7 @@ constexpr int kKeep = 128;         // sample values kept per query between chunk
 // microseconds, so the plan keeps the expected repairs per call (T S P)
 // below kMaxRepairs.
 constexpr double kMaxRepairs = 0.01;
-constexpr float kMargins[] = {2.0f, 2.5f, 3.0f, 4.0f};
+constexpr float kMargins[] = {1.75f, 2.0f, 2.5f, 3.0f, 4.0f};
 
 // P(X >= j) for X ~ Poisson(lambda), j >= 1 (host).
 double poisson_tail(double lambda, int j) {
@@ -796,10 +796,9 @@ __global__ void prefill_clear_kernel(int32_t* fail_count) {
 //  1. one pass over the candidates (the S segments viewed as one list: entry
 //     c lies in segment s with pre[s] <= c < pre[s+1]; thread t holds
 //     entries t + NT u in registers, all of its loads in flight at once)
-//     builds an LDS histogram of their digits relative to the digit of
-//     tau_min (every candidate is >= tau_min) and counts the candidates
-//     >= tau_max;
-//  2. the digit b* holding the k-th best comes from a block scan of the
+//     builds an LDS histogram of their relative bins (RelBins: from tau_min,
+//     which every candidate reaches) and counts the candidates >= tau_max;
+//  2. the bin b* holding the k-th best comes from a block scan of the
 //     histogram;
 //  3. per-wave counts (one barrier) and wave ballots place the entries
 //     above b* in the output and those at b* in an LDS list;
@@ -836,7 +835,7 @@ struct PSelSmem {
   int scan_tmp[32];
   int digit, above, count, nge, bad;
   int wtot[kTopkThreadsSel / kWave];  // per-wave packed counts above / at b* (up to 16 waves)
-  uint32_t dmin, dmax;                 // candidate digit range (tau_min = -inf)
+  uint32_t dmin, dmax;                 // candidate coarse-key range (tau_min = -inf)
   float tau_max, tau_min;
 };
 
@@ -933,13 +932,20 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
   }
   __syncthreads();
   const int wave_e = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  // Lane u reads the table entry of this wave's chunk of register slot u
+  // (one LDS read per wave; slot u then takes it with a lane read).
+  static_assert(NR <= kWave, "one table entry per lane");
+  int ctv = kChunkMixed;
+  {
+    const int j = lane * (NT / 64) + wave_e;
+    if (lane < NR && j < nchunk) ctv = sm.ctab[j];
+  }
   uint2 e[NR];
 #pragma unroll
   for (int u = 0; u < NR; ++u) {
     const int c = u * NT + static_cast<int>(threadIdx.x);
     if (u * NT < total) {
-      const int j = (u * NT) / 64 + wave_e;  // this wave's chunk (uniform)
-      const int o = j < nchunk ? __builtin_amdgcn_readfirstlane(sm.ctab[j]) : kChunkMixed;
+      const int o = __builtin_amdgcn_readlane(ctv, u);  // this wave's chunk (uniform)
       if (c >= total) e[u] = make_uint2(0u, 0u);
       else if (o != kChunkMixed) e[u] = buffer_load_u32x2(crs, static_cast<uint32_t>(c + o) * 8u);
       else e[u] = entry(c);
@@ -947,22 +953,21 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
       e[u] = make_uint2(0u, 0u);
     }
   }
-  // Relative digit (d - d0) >> shift.  Every candidate is >= tau_min, so
-  // with a finite tau_min, d0 = its digit (and digits more than kRelBins
-  // above it share the top bin).  When some split kept every key, the
-  // candidates' own digit range [dmin, dmax] sets d0 = dmin and the shift
-  // that fits the range in kRelBins bins.
+  // Relative bins (RelBins).  Every candidate is >= tau_min, so with a
+  // finite tau_min the bins start at its coarse key.  When some split kept
+  // every key, the candidates' own coarse-key range sets the base and the
+  // shift.
   const float tmin = sm.tau_min;
-  uint32_t d0 = 0, shift = 0;
+  RelBins rb;
   if (tmin != -__builtin_inff()) {
-    d0 = key_digit(tmin);
+    rb = RelBins::above(tmin);
   } else {
-    uint32_t dmin = 0xFFFFFFFFu, dmax = 0u;
+    uint32_t gmin = 0xFFFFFFFFu, gmax = 0u;
     auto range_entry = [&](int c, uint2 x) __attribute__((always_inline)) {
       if (c < total) {
-        const uint32_t d = key_digit(__uint_as_float(x.x));
-        dmin = min(dmin, d);
-        dmax = max(dmax, d);
+        const uint32_t g = float_key(__uint_as_float(x.x)) >> 16;
+        gmin = min(gmin, g);
+        gmax = max(gmax, g);
       }
     };
 #pragma unroll
@@ -973,34 +978,37 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
                   c0 + static_cast<int>(threadIdx.x) < total ? entry(c0 + threadIdx.x) : make_uint2(0u, 0u));
 #pragma unroll
     for (int o = kWave / 2; o >= 1; o >>= 1) {
-      dmin = min(dmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(dmin), o, kWave)));
-      dmax = max(dmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(dmax), o, kWave)));
+      gmin = min(gmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(gmin), o, kWave)));
+      gmax = max(gmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(gmax), o, kWave)));
     }
     if (lane == 0) {
-      atomicMin(&sm.dmin, dmin);
-      atomicMax(&sm.dmax, dmax);
+      atomicMin(&sm.dmin, gmin);
+      atomicMax(&sm.dmax, gmax);
     }
     __syncthreads();
-    d0 = sm.dmin;
-    const uint32_t span = sm.dmax - sm.dmin;
-    shift = span < static_cast<uint32_t>(kRelBins) ? 0u : static_cast<uint32_t>(32 - __clz(static_cast<int>(span)) - 11);
+    rb = RelBins::range(sm.dmin, sm.dmax);  // total > 0 here, so gmin <= gmax
   }
-  auto rel = [=](float v) -> uint32_t {
-    const uint32_t d = (key_digit(v) - d0) >> shift;  // >= 0 for candidates
-    return d < static_cast<uint32_t>(kRelBins) ? d : static_cast<uint32_t>(kRelBins - 1);
-  };
-  // Histogram and certificate count.
+  static_assert(kRelBins == kRelBinCount, "select bins are relative bins");
+  // Histogram and certificate count (register slots that every lane fills
+  // skip the per-entry test).
   int nge = 0;
   auto count_entry = [&](int c, uint2 x) __attribute__((always_inline)) {
     if (c < total) {
       const float v = __uint_as_float(x.x);
-      atomicAdd(&sm.hist[rel(v)], 1u);
+      atomicAdd(&sm.hist[rb.bin(v)], 1u);
       nge += v >= tm ? 1 : 0;
     }
   };
 #pragma unroll
-  for (int u = 0; u < NR; ++u)
-    if (u * NT < total) count_entry(u * NT + static_cast<int>(threadIdx.x), e[u]);
+  for (int u = 0; u < NR; ++u) {
+    if ((u + 1) * NT <= total) {  // every lane's slot u holds an entry (uniform)
+      const float v = __uint_as_float(e[u].x);
+      atomicAdd(&sm.hist[rb.bin(v)], 1u);
+      nge += v >= tm ? 1 : 0;
+    } else if (u * NT < total) {
+      count_entry(u * NT + static_cast<int>(threadIdx.x), e[u]);
+    }
+  }
   for (int c0 = NR * NT; c0 < total; c0 += NO * NT) {  // beyond the registers
     uint2 f[NO];
 #pragma unroll
@@ -1019,7 +1027,7 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
     if (threadIdx.x == 0) fail_list[atomicAdd(fail_count, 1)] = static_cast<int32_t>(r);
     return;
   }
-  // 2. b*: thread t owns relative digits kRelBins-1-t*BPT downwards.
+  // 2. b*: thread t owns relative bins kRelBins-1-t*BPT downwards.
   {
     constexpr int BPT = kRelBins / NT;
     int local[BPT];
@@ -1049,17 +1057,15 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
     if (threadIdx.x == 0) fail_list[atomicAdd(fail_count, 1)] = static_cast<int32_t>(r);
     return;
   }
-  // 3. compaction by relative digit: per-thread counts above and at b*
+  // 3. compaction by relative bin: per-thread counts above and at b*
   // (packed: above in the low 16 bits, total < k <= 8192; at-b* high, total
   // <= kPCandCap), one block scan for the positions.
   // Positions: each wave's entries above b* (at b*) take one run of the
   // output (list), after those of the lower waves; inside the run, entry
   // slot by slot (ballots), so the stores of a slot coalesce.
-  // Relative bin b* as a key interval [blo, bhi] (the last relative bin
-  // holds every higher digit too).
-  const uint32_t dlo = d0 + (bstar << shift), dhi = d0 + ((bstar + 1) << shift) - 1u;
-  const uint32_t blo = digit_lo_key(dlo);
-  const uint32_t bhi = (bstar == static_cast<uint32_t>(kRelBins - 1) || dhi >= kTopDigit) ? 0xFFFFFFFFu : digit_hi_key(dhi);
+  // Relative bin b* as a key interval [blo, bhi].
+  uint32_t blo, bhi;
+  rb.interval(bstar, blo, bhi);
   auto classify = [&](const uint2* ev, int n, int c0, uint64_t& mh, uint64_t& ma) __attribute__((always_inline)) {
     mh = 0;
     ma = 0;
@@ -1139,7 +1145,7 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
   if (resolve_list<NT>(sm.cand_score, sm.cand_idx, bcount, k - above, out + above,
                        out_s ? out_s + above : nullptr, sm.rs))
     return;
-  // A bin of more than kRankMax equal-digit entries: exact fallback, reusing
+  // A b* bin of more than kRankMax entries: exact fallback, reusing
   // the resolve area (no longer needed) for the radix select.
   __syncthreads();
   TopkSmem& tsm = sm.ts;

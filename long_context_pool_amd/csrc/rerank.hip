@@ -11,8 +11,8 @@
 // straight into B registers instead (rerank_gather_kernel).
 // fp32: one thread per candidate (query rows staged in LDS).
 // Then one workgroup per query selects the k best of its k' scores in
-// registers: a digit histogram in LDS, the threshold digit from a block scan,
-// a block-scan compaction, and an exact resolve of the threshold digit.
+// registers: a histogram of relative bins in LDS, the threshold bin from a
+// block scan, a block-scan compaction, and an exact resolve of that bin.
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma.hpp"
@@ -253,8 +253,8 @@ __global__ __launch_bounds__(kRRThreads) void rerank_gather_kernel(
 }
 
 // Top-k of one query's k' (score, candidate) list, in one workgroup: the
-// list is read once into registers, a digit histogram (LDS) gives the
-// threshold digit b*; each wave's entries above b* take one run of the
+// list is read once into registers, a histogram of relative bins (LDS) gives
+// the threshold bin b*; each wave's entries above b* take one run of the
 // output after those of the lower waves (slot by slot, wave ballots, so
 // the stores coalesce) and those at b* go to an LDS list, which is resolved
 // exactly.  Invalid candidates carry score -inf and a distinct negative id
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(kRRThreads) void rerank_gather_kernel(
 // another's load and barrier latency (C5: 277 -> 242 us against 512
 // threads, three per CU).
 constexpr int kLSCap = 2048;
-constexpr int kLSBins = 2048;  // relative digit bins
+constexpr int kLSBins = 2048;  // relative bins
 constexpr int kLSBlk = 512;    // block candidates: blocks staged in LDS (m B <= 8192, B >= 16)
 
 template <int kLSThreads>
@@ -313,7 +313,7 @@ __device__ __forceinline__ void list_select_row(const float* __restrict__ srow, 
     blk_lds = m <= kLSBlk;
     if (blk_lds)
       for (int i = threadIdx.x; i < m; i += kLSThreads) sm.blk[i] = crow.blk[i];
-    // (published by the barrier after the digit range below)
+    // (published by the barrier after the coarse-key range below)
   }
 #pragma unroll
   for (int j = 0; j < kLSPer; ++j) {
@@ -340,33 +340,32 @@ __device__ __forceinline__ void list_select_row(const float* __restrict__ srow, 
       return id[j];
     }
   };
-  // Relative digit (d - dmin) >> shift over the list's digit range [dmin,
-  // dmax], the shift fitting the range in kLSBins bins.
-  // CACHE: each entry's digit is computed once and kept, two 13-bit digits
-  // per register (where the registers allow); the histogram and the
+  // Relative bins (RelBins) over the list's coarse-key range [gmin, gmax].
+  // CACHE: each entry's coarse key is computed once and kept, two 16-bit
+  // keys per register (where the registers allow); the histogram and the
   // classification below then work on it (an entry lies above / in the
-  // threshold bin exactly when its digit does).
+  // threshold bin exactly when its coarse key does).
   uint32_t dgp[CACHE ? (kLSPer + 1) / 2 : 1];
   if constexpr (CACHE) {
 #pragma unroll
     for (int j = 0; j < kLSPer; j += 2) {
-      const uint32_t d0j = key_digit(v[j]);
-      const uint32_t d1j = j + 1 < kLSPer ? key_digit(v[j + 1]) : 0u;
-      dgp[j / 2] = d0j | (d1j << 16);
+      const uint32_t g0j = float_key(v[j]) >> 16;
+      const uint32_t g1j = j + 1 < kLSPer ? float_key(v[j + 1]) >> 16 : 0u;
+      dgp[j / 2] = g0j | (g1j << 16);
     }
   }
-  auto digit_of = [&](int j) -> uint32_t {
+  auto coarse_of = [&](int j) -> uint32_t {
     if constexpr (CACHE) return (dgp[j / 2] >> (16 * (j & 1))) & 0xFFFFu;
-    else return key_digit(v[j]);
+    else return float_key(v[j]) >> 16;
   };
   {
     uint32_t dmin = 0xFFFFFFFFu, dmax = 0u;
 #pragma unroll
     for (int j = 0; j < kLSPer; ++j)
       if (j * kLSThreads + static_cast<int>(threadIdx.x) < kprime) {
-        const uint32_t d = CACHE ? digit_of(j) : key_digit(v[j]);
-        dmin = min(dmin, d);
-        dmax = max(dmax, d);
+        const uint32_t g = coarse_of(j);
+        dmin = min(dmin, g);
+        dmax = max(dmax, g);
       }
 #pragma unroll
     for (int o = kWave / 2; o >= 1; o >>= 1) {
@@ -379,23 +378,12 @@ __device__ __forceinline__ void list_select_row(const float* __restrict__ srow, 
     }
   }
   __syncthreads();
-  const uint32_t d0 = sm.dmin;
-  const uint32_t span = sm.dmax - d0;
-  const uint32_t shift = span < static_cast<uint32_t>(kLSBins) ? 0u : static_cast<uint32_t>(32 - __clz(static_cast<int>(span)) - 11);
-  static_assert(kLSBins == 2048, "shift fits the span in 11 bits");
-  auto rel_of = [&](int j) -> uint32_t {
-    return min((digit_of(j) - d0) >> shift, static_cast<uint32_t>(kLSBins - 1));
-  };
-  if constexpr (CACHE) {
+  const RelBins rb = RelBins::range(sm.dmin, sm.dmax);  // kprime >= 1 entries
+  static_assert(kLSBins == kRelBinCount, "list bins are relative bins");
+  auto rel_of = [&](int j) -> uint32_t { return rb.bin_of_coarse(coarse_of(j)); };
 #pragma unroll
-    for (int j = 0; j < kLSPer; ++j)
-      if (j * kLSThreads + static_cast<int>(threadIdx.x) < kprime) atomicAdd(&sm.hist[rel_of(j)], 1u);
-  } else {
-#pragma unroll
-    for (int j = 0; j < kLSPer; ++j)
-      if (j * kLSThreads + static_cast<int>(threadIdx.x) < kprime)
-        atomicAdd(&sm.hist[min((key_digit(v[j]) - d0) >> shift, static_cast<uint32_t>(kLSBins - 1))], 1u);
-  }
+  for (int j = 0; j < kLSPer; ++j)
+    if (j * kLSThreads + static_cast<int>(threadIdx.x) < kprime) atomicAdd(&sm.hist[rel_of(j)], 1u);
   __syncthreads();
   {
     constexpr int BPT = kLSBins / kLSThreads;
@@ -435,8 +423,8 @@ __device__ __forceinline__ void list_select_row(const float* __restrict__ srow, 
     for (int p = threadIdx.x; p < k; p += kLSThreads)
       if (out[p] < 0) out[p] = -1;
   } else {
-    // Above / in the relative bin b*: by the cached digits, or by the key
-    // interval of b*'s digits (the last bin also holds every higher digit).
+    // Above / in the relative bin b*: by the cached coarse keys, or by the
+    // key interval of b*.
     uint32_t mh = 0, ma = 0;
     if constexpr (CACHE) {
 #pragma unroll
@@ -447,9 +435,8 @@ __device__ __forceinline__ void list_select_row(const float* __restrict__ srow, 
         ma |= (in && rb == bstar) ? (1u << j) : 0u;
       }
     } else {
-      const uint32_t dlo = d0 + (bstar << shift), dhi = d0 + ((bstar + 1) << shift) - 1u;
-      const uint32_t lo = digit_lo_key(dlo);
-      const uint32_t hi = (bstar == static_cast<uint32_t>(kLSBins - 1) || dhi >= kTopDigit) ? 0xFFFFFFFFu : digit_hi_key(dhi);
+      uint32_t lo, hi;
+      rb.interval(bstar, lo, hi);
 #pragma unroll
       for (int j = 0; j < kLSPer; ++j) {
         const bool in = j * kLSThreads + static_cast<int>(threadIdx.x) < kprime;

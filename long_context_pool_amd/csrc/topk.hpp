@@ -184,6 +184,61 @@ __host__ __device__ __forceinline__ uint32_t digit_hi_key(uint32_t d) {
   return d >= kTopDigit ? 0xFFFFFFFFu : digit_lo_key(d + 1) - 1u;
 }
 
+// ---------------------------------------------------------------- relative bins
+//
+// Candidate lists (the prefill candidates, the re-ranked lists) are binned
+// relative to their own range.  A score's coarse key g = float_key >> 16
+// keeps the sign, the exponent and the top 7 mantissa bits: monotone in the
+// score, 128 bins per binade, four instructions cheaper per entry than the
+// digit above.  bin = min((max(g, gb) - gb) >> shift, kRelBinCount - 1):
+// every key below gb shares bin 0, every key far above shares the last bin.
+constexpr int kRelBinCount = 2048;
+constexpr int kRelBinBits = 11;
+// Coarse key of 2^-31: in a list's own range, values below it (zeros,
+// negatives, subnormals) share the lowest bin, as they share the lowest
+// digits above.
+constexpr uint32_t kCoarseFloor = (0x80000000u | (static_cast<uint32_t>(127 - 31) << 23)) >> 16;
+
+struct RelBins {
+  uint32_t gb;     // coarse key of bin 0's upper part
+  uint32_t shift;  // coarse keys per bin: 2^shift
+
+  // A list whose every entry scores >= tau (the candidate threshold).
+  __host__ __device__ static RelBins above(float tau) { return RelBins{float_key(tau) >> 16, 0u}; }
+  // A list whose valid entries have coarse keys in [gmin, gmax] (gmin <=
+  // gmax): bins of 2^shift coarse keys from max(gmin, kCoarseFloor), the
+  // shift fitting the range in kRelBinCount bins.
+  __host__ __device__ static RelBins range(uint32_t gmin, uint32_t gmax) {
+    const uint32_t lo = gmin > kCoarseFloor ? gmin : kCoarseFloor;
+    const uint32_t hi = gmax > kCoarseFloor ? gmax : kCoarseFloor;
+    const uint32_t span = hi - lo;
+    const uint32_t sh = span < static_cast<uint32_t>(kRelBinCount)
+                            ? 0u
+                            : static_cast<uint32_t>(32 - __builtin_clz(span) - kRelBinBits);
+    return RelBins{lo, sh};
+  }
+  __host__ __device__ uint32_t bin_of_coarse(uint32_t g) const {
+    const uint32_t x = ((g > gb ? g : gb) - gb) >> shift;
+    return x < static_cast<uint32_t>(kRelBinCount) ? x : static_cast<uint32_t>(kRelBinCount - 1);
+  }
+  __host__ __device__ uint32_t bin(float v) const { return bin_of_coarse(float_key(v) >> 16); }
+  // Keys [lo, hi] of bin b: every key with bin_of_coarse(key >> 16) == b
+  // lies in it (bin 0 reaches down to key 0, the last bin up to the largest
+  // key).  A bin past every key gets the empty interval lo > hi.
+  __host__ __device__ void interval(uint32_t b, uint32_t& lo, uint32_t& hi) const {
+    const uint64_t g0 = static_cast<uint64_t>(gb) + (static_cast<uint64_t>(b) << shift);
+    const uint64_t g1 = static_cast<uint64_t>(gb) + (static_cast<uint64_t>(b + 1) << shift);
+    if (b != 0 && g0 > 0xFFFFu) {
+      lo = 0xFFFFFFFFu;
+      hi = 0xFFFFFFFEu;
+      return;
+    }
+    lo = b == 0 ? 0u : static_cast<uint32_t>(g0 << 16);
+    hi = (b + 1 >= static_cast<uint32_t>(kRelBinCount) || g1 > 0xFFFFu) ? 0xFFFFFFFFu
+                                                                      : static_cast<uint32_t>((g1 << 16) - 1u);
+  }
+};
+
 // ---------------------------------------------------------------- candidate certificate
 //
 // A threshold-filtered candidate list (every key of split s scoring >= tau_s

@@ -9,6 +9,12 @@
 //               consecutive digits tile the key space.
 //   certificate the candidate-list verdicts of cand_verdict() on the cases
 //               that decide between repair, take-all and counting.
+//   relbins     the relative bins of candidate lists (RelBins), for bins set
+//               from thresholds and from coarse-key ranges: over every coarse
+//               key (a key's bin depends on its top 16 bits only, and interval
+//               ends are multiples of 2^16) the bin is monotone, both end keys
+//               of each coarse key lie in its bin's interval, and the
+//               intervals of the bins that keys reach tile the key space.
 //
 // Prints "ok <what>" per passed check; exits non-zero on the first failure.
 #include "topk.hpp"
@@ -84,6 +90,69 @@ int check_digits() {
   return 0;
 }
 
+int check_relbins_one(const misa::RelBins& rb, const char* what) {
+  uint32_t prev_b = 0;
+  uint32_t next_lo = 0;  // the first key the next reached bin must start at
+  for (uint32_t g = 0; g <= 0xFFFFu; ++g) {
+    const uint32_t b = rb.bin_of_coarse(g);
+    if (b >= static_cast<uint32_t>(misa::kRelBinCount) || (g > 0 && b < prev_b)) {
+      std::printf("FAIL relbins %s (gb %u shift %u): coarse %04x bin %u after %u\n", what, rb.gb, rb.shift, g, b,
+                  prev_b);
+      return 1;
+    }
+    uint32_t lo, hi;
+    rb.interval(b, lo, hi);
+    const uint32_t k0 = g << 16, k1 = k0 | 0xFFFFu;
+    if (k0 < lo || k1 > hi) {
+      std::printf("FAIL relbins %s (gb %u shift %u): keys %08x-%08x outside bin %u [%08x, %08x]\n", what, rb.gb,
+                  rb.shift, k0, k1, b, lo, hi);
+      return 1;
+    }
+    if (g == 0 || b != prev_b) {  // a new reached bin: it starts where the last one ended
+      if (lo != next_lo) {
+        std::printf("FAIL relbins %s (gb %u shift %u): bin %u starts at %08x, want %08x\n", what, rb.gb, rb.shift, b,
+                    lo, next_lo);
+        return 1;
+      }
+      next_lo = hi + 1u;
+      if (float_of_key(k0) == float_of_key(k0) && rb.bin(float_of_key(k0)) != b && misa::float_key(float_of_key(k0)) == k0) {
+        std::printf("FAIL relbins %s: bin(v) != bin_of_coarse\n", what);
+        return 1;
+      }
+    }
+    prev_b = b;
+  }
+  if (next_lo != 0u) {  // the last reached bin ends at the largest key (hi + 1 wraps to 0)
+    std::printf("FAIL relbins %s (gb %u shift %u): the bins stop short of the largest key\n", what, rb.gb, rb.shift);
+    return 1;
+  }
+  return 0;
+}
+
+int check_relbins() {
+  int n = 0;
+  const float taus[] = {1e-30f, 1e-9f, 0.001f, 0.37f, 1.0f, 3.5f, 1000.0f, 3e9f, 1e30f, 0.0f, -0.0f, -1.0f, -1e20f};
+  for (float t : taus) {
+    if (check_relbins_one(misa::RelBins::above(t), "above")) return 1;
+    ++n;
+  }
+  const uint32_t gs[] = {0u, 0x007Fu, 0x3F80u, 0x8000u, 0xA000u, misa::kCoarseFloor - 1, misa::kCoarseFloor,
+                         misa::kCoarseFloor + 1, 0xBF00u, 0xBF80u, 0xC000u, 0xC120u, 0xF000u, 0xFF7Fu, 0xFFFFu};
+  for (uint32_t a : gs)
+    for (uint32_t b : gs) {
+      if (a > b) continue;
+      if (check_relbins_one(misa::RelBins::range(a, b), "range")) return 1;
+      ++n;
+    }
+  for (uint32_t w = 1; w <= 0xFFFFu; w = w * 3 + 1) {  // spans around every shift
+    const uint32_t a = misa::kCoarseFloor, b = a + w > 0xFFFFu ? 0xFFFFu : a + w;
+    if (check_relbins_one(misa::RelBins::range(a, b), "span")) return 1;
+    ++n;
+  }
+  std::printf("ok relbins (%d bin sets)\n", n);
+  return 0;
+}
+
 int check_certificate() {
   const float inf = INFINITY;
   struct Case {
@@ -122,5 +191,6 @@ int main(int argc, char** argv) {
   int rc = 0;
   if (!std::strcmp(what, "all") || !std::strcmp(what, "certificate")) rc |= check_certificate();
   if (!std::strcmp(what, "all") || !std::strcmp(what, "digits")) rc |= check_digits();
+  if (!std::strcmp(what, "all") || !std::strcmp(what, "relbins")) rc |= check_relbins();
   return rc;
 }

@@ -7,7 +7,9 @@ on the CPU:
   intervals the top-k kernels classify with (monotone digit, key inside
   [digit_lo_key(d), digit_hi_key(d)], intervals tiling the key space);
 * the candidate-list certificate verdicts, including a list of exactly k
-  candidates under a finite threshold (it must be counted, not taken whole).
+  candidates under a finite threshold (it must be counted, not taken whole);
+* the relative bins of candidate lists over every coarse key (monotone bins,
+  each key inside its bin's interval, the reached bins tiling the key space).
 """
 
 import os
@@ -50,3 +52,7 @@ def test_digit_intervals_over_all_keys(host_checks):
     # Every non-NaN float image: 2^32 - 2 * (2^23 - 1) NaN patterns - 1 (the
     # key of -0 is that of +0).
     assert f"({2**32 - 2 * (2**23 - 1) - 1} keys)" in out
+
+
+def test_relative_bins_over_all_coarse_keys(host_checks):
+    assert "ok relbins" in _run(host_checks, "relbins")
