@@ -1082,6 +1082,12 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
   };
   const int wave = threadIdx.x / kWave;
   int run_h = 0, run_a = 0;  // entries placed by earlier rounds (block totals)
+  // The output goes through buffer resources of k entries (the scores': of
+  // none when out_s is null).  A lane that places nothing stores past the
+  // end, where the range check drops it, so placing takes no branch.
+  const __amdgpu_buffer_rsrc_t rout = buffer_rsrc(uniform_ptr(out), k * 4);
+  const __amdgpu_buffer_rsrc_t routs =
+      buffer_rsrc(uniform_ptr(out_s ? reinterpret_cast<int32_t*>(out_s) : out), out_s ? k * 4 : 0);
   auto place = [&](const uint2* ev, int n, int c0, uint64_t mh, uint64_t ma) __attribute__((always_inline)) {
     int wt = __popcll(mh) | (__popcll(ma) << 16);
 #pragma unroll
@@ -1095,7 +1101,9 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
       base += w < wave ? v : 0;
       all += v;
     }
-    int ph = run_h + (base & 0xFFFF), pa = run_a + (base >> 16);
+    // The wave's output and list positions (uniform).
+    int ph = __builtin_amdgcn_readfirstlane(run_h + (base & 0xFFFF));
+    int pa = __builtin_amdgcn_readfirstlane(run_a + (base >> 16));
     const int nu = min(n, (total - c0 + NT - 1) / NT);  // slots holding entries (uniform)
 #pragma unroll
     for (int u = 0; u < n; ++u) {
@@ -1103,22 +1111,21 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
       const bool h = (mh >> u) & 1u;
       const bool at = (ma >> u) & 1u;
       const uint64_t bh = __ballot(h);
-      const uint64_t ba = __ballot(at);
-      if (h) {
-        const int pos = ph + lanes_below(bh);
-        if (pos < k) {
-          out[pos] = static_cast<int32_t>(ev[u].y);
-          if (out_s) out_s[pos] = __uint_as_float(ev[u].x);
-        }
-      } else if (at) {
-        const int pos = pa + lanes_below(ba);
-        if (pos < kPCandCap) {
-          sm.cand_score[pos] = __uint_as_float(ev[u].x);
-          sm.cand_idx[pos] = static_cast<int32_t>(ev[u].y);
-        }
-      }
+      const uint32_t off = h ? static_cast<uint32_t>(ph + lanes_below(bh)) * 4u : 0x80000000u;
+      __builtin_amdgcn_raw_buffer_store_b32(ev[u].y, rout, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(ev[u].x, routs, off, 0, 0);
       ph += __popcll(bh);
-      pa += __popcll(ba);
+      const uint64_t ba = __ballot(at);
+      if (ba != 0) {  // entries of the threshold bin (few)
+        if (at) {
+          const int pos = pa + lanes_below(ba);
+          if (pos < kPCandCap) {
+            sm.cand_score[pos] = __uint_as_float(ev[u].x);
+            sm.cand_idx[pos] = static_cast<int32_t>(ev[u].y);
+          }
+        }
+        pa += __popcll(ba);
+      }
     }
     run_h += all & 0xFFFF;
     run_a += all >> 16;
