@@ -794,8 +794,10 @@ __global__ void prefill_clear_kernel(int32_t* fail_count) {
 // segment overflowed and at least k candidates score >= tau_max = max over
 // splits of tau (every non-candidate of split s scores below tau_s).  Then:
 //  1. one pass over the candidates (the S segments viewed as one list: entry
-//     c lies in segment s with pre[s] <= c < pre[s+1]; thread t holds
-//     entries t + NT u in registers, all of its loads in flight at once)
+//     c lies in segment s with pre[s] <= c < pre[s+1]; wave w holds the
+//     R 64-entry chunks from chunk R w in registers, R <= NR as few as hold
+//     the list, lane l entry 64 (R w + u) + l in slot u, all of its loads in
+//     flight at once)
 //     builds an LDS histogram of their relative bins (RelBins: from tau_min,
 //     which every candidate reaches) and counts the candidates >= tau_max;
 //  2. the bin b* holding the k-th best comes from a block scan of the
@@ -804,20 +806,25 @@ __global__ void prefill_clear_kernel(int32_t* fail_count) {
 //     above b* in the output and those at b* in an LDS list;
 //  4. the list is resolved exactly (ties: lower token).
 // Entries beyond the registers' NR * NT are read again from global memory,
-// 8 NT at a time.
+// 8 NT at a time (wave w: 8 consecutive 64-entry chunks).  Each wave holding
+// a consecutive run of the list makes the output come out in list order:
+// sorted by split and token.
 constexpr int kPCandCap = 1024;
 // Workgroup size and candidates held in registers per thread: 256 threads x
 // kSelRegsSmall while the expected count (about margin k) fits
 // comfortably (120 registers: four workgroups per CU), else 512 threads x
-// kSelRegsLarge (two per CU).  Queries are independent, so more workgroups
-// per CU overlap more of each one's load and barrier latency: 256 x 32 took
-// the C3 select from 133 to 111 us against 512 x 16 (three per CU).
+// kSelRegsLarge (two per CU; 34 keeps it within 128 registers without
+// spills, and holds about 1.2 times the expected count of k = 8192 at the
+// lowest margin, so that few queries need a round from memory).  Queries
+// are independent, so more workgroups per CU overlap more of each one's load
+// and barrier latency: 256 x 32 took the C3 select from 133 to 111 us
+// against 512 x 16 (three per CU).
 constexpr int kSelThreadsSmall = 256;
 constexpr int kSelRegsSmall = 32;
 constexpr int kSelThreadsLarge = 512;
-constexpr int kSelRegsLarge = 38;
+constexpr int kSelRegsLarge = 34;
 constexpr int kRelBins = 2048;
-// 64-entry chunks of the register-held entries (at most 512 x 38 of them);
+// 64-entry chunks of the register-held entries (at most 512 x 34 of them);
 // a chunk that straddles a segment boundary is marked mixed.
 constexpr int kSelChunks = (kSelThreadsLarge * kSelRegsLarge + 63) / 64;
 constexpr int kChunkMixed = -0x7FFFFFFF;
@@ -913,11 +920,11 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
     }
     return;
   }
-  // 1. entries t + NT u (u < NR) into registers.  Entry c of segment s sits
-  // at slot c + s seg - pre[s]; the 64 entries a wave loads per step form one
-  // chunk, and for a chunk within one segment that offset is taken from a
-  // table built here (one entry per thread), so only the few chunks that
-  // straddle a boundary search the segments lane by lane.
+  // 1. entries 64 (R w + u) + l (u < R) into registers.  Entry c of
+  // segment s sits at slot c + s seg - pre[s]; the 64 entries a wave loads
+  // per step form one chunk, and for a chunk within one segment that offset
+  // is taken from a table built here (one entry per thread), so only the few
+  // chunks that straddle a boundary search the segments lane by lane.
   static_assert(NT % kWave == 0 && NT * NR <= kSelChunks * 64, "chunk table covers the registers");
   const int nchunk = (min(total, NR * NT) + 63) / 64;
   for (int j = threadIdx.x; j < nchunk; j += NT) {
@@ -932,19 +939,40 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
   }
   __syncthreads();
   const int wave_e = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  // Round entries: slot u of this wave in a round of n slots per wave
+  // starting at list entry c0 is entry c0 + 64 (n w + u) + lane; its first
+  // entry (uniform) is c0 + 64 (n w + u), and it holds entries when u < n
+  // and that first entry is below total.  The register round takes R slots
+  // per wave, as few as hold the list (so the waves share it evenly).
+  constexpr int NW = NT / kWave;
+  const int R = min(NR, (nchunk + NW - 1) / NW);
+  struct Round {
+    int base, nu, nf, lane;  // this wave's first entry; slots holding entries; full slots
+    __device__ bool used(int u) const { return u < nu; }
+    __device__ bool full(int u) const { return u < nf; }
+    __device__ int entry(int u) const { return base + 64 * u + lane; }
+  };
+  auto make_round = [=](int c0, int n) {
+    const int base = c0 + 64 * n * wave_e;
+    const int rem = total - base;
+    const int nu = min(max((rem + 63) >> 6, 0), n), nf = min(max(rem >> 6, 0), n);
+    return Round{__builtin_amdgcn_readfirstlane(base), __builtin_amdgcn_readfirstlane(nu),
+                 __builtin_amdgcn_readfirstlane(nf), lane};
+  };
   // Lane u reads the table entry of this wave's chunk of register slot u
   // (one LDS read per wave; slot u then takes it with a lane read).
   static_assert(NR <= kWave, "one table entry per lane");
   int ctv = kChunkMixed;
   {
-    const int j = lane * (NT / 64) + wave_e;
-    if (lane < NR && j < nchunk) ctv = sm.ctab[j];
+    const int j = wave_e * R + lane;
+    if (lane < R && j < nchunk) ctv = sm.ctab[j];
   }
+  const Round r0 = make_round(0, R);
   uint2 e[NR];
 #pragma unroll
   for (int u = 0; u < NR; ++u) {
-    const int c = u * NT + static_cast<int>(threadIdx.x);
-    if (u * NT < total) {
+    const int c = r0.entry(u);
+    if (r0.used(u)) {
       const int o = __builtin_amdgcn_readlane(ctv, u);  // this wave's chunk (uniform)
       if (c >= total) e[u] = make_uint2(0u, 0u);
       else if (o != kChunkMixed) e[u] = buffer_load_u32x2(crs, static_cast<uint32_t>(c + o) * 8u);
@@ -972,7 +1000,7 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
     };
 #pragma unroll
     for (int u = 0; u < NR; ++u)
-      if (u * NT < total) range_entry(u * NT + static_cast<int>(threadIdx.x), e[u]);
+      if (r0.used(u)) range_entry(r0.entry(u), e[u]);
     for (int c0 = NR * NT; c0 < total; c0 += NT)  // beyond the registers
       range_entry(c0 + static_cast<int>(threadIdx.x),
                   c0 + static_cast<int>(threadIdx.x) < total ? entry(c0 + threadIdx.x) : make_uint2(0u, 0u));
@@ -1001,23 +1029,24 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
   };
 #pragma unroll
   for (int u = 0; u < NR; ++u) {
-    if ((u + 1) * NT <= total) {  // every lane's slot u holds an entry (uniform)
+    if (r0.full(u)) {  // every lane's slot u holds an entry (uniform)
       const float v = __uint_as_float(e[u].x);
       atomicAdd(&sm.hist[rb.bin(v)], 1u);
       nge += v >= tm ? 1 : 0;
-    } else if (u * NT < total) {
-      count_entry(u * NT + static_cast<int>(threadIdx.x), e[u]);
+    } else if (r0.used(u)) {
+      count_entry(r0.entry(u), e[u]);
     }
   }
   for (int c0 = NR * NT; c0 < total; c0 += NO * NT) {  // beyond the registers
+    const Round rr = make_round(c0, NO);
     uint2 f[NO];
 #pragma unroll
     for (int u = 0; u < NO; ++u) {
-      const int c = c0 + u * NT + static_cast<int>(threadIdx.x);
+      const int c = rr.entry(u);
       f[u] = c < total ? entry(c) : make_uint2(0u, 0u);
     }
 #pragma unroll
-    for (int u = 0; u < NO; ++u) count_entry(c0 + u * NT + static_cast<int>(threadIdx.x), f[u]);
+    for (int u = 0; u < NO; ++u) count_entry(rr.entry(u), f[u]);
   }
 #pragma unroll
   for (int o = kWave / 2; o >= 1; o >>= 1) nge += __shfl_xor(nge, o, kWave);
@@ -1066,14 +1095,13 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
   // Relative bin b* as a key interval [blo, bhi].
   uint32_t blo, bhi;
   rb.interval(bstar, blo, bhi);
-  auto classify = [&](const uint2* ev, int n, int c0, uint64_t& mh, uint64_t& ma) __attribute__((always_inline)) {
+  auto classify = [&](const uint2* ev, int n, const Round& rnd, uint64_t& mh, uint64_t& ma) __attribute__((always_inline)) {
     mh = 0;
     ma = 0;
-    const int nu = (total - c0 + NT - 1) / NT;  // slots holding entries (uniform)
 #pragma unroll
     for (int u = 0; u < n; ++u) {
-      if (u < nu) {
-        const int c = c0 + u * NT + static_cast<int>(threadIdx.x);
+      if (rnd.used(u)) {  // (uniform)
+        const int c = rnd.entry(u);
         const uint32_t key = float_key(__uint_as_float(ev[u].x));
         mh |= (c < total && key > bhi) ? (uint64_t{1} << u) : uint64_t{0};
         ma |= (c < total && key >= blo && key <= bhi) ? (uint64_t{1} << u) : uint64_t{0};
@@ -1088,7 +1116,7 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
   const __amdgpu_buffer_rsrc_t rout = buffer_rsrc(uniform_ptr(out), k * 4);
   const __amdgpu_buffer_rsrc_t routs =
       buffer_rsrc(uniform_ptr(out_s ? reinterpret_cast<int32_t*>(out_s) : out), out_s ? k * 4 : 0);
-  auto place = [&](const uint2* ev, int n, int c0, uint64_t mh, uint64_t ma) __attribute__((always_inline)) {
+  auto place = [&](const uint2* ev, int n, const Round& rnd, uint64_t mh, uint64_t ma) __attribute__((always_inline)) {
     int wt = __popcll(mh) | (__popcll(ma) << 16);
 #pragma unroll
     for (int o = kWave / 2; o >= 1; o >>= 1) wt += __shfl_xor(wt, o, kWave);
@@ -1104,10 +1132,9 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
     // The wave's output and list positions (uniform).
     int ph = __builtin_amdgcn_readfirstlane(run_h + (base & 0xFFFF));
     int pa = __builtin_amdgcn_readfirstlane(run_a + (base >> 16));
-    const int nu = min(n, (total - c0 + NT - 1) / NT);  // slots holding entries (uniform)
 #pragma unroll
     for (int u = 0; u < n; ++u) {
-      if (u >= nu) continue;
+      if (!rnd.used(u)) continue;  // (uniform)
       const bool h = (mh >> u) & 1u;
       const bool at = (ma >> u) & 1u;
       const uint64_t bh = __ballot(h);
@@ -1133,19 +1160,20 @@ __global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
   };
   {
     uint64_t mh, ma;
-    classify(e, NR, 0, mh, ma);
-    place(e, NR, 0, mh, ma);
+    classify(e, NR, r0, mh, ma);
+    place(e, NR, r0, mh, ma);
   }
   for (int c0 = NR * NT; c0 < total; c0 += NO * NT) {  // beyond the registers
+    const Round rr = make_round(c0, NO);
     uint2 f[NO];
 #pragma unroll
     for (int u = 0; u < NO; ++u) {
-      const int c = c0 + u * NT + static_cast<int>(threadIdx.x);
+      const int c = rr.entry(u);
       f[u] = c < total ? entry(c) : make_uint2(0u, 0u);
     }
     uint64_t mh, ma;
-    classify(f, NO, c0, mh, ma);
-    place(f, NO, c0, mh, ma);
+    classify(f, NO, rr, mh, ma);
+    place(f, NO, rr, mh, ma);
   }
   __syncthreads();
   // 4. the (k - above) best of the b* list.
