@@ -1263,6 +1263,16 @@ hipError_t launch_decode_mq_score_topk(const Shape& s, int32_t nh, const int32_t
   return hipGetLastError();
 }
 
+// Keys per wave of decode_score_kernel: 512 while the grid keeps at least
+// 512 workgroups, else 256.  Each workgroup clears and flushes a histogram of
+// kDigits bins, so larger chunks take that fixed cost over more keys (C2
+// dense 70 -> 64 us, C4 62 -> 59 us); small batches keep more workgroups.
+int32_t decode_keys_per_wave(const Shape& s) {
+  constexpr int64_t kLarge = 512;
+  const int64_t wgs = static_cast<int64_t>(s.batch) * ((s.L + kDecWaves * kLarge - 1) / (kDecWaves * kLarge));
+  return wgs >= 512 ? static_cast<int32_t>(kLarge) : MISA_DECODE_KEYS_PER_WAVE;
+}
+
 hipError_t launch_decode_score_topk(const Shape& s, int32_t nh, const int32_t* heads, int32_t k,
                                     const void* q, const float* q_scale, const float* w,
                                     const void* kk, const float* k_scale, int32_t* idx,
@@ -1271,7 +1281,7 @@ hipError_t launch_decode_score_topk(const Shape& s, int32_t nh, const int32_t* h
   const int64_t nz = d.zero_words;
   clear_kernel<<<static_cast<unsigned>((nz + 1023) / 1024), 256, 0, st>>>(d.cnt, nz);
   DecodeArgs a{q, q_scale, w, kk, k_scale, heads, nh, nullptr, 0, 0, nullptr, nullptr, 0,
-               d.rows, d.ghist, s.L, s.H, MISA_DECODE_KEYS_PER_WAVE};
+               d.rows, d.ghist, s.L, s.H, decode_keys_per_wave(s)};
   if (s.dtype == kBF16) launch_score<kBF16, false>(s, a, st);
   else launch_score<kFP8, false>(s, a, st);
   launch_select(s, d, k, idx, scores_out, st);
@@ -1306,7 +1316,7 @@ hipError_t launch_decode_step(const Shape& s, int32_t h, int32_t k, const void* 
     step_route_kernel<kFP8><<<g1, 256, 0, st>>>(q, pooled, kk, k_scale, d.part, d.cnt, nz, s.L,
                                                 s.H, s.B, M, nmain);
   DecodeArgs a{q, q_scale, w, kk, k_scale, nullptr, h, d.part, nch, h, heads, E_out, M,
-               d.rows, d.ghist, s.L, s.H, MISA_DECODE_KEYS_PER_WAVE};
+               d.rows, d.ghist, s.L, s.H, decode_keys_per_wave(s)};
   if (s.dtype == kBF16) launch_score<kBF16, true>(s, a, st);
   else launch_score<kFP8, true>(s, a, st);
   launch_select(s, d, k, idx, scores_out, st);
