@@ -128,7 +128,10 @@ misa_status misa_score_topk(const misa_shape* shape, int32_t h, int32_t k, const
  * cand[b,t,:] (entries < 0 are padding and ignored), the full-head score
  *   I[b,t,s] = sum_{j < H} w[b,t,j] * ReLU(q[b,t,j,:] . k[b,s,:]),
  * then idx[b,t,:] = the k candidates of largest I.  Candidates must be
- * distinct token positions within query t's prefix.
+ * distinct token positions within query t's prefix.  Key rows are gathered
+ * in list order, so a list sorted by token position runs faster (prefill
+ * lists of misa_score_topk come out that way, apart from the few entries of
+ * the threshold bin at their end); the result does not depend on the order.
  *   cand       [batch, T, kprime]  int32 (e.g. idx of misa_score_topk with k')
  *   idx        [batch, T, k]       int32, written
  *   scores_out [batch, T, k]       fp32, written if non-NULL */
