@@ -847,7 +847,7 @@ struct PSelSmem {
 };
 
 template <int NT, int NR>
-__global__ __launch_bounds__(NT, 2048 / NT) void prefill_select_kernel(
+__global__ __launch_bounds__(NT, 4) void prefill_select_kernel(
     const uint2* __restrict__ cand, const int32_t* __restrict__ cnt, const float* __restrict__ tau,
     int32_t S, int32_t cap, int32_t seg, int32_t k, int32_t* __restrict__ idx,
     float* __restrict__ scores_out, int32_t* __restrict__ fail_count, int32_t* __restrict__ fail_list) {

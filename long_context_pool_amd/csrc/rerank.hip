@@ -510,7 +510,7 @@ __global__ __launch_bounds__(kLSThreads, kLSThreads == 256 ? 4 : 1) void list_se
   const int64_t pos = static_cast<int64_t>(L) - T + blockIdx.x;
   float* so = scores_out ? scores_out + r * k : nullptr;
   // 256 threads (32 entries each, four workgroups per CU): no room to keep
-  // the digits.
+  // the coarse keys.
   constexpr bool kCache = kLSThreads != 256;
   if constexpr (BLK)
     list_select_row<kLSThreads, kCache>(sc + r * kprime, BlockIds(cand + r * m, B, m), kprime, pos,
