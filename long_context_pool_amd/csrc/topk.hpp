@@ -295,22 +295,39 @@ __device__ __forceinline__ uint64_t rank_key(float s, int32_t id) {
   return (static_cast<uint64_t>(float_key(s)) << 32) | static_cast<uint32_t>(~id);
 }
 
+// The comparisons of each entry are split over P = NT / n threads (at most
+// 16): thread q n + e counts the entries of part q that beat entry e, and the
+// part counts meet in racc (LDS, at least n words).  A list of n <= NT / 4
+// then takes n / 4 rounds of compares instead of n on one thread.  All NT
+// threads call; racc is free again when it returns.
 template <int NT>
 __device__ __forceinline__ void rank_write(const float* cs, const int32_t* ci, int n, int need,
-                                           int32_t* out_idx, float* out_score) {
+                                           int32_t* out_idx, float* out_score, uint32_t* racc) {
+  if (n <= 0) return;  // (uniform)
+  const int P = min(max(NT / n, 1), 16);
+  const int per = ((n + P - 1) / P + 3) & ~3;  // entries per part, a multiple of 4
   const float4* cs4 = reinterpret_cast<const float4*>(cs);
   const int4* ci4 = reinterpret_cast<const int4*>(ci);
-  for (int t = threadIdx.x; t < n; t += NT) {
-    const uint64_t me = rank_key(cs[t], ci[t]);
+  for (int t = threadIdx.x; t < n; t += NT) racc[t] = 0;
+  __syncthreads();
+  for (int t = threadIdx.x; t < n * P; t += NT) {
+    const int e = t % n, q = t / n;
+    const uint64_t me = rank_key(cs[e], ci[e]);
+    const int j0 = q * per, j1 = min(n, j0 + per);
     int rank = 0;
-    for (int j0 = 0; j0 < n; j0 += 4) {
-      const float4 c = cs4[j0 / 4];
-      const int4 d = ci4[j0 / 4];
-      rank += (j0 + 0 < n && rank_key(c.x, d.x) > me) ? 1 : 0;
-      rank += (j0 + 1 < n && rank_key(c.y, d.y) > me) ? 1 : 0;
-      rank += (j0 + 2 < n && rank_key(c.z, d.z) > me) ? 1 : 0;
-      rank += (j0 + 3 < n && rank_key(c.w, d.w) > me) ? 1 : 0;
+    for (int j = j0; j < j1; j += 4) {
+      const float4 c = cs4[j / 4];
+      const int4 d = ci4[j / 4];
+      rank += (j + 0 < j1 && rank_key(c.x, d.x) > me) ? 1 : 0;
+      rank += (j + 1 < j1 && rank_key(c.y, d.y) > me) ? 1 : 0;
+      rank += (j + 2 < j1 && rank_key(c.z, d.z) > me) ? 1 : 0;
+      rank += (j + 3 < j1 && rank_key(c.w, d.w) > me) ? 1 : 0;
     }
+    if (rank) atomicAdd(&racc[e], static_cast<uint32_t>(rank));
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < n; t += NT) {
+    const int rank = static_cast<int>(racc[t]);
     if (rank < need) {
       out_idx[rank] = ci[t] < 0 ? -1 : ci[t];  // negative ids: distinct padding, printed as -1
       if (out_score) out_score[rank] = cs[t];
@@ -324,8 +341,7 @@ __device__ __forceinline__ bool resolve_list(const float* cs, const int32_t* ci,
   // Every slot gets one rank when the tokens are distinct; -1 guards the rest.
   for (int p = threadIdx.x; p < need; p += NT) out_idx[p] = -1;
   if (n <= kDirectRank) {
-    __syncthreads();
-    rank_write<NT>(cs, ci, n, need, out_idx, out_score);
+    rank_write<NT>(cs, ci, n, need, out_idx, out_score, rs.hist);  // (its first barrier)
     return true;
   }
   if (threadIdx.x == 0) {
@@ -417,7 +433,7 @@ __device__ __forceinline__ bool resolve_list(const float* cs, const int32_t* ci,
   }
   __syncthreads();
   rank_write<NT>(rs.s2, rs.i2, cnt2, need - above, out_idx + above,
-                 out_score ? out_score + above : nullptr);
+                 out_score ? out_score + above : nullptr, rs.hist);
   return true;
 }
 
